@@ -1,0 +1,173 @@
+"""CPU oracle for the selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's CPU-baseline leg may
+import this package.  The library path never does.
+
+* ``scan`` / ``step`` call the plain fp64 C loop in ``ss_oracle.c``
+  (Mamba walk-through section 3.3 ``selective_scan`` plus the block's D skip and
+  silu(z) gate, section 3.4).
+* ``twin_scan`` (in ``twin.py``) is an independent NumPy statement of the same
+  definition, used only to cross-check the C loop on tiny shapes.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(closed forms, the LTI convolution identity, brute force, invariants and a
+hand-worked fixture); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ss_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ss_oracle.c into liboracle.so next to it (gcc, -O2, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
+               "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class OracleLib:
+    """ctypes view of one compiled oracle library (the default one, or a test build)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, i64, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, i64,
+                                    vp, i64, vp, vp, vp, i64, vp, ip]
+        lib.oracle_scan.restype = ctypes.c_int
+        lib.oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, vp]
+        lib.oracle_step.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def scan(self, *args, **kwargs):
+        return scan(*args, _lib=self.lib, **kwargs)
+
+    def step(self, *args, **kwargs):
+        return step(*args, _lib=self.lib, **kwargs)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = OracleLib(_LIB).lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_of(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("operand dtype must be float32 or uint16 (bf16 bits), got %s" % a.dtype)
+
+
+def _c(a: Optional[np.ndarray], dt=None) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    return np.ascontiguousarray(a if dt is None else a.astype(dt, copy=False))
+
+
+def scan(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
+         D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
+         h0: Optional[np.ndarray] = None, lanes: Optional[Sequence[int]] = None,
+         record_t: Optional[Sequence[int]] = None, threads: int = 1, _lib=None) -> Dict[str, np.ndarray]:
+    """fp64 scan.  u, delta, z: (B,L,D); B, C: (B,L,N) in float32 or bf16 bits (uint16);
+    A (D,N) and D (D,) float32; h0 (B,D,N) any float (widened to double).
+
+    Returns ``y`` (B,L,D) -- or (n_lanes, L) when ``lanes`` (flat b*D+d) is given --
+    ``h_last`` (B,D,N) / (n_lanes, N), and ``h_rec`` (n_lanes, len(record_t), N) with the
+    state right after each timestep in ``record_t``.
+    """
+    lib = _lib or _load()
+    dt = _dtype_of(u)
+    batch, seqlen, dim = u.shape
+    dstate = A.shape[1]
+    for name, arr, shp in (("delta", delta, u.shape), ("B", B, (batch, seqlen, dstate)),
+                           ("C", C, (batch, seqlen, dstate))):
+        if tuple(arr.shape) != tuple(shp) or _dtype_of(arr) != dt:
+            raise ValueError("%s has shape %s dtype %s" % (name, arr.shape, arr.dtype))
+    if z is not None and (tuple(z.shape) != tuple(u.shape) or _dtype_of(z) != dt):
+        raise ValueError("z mismatch")
+    u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
+    A = _c(A, np.float32)
+    D = _c(D, np.float32)
+    h0 = _c(h0, np.float64)
+    lane_arr = None if lanes is None else np.ascontiguousarray(np.asarray(lanes, dtype=np.int64))
+    n_lanes = batch * dim if lane_arr is None else lane_arr.size
+    rec = None if record_t is None else np.ascontiguousarray(np.asarray(record_t, dtype=np.int64))
+    n_rec = 0 if rec is None else rec.size
+    y = np.empty((n_lanes, seqlen), dtype=np.float64)
+    h_last = np.empty((n_lanes, dstate), dtype=np.float64)
+    h_rec = np.empty((n_lanes, max(n_rec, 1), dstate), dtype=np.float64)
+    rc = lib.oracle_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                         dt, batch, seqlen, dim, dstate, _ptr(lane_arr), n_lanes,
+                         _ptr(y), _ptr(h_last), _ptr(rec), n_rec,
+                         _ptr(h_rec) if rec is not None else None, int(threads))
+    if rc != 0:
+        raise ValueError("oracle_scan rejected its arguments")
+    out = {"h_rec": h_rec[:, :n_rec]}
+    if lane_arr is None:
+        out["y"] = y.reshape(batch, dim, seqlen).transpose(0, 2, 1).copy()
+        out["h_last"] = h_last.reshape(batch, dim, dstate)
+    else:
+        out["y"] = y
+        out["h_last"] = h_last
+    return out
+
+
+def step(h: np.ndarray, u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray,
+         C: np.ndarray, D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
+         lanes: Optional[Sequence[int]] = None, _lib=None) -> np.ndarray:
+    """One recurrent token.  h: float64 (B,D,N), or (n_lanes, N) with ``lanes``; updated
+    in place.  u, delta, z: (B,D); B, C: (B,N).  Returns y float64 (B,D) / (n_lanes,)."""
+    lib = _lib or _load()
+    if h.dtype != np.float64 or not h.flags.c_contiguous:
+        raise TypeError("h must be a C-contiguous float64 array (updated in place)")
+    dt = _dtype_of(u)
+    batch, dim = u.shape
+    dstate = A.shape[1]
+    u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
+    A = _c(A, np.float32)
+    D = _c(D, np.float32)
+    lane_arr = None if lanes is None else np.ascontiguousarray(np.asarray(lanes, dtype=np.int64))
+    n_lanes = batch * dim if lane_arr is None else lane_arr.size
+    if h.size != n_lanes * dstate:
+        raise ValueError("h has %d values, expected %d" % (h.size, n_lanes * dstate))
+    y = np.empty(n_lanes, dtype=np.float64)
+    rc = lib.oracle_step(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                         dt, batch, dim, dstate, _ptr(lane_arr), n_lanes, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_step rejected its arguments")
+    return y.reshape(batch, dim) if lane_arr is None else y
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """Exact float64 view of a float32 or bf16-bits operand."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+from .twin import twin_scan  # noqa: E402  (NumPy statement of the same definition)

@@ -1,0 +1,351 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes an oracle object exposing ``scan(...)`` and ``step(...)``
+(the ``oracle`` package itself, or a deliberately broken build of it) and
+raises ``AssertionError`` when the oracle disagrees.  None of them re-types the
+oracle's loop: each compares with a different statement of the result.
+
+Sources on the pages:
+* Mamba walk-through (youngju.dev), section 2.2: Abar = exp(delta A), discrete
+  recurrence h_t = Abar h_{t-1} + Bbar x_t, y_t = C h_t.
+* same page, section 3.3: selective_scan shapes and the Euler input term
+  delta*B*x; y read from the updated state.
+* same page, section 3.4: D skip, y * silu(z) gate, A = -(n+1).
+* LTI chapter (booiljung.github.io, 3.1), section 0.2.2: with fixed
+  parameters y = x * Kbar, Kbar = (C Bbar, C Abar Bbar, ..., C Abar^{L-1} Bbar).
+* LTI chapter, section 0.4.2: delta -> 0 keeps the state (Abar -> I), large
+  delta with negative A resets it (Abar -> 0).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.signal
+
+from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _rand_case(rng, batch, seqlen, dim, dstate, *, dtype="f32", has_D=False, has_z=False,
+               has_h0=False, delta_scale=0.5):
+    """Small random inputs (float32, or bf16 bits) for the pins."""
+    def cast(x):
+        x = np.asarray(x, dtype=np.float32)
+        return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    u = cast(rng.standard_normal((batch, seqlen, dim)))
+    delta = cast(np.log1p(np.exp(rng.normal(-1.0, 0.7, (batch, seqlen, dim)))) * delta_scale * 2)
+    A = (-(np.arange(1, dstate + 1))[None, :] * np.exp(rng.uniform(-0.5, 0.5, (dim, dstate)))).astype(np.float32)
+    B = cast(rng.standard_normal((batch, seqlen, dstate)))
+    C = cast(rng.standard_normal((batch, seqlen, dstate)))
+    D = rng.standard_normal(dim).astype(np.float32) if has_D else None
+    z = cast(rng.standard_normal((batch, seqlen, dim))) if has_z else None
+    h0 = rng.standard_normal((batch, dim, dstate)).astype(np.float32) if has_h0 else None
+    return dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h0)
+
+
+def _close(got, want, rtol, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, "%s: shape %s vs %s" % (what, got.shape, want.shape)
+    scale = max(float(np.max(np.abs(want))) if want.size else 0.0, 1e-300)
+    err = float(np.max(np.abs(got - want))) / scale if want.size else 0.0
+    assert err <= rtol, "%s: scaled error %.3e > %.1e" % (what, err, rtol)
+
+
+# ---------------------------------------------------------------------------
+# 1. hand-worked three-step example (tests/golden/hand_worked_3step.json)
+# ---------------------------------------------------------------------------
+def _eval(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"exp": math.exp}))
+
+
+def pin_hand_worked(orc):
+    with open(os.path.join(GOLDEN, "hand_worked_3step.json")) as f:
+        g = json.load(f)
+    L = g["shape"]["seqlen"]
+    u = np.array(g["u"], dtype=np.float32).reshape(1, L, 1)
+    delta = np.array(g["delta"], dtype=np.float32).reshape(1, L, 1)
+    A = np.array(g["A"], dtype=np.float32)
+    B = np.array(g["B"], dtype=np.float32).reshape(1, L, 2)
+    C = np.array(g["C"], dtype=np.float32).reshape(1, L, 2)
+    D = np.array(g["D"], dtype=np.float32)
+    z = np.array(g["z"], dtype=np.float32).reshape(1, L, 1)
+
+    plain = orc.scan(u, delta, A, B, C)
+    _close(plain["y"].reshape(-1), [_eval(e) for e in g["expected_y_plain"]], 1e-14, "hand y")
+    _close(plain["h_last"].reshape(-1), [_eval(e) for e in g["expected_h_last"]], 1e-14, "hand h_last")
+    withd = orc.scan(u, delta, A, B, C, D=D)
+    _close(withd["y"].reshape(-1), [_eval(e) for e in g["expected_y_with_D"]], 1e-14, "hand y+D")
+    gated = orc.scan(u, delta, A, B, C, D=D, z=z)
+    want = [_eval(a) * _eval(s) for a, s in zip(g["expected_y_with_D"], g["expected_silu_z"])]
+    _close(gated["y"].reshape(-1), want, 1e-14, "hand gated y")
+
+
+# ---------------------------------------------------------------------------
+# 2. L = 1 closed form: h_0 = exp(delta A) h0 + delta u B, y_0 = C.h_0 (+D u)(*silu z)
+# ---------------------------------------------------------------------------
+def pin_single_step_closed_form(orc):
+    rng = np.random.default_rng(11)
+    for dtype in ("f32", "bf16"):
+        for has_h0 in (False, True):
+            c = _rand_case(rng, 2, 1, 5, 16, dtype=dtype, has_D=True, has_z=True, has_h0=has_h0)
+            out = orc.scan(**c)
+            dl = _f64(c["delta"])[:, 0, :]          # (B, D)
+            x = _f64(c["u"])[:, 0, :]
+            A = c["A"].astype(np.float64)
+            Bm = _f64(c["B"])[:, 0, :]              # (B, N)
+            Cm = _f64(c["C"])[:, 0, :]
+            h = (dl * x)[:, :, None] * Bm[:, None, :]
+            if has_h0:
+                h = h + np.exp(dl[:, :, None] * A[None]) * c["h0"].astype(np.float64)
+            y = np.einsum("bdn,bn->bd", h, Cm) + c["D"].astype(np.float64)[None] * x
+            y = y * _silu(_f64(c["z"])[:, 0, :])
+            _close(out["y"][:, 0, :], y, 1e-13, "L=1 y (%s, h0=%s)" % (dtype, has_h0))
+            _close(out["h_last"], h, 1e-13, "L=1 h (%s, h0=%s)" % (dtype, has_h0))
+
+
+# ---------------------------------------------------------------------------
+# 3. LTI identity: fixed delta, B, C over time => y = causal conv(u, Kbar)
+# ---------------------------------------------------------------------------
+def pin_lti_convolution(orc):
+    rng = np.random.default_rng(12)
+    for (dim, dstate, L) in ((3, 4, 64), (5, 16, 96)):
+        deltas = np.array([0.05, 0.3, 1.1, 0.7, 0.2][:dim], dtype=np.float32)
+        A = (-(np.arange(1, dstate + 1))[None, :] * np.exp(rng.uniform(-0.5, 0.5, (dim, dstate)))).astype(np.float32)
+        bvec = rng.standard_normal(dstate).astype(np.float32)
+        cvec = rng.standard_normal(dstate).astype(np.float32)
+        u = rng.standard_normal((1, L, dim)).astype(np.float32)
+        delta = np.broadcast_to(deltas[None, None, :], (1, L, dim)).copy()
+        B = np.broadcast_to(bvec[None, None, :], (1, L, dstate)).copy()
+        C = np.broadcast_to(cvec[None, None, :], (1, L, dstate)).copy()
+        y = orc.scan(u, delta, A, B, C)["y"][0]    # (L, D)
+
+        k = np.arange(L, dtype=np.float64)
+        for d in range(dim):
+            dd = float(deltas[d])
+            abar = np.exp(dd * A[d].astype(np.float64))                    # (N,)
+            kernel = (cvec.astype(np.float64)[None, :] * abar[None, :] ** k[:, None]
+                      * (dd * bvec.astype(np.float64))[None, :]).sum(axis=1)  # Kbar_k
+            conv = np.convolve(u[0, :, d].astype(np.float64), kernel)[:L]
+            _close(y[:, d], conv, 1e-12, "LTI convolve d=%d" % d)
+            filt = np.zeros(L)
+            for n in range(dstate):
+                filt += cvec[n] * scipy.signal.lfilter([dd * float(bvec[n])], [1.0, -abar[n]],
+                                                       u[0, :, d].astype(np.float64))
+            _close(y[:, d], filt, 1e-12, "LTI lfilter d=%d" % d)
+
+
+# ---------------------------------------------------------------------------
+# 4. zero input: h stays exactly 0; with h0 the state only decays
+# ---------------------------------------------------------------------------
+def pin_zero_input(orc):
+    rng = np.random.default_rng(13)
+    for dtype in ("f32", "bf16"):
+        c = _rand_case(rng, 2, 33, 4, 16, dtype=dtype, has_D=True, has_z=True)
+        c["u"] = np.zeros_like(c["u"])
+        out = orc.scan(**c)
+        assert np.all(out["y"] == 0.0), "u=0, h0=0 must give y == 0 exactly"
+        assert np.all(out["h_last"] == 0.0), "u=0, h0=0 must leave h == 0 exactly"
+        c["h0"] = rng.standard_normal((2, 4, 16)).astype(np.float32)
+        c["z"] = None
+        c["D"] = None
+        out = orc.scan(**c)
+        total = _f64(c["delta"]).sum(axis=1)                                 # (B, D)
+        want = np.exp(total[:, :, None] * c["A"].astype(np.float64)[None]) * c["h0"]
+        _close(out["h_last"], want, 1e-12, "u=0 decay of h0 (%s)" % dtype)
+
+
+# ---------------------------------------------------------------------------
+# 5. brute force: h_t = sum_s exp(A sum_{r=s+1..t} delta_r) delta_s B_s u_s (+ decayed h0)
+# ---------------------------------------------------------------------------
+def brute_force(c):
+    x = _f64(c["u"])
+    dl = _f64(c["delta"])
+    A = c["A"].astype(np.float64)
+    Bm = _f64(c["B"])
+    Cm = _f64(c["C"])
+    nb, L, nd = x.shape
+    nn = A.shape[1]
+    cum = np.concatenate([np.zeros((nb, 1, nd)), np.cumsum(dl, axis=1)], axis=1)  # cum[:, t+1] = sum_{r<=t}
+    y = np.zeros((nb, L, nd))
+    h_last = None
+    for t in range(L):
+        h = np.zeros((nb, nd, nn))
+        for s in range(t + 1):
+            gap = cum[:, t + 1, :] - cum[:, s + 1, :]                           # sum_{r=s+1..t}
+            h += np.exp(gap[:, :, None] * A[None]) * (dl[:, s, :] * x[:, s, :])[:, :, None] * Bm[:, s, None, :]
+        if c.get("h0") is not None:
+            h += np.exp(cum[:, t + 1, :][:, :, None] * A[None]) * c["h0"].astype(np.float64)
+        y[:, t, :] = np.einsum("bdn,bn->bd", h, Cm[:, t, :])
+        h_last = h
+    if c.get("D") is not None:
+        y += c["D"].astype(np.float64)[None, None, :] * x
+    if c.get("z") is not None:
+        y *= _silu(_f64(c["z"]))
+    return y, h_last
+
+
+def pin_brute_force(orc):
+    rng = np.random.default_rng(14)
+    shapes = [(1, 1, 1, 1), (2, 7, 3, 2), (1, 24, 2, 16), (3, 13, 1, 4), (2, 19, 3, 5)]
+    for i, (nb, L, nd, nn) in enumerate(shapes):
+        c = _rand_case(rng, nb, L, nd, nn, dtype="bf16" if i % 2 else "f32",
+                       has_D=i % 2 == 0, has_z=i % 3 == 0, has_h0=i % 2 == 1)
+        out = orc.scan(**c)
+        y, h = brute_force(c)
+        _close(out["y"], y, 1e-11, "brute force y %s" % ((nb, L, nd, nn),))
+        _close(out["h_last"], h, 1e-11, "brute force h %s" % ((nb, L, nd, nn),))
+
+
+# ---------------------------------------------------------------------------
+# 6. geometric series: one active state, u = 1, constant delta, B = C = 1
+# ---------------------------------------------------------------------------
+def pin_geometric(orc):
+    L, N = 50, 16
+    d0 = 0.25
+    A = -(np.arange(1, N + 1, dtype=np.float32))[None, :] * np.float32(1.5)
+    u = np.ones((1, L, 1), dtype=np.float32)
+    delta = np.full((1, L, 1), d0, dtype=np.float32)
+    B = np.zeros((1, L, N), dtype=np.float32)
+    C = np.zeros((1, L, N), dtype=np.float32)
+    B[..., 0] = 1.0
+    C[..., 0] = 1.0
+    y = orc.scan(u, delta, A, B, C)["y"][0, :, 0]
+    a = math.exp(d0 * float(A[0, 0]))
+    t = np.arange(L)
+    _close(y, d0 * (1.0 - a ** (t + 1)) / (1.0 - a), 1e-13, "geometric")
+
+
+# ---------------------------------------------------------------------------
+# 7. delta limits (LTI chapter, section 0.4.2)
+# ---------------------------------------------------------------------------
+def pin_delta_limits(orc):
+    rng = np.random.default_rng(15)
+    c = _rand_case(rng, 2, 9, 3, 16, has_D=True, has_h0=True)
+    c["delta"] = np.zeros_like(c["delta"])
+    out = orc.scan(**c)
+    assert np.array_equal(out["h_last"], c["h0"].astype(np.float64)), "delta=0 must keep h bit-unchanged"
+    want = np.einsum("bdn,btn->btd", c["h0"].astype(np.float64), _f64(c["C"])) \
+        + c["D"].astype(np.float64)[None, None] * _f64(c["u"])
+    _close(out["y"], want, 1e-14, "delta=0 output")
+
+    c = _rand_case(rng, 1, 12, 2, 16, has_h0=True)
+    c["A"] = np.broadcast_to(-(np.arange(1, 17, dtype=np.float32))[None], (2, 16)).copy()
+    c["delta"] = np.full_like(c["delta"], 50.0)
+    out = orc.scan(**c, record_t=[0, 5, 11])
+    for k, t in enumerate([0, 5, 11]):
+        want = 50.0 * _f64(c["u"])[0, t, :, None] * _f64(c["B"])[0, t, None, :]
+        _close(out["h_rec"][:, k, :], want, 1e-15, "large delta resets the state, t=%d" % t)
+
+
+# ---------------------------------------------------------------------------
+# 8. chaining: split sequences and L single steps give the same result
+# ---------------------------------------------------------------------------
+def pin_chaining(orc):
+    rng = np.random.default_rng(16)
+    c = _rand_case(rng, 2, 40, 3, 16, dtype="bf16", has_D=True, has_z=True, has_h0=True)
+    full = orc.scan(**c)
+    L1 = 17
+    first = orc.scan(**{k: (v[:, :L1] if k in ("u", "delta", "B", "C", "z") and v is not None else v)
+                        for k, v in c.items()})
+    rest = dict(c)
+    for k in ("u", "delta", "B", "C", "z"):
+        rest[k] = np.ascontiguousarray(c[k][:, L1:])
+    rest["h0"] = first["h_last"]
+    second = orc.scan(**rest)
+    assert np.array_equal(np.concatenate([first["y"], second["y"]], axis=1), full["y"]), "split scan y"
+    assert np.array_equal(second["h_last"], full["h_last"]), "split scan h_last"
+
+    h = c["h0"].astype(np.float64).copy()
+    for t in range(40):
+        yt = orc.step(h, c["u"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
+                      D=c["D"], z=c["z"][:, t])
+        assert np.array_equal(yt, full["y"][:, t]), "step y at t=%d" % t
+    assert np.array_equal(h, full["h_last"]), "stepped state vs scan h_last"
+
+
+# ---------------------------------------------------------------------------
+# 9. causality and linearity
+# ---------------------------------------------------------------------------
+def pin_causality_linearity(orc):
+    rng = np.random.default_rng(17)
+    c = _rand_case(rng, 1, 30, 4, 16, has_D=True)
+    base = orc.scan(**c)["y"]
+    c2 = dict(c)
+    c2["u"] = c["u"].copy()
+    c2["u"][:, 10, :] += np.float32(1.0)
+    pert = orc.scan(**c2)["y"]
+    assert np.array_equal(pert[:, :10], base[:, :10]), "outputs before the perturbation must not change"
+    assert np.all(pert[:, 10] != base[:, 10]), "the perturbed timestep must change"
+
+    c3 = dict(c)
+    c3["u"] = c["u"] * np.float32(2.0)
+    assert np.array_equal(orc.scan(**c3)["y"], 2.0 * base), "y is linear in u (power-of-two scale)"
+    even = c["u"].copy()
+    even[:, 1::2] = 0
+    odd = c["u"] - even
+    ye = orc.scan(**dict(c, u=even))["y"]
+    yo = orc.scan(**dict(c, u=odd))["y"]
+    _close(ye + yo, base, 1e-13, "superposition")
+
+
+# ---------------------------------------------------------------------------
+# 10. bookkeeping: recorded states, lane subsets, threads, bf16 widening
+# ---------------------------------------------------------------------------
+def pin_bookkeeping(orc):
+    rng = np.random.default_rng(18)
+    c = _rand_case(rng, 2, 37, 5, 16, dtype="bf16", has_D=True, has_z=True, has_h0=True)
+    full = orc.scan(**c, record_t=[0, 8, 36])
+    for k, t in enumerate([0, 8, 36]):
+        trunc = {kk: (v[:, :t + 1] if kk in ("u", "delta", "B", "C", "z") else v) for kk, v in c.items()}
+        ht = orc.scan(**trunc)["h_last"].reshape(10, 16)
+        assert np.array_equal(full["h_rec"][:, k], ht), "recorded state at t=%d" % t
+    lanes = [7, 0, 9, 3]
+    sub = orc.scan(**c, lanes=lanes)
+    yfull = full["y"].transpose(0, 2, 1).reshape(10, 37)
+    assert np.array_equal(sub["y"], yfull[lanes]), "lane subset y"
+    assert np.array_equal(sub["h_last"], full["h_last"].reshape(10, 16)[lanes]), "lane subset h"
+    thr = orc.scan(**c, threads=4)
+    assert np.array_equal(thr["y"], full["y"]), "threaded run must be bit-identical"
+    cf = dict(c)
+    for k in ("u", "delta", "B", "C", "z"):
+        cf[k] = bf16_bits_to_f32(c[k])
+    assert np.array_equal(orc.scan(**cf)["y"], full["y"]), "bf16 bits widen exactly"
+
+
+# ---------------------------------------------------------------------------
+# 11. NumPy twin (materialised operands, vectorised over lanes)
+# ---------------------------------------------------------------------------
+def pin_twin(orc):
+    from oracle.twin import twin_scan
+
+    rng = np.random.default_rng(19)
+    for i, shp in enumerate([(1, 16, 4, 16), (2, 33, 3, 8), (3, 5, 7, 1)]):
+        c = _rand_case(rng, *shp, dtype="bf16" if i == 1 else "f32", has_D=i != 2, has_z=i != 0,
+                       has_h0=i == 1)
+        out = orc.scan(**c)
+        y, h = twin_scan(**c)
+        _close(out["y"], y, 1e-13, "twin y %s" % (shp,))
+        _close(out["h_last"], h, 1e-13, "twin h %s" % (shp,))
+
+
+ALL_PINS = [pin_hand_worked, pin_single_step_closed_form, pin_lti_convolution, pin_zero_input,
+            pin_brute_force, pin_geometric, pin_delta_limits, pin_chaining,
+            pin_causality_linearity, pin_bookkeeping, pin_twin]
