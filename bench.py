@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one ss_scan_fwd call over the large-layer workload (B=8, L=2048,
+D=5120, N=16; bf16 u/delta/B/C/z and y, fp32 A/D and state, D skip and silu(z)
+gate), inputs already resident in device memory.  Prints ONE JSON line:
+elements/s (B*L*D*N per second), the roofline of the scan kernel (algorithmic
+HBM bytes per launch over its event-timed duration, against 8 TB/s), and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Extra objects: ``decode_step`` (ss_step on the B=256, D=5120 recurrent-step
+workload), ``parity`` (timed output vs the oracle on sampled channels) and
+``flushed`` (the same scan timed with the 256 MB last-level cache flushed
+before every step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "selective-scan elements/s (B·L·D·N) + achieved HBM GB/s vs peak, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_large_layer.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-extras", action="store_true", help="skip decode step, flushed timing and parity")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_85_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel sources; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the scan would shard over batch and channels with no exchange). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    import selective_state_space_85_amd as ss
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    w = wl.WORKLOADS["large"]
+
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    log("generating %s inputs (B=%d L=%d D=%d N=%d, %s)" % (w.name, w.batch, w.seqlen, w.dim, w.dstate, w.dtype))
+    inp = wl.workload_inputs(w, seed=0)
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(a).to(device)
+
+    t = {k: to_dev(v) for k, v in inp.items()}
+    T, K = ss.scan_plan(w.batch, w.seqlen, w.dim, w.dstate)
+    ws_bytes = ss.scan_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+    y = torch.empty_like(t["u"])
+    stream = torch.cuda.current_stream(device)
+
+    def step():
+        ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=y, workspace=ws)
+
+    log("plan: chunk_len=%d n_chunks=%d, workspace %d bytes; warmup %d" % (T, K, ws_bytes, args.warmup))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, events on the launch stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    log("timed %d steps: %.3f ms/step (events), wall %.3f s" % (args.steps, ms_step, wall))
+
+    elements = w.elements
+    alg_bytes = wl.algorithmic_bytes_scan(w.batch, w.seqlen, w.dim, w.dstate, w.dtype, w.has_D, w.has_z)
+    achieved_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    value = elements / (ms_step * 1e-3)
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(src_hash)
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; u,B,C,z~N(0,1), delta=softplus(N(-2,1)), A=-(n+1)exp(U(-.5,.5)), D~N(0,1))",
+        "config": {"workload": "large-model layer B=8 L=2048 D=5120 N=16, bf16 I/O, fp32 state, D skip + silu(z) gate",
+                   "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+                   "chunk_len": T, "n_chunks": K},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "kernel": "ss_scan_fwd (scan_chunk_kernel%s)" % (" + carry" if K > 1 else ""),
+                     "kernel_source_hash": src_hash},
+    }
+
+    if args.copy_reference:
+        n = 256 << 20  # 1 GiB of fp32 read, 1 GiB written
+        a = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        result["copy_reference"] = {"bytes_read": n * 4, "bytes_written": n * 4, "ms": ms,
+                                    "GB/s": 2 * n * 4 / (ms * 1e-3) / 1e9}
+        del a, b
+
+    if not args.no_extras:
+        # the same scan with the last-level cache flushed before each step
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)  # 1 GiB
+        times = []
+        for _ in range(10):
+            scratch.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        fl = float(np.median(times))
+        result["flushed"] = {"ms_per_step_median": fl, "elements/s": elements / (fl * 1e-3),
+                             "alg_GB/s": alg_bytes / (fl * 1e-3) / 1e9}
+
+        # parity of the timed output on sampled channels
+        import oracle
+        rng = np.random.default_rng(1)
+        lanes = np.unique(np.concatenate([[0, w.dim - 1, w.batch * w.dim - 1],
+                                          rng.integers(0, w.batch * w.dim, 61)])).astype(np.int64)
+        ref = oracle.scan(**inp, lanes=lanes, threads=min(16, os.cpu_count() or 1))["y"]
+        yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        yg = (yb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        yl = yg[lanes // w.dim, :, lanes % w.dim]
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        err = float(np.max(np.abs(yl - ref) / np.maximum(np.abs(ref), rms)))
+        result["parity"] = {"max_rel_err": err, "tol": 2e-2, "lanes": int(lanes.size)}
+
+        # recurrent step workload: one token for B=256, D=5120, state in place
+        sw = wl.WORKLOADS["step"]
+        sp = wl.step_params(sw)
+        si = wl.step_inputs(sw, 0)
+        st = {k: to_dev(v) for k, v in si.items()}
+        A5, D5, h5 = to_dev(sp["A"]), to_dev(sp["D"]), to_dev(sp["h0"])
+        y5 = torch.empty_like(st["u"])
+
+        def dstep():
+            ss.step(h5, st["u"], st["delta"], A5, st["B"], st["C"], D=D5, z=st["z"], out=y5)
+
+        for _ in range(5):
+            dstep()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(100):
+            dstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 100
+        sb = wl.algorithmic_bytes_step(sw.batch, sw.dim, sw.dstate, sw.dtype, sw.has_D, sw.has_z)
+        result["decode_step"] = {"workload": "recurrent step B=256 D=5120 N=16, bf16, state (84 MB) in place",
+                                 "us_per_token": us, "elements/s": sw.elements / (us * 1e-6),
+                                 "alg_GB/s": sb / (us * 1e-6) / 1e9, "note": "chained, state warm in cache"}
+
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(16, os.cpu_count() or 1)
+        rows = 4  # batch rows 0..3: half the workload
+        lanes = np.arange(rows * w.dim, dtype=np.int64)
+        log("timing the CPU oracle on %d channels x %d steps, %d threads" % (lanes.size, w.seqlen, threads))
+        c0 = time.perf_counter()
+        oracle.scan(**inp, lanes=lanes, threads=threads)
+        cdt = time.perf_counter() - c0
+        n_el = lanes.size * w.seqlen * w.dstate
+        result["cpu_baseline"] = {"value": n_el / cdt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+                                  "sample": "batch rows 0-%d of the large-layer workload (%d channels x %d steps x %d "
+                                            "states = %d elements), fp64, %.2f s" % (rows - 1, lanes.size, w.seqlen,
+                                                                                     w.dstate, n_el, cdt)}
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

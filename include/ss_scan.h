@@ -1,0 +1,149 @@
+/*
+ * ss_scan.h -- C ABI of the MI355X (gfx950) selective-scan library (libssscan.so).
+ *
+ * The operation (Mamba walk-through, section 3.3 "selective_scan" and the
+ * discrete recurrence of section 2.2; D skip and silu(z) gate of the Mamba
+ * block, section 3.4; LTI chapter 3.1, section 0.4.2 for the shapes):
+ *
+ *   for every lane (b, d) and state index n, from h = h0 (zeros if absent):
+ *     h_t[n] = exp(delta[b,t,d] * A[d,n]) * h_{t-1}[n] + delta[b,t,d] * B[b,t,n] * u[b,t,d]
+ *     y[b,t,d] = sum_n C[b,t,n] * h_t[n]                       (state after the update)
+ *              + Dskip[d] * u[b,t,d]                           (if Dskip != NULL)
+ *     y[b,t,d] *= z[b,t,d] / (1 + exp(-z[b,t,d]))              (if z != NULL: silu gate)
+ *
+ * delta is taken as given (already positive); no softplus is applied.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer, caller-owned, contiguous and
+ *    row-major in the shape stated next to it.  The library allocates no
+ *    memory and keeps no state besides a thread-local "last HIP error".
+ *  - `dtype` (ss_dtype) is the element type of u, delta, B, C, z and y.
+ *    bf16 is the 16-bit brain-float pattern; y is rounded once from fp32 with
+ *    round-to-nearest-even.  A, Dskip and every state (h0, h_last, h) are fp32.
+ *    All arithmetic is fp32.
+ *  - Alignment: A, h0, h_last, h and the workspace must be 16-byte aligned;
+ *    every other tensor must be aligned to its element size.
+ *  - Calls are asynchronous on `stream` (NULL = the default stream): SS_OK
+ *    means every kernel was enqueued.  Arguments are validated on the host,
+ *    synchronously, before anything is enqueued; a rejected call enqueues
+ *    nothing.  NaN/Inf inputs are not checked and propagate.
+ *  - Errors: SS_ERR_INVALID_ARG (NULL required pointer, size <= 0, size
+ *    overflow, misalignment, forbidden overlap), SS_ERR_UNSUPPORTED (dstate
+ *    other than 16, unknown dtype), SS_ERR_WORKSPACE (workspace too small or
+ *    NULL when one is needed), SS_ERR_HIP (a HIP call or launch failed; see
+ *    ss_last_hip_error()).  No exceptions cross the ABI.
+ */
+#ifndef SS_SCAN_H
+#define SS_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SS_OK = 0,
+    SS_ERR_INVALID_ARG = 1,
+    SS_ERR_UNSUPPORTED = 2,
+    SS_ERR_WORKSPACE = 3,
+    SS_ERR_HIP = 4
+} ss_status;
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/*
+ * ss_scan_plan -- how ss_scan_fwd splits the sequence axis.
+ *
+ * The scan is cut into n_chunks = ceil(seqlen / chunk_len) chunks; chunk c
+ * covers timesteps [c*chunk_len, min((c+1)*chunk_len, seqlen)).  Chunks are
+ * joined by an exact associative combine of affine pairs (LTI chapter 3.1,
+ * section 3.1.5.2, parallel scan over an associative operator):
+ * (a1, b1) then (a2, b2) gives (a2*a1, a2*b1 + b2).
+ *
+ * chunk_len_request: 0 lets the library choose (a power of two, from the
+ * shape only: pure, host-only, deterministic); a positive value forces that
+ * chunk length.  Writes *chunk_len and *n_chunks (either may be NULL).
+ * Returns SS_ERR_INVALID_ARG for sizes <= 0 or a negative request.
+ */
+ss_status ss_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int64_t chunk_len_request, int64_t* chunk_len, int64_t* n_chunks);
+
+/*
+ * ss_scan_workspace_bytes -- device workspace ss_scan_fwd needs for this
+ * shape and chunk request (0 when the plan has a single chunk; (size_t)-1 for
+ * invalid sizes).
+ *
+ * Workspace layout (fp32, K = n_chunks, BD = batch*dim, N = dstate), valid
+ * after the call completes when K > 1:
+ *   [0, K*BD*N)            state slots (K, batch, dim, N): slot 0 holds the
+ *                          initial state (h0, or zeros); slot c, 1 <= c < K,
+ *                          holds the state right after timestep c*chunk_len-1,
+ *                          i.e. the carry into chunk c.
+ *   [K*BD*N, +(K-1)*BD)    sum of delta over chunk c, (K-1, batch, dim).
+ */
+size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                               int64_t chunk_len_request);
+
+/*
+ * ss_scan_fwd -- the selective scan over full sequences (Mamba walk-through,
+ * section 3.3; fused as the hardware-aware path of section 3.3 and LTI chapter
+ * section 3.1.5.3 describe: the discretised operands and the per-timestep
+ * states are never written to memory).
+ *
+ *   u, delta, z : (batch, seqlen, dim)   dtype      (z NULL: no gate)
+ *   A           : (dim, dstate)          fp32
+ *   B, C        : (batch, seqlen, dstate) dtype
+ *   Dskip       : (dim,)                 fp32       (NULL: no skip term)
+ *   h0          : (batch, dim, dstate)   fp32       (NULL: zero initial state)
+ *   y           : (batch, seqlen, dim)   dtype      output
+ *   h_last      : (batch, dim, dstate)   fp32       output, state after the
+ *                                                   last timestep (NULL: not written)
+ *   workspace   : ss_scan_workspace_bytes(...) bytes of device memory
+ *                 (may be NULL when that is 0)
+ *   chunk_len_request : as for ss_scan_plan (0 = library's choice)
+ *
+ * y must not overlap any other tensor; h_last must not overlap any input
+ * except that it may be exactly h0 (in-place continuation of a state).  The
+ * workspace must not overlap any tensor.  dstate must be 16.
+ */
+ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* Dskip, const void* z, const float* h0,
+                      void* y, float* h_last,
+                      void* workspace, size_t workspace_bytes,
+                      int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                      int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
+
+/*
+ * ss_step -- one token of the recurrent (constant-state) mode: the walk-
+ * through's section 6 (O(1) state per generated token) and the interactive
+ * demo page ("only h survives between steps").  The same update as one
+ * timestep of ss_scan_fwd, applied in place to h:
+ *
+ *   h     : (batch, dim, dstate) fp32, read and overwritten
+ *   u, delta, z : (batch, dim)    dtype   (z NULL: no gate)
+ *   A     : (dim, dstate)         fp32
+ *   B, C  : (batch, dstate)       dtype
+ *   Dskip : (dim,)                fp32    (NULL: no skip term)
+ *   y     : (batch, dim)          dtype   output
+ *
+ * h and y must not overlap each other or any input.  dstate must be 16.
+ */
+ss_status ss_step(float* h, const void* u, const void* delta, const float* A, const void* B,
+                  const void* C, const float* Dskip, const void* z, void* y,
+                  int64_t batch, int64_t dim, int64_t dstate, ss_dtype dtype, hipStream_t stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* ss_status_string(ss_status s);
+
+/* hipError_t value behind the last SS_ERR_HIP returned on this thread (0 if none). */
+int ss_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_SCAN_H */

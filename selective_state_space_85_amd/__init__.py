@@ -1,0 +1,13 @@
+"""MI355X (gfx950) selective scan: a C-ABI HIP library plus a thin torch binding.
+
+    from selective_state_space_85_amd import scan_fwd, step
+    y = scan_fwd(u, delta, A, B, C, D=Dskip, z=z)          # (B, L, D)
+    y_t = step(h, u_t, delta_t, A, B_t, C_t, D=Dskip, z=z_t)  # h (B, D, N) updated in place
+
+The library itself is ``libssscan.so`` (``include/ss_scan.h``), built by
+``selective_state_space_85_amd.build``.
+"""
+from ._lib import LIB_PATH, SSError, load as load_library  # noqa: F401
+from .ops import scan_fwd, scan_plan, scan_workspace_bytes, step  # noqa: F401
+
+__all__ = ["scan_fwd", "step", "scan_plan", "scan_workspace_bytes", "load_library", "LIB_PATH", "SSError"]

@@ -1,0 +1,268 @@
+// C ABI of libssscan.so: argument validation, the chunk plan, workspace
+// sizing and kernel dispatch.  Validation runs on the host before anything is
+// enqueued, so every rejection path works without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "ss_internal.h"
+#include "ss_scan.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kWave = 64;
+constexpr int64_t kMinAutoChunk = 64;   // the automatic plan never cuts finer
+constexpr int64_t kTargetWaves = 2048;  // ~2 waves per SIMD on 256 CUs x 4 SIMDs
+constexpr int64_t kMaxGridYZ = 65535;
+// A chunk's (B, L, D) slab is addressed with 32-bit buffer offsets, and idle
+// lanes use offsets at and above 2^31: one chunk of rows must stay below 2^31
+// bytes at 4 bytes per element.
+constexpr int64_t kMaxChunkBytes = int64_t(1) << 31;
+
+bool mul(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi); empty when the pointer is NULL
+};
+
+Range span(const void* p, int64_t bytes)
+{
+    if (!p) return {0, 0};
+    return {reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) % al) == 0; }
+
+struct Sizes {
+    int64_t rows;    // batch*seqlen*dim
+    int64_t srows;   // batch*seqlen*dstate
+    int64_t states;  // batch*dim*dstate
+    int64_t an;      // dim*dstate
+};
+
+// Element counts and their fp32 byte sizes must fit in int64.
+bool shape_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, Sizes* s)
+{
+    if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0) return false;
+    int64_t bl, tmp;
+    if (!mul(batch, seqlen, &bl)) return false;
+    if (!mul(bl, dim, &s->rows) || !mul(s->rows, 4, &tmp)) return false;
+    if (!mul(bl, dstate, &s->srows) || !mul(s->srows, 4, &tmp)) return false;
+    if (!mul(batch, dim, &tmp) || !mul(tmp, dstate, &s->states) || !mul(s->states, 4, &tmp)) return false;
+    if (!mul(dim, dstate, &s->an) || !mul(s->an, 4, &tmp)) return false;
+    return true;
+}
+
+// Plan: chunk length and count.  Automatic plans start from one chunk and
+// halve the chunk length (staying a power of two, never below kMinAutoChunk)
+// until the emit launch has at least kTargetWaves waves.
+bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* T, int64_t* K)
+{
+    if (request < 0) return false;
+    int64_t t = request;
+    if (t == 0) {
+        t = 1;
+        while (t < seqlen) t <<= 1;
+        int64_t lane_blocks;
+        if (!mul(batch, ceil_div(dim, kWave), &lane_blocks)) lane_blocks = INT64_MAX;
+        while (t > kMinAutoChunk) {
+            int64_t waves;
+            if (!mul(lane_blocks, ceil_div(seqlen, t), &waves) || waves >= kTargetWaves) break;
+            t >>= 1;
+        }
+        int64_t bytes;
+        while (t > 1 && (!mul(t, dim, &bytes) || !mul(bytes, 4, &bytes) || bytes >= kMaxChunkBytes)) t >>= 1;
+    }
+    *T = t;
+    *K = ceil_div(seqlen, t);
+    return true;
+}
+
+// Workspace bytes for K chunks (0 for K == 1); false on overflow.
+bool ws_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t K, int64_t* out)
+{
+    if (K <= 1) {
+        *out = 0;
+        return true;
+    }
+    int64_t bd, slots, dsums, total;
+    if (!mul(batch, dim, &bd)) return false;
+    if (!mul(bd, dstate, &slots) || !mul(slots, K, &slots)) return false;
+    if (!mul(bd, K - 1, &dsums)) return false;
+    if (__builtin_add_overflow(slots, dsums, &total) || !mul(total, 4, out)) return false;
+    return true;
+}
+
+ss_status hip_fail(hipError_t e)
+{
+    g_last_hip_error = static_cast<int>(e);
+    return SS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t chunk_len_request,
+                       int64_t* chunk_len, int64_t* n_chunks)
+{
+    Sizes s;
+    if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
+    int64_t T, K;
+    if (!plan(batch, seqlen, dim, chunk_len_request, &T, &K)) return SS_ERR_INVALID_ARG;
+    if (chunk_len) *chunk_len = T;
+    if (n_chunks) *n_chunks = K;
+    return SS_OK;
+}
+
+size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                               int64_t chunk_len_request)
+{
+    Sizes s;
+    int64_t T, K, bytes;
+    if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return static_cast<size_t>(-1);
+    if (!plan(batch, seqlen, dim, chunk_len_request, &T, &K)) return static_cast<size_t>(-1);
+    if (!ws_bytes(batch, dim, dstate, K, &bytes)) return static_cast<size_t>(-1);
+    return static_cast<size_t>(bytes);
+}
+
+ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* Dskip, const void* z, const float* h0, void* y, float* h_last,
+                      void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+                      int64_t dstate, int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream)
+{
+    if (!u || !delta || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
+    Sizes s;
+    if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
+    int64_t T, K, need;
+    if (!plan(batch, seqlen, dim, chunk_len_request, &T, &K)) return SS_ERR_INVALID_ARG;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
+    if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
+    if (batch > kMaxGridYZ || K > kMaxGridYZ || batch * dim > INT32_MAX) return SS_ERR_UNSUPPORTED;
+    if (!ws_bytes(batch, dim, dstate, K, &need)) return SS_ERR_INVALID_ARG;
+
+    const uintptr_t es = dtype == SS_F32 ? 4 : 2;
+    int64_t chunk_bytes;
+    if (!mul(T < seqlen ? T : seqlen, dim, &chunk_bytes) || !mul(chunk_bytes, int64_t(es), &chunk_bytes) ||
+        chunk_bytes >= kMaxChunkBytes)
+        return SS_ERR_UNSUPPORTED;
+    const void* elem_ptrs[] = {u, delta, B, C, z, y};
+    for (const void* p : elem_ptrs)
+        if (p && !aligned(p, es)) return SS_ERR_INVALID_ARG;
+    const void* vec_ptrs[] = {A, h0, h_last};
+    for (const void* p : vec_ptrs)
+        if (p && !aligned(p, 16)) return SS_ERR_INVALID_ARG;
+    if (Dskip && !aligned(Dskip, 4)) return SS_ERR_INVALID_ARG;
+
+    const int64_t e = static_cast<int64_t>(es);
+    const Range r_u = span(u, s.rows * e), r_dl = span(delta, s.rows * e), r_z = span(z, s.rows * e);
+    const Range r_B = span(B, s.srows * e), r_C = span(C, s.srows * e);
+    const Range r_A = span(A, s.an * 4), r_D = span(Dskip, dim * 4);
+    const Range r_h0 = span(h0, s.states * 4), r_hl = span(h_last, s.states * 4);
+    const Range r_y = span(y, s.rows * e);
+    const Range inputs[] = {r_u, r_dl, r_z, r_B, r_C, r_A, r_D, r_h0};
+    for (const Range& r : inputs)
+        if (overlap(r_y, r)) return SS_ERR_INVALID_ARG;
+    if (overlap(r_y, r_hl)) return SS_ERR_INVALID_ARG;
+    for (const Range& r : inputs) {
+        if (&r == &inputs[7] && h_last == h0) continue;  // exact in-place continuation is allowed
+        if (overlap(r_hl, r)) return SS_ERR_INVALID_ARG;
+    }
+
+    if (need > 0) {
+        if (!workspace || workspace_bytes < static_cast<size_t>(need)) return SS_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return SS_ERR_INVALID_ARG;
+        const Range r_ws = span(workspace, need);
+        for (const Range& r : inputs)
+            if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
+        if (overlap(r_ws, r_y) || overlap(r_ws, r_hl)) return SS_ERR_INVALID_ARG;
+    }
+
+    ssk::ScanArgs a;
+    a.u = u;
+    a.delta = delta;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.Dskip = Dskip;
+    a.z = z;
+    a.h0 = h0;
+    a.y = y;
+    a.h_last = h_last;
+    a.ws_state = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.ws_dsum = need > 0 ? static_cast<float*>(workspace) + K * batch * dim * dstate : nullptr;
+    a.batch = batch;
+    a.seqlen = seqlen;
+    a.dim = dim;
+    a.chunk_len = T;
+    a.n_chunks = K;
+    const hipError_t err = ssk::launch_scan(a, dtype == SS_F32 ? 0 : 1, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    return SS_OK;
+}
+
+ss_status ss_step(float* h, const void* u, const void* delta, const float* A, const void* B, const void* C,
+                  const float* Dskip, const void* z, void* y, int64_t batch, int64_t dim, int64_t dstate,
+                  ss_dtype dtype, hipStream_t stream)
+{
+    if (!h || !u || !delta || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
+    Sizes s;
+    if (!shape_sizes(batch, 1, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
+    if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
+    int64_t threads;
+    if (!mul(s.rows, 4, &threads) || ceil_div(threads, 256) > INT32_MAX) return SS_ERR_UNSUPPORTED;
+
+    const uintptr_t es = dtype == SS_F32 ? 4 : 2;
+    const void* elem_ptrs[] = {u, delta, B, C, z, y};
+    for (const void* p : elem_ptrs)
+        if (p && !aligned(p, es)) return SS_ERR_INVALID_ARG;
+    if (!aligned(h, 16) || !aligned(A, 16)) return SS_ERR_INVALID_ARG;
+    if (Dskip && !aligned(Dskip, 4)) return SS_ERR_INVALID_ARG;
+
+    const int64_t e = static_cast<int64_t>(es);
+    const Range r_h = span(h, s.states * 4), r_y = span(y, s.rows * e);
+    const Range inputs[] = {span(u, s.rows * e), span(delta, s.rows * e), span(z, s.rows * e),
+                            span(B, s.srows * e), span(C, s.srows * e), span(A, s.an * 4),
+                            span(Dskip, dim * 4)};
+    if (overlap(r_h, r_y)) return SS_ERR_INVALID_ARG;
+    for (const Range& r : inputs)
+        if (overlap(r_h, r) || overlap(r_y, r)) return SS_ERR_INVALID_ARG;
+
+    ssk::StepArgs a;
+    a.h = h;
+    a.u = u;
+    a.delta = delta;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.Dskip = Dskip;
+    a.z = z;
+    a.y = y;
+    a.batch = batch;
+    a.dim = dim;
+    const hipError_t err = ssk::launch_step(a, dtype == SS_F32 ? 0 : 1, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    return SS_OK;
+}
+
+const char* ss_status_string(ss_status st)
+{
+    switch (st) {
+        case SS_OK: return "SS_OK";
+        case SS_ERR_INVALID_ARG: return "SS_ERR_INVALID_ARG: invalid argument";
+        case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED: unsupported dstate, dtype or size";
+        case SS_ERR_WORKSPACE: return "SS_ERR_WORKSPACE: workspace missing or too small";
+        case SS_ERR_HIP: return "SS_ERR_HIP: a HIP launch or call failed";
+    }
+    return "unknown status";
+}
+
+int ss_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+"""torch-facing wrappers of the C ABI: argument marshalling only.
+
+Every step of the scan runs in the HIP kernels of libssscan.so; torch supplies
+device memory and the current stream.  Names and argument order follow the
+C entry points (``ss_scan_fwd`` -> ``scan_fwd``, ``ss_step`` -> ``step``).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple, Union
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.SS_F32, torch.bfloat16: _lib.SS_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def scan_plan(batch: int, seqlen: int, dim: int, dstate: int, chunk_len: int = 0) -> Tuple[int, int]:
+    """(chunk_len, n_chunks) that ``ss_scan_fwd`` uses for this shape."""
+    T = ctypes.c_int64()
+    K = ctypes.c_int64()
+    _lib.check("ss_scan_plan", _lib.load().ss_scan_plan(batch, seqlen, dim, dstate, chunk_len,
+                                                         ctypes.byref(T), ctypes.byref(K)))
+    return T.value, K.value
+
+
+def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, chunk_len: int = 0) -> int:
+    n = _lib.load().ss_scan_workspace_bytes(batch, seqlen, dim, dstate, chunk_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid scan shape")
+    return int(n)
+
+
+def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             h0: Optional[torch.Tensor] = None, *, return_last_state: bool = False,
+             chunk_len: int = 0, out: Optional[torch.Tensor] = None,
+             h_last: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+             ) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+    """Selective scan ``ss_scan_fwd`` on device tensors.
+
+    u, delta, z: (B, L, D); B, C: (B, L, N) -- all float32 or all bfloat16.
+    A: (D, N) float32; D: (D,) float32; h0: (B, D, N) float32.
+    Returns y (B, L, D) in the input dtype, and h_last (B, D, N) float32 if asked.
+    ``out`` / ``h_last`` / ``workspace`` may be passed in to avoid allocation.
+    """
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, seqlen, dim)")
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd runs on the GPU; u is on %s" % dev)
+    dt = u.dtype
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    nb, nl, nd = u.shape
+    nn = A.shape[-1]
+    _need(u, "u", (nb, nl, nd), dt, dev)
+    _need(delta, "delta", (nb, nl, nd), dt, dev)
+    _need(A, "A", (nd, nn), torch.float32, dev)
+    _need(B, "B", (nb, nl, nn), dt, dev)
+    _need(C, "C", (nb, nl, nn), dt, dev)
+    if D is not None:
+        _need(D, "D", (nd,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (nb, nl, nd), dt, dev)
+    if h0 is not None:
+        _need(h0, "h0", (nb, nd, nn), torch.float32, dev)
+    y = out if out is not None else torch.empty((nb, nl, nd), dtype=dt, device=dev)
+    _need(y, "out", (nb, nl, nd), dt, dev)
+    hl = h_last
+    if return_last_state and hl is None:
+        hl = torch.empty((nb, nd, nn), dtype=torch.float32, device=dev)
+    if hl is not None:
+        _need(hl, "h_last", (nb, nd, nn), torch.float32, dev)
+    need = scan_workspace_bytes(nb, nl, nd, nn, chunk_len)
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    with torch.cuda.device(dev):
+        st = _lib.load().ss_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                     _ptr(h0), _ptr(y), _ptr(hl), _ptr(ws), ws_bytes,
+                                     nb, nl, nd, nn, chunk_len, _DTYPES[dt], _stream(dev))
+    _lib.check("ss_scan_fwd", st)
+    if return_last_state:
+        return y, hl
+    return y
+
+
+def step(h: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+         C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+         *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent token ``ss_step``: h (B, D, N) float32 is updated in place.
+
+    u, delta, z: (B, D); B, C: (B, N), float32 or bfloat16; A (D, N), D (D,) float32.
+    Returns y (B, D) in the input dtype.
+    """
+    if u.dim() != 2:
+        raise ValueError("u must be (batch, dim)")
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("step runs on the GPU; u is on %s" % dev)
+    dt = u.dtype
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    nb, nd = u.shape
+    nn = A.shape[-1]
+    _need(h, "h", (nb, nd, nn), torch.float32, dev)
+    _need(delta, "delta", (nb, nd), dt, dev)
+    _need(A, "A", (nd, nn), torch.float32, dev)
+    _need(B, "B", (nb, nn), dt, dev)
+    _need(C, "C", (nb, nn), dt, dev)
+    if D is not None:
+        _need(D, "D", (nd,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (nb, nd), dt, dev)
+    y = out if out is not None else torch.empty((nb, nd), dtype=dt, device=dev)
+    _need(y, "out", (nb, nd), dt, dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().ss_step(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(y), nb, nd, nn, _DTYPES[dt], _stream(dev))
+    _lib.check("ss_step", st)
+    return y

@@ -22,8 +22,9 @@ Recipe (one place, so every consumer draws identical bits):
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import Dict, Optional
+from typing import Dict, Iterator, Optional
 
 import numpy as np
 
@@ -81,16 +82,22 @@ def _rng(seed: int, cfg_id: int, tensor: str, step: int = 0) -> np.random.Genera
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bf16 (round to nearest, ties to even); return uint16 bits."""
+    """Round float32 to bf16 (round to nearest, ties to even); return uint16 bits.
+
+    Inputs must be finite: the largest finite pattern plus the rounding bias
+    still fits in 32 bits, so the arithmetic stays in uint32.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16 rounding expects finite values")
     bits = x.view(np.uint32)
     out = np.empty(bits.shape, dtype=np.uint16)
     flat_in = bits.reshape(-1)
     flat_out = out.reshape(-1)
     for s in range(0, flat_in.size, _CHUNK):
-        b = flat_in[s:s + _CHUNK].astype(np.uint64)
-        lsb = (b >> np.uint64(16)) & np.uint64(1)
-        flat_out[s:s + _CHUNK] = ((b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+        b = flat_in[s:s + _CHUNK]
+        bias = np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+        flat_out[s:s + _CHUNK] = ((b + bias) >> np.uint32(16)).astype(np.uint16)
     return out
 
 
@@ -115,7 +122,9 @@ def _normal(rng: np.random.Generator, shape, mu: float = 0.0, sigma: float = 1.0
 def _softplus_normal(rng: np.random.Generator, shape, mu: float, sigma: float) -> np.ndarray:
     v = _normal(rng, shape, mu, sigma).reshape(-1)
     for s in range(0, v.size, _CHUNK):
-        v[s:s + _CHUNK] = np.logaddexp(np.float32(0.0), v[s:s + _CHUNK])
+        x = v[s:s + _CHUNK]
+        # log(1 + e^x) = max(x, 0) + log(1 + e^-|x|), no overflow for large |x|
+        v[s:s + _CHUNK] = np.maximum(x, np.float32(0.0)) + np.log1p(np.exp(-np.abs(x)))
     return v.reshape(shape)
 
 
@@ -187,6 +196,25 @@ def step_inputs(w: Workload, step: int, seed: int = 0) -> Dict[str, Optional[np.
         "C": _store(_normal(_rng(seed, w.cfg_id, "C", s), shp_s), w.dtype),
         "z": _store(_normal(_rng(seed, w.cfg_id, "z", s), shp_x), w.dtype) if w.has_z else None,
     }
+
+
+def iter_step_inputs(w: Workload, steps: int, seed: int = 0, workers: int = 1) -> Iterator[Dict]:
+    """step_inputs(w, 0..steps-1) in order.  With workers > 1 the steps are drawn
+    ahead by a thread pool (numpy releases the GIL while it fills arrays); each
+    step has its own seeded streams, so the result does not depend on it."""
+    if workers <= 1:
+        for s in range(steps):
+            yield step_inputs(w, s, seed)
+        return
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        ahead = 2 * workers
+        futs = [ex.submit(step_inputs, w, s, seed) for s in range(min(ahead, steps))]
+        for s in range(steps):
+            item = futs[s].result()
+            futs[s] = None
+            if s + ahead < steps:
+                futs.append(ex.submit(step_inputs, w, s + ahead, seed))
+            yield item
 
 
 def algorithmic_bytes_scan(batch: int, seqlen: int, dim: int, dstate: int, dtype: str,
