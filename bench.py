@@ -160,7 +160,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes,
-                     "kernel": "ss_scan_fwd (scan_chunk_kernel%s)" % (" + carry" if K > 1 else ""),
+                     "kernel": "ss_scan_fwd: scan_kernel (emit)%s" % (" + aggregate + carry" if K > 1 else ""),
                      "kernel_source_hash": src_hash},
     }
 
@@ -244,7 +244,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = min(16, os.cpu_count() or 1)
-        rows = 4  # batch rows 0..3: half the workload
+        rows = w.batch  # every batch row: the whole workload
         lanes = np.arange(rows * w.dim, dtype=np.int64)
         log("timing the CPU oracle on %d channels x %d steps, %d threads" % (lanes.size, w.seqlen, threads))
         c0 = time.perf_counter()
@@ -252,7 +252,7 @@ def main():
         cdt = time.perf_counter() - c0
         n_el = lanes.size * w.seqlen * w.dstate
         result["cpu_baseline"] = {"value": n_el / cdt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-                                  "sample": "batch rows 0-%d of the large-layer workload (%d channels x %d steps x %d "
+                                  "sample": "the whole large-layer workload, batch rows 0-%d (%d channels x %d steps x %d "
                                             "states = %d elements), fp64, %.2f s" % (rows - 1, lanes.size, w.seqlen,
                                                                                      w.dstate, n_el, cdt)}
 

@@ -12,6 +12,7 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kWave = 64;
+constexpr int64_t kWavesPerBlock = ssk::kScanWaves;  // a scan workgroup: 64 channels, the states split over its waves
 constexpr int64_t kMinAutoChunk = 64;   // the automatic plan never cuts finer
 constexpr int64_t kTargetWaves = 2048;  // ~2 waves per SIMD on 256 CUs x 4 SIMDs
 constexpr int64_t kMaxGridYZ = 65535;
@@ -60,7 +61,8 @@ bool shape_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, Siz
 
 // Plan: chunk length and count.  Automatic plans start from one chunk and
 // halve the chunk length (staying a power of two, never below kMinAutoChunk)
-// until the emit launch has at least kTargetWaves waves.
+// until the emit launch has at least kTargetWaves waves (4 per 64 channels
+// per chunk).
 bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* T, int64_t* K)
 {
     if (request < 0) return false;
@@ -69,7 +71,7 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
         t = 1;
         while (t < seqlen) t <<= 1;
         int64_t lane_blocks;
-        if (!mul(batch, ceil_div(dim, kWave), &lane_blocks)) lane_blocks = INT64_MAX;
+        if (!mul(batch, ceil_div(dim, kWave) * kWavesPerBlock, &lane_blocks)) lane_blocks = INT64_MAX;
         while (t > kMinAutoChunk) {
             int64_t waves;
             if (!mul(lane_blocks, ceil_div(seqlen, t), &waves) || waves >= kTargetWaves) break;

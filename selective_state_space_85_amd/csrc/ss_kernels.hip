@@ -2,27 +2,42 @@
 // "selective_scan"; discrete recurrence of section 2.2; D skip and silu(z)
 // gate of section 3.4) and of the single-token recurrent update.
 //
-// Work decomposition
-//  * one lane owns one channel (b, d) and all 16 state entries h[n] in
-//    registers; a wave covers 64 consecutive d of one batch row, so B[b,t,:]
-//    and C[b,t,:] are wave-uniform (scalar loads) and u/delta/z/y rows are
-//    read and written as 64 consecutive elements;
-//  * the sequence is cut into chunks (LTI chapter 3.1, section 3.1.5.2: the
-//    recurrence is a scan over an associative operator).  For K > 1 chunks:
-//      1. scan_chunk_kernel<aggregate> runs chunks 0..K-2 from a zero state and
-//         keeps only the chunk's end state S_c and its delta sum;
-//      2. carry_kernel turns the per-chunk affine pairs (P_c, S_c), with
-//         P_c = exp(A * sum_t delta_t), into carries by a wave-level
-//         inclusive prefix combine over chunks (64 chunks per pass, the last
-//         lane's value carried to the next pass);
-//      3. scan_chunk_kernel<emit> reruns every chunk from its carry and writes y.
-//    Only y, the chunk carries and h_last ever reach memory; the per-timestep
-//    states and the discretised operands exp(delta*A), delta*B*u stay in
-//    registers (the fused, state-in-fast-memory point of section 3.3 and of
-//    LTI chapter section 3.1.5.3).
+// Scan work decomposition
+//  * A workgroup of 4 waves owns 64 consecutive channels d of one batch row b
+//    (lane = channel) and one chunk of the sequence.  Wave w holds state
+//    entries n = 4w..4w+3 of every channel in registers, so B[b,t,n] and
+//    C[b,t,n] are the same for all lanes of a wave: they come in through
+//    scalar loads and are used as scalar operands.  Per element the wave
+//    issues one multiply (delta*A), one exp2, one multiply (delta*u*B), one
+//    fma (state) and one fma (C.h) -- no MFMA: nothing here is a dense
+//    contraction.
+//  * The sequence is processed in tiles of rows.  Per tile, each wave widens
+//    its share of the rows' u and delta once and publishes (delta, delta*u) in
+//    LDS for the other three waves; each wave leaves its partial C.h per row
+//    in LDS; each wave then finishes its share of rows (sum of the four
+//    partials, D skip, silu(z) gate, rounding, store).  LDS buffers alternate
+//    between even and odd tiles, so one barrier per tile suffices.
+//  * Prefetch: u/delta/z rows two tiles ahead (raw buffer loads, the channel
+//    as vector offset and the row as scalar offset, so stepping in t costs no
+//    vector instruction); the wave's B/C words one tile ahead, issued right
+//    after the tile's LDS reads so that no LDS wait has to drain them.
+//  * The sequence can be cut into chunks (LTI chapter 3.1, section 3.1.5.2:
+//    the recurrence is a scan over an associative operator).  For K > 1:
+//      1. scan_kernel<aggregate> runs chunks 0..K-2 from a zero state and
+//         keeps only each chunk's end state S_c and its delta sum;
+//      2. carry_kernel combines the affine pairs (P_c, S_c),
+//         P_c = exp(A * sum_t delta_t), with a wave-level inclusive prefix over
+//         chunks (64 chunks per pass) into the carry of every chunk;
+//      3. scan_kernel<emit> reruns every chunk from its carry and writes y.
+//    Only y, the chunk carries and h_last reach memory: the per-timestep
+//    states and the discretised operands exp(delta*A), delta*B*u never do (the
+//    fused, state-in-fast-memory point of section 3.3 and of LTI chapter
+//    section 3.1.5.3).
 //  * exp(x) is evaluated as exp2(x * log2 e) on the hardware exp2 unit, with
 //    A pre-scaled by log2 e once per lane.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "ss_internal.h"
 
@@ -32,6 +47,9 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int N = kDState;
 constexpr int kWave = 64;
+constexpr int kGroups = kScanWaves;  // waves per scan workgroup = state groups
+constexpr int kNS = N / kGroups;  // state entries per wave
+constexpr int kThreads = kWave * kGroups;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
@@ -59,47 +77,14 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e)); }
 
-// B[b,t,:] and C[b,t,:] are the same for every lane of a wave: read them
-// through the constant address space so they arrive as scalar loads, and
-// widen bf16 on the scalar unit.
+// Scalar (wave-uniform) reads go through the constant address space so they
+// are issued as scalar loads.
 #define SS_CONST __attribute__((address_space(4)))
 
-template <int DT>
-struct Row;
-template <>
-struct Row<0> {  // 16 fp32 = 16 dwords per timestep
-    static constexpr int kWords = 16;
-    static __device__ __forceinline__ void widen(const uint32_t (&w)[kWords], float (&v)[N])
-    {
-#pragma unroll
-        for (int n = 0; n < N; ++n) v[n] = __uint_as_float(w[n]);
-    }
-};
-template <>
-struct Row<1> {  // 16 bf16 = 8 dwords per timestep
-    static constexpr int kWords = 8;
-    static __device__ __forceinline__ void widen(const uint32_t (&w)[kWords], float (&v)[N])
-    {
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-};
-
-template <int W>
-__device__ __forceinline__ void load_words(const SS_CONST uint32_t* p, uint32_t (&w)[W])
-{
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = p[i];
-}
-
 // Raw buffer access for the (B, L, D) row streams.  The resource is based at
-// the chunk's first row; the lane's channel is the vector offset and the row
-// is a scalar offset, so moving along t costs no vector instruction.  Lanes
-// past the last channel get an out-of-range vector offset: their loads read
-// 0 and their stores are dropped by the hardware range check.
+// the chunk's first row; the lane's channel is the vector offset and the row a
+// scalar offset.  Lanes past the last channel get an out-of-range vector
+// offset: their loads read 0 and their stores are dropped by the range check.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw (untyped) buffer, gfx9 family
 constexpr uint32_t kIdleOffset = 0x80000000u;
 
@@ -139,38 +124,80 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), int(kRsrcWord3));
 }
 
-constexpr int kBlock = 8;  // timesteps per vector-prefetch block
+// Tile geometry per operand type: rows per tile, and the 32-bit words of one
+// B (or C) row that hold one wave's kNS entries.  The scalar words of two
+// tiles (current and next, B and C) must fit the scalar register file.
+template <int DT>
+struct Tile;
+// rows per tile: a multiple of the wave count, scalar words of two tiles <= 64
+#ifndef SS_TILE_ROWS_BF16
+#define SS_TILE_ROWS_BF16 8
+#endif
+template <>
+struct Tile<0> {
+    static constexpr int kRows = kGroups > 4 ? kGroups : 4;
+    static constexpr int kWaveWords = kNS;  // fp32 entries
+    static constexpr int kRowWords = N;
+    static __device__ __forceinline__ void widen(const uint32_t (&w)[kWaveWords], float (&v)[kNS])
+    {
+#pragma unroll
+        for (int i = 0; i < kNS; ++i) v[i] = __uint_as_float(w[i]);
+    }
+};
+template <>
+struct Tile<1> {
+    static constexpr int kRows = SS_TILE_ROWS_BF16;
+    static constexpr int kWaveWords = kNS / 2;  // bf16 pairs
+    static constexpr int kRowWords = N / 2;
+    static __device__ __forceinline__ void widen(const uint32_t (&w)[kWaveWords], float (&v)[kNS])
+    {
+#pragma unroll
+        for (int i = 0; i < kWaveWords; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+template <int V>
+using Slot = std::integral_constant<int, V>;
 
 // ---------------------------------------------------------------------------
-// Chunk kernel.  grid = (ceil(dim/64), batch, chunks), block = 64.
+// Scan kernel.  grid = (ceil(dim/64), batch, chunks), block = 256 (4 waves).
 // EMIT: start from the chunk's carry (or h0), write y and, for the last chunk,
 //       h_last.
 // !EMIT (aggregate): start from zero, write the chunk's end state into state
 //       slot c+1 and its delta sum.
-// Software pipeline: u/delta/z of the next kBlock timesteps are requested
-// while the current block is computed (rows past the chunk end are clamped to
-// its last row); the scalar B/C row of timestep t+1 is requested right after
-// row t has been consumed (scalar loads may return out of order, so a wait
-// always covers every one in flight).
 // Host guarantees: chunk_len * dim * element size < 2^31.
 // ---------------------------------------------------------------------------
 template <int DT, bool EMIT, bool HAS_D, bool HAS_Z>
-__global__ __launch_bounds__(kWave) void scan_chunk_kernel(ScanArgs a)
+__global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
 {
     using T = typename Elem<DT>::T;
-    using R = Row<DT>;
     using V = Buf<DT>;
     using Raw = typename V::Raw;
-    constexpr int W = R::kWords;
+    using TL = Tile<DT>;
+    constexpr int TT = TL::kRows;
+    constexpr int RPW = TT / kGroups;  // rows each wave widens and finishes per tile
+    static_assert(RPW * kGroups == TT, "tile rows must split evenly across the waves");
+    constexpr int WW = TL::kWaveWords;
+    constexpr int RW = TL::kRowWords;
 
+    __shared__ float2 s_xd[2][TT][kWave];                       // (delta, delta*u) per row and channel
+    __shared__ float s_part[EMIT ? 2 : 1][kGroups][TT][kWave];  // partial C.h per wave
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t D = a.dim, L = a.seqlen, BD = a.batch * a.dim;
-    const int64_t d_raw = int64_t(blockIdx.x) * kWave + threadIdx.x;
+    const int64_t d_raw = int64_t(blockIdx.x) * kWave + lane;
     const bool active = d_raw < D;
     const int64_t d = active ? d_raw : D - 1;  // idle lanes shadow the last channel
     const int64_t b = blockIdx.y;
     const int64_t c = blockIdx.z;
     const int64_t t0 = c * a.chunk_len;
     const int len = int(((t0 + a.chunk_len < L) ? t0 + a.chunk_len : L) - t0);
+    // an even number of tiles; rows past the chunk end are neutral (see publish_rows)
+    const int ntiles = (((len + TT - 1) / TT) + 1) & ~1;
     const int64_t bd = b * D + d;
     const int64_t row0 = (b * L + t0) * D;  // first element of the chunk's first row
 
@@ -181,120 +208,195 @@ __global__ __launch_bounds__(kWave) void scan_chunk_kernel(ScanArgs a)
     const __amdgpu_buffer_rsrc_t r_dl = make_rsrc(static_cast<const T*>(a.delta) + row0, span);
     const __amdgpu_buffer_rsrc_t r_z = make_rsrc(HAS_Z ? static_cast<const T*>(a.z) + row0 : nullptr, span);
     const __amdgpu_buffer_rsrc_t r_y = make_rsrc(EMIT ? static_cast<T*>(a.y) + row0 : nullptr, span);
-    // address-space casts need the C cast form
-    const SS_CONST uint32_t* pB = (const SS_CONST uint32_t*)(static_cast<const T*>(a.B) + (b * L + t0) * N);
-    const SS_CONST uint32_t* pC = (const SS_CONST uint32_t*)(static_cast<const T*>(a.C) + (b * L + t0) * N);
+    // the wave's words of the chunk's B and C rows (address-space casts need the C cast form)
+    const SS_CONST uint32_t* pB =
+        (const SS_CONST uint32_t*)(static_cast<const T*>(a.B) + (b * L + t0) * N) + w * WW;
+    const SS_CONST uint32_t* pC =
+        (const SS_CONST uint32_t*)(static_cast<const T*>(a.C) + (b * L + t0) * N) + w * WW;
 
-    float A2[N];
+    const int64_t sbase = bd * N + w * kNS;  // this lane's entries in a (B, D, N) state array
+    float A2[kNS];
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] = a.A[d * N + n] * kLog2e;
+    for (int i = 0; i < kNS; ++i) A2[i] = a.A[d * N + w * kNS + i] * kLog2e;
 
-    float h[N];
+    float h[kNS];
     const bool from_ws = EMIT && a.n_chunks > 1;
     const bool from_h0 = EMIT && a.n_chunks == 1 && a.h0 != nullptr;
     if (from_ws || from_h0) {
-        const float* init = from_ws ? a.ws_state + (c * BD + bd) * N : a.h0 + bd * N;
+        const float* init = from_ws ? a.ws_state + c * BD * N + sbase : a.h0 + sbase;
 #pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = init[n];
+        for (int i = 0; i < kNS; ++i) h[i] = init[i];
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = 0.0f;
+        for (int i = 0; i < kNS; ++i) h[i] = 0.0f;
     }
-
     const float dskip = (EMIT && HAS_D) ? a.Dskip[d] : 0.0f;
     float dsum = 0.0f;
 
-    // row r of the chunk, clamped to the last one, as a scalar byte offset
-    auto row_off = [&](int r) -> uint32_t { return uint32_t(r < len ? r : len - 1) * row_bytes; };
+    Raw rdl[2][RPW], ru[2][RPW], rz[2][RPW];  // raw rows in flight, by tile parity
+    float xf[2][RPW], zf[2][RPW];             // widened u, z kept for the epilogue
+    uint32_t bw[2][TT][WW], cw[2][TT][WW];    // scalar words, by tile parity
 
-    Raw dl_c[kBlock], x_c[kBlock], z_c[kBlock];
-#pragma unroll
-    for (int j = 0; j < kBlock; ++j) {
-        const uint32_t so = row_off(j);
-        dl_c[j] = V::load(r_dl, voff, so);
-        x_c[j] = V::load(r_u, voff, so);
-        if (EMIT && HAS_Z) z_c[j] = V::load(r_z, voff, so);
-    }
-    uint32_t bw[W], cw[W];
-    load_words(pB, bw);
-    if (EMIT) load_words(pC, cw);
+    // row r of the chunk, clamped to the last one
+    auto clamp_row = [&](int r) { return r < len ? r : len - 1; };
 
-    for (int i0 = 0; i0 < len; i0 += kBlock) {
-        Raw dl_n[kBlock], x_n[kBlock], z_n[kBlock];
+    auto issue_rows = [&](int tile, auto slot) {
+        constexpr int S = decltype(slot)::value;
 #pragma unroll
-        for (int j = 0; j < kBlock; ++j) {
-            const uint32_t so = row_off(i0 + kBlock + j);
-            dl_n[j] = V::load(r_dl, voff, so);
-            x_n[j] = V::load(r_u, voff, so);
-            if (EMIT && HAS_Z) z_n[j] = V::load(r_z, voff, so);
+        for (int j = 0; j < RPW; ++j) {
+            const uint32_t so = uint32_t(clamp_row(tile * TT + w * RPW + j)) * row_bytes;
+            rdl[S][j] = V::load(r_dl, voff, so);
+            ru[S][j] = V::load(r_u, voff, so);
+            if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, voff, so);
         }
+    };
+    // widen this wave's rows of a tile and publish (delta, delta*u).  Rows past
+    // the chunk end are published as (0, 0): exp2(0) = 1 and 0*B = 0 leave the
+    // state bit-unchanged, so the last tiles need no row-count branches.
+    auto publish_rows = [&](int tile, auto slot) {
+        constexpr int S = decltype(slot)::value;
 #pragma unroll
-        for (int j = 0; j < kBlock; ++j) {
-            const int i = i0 + j;
-            if (i >= len) break;
-            float bv[N], cv[N];
-            R::widen(bw, bv);
-            if (EMIT) R::widen(cw, cv);
-            // keep the next row's scalar loads behind this row's first use
-            if (EMIT)
-                __asm__ volatile("" ::"s"(bw[0]), "s"(cw[0]) : "memory");
-            else
-                __asm__ volatile("" ::"s"(bw[0]) : "memory");
-            if (i + 1 < len) {
-                load_words(pB + (i + 1) * W, bw);
-                if (EMIT) load_words(pC + (i + 1) * W, cw);
-            }
-            const float dl = V::widen(dl_c[j]);
-            const float x = V::widen(x_c[j]);
-            const float xb = dl * x;
-            float acc = 0.0f;
-#pragma unroll
-            for (int n = 0; n < N; ++n) {
-                const float abar = exp2_hw(dl * A2[n]);
-                h[n] = fmaf(abar, h[n], xb * bv[n]);
-                if (EMIT) acc = fmaf(cv[n], h[n], acc);
-            }
+        for (int j = 0; j < RPW; ++j) {
+            const bool in = tile * TT + w * RPW + j < len;
+            const float dl = in ? V::widen(rdl[S][j]) : 0.0f;
+            const float x = V::widen(ru[S][j]);
+            s_xd[S][w * RPW + j][lane] = make_float2(dl, dl * x);
             if (EMIT) {
-                if (HAS_D) acc = fmaf(dskip, x, acc);
-                if (HAS_Z) acc *= silu(V::widen(z_c[j]));
-                V::store(r_y, voff, uint32_t(i) * row_bytes, acc);
+                xf[S][j] = x;
+                if (HAS_Z) zf[S][j] = V::widen(rz[S][j]);
+            }
+        }
+    };
+    // 32-bit byte offsets from one 64-bit base: scalar loads with an SGPR offset
+    auto issue_words = [&](int tile, auto slot) {
+        constexpr int S = decltype(slot)::value;
+#pragma unroll
+        for (int r = 0; r < TT; ++r) {
+            const uint32_t off = uint32_t(clamp_row(tile * TT + r)) * uint32_t(RW * 4);
+            const SS_CONST uint32_t* qb = (const SS_CONST uint32_t*)((const SS_CONST char*)pB + off);
+            const SS_CONST uint32_t* qc = (const SS_CONST uint32_t*)((const SS_CONST char*)pC + off);
+#pragma unroll
+            for (int q = 0; q < WW; ++q) {
+                bw[S][r][q] = qb[q];
+                if (EMIT) cw[S][r][q] = qc[q];
+            }
+        }
+    };
+    // finish this wave's rows of a tile: sum the partials, skip, gate, store
+    auto finish_rows = [&](int tile, auto slot) {
+        constexpr int S = decltype(slot)::value;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int r = w * RPW + j;
+            const int t = tile * TT + r;
+            if (t < len) {
+                float acc = s_part[S][0][r][lane];
+#pragma unroll
+                for (int g = 1; g < kGroups; ++g) acc += s_part[S][g][r][lane];
+                if (HAS_D) acc = fmaf(dskip, xf[S][j], acc);
+                if (HAS_Z) acc *= silu(zf[S][j]);
+                V::store(r_y, voff, uint32_t(t) * row_bytes, acc);
+            }
+        }
+    };
+    // the recurrence over one tile for this wave's state entries
+    auto scan_rows = [&](int tile, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        float2 xd[TT];
+#pragma unroll
+        for (int r = 0; r < TT; ++r) xd[r] = s_xd[S][r][lane];
+        // the next tile's scalar loads go out only after this tile's LDS reads
+        // have landed, so no later LDS wait has to drain them
+        __asm__ volatile("" ::"v"(xd[TT - 1].x) : "memory");
+        issue_words(tile + 1, Slot<1 - S>{});
+#pragma unroll
+        for (int r = 0; r < TT; ++r) {
+            float bv[kNS];
+            TL::widen(bw[S][r], bv);
+            const float dl = xd[r].x;
+            const float xb = xd[r].y;
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) h[i] = fmaf(exp2_hw(dl * A2[i]), h[i], xb * bv[i]);
+            if constexpr (EMIT) {
+                float cv[kNS];
+                TL::widen(cw[S][r], cv);
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kNS; ++i) acc = fmaf(cv[i], h[i], acc);
+                s_part[S][w][r][lane] = acc;
             } else {
                 dsum += dl;
             }
         }
-#pragma unroll
-        for (int j = 0; j < kBlock; ++j) {
-            dl_c[j] = dl_n[j];
-            x_c[j] = x_n[j];
-            if (EMIT && HAS_Z) z_c[j] = z_n[j];
+    };
+    // one tile step: finish tile k-1, publish tile k+1, scan tile k
+    // every load below is clamped to a valid row, so all of it runs unconditionally
+    auto step = [&](int k, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        if constexpr (EMIT) {
+            if (k >= 1) finish_rows(k - 1, Slot<1 - S>{});
         }
+        publish_rows(k + 1, Slot<1 - S>{});
+        issue_rows(k + 3, Slot<1 - S>{});
+        scan_rows(k, Slot<S>{});
+        __syncthreads();
+    };
+
+    issue_rows(0, Slot<0>{});
+    issue_rows(1, Slot<1>{});
+    publish_rows(0, Slot<0>{});
+    issue_rows(2, Slot<0>{});
+    issue_words(0, Slot<0>{});
+    __syncthreads();
+
+    for (int k = 0; k < ntiles; k += 2) {
+        step(k, Slot<0>{});
+        step(k + 1, Slot<1>{});
     }
+    if constexpr (EMIT) finish_rows(ntiles - 1, Slot<1>{});
 
     if (!active) return;
     if (EMIT) {
         if (c == a.n_chunks - 1 && a.h_last) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) a.h_last[bd * N + n] = h[n];
+            for (int i = 0; i < kNS; ++i) a.h_last[sbase + i] = h[i];
         }
     } else {
-        float* dst = a.ws_state + ((c + 1) * BD + bd) * N;
+        float* dst = a.ws_state + (c + 1) * BD * N + sbase;
 #pragma unroll
-        for (int n = 0; n < N; ++n) dst[n] = h[n];
-        a.ws_dsum[c * BD + bd] = dsum;
+        for (int i = 0; i < kNS; ++i) dst[i] = h[i];
+        if (w == 0) a.ws_dsum[c * BD + bd] = dsum;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Carry kernel.  grid = batch*dim (one wave per channel), block = 64.
 // Lane i of pass p owns chunk c = 64p + i and its affine pair
-// (P_c, S_c) = (exp(A * sum delta over c), end state of c from zero).
+// (P_c, S_c) = (exp(A * sum of delta over chunk c), end state of c from zero).
 // An inclusive Hillis-Steele combine over the lanes, earlier pair first,
 //   (a1, b1) then (a2, b2) -> (a2*a1, a2*b1 + b2),
-// gives each lane the composite map of chunks 0..c; applied to the incoming
-// state it yields the carry H_c (state after chunk c), stored in slot c+1.
-// Slot 0 receives the initial state.  Lanes past the last chunk hold the
-// identity pair (1, 0), so lane 63 always ends with the pass's total.
+// built from DPP row shifts (1, 2, 4, 8 within each row of 16 lanes) and row
+// broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3), gives each
+// lane the composite map of chunks 0..c; applied to the incoming state it
+// yields the carry H_c (state after chunk c), stored in slot c+1.  Slot 0
+// receives the initial state.  Lanes past the last chunk hold the identity
+// pair (1, 0), so lane 63 always ends with the pass's total.
 // ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void combine_from(float& P, float& S)
+{
+    // a source outside the row (or a row left out by ROW_MASK) reads the identity (1, 0)
+    const float Pp = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(P), CTRL, ROW_MASK, 0xf, false));
+    const float Sp = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(0.0f), __float_as_int(S), CTRL, ROW_MASK, 0xf, false));
+    S = fmaf(P, Sp, S);
+    P *= Pp;
+}
+
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
 __global__ __launch_bounds__(kWave) void carry_kernel(ScanArgs a)
 {
     const int64_t bd = blockIdx.x;
@@ -316,22 +418,22 @@ __global__ __launch_bounds__(kWave) void carry_kernel(ScanArgs a)
         const bool valid = c < n_carry;
         const float dsum = valid ? a.ws_dsum[c * BD + bd] : 0.0f;
         float* slot = a.ws_state + ((c + 1) * BD + bd) * N;
+        float S[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) S[n] = valid ? slot[n] : 0.0f;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             float P = valid ? exp2_hw(A2[n] * dsum) : 1.0f;
-            float S = valid ? slot[n] : 0.0f;
-#pragma unroll
-            for (int k = 1; k < kWave; k <<= 1) {
-                const float Pp = __shfl_up(P, k, kWave);
-                const float Sp = __shfl_up(S, k, kWave);
-                if (lane >= k) {
-                    S = fmaf(P, Sp, S);
-                    P *= Pp;
-                }
-            }
-            const float H = fmaf(P, hin[n], S);
+            float Sn = S[n];
+            combine_from<kDppRowShr1, 0xf>(P, Sn);
+            combine_from<kDppRowShr2, 0xf>(P, Sn);
+            combine_from<kDppRowShr4, 0xf>(P, Sn);
+            combine_from<kDppRowShr8, 0xf>(P, Sn);
+            combine_from<kDppRowBcast15, 0xa>(P, Sn);
+            combine_from<kDppRowBcast31, 0xc>(P, Sn);
+            const float H = fmaf(P, hin[n], Sn);
             if (valid) slot[n] = H;
-            hin[n] = __shfl(H, kWave - 1, kWave);
+            hin[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(H), kWave - 1));
         }
     }
 }
@@ -394,12 +496,12 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
 {
     const unsigned nblk = unsigned((a.dim + kWave - 1) / kWave);
     if (a.n_chunks > 1) {
-        scan_chunk_kernel<DT, false, false, false>
-            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), dim3(kWave), 0, s>>>(a);
+        scan_kernel<DT, false, false, false>
+            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), dim3(kThreads), 0, s>>>(a);
         carry_kernel<<<dim3(unsigned(a.batch * a.dim)), dim3(kWave), 0, s>>>(a);
     }
-    scan_chunk_kernel<DT, true, HAS_D, HAS_Z>
-        <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), dim3(kWave), 0, s>>>(a);
+    scan_kernel<DT, true, HAS_D, HAS_Z>
+        <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
