@@ -11,7 +11,7 @@ constexpr int kDState = 16;  // the state width the kernels are built for
 
 // Waves per scan workgroup; the 16 state entries are split evenly across them.
 #ifndef SS_SCAN_WAVES
-#define SS_SCAN_WAVES 4
+#define SS_SCAN_WAVES 8
 #endif
 constexpr int kScanWaves = SS_SCAN_WAVES;
 static_assert(kScanWaves == 2 || kScanWaves == 4 || kScanWaves == 8, "state split must divide 16");

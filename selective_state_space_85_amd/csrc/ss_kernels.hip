@@ -162,6 +162,25 @@ struct Tile<1> {
 template <int V>
 using Slot = std::integral_constant<int, V>;
 
+// An empty asm statement that reads and rewrites a whole group of values: all of
+// them are computed before it and nothing that consumes them moves above it.
+template <int R, int C>
+__device__ __forceinline__ void pin_rows(float (&v)[R][C])
+{
+    static_assert(C == 4 || C == 2 || C == 8, "row width");
+#pragma unroll
+    for (int r = 0; r + 1 < R; r += 2) {
+        if constexpr (C == 4)
+            __asm__ volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r][2]), "+v"(v[r][3]), "+v"(v[r + 1][0]),
+                             "+v"(v[r + 1][1]), "+v"(v[r + 1][2]), "+v"(v[r + 1][3]));
+        else if constexpr (C == 2)
+            __asm__ volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r + 1][0]), "+v"(v[r + 1][1]));
+        else
+            __asm__ volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r][2]), "+v"(v[r][3]), "+v"(v[r][4]),
+                             "+v"(v[r][5]), "+v"(v[r][6]), "+v"(v[r][7]));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Scan kernel.  grid = (ceil(dim/64), batch, chunks), block = 256 (4 waves).
 // EMIT: start from the chunk's carry (or h0), write y and, for the last chunk,
@@ -309,14 +328,29 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
         // have landed, so no later LDS wait has to drain them
         __asm__ volatile("" ::"v"(xd[TT - 1].x) : "memory");
         issue_words(tile + 1, Slot<1 - S>{});
+        // All delta*A products of the tile are formed before the first exp2 is
+        // issued (the empty asm statements pin them in registers), so every
+        // exp2 reads an operand produced many instructions earlier instead of
+        // waiting on the multiply right before it.
+        float e[TT][kNS];
+#pragma unroll
+        for (int r = 0; r < TT; ++r) {
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) e[r][i] = xd[r].x * A2[i];
+        }
+        pin_rows(e);
+#pragma unroll
+        for (int r = 0; r < TT; ++r) {
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) e[r][i] = exp2_hw(e[r][i]);
+        }
 #pragma unroll
         for (int r = 0; r < TT; ++r) {
             float bv[kNS];
             TL::widen(bw[S][r], bv);
-            const float dl = xd[r].x;
             const float xb = xd[r].y;
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) h[i] = fmaf(exp2_hw(dl * A2[i]), h[i], xb * bv[i]);
+            for (int i = 0; i < kNS; ++i) h[i] = fmaf(e[r][i], h[i], xb * bv[i]);
             if constexpr (EMIT) {
                 float cv[kNS];
                 TL::widen(cw[S][r], cv);
@@ -325,10 +359,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
                 for (int i = 0; i < kNS; ++i) acc = fmaf(cv[i], h[i], acc);
                 s_part[S][w][r][lane] = acc;
             } else {
-                dsum += dl;
+                dsum += xd[r].x;
             }
         }
     };
+
     // one tile step: finish tile k-1, publish tile k+1, scan tile k
     // every load below is clamped to a valid row, so all of it runs unconditionally
     auto step = [&](int k, auto slot) {
