@@ -21,8 +21,8 @@
  *    bf16 is the 16-bit brain-float pattern; y is rounded once from fp32 with
  *    round-to-nearest-even.  A, Dskip and every state (h0, h_last, h) are fp32.
  *    All arithmetic is fp32.
- *  - Alignment: A, h0, h_last, h and the workspace must be 16-byte aligned;
- *    every other tensor must be aligned to its element size.
+ *  - Alignment: A, h0, h_last and h must be 16-byte aligned, the workspace
+ *    256-byte aligned; every other tensor must be aligned to its element size.
  *  - Calls are asynchronous on `stream` (NULL = the default stream): SS_OK
  *    means every kernel was enqueued.  Arguments are validated on the host,
  *    synchronously, before anything is enqueued; a rejected call enqueues
@@ -30,7 +30,7 @@
  *  - Errors: SS_ERR_INVALID_ARG (NULL required pointer, size <= 0, size
  *    overflow, misalignment, forbidden overlap), SS_ERR_UNSUPPORTED (dstate
  *    other than 16, unknown dtype), SS_ERR_WORKSPACE (workspace too small or
- *    NULL when one is needed), SS_ERR_HIP (a HIP call or launch failed; see
+ *    NULL), SS_ERR_HIP (a HIP call or launch failed; see
  *    ss_last_hip_error()).  No exceptions cross the ABI.
  */
 #ifndef SS_SCAN_H
@@ -74,16 +74,21 @@ ss_status ss_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
 
 /*
  * ss_scan_workspace_bytes -- device workspace ss_scan_fwd needs for this
- * shape and chunk request (0 when the plan has a single chunk; (size_t)-1 for
- * invalid sizes).
+ * shape and chunk request ((size_t)-1 for invalid sizes).  Always > 0.
  *
- * Workspace layout (fp32, K = n_chunks, BD = batch*dim, N = dstate), valid
- * after the call completes when K > 1:
+ * Workspace layout (fp32 words, K = n_chunks, BD = batch*dim, N = dstate),
+ * valid after the call completes:
+ *   when K > 1:
  *   [0, K*BD*N)            state slots (K, batch, dim, N): slot 0 holds the
  *                          initial state (h0, or zeros); slot c, 1 <= c < K,
  *                          holds the state right after timestep c*chunk_len-1,
  *                          i.e. the carry into chunk c.
  *   [K*BD*N, +(K-1)*BD)    sum of delta over chunk c, (K-1, batch, dim).
+ *   always, from the next multiple of 256 bytes to the end:
+ *                          an fp32 copy of B and C, per (batch row, chunk),
+ *                          regrouped in the order the scan kernels read it
+ *                          and zero-padded past each chunk's end; its
+ *                          arrangement is internal to the library.
  */
 size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                int64_t chunk_len_request);
@@ -103,7 +108,6 @@ size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64
  *   h_last      : (batch, dim, dstate)   fp32       output, state after the
  *                                                   last timestep (NULL: not written)
  *   workspace   : ss_scan_workspace_bytes(...) bytes of device memory
- *                 (may be NULL when that is 0)
  *   chunk_len_request : as for ss_scan_plan (0 = library's choice)
  *
  * y must not overlap any other tensor; h_last must not overlap any input

@@ -85,18 +85,35 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
     return true;
 }
 
-// Workspace bytes for K chunks (0 for K == 1); false on overflow.
-bool ws_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t K, int64_t* out)
+// Workspace layout for K chunks of T rows (fp32 words):
+//   K > 1: K state slots of batch*dim*dstate, then (K-1)*batch*dim delta sums;
+//   then, at the next multiple of 256 bytes, the B/C panel of
+//   batch*K*2*panel_rows(min(T, seqlen))*dstate words.
+struct WsLayout {
+    int64_t panel_offset;  // bytes
+    int64_t panel_words;
+    int64_t panel_rows;
+    int64_t total;  // bytes
+};
+
+bool ws_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t T, int64_t K, WsLayout* w)
 {
-    if (K <= 1) {
-        *out = 0;
-        return true;
+    int64_t front = 0;
+    if (K > 1) {
+        int64_t bd, slots, dsums;
+        if (!mul(batch, dim, &bd)) return false;
+        if (!mul(bd, dstate, &slots) || !mul(slots, K, &slots)) return false;
+        if (!mul(bd, K - 1, &dsums)) return false;
+        if (__builtin_add_overflow(slots, dsums, &front) || !mul(front, 4, &front)) return false;
     }
-    int64_t bd, slots, dsums, total;
-    if (!mul(batch, dim, &bd)) return false;
-    if (!mul(bd, dstate, &slots) || !mul(slots, K, &slots)) return false;
-    if (!mul(bd, K - 1, &dsums)) return false;
-    if (__builtin_add_overflow(slots, dsums, &total) || !mul(total, 4, out)) return false;
+    if (__builtin_add_overflow(front, int64_t(255), &front)) return false;
+    w->panel_offset = front & ~int64_t(255);
+    w->panel_rows = ssk::panel_rows(T < seqlen ? T : seqlen);
+    int64_t words, bytes;
+    if (!mul(batch, K, &words) || !mul(words, 2 * w->panel_rows, &words) || !mul(words, dstate, &words))
+        return false;
+    w->panel_words = words;
+    if (!mul(words, 4, &bytes) || __builtin_add_overflow(w->panel_offset, bytes, &w->total)) return false;
     return true;
 }
 
@@ -126,11 +143,12 @@ size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64
                                int64_t chunk_len_request)
 {
     Sizes s;
-    int64_t T, K, bytes;
+    int64_t T, K;
+    WsLayout wl;
     if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return static_cast<size_t>(-1);
     if (!plan(batch, seqlen, dim, chunk_len_request, &T, &K)) return static_cast<size_t>(-1);
-    if (!ws_bytes(batch, dim, dstate, K, &bytes)) return static_cast<size_t>(-1);
-    return static_cast<size_t>(bytes);
+    if (!ws_layout(batch, seqlen, dim, dstate, T, K, &wl)) return static_cast<size_t>(-1);
+    return static_cast<size_t>(wl.total);
 }
 
 ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -141,12 +159,16 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
     if (!u || !delta || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
     Sizes s;
     if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
-    int64_t T, K, need;
+    int64_t T, K;
     if (!plan(batch, seqlen, dim, chunk_len_request, &T, &K)) return SS_ERR_INVALID_ARG;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
     if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
     if (batch > kMaxGridYZ || K > kMaxGridYZ || batch * dim > INT32_MAX) return SS_ERR_UNSUPPORTED;
-    if (!ws_bytes(batch, dim, dstate, K, &need)) return SS_ERR_INVALID_ARG;
+    WsLayout wl;
+    if (!ws_layout(batch, seqlen, dim, dstate, T, K, &wl)) return SS_ERR_INVALID_ARG;
+    // the panel kernel runs one thread per word in a one-dimensional grid
+    if (ceil_div(wl.panel_words, 256) > int64_t(UINT32_MAX)) return SS_ERR_UNSUPPORTED;
+    const int64_t need = wl.total;
 
     const uintptr_t es = dtype == SS_F32 ? 4 : 2;
     int64_t chunk_bytes;
@@ -176,14 +198,12 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
         if (overlap(r_hl, r)) return SS_ERR_INVALID_ARG;
     }
 
-    if (need > 0) {
-        if (!workspace || workspace_bytes < static_cast<size_t>(need)) return SS_ERR_WORKSPACE;
-        if (!aligned(workspace, 16)) return SS_ERR_INVALID_ARG;
-        const Range r_ws = span(workspace, need);
-        for (const Range& r : inputs)
-            if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
-        if (overlap(r_ws, r_y) || overlap(r_ws, r_hl)) return SS_ERR_INVALID_ARG;
-    }
+    if (!workspace || workspace_bytes < static_cast<size_t>(need)) return SS_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SS_ERR_INVALID_ARG;
+    const Range r_ws = span(workspace, need);
+    for (const Range& r : inputs)
+        if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
+    if (overlap(r_ws, r_y) || overlap(r_ws, r_hl)) return SS_ERR_INVALID_ARG;
 
     ssk::ScanArgs a;
     a.u = u;
@@ -196,8 +216,10 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
     a.h0 = h0;
     a.y = y;
     a.h_last = h_last;
-    a.ws_state = need > 0 ? static_cast<float*>(workspace) : nullptr;
-    a.ws_dsum = need > 0 ? static_cast<float*>(workspace) + K * batch * dim * dstate : nullptr;
+    a.ws_state = K > 1 ? static_cast<float*>(workspace) : nullptr;
+    a.ws_dsum = K > 1 ? static_cast<float*>(workspace) + K * batch * dim * dstate : nullptr;
+    a.ws_panel = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.panel_offset);
+    a.panel_rows = wl.panel_rows;
     a.batch = batch;
     a.seqlen = seqlen;
     a.dim = dim;

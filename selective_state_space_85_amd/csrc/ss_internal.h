@@ -15,6 +15,25 @@ constexpr int kDState = 16;  // the state width the kernels are built for
 #endif
 constexpr int kScanWaves = SS_SCAN_WAVES;
 static_assert(kScanWaves == 2 || kScanWaves == 4 || kScanWaves == 8, "state split must divide 16");
+constexpr int kGroupStates = kDState / kScanWaves;  // state entries per wave
+
+// Rows of the sequence per scan tile (one LDS barrier per tile).
+#ifndef SS_TILE_ROWS
+#define SS_TILE_ROWS 8
+#endif
+constexpr int kTileRows = SS_TILE_ROWS;
+static_assert(kTileRows % kScanWaves == 0, "tile rows must split evenly across the waves");
+static_assert((kTileRows * kGroupStates) % 16 == 0, "a wave's tile of B (or C) is loaded 16 words at a time");
+
+// Rows of one chunk in the fp32 B/C panel: the chunk's tiles rounded up to an
+// even count (the scan loop runs tiles in pairs) plus one tile that the last
+// tile's prefetch reads.  Rows past the chunk end hold zeros.
+inline int64_t panel_rows(int64_t chunk_rows)
+{
+    int64_t tiles = (chunk_rows + kTileRows - 1) / kTileRows;
+    tiles = (tiles + 1) & ~int64_t(1);
+    return (tiles + 1) * kTileRows;
+}
 
 struct ScanArgs {
     const void* u;
@@ -29,6 +48,10 @@ struct ScanArgs {
     float* h_last;       // nullable
     float* ws_state;     // (K, batch, dim, N) state slots, nullable when K == 1
     float* ws_dsum;      // (K-1, batch, dim) per-chunk delta sums
+    // (batch, K, waves, {B, C}, panel_rows, kGroupStates) fp32 copy of B and C,
+    // regrouped so that a wave's entries of consecutive rows are contiguous
+    float* ws_panel;
+    int64_t panel_rows;
     int64_t batch, seqlen, dim;
     int64_t chunk_len, n_chunks;
 };

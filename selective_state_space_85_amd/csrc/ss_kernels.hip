@@ -124,40 +124,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), int(kRsrcWord3));
 }
 
-// Tile geometry per operand type: rows per tile, and the 32-bit words of one
-// B (or C) row that hold one wave's kNS entries.  The scalar words of two
-// tiles (current and next, B and C) must fit the scalar register file.
-template <int DT>
-struct Tile;
-// rows per tile: a multiple of the wave count, scalar words of two tiles <= 64
-#ifndef SS_TILE_ROWS_BF16
-#define SS_TILE_ROWS_BF16 8
-#endif
-template <>
-struct Tile<0> {
-    static constexpr int kRows = kGroups > 4 ? kGroups : 4;
-    static constexpr int kWaveWords = kNS;  // fp32 entries
-    static constexpr int kRowWords = N;
-    static __device__ __forceinline__ void widen(const uint32_t (&w)[kWaveWords], float (&v)[kNS])
-    {
-#pragma unroll
-        for (int i = 0; i < kNS; ++i) v[i] = __uint_as_float(w[i]);
-    }
-};
-template <>
-struct Tile<1> {
-    static constexpr int kRows = SS_TILE_ROWS_BF16;
-    static constexpr int kWaveWords = kNS / 2;  // bf16 pairs
-    static constexpr int kRowWords = N / 2;
-    static __device__ __forceinline__ void widen(const uint32_t (&w)[kWaveWords], float (&v)[kNS])
-    {
-#pragma unroll
-        for (int i = 0; i < kWaveWords; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-};
+// Sixteen 32-bit words: one scalar load of a wave's B (or C) entries for
+// 16 / kNS consecutive rows of the fp32 panel.
+typedef uint32_t Words16 __attribute__((ext_vector_type(16)));
 
 template <int V>
 using Slot = std::integral_constant<int, V>;
@@ -182,7 +151,39 @@ __device__ __forceinline__ void pin_rows(float (&v)[R][C])
 }
 
 // ---------------------------------------------------------------------------
-// Scan kernel.  grid = (ceil(dim/64), batch, chunks), block = 256 (4 waves).
+// Panel kernel: the fp32 B/C panel of every (batch row, chunk),
+//   panel[b][c][w][part][p][i] = (part ? C : B)[b, c*chunk_len + p, w*kNS + i]
+// for rows p inside the chunk and 0 for the rest of the chunk's panel_rows.
+// One thread per panel word; grid = ceil(words / 256), block = 256.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    const int64_t P = a.panel_rows;
+    const int64_t total = a.batch * a.n_chunks * kGroups * 2 * P * kNS;
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int i = int(idx % kNS);
+    int64_t rest = idx / kNS;
+    const int64_t p = rest % P;
+    rest /= P;
+    const int part = int(rest % 2);
+    rest /= 2;
+    const int g = int(rest % kGroups);
+    rest /= kGroups;
+    const int64_t c = rest % a.n_chunks;
+    const int64_t b = rest / a.n_chunks;
+    const int64_t t0 = c * a.chunk_len;
+    const int64_t len = (a.seqlen - t0 < a.chunk_len) ? a.seqlen - t0 : a.chunk_len;
+    float v = 0.0f;
+    if (p < len) v = E::load(static_cast<const T*>(part ? a.C : a.B), (b * a.seqlen + t0 + p) * N + g * kNS + i);
+    a.ws_panel[idx] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Scan kernel.  grid = (ceil(dim/64), batch, chunks), block = 64 * kGroups.
 // EMIT: start from the chunk's carry (or h0), write y and, for the last chunk,
 //       h_last.
 // !EMIT (aggregate): start from zero, write the chunk's end state into state
@@ -195,12 +196,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
     using T = typename Elem<DT>::T;
     using V = Buf<DT>;
     using Raw = typename V::Raw;
-    using TL = Tile<DT>;
-    constexpr int TT = TL::kRows;
-    constexpr int RPW = TT / kGroups;  // rows each wave widens and finishes per tile
-    static_assert(RPW * kGroups == TT, "tile rows must split evenly across the waves");
-    constexpr int WW = TL::kWaveWords;
-    constexpr int RW = TL::kRowWords;
+    constexpr int TT = kTileRows;
+    constexpr int RPW = TT / kGroups;     // rows each wave widens and finishes per tile
+    constexpr int PW = TT * kNS / 16;     // 16-word panel loads per tile and plane
 
     __shared__ float2 s_xd[2][TT][kWave];                       // (delta, delta*u) per row and channel
     __shared__ float s_part[EMIT ? 2 : 1][kGroups][TT][kWave];  // partial C.h per wave
@@ -227,11 +225,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
     const __amdgpu_buffer_rsrc_t r_dl = make_rsrc(static_cast<const T*>(a.delta) + row0, span);
     const __amdgpu_buffer_rsrc_t r_z = make_rsrc(HAS_Z ? static_cast<const T*>(a.z) + row0 : nullptr, span);
     const __amdgpu_buffer_rsrc_t r_y = make_rsrc(EMIT ? static_cast<T*>(a.y) + row0 : nullptr, span);
-    // the wave's words of the chunk's B and C rows (address-space casts need the C cast form)
-    const SS_CONST uint32_t* pB =
-        (const SS_CONST uint32_t*)(static_cast<const T*>(a.B) + (b * L + t0) * N) + w * WW;
-    const SS_CONST uint32_t* pC =
-        (const SS_CONST uint32_t*)(static_cast<const T*>(a.C) + (b * L + t0) * N) + w * WW;
+    // the wave's B and C planes of the chunk's panel (address-space casts need the C cast form)
+    const int64_t plane = a.panel_rows * kNS;
+    const SS_CONST char* pB =
+        (const SS_CONST char*)(a.ws_panel + ((b * a.n_chunks + c) * kGroups + w) * 2 * plane);
+    const SS_CONST char* pC = pB + plane * 4;
 
     const int64_t sbase = bd * N + w * kNS;  // this lane's entries in a (B, D, N) state array
     float A2[kNS];
@@ -254,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
 
     Raw rdl[2][RPW], ru[2][RPW], rz[2][RPW];  // raw rows in flight, by tile parity
     float xf[2][RPW], zf[2][RPW];             // widened u, z kept for the epilogue
-    uint32_t bw[2][TT][WW], cw[2][TT][WW];    // scalar words, by tile parity
+    Words16 bw[2][PW], cw[2][PW];             // the tile's panel words, by tile parity
 
     // row r of the chunk, clamped to the last one
     auto clamp_row = [&](int r) { return r < len ? r : len - 1; };
@@ -286,20 +284,24 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
             }
         }
     };
-    // 32-bit byte offsets from one 64-bit base: scalar loads with an SGPR offset
+    // a tile's panel rows are contiguous: 16-word scalar loads at a 32-bit
+    // byte offset from the plane's 64-bit base, no clamping (the panel holds
+    // zero rows past the chunk end and one spare tile)
     auto issue_words = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
+        const uint32_t off = uint32_t(tile) * uint32_t(TT * kNS * 4);
+        const SS_CONST Words16* qb = (const SS_CONST Words16*)(pB + off);
+        const SS_CONST Words16* qc = (const SS_CONST Words16*)(pC + off);
 #pragma unroll
-        for (int r = 0; r < TT; ++r) {
-            const uint32_t off = uint32_t(clamp_row(tile * TT + r)) * uint32_t(RW * 4);
-            const SS_CONST uint32_t* qb = (const SS_CONST uint32_t*)((const SS_CONST char*)pB + off);
-            const SS_CONST uint32_t* qc = (const SS_CONST uint32_t*)((const SS_CONST char*)pC + off);
-#pragma unroll
-            for (int q = 0; q < WW; ++q) {
-                bw[S][r][q] = qb[q];
-                if (EMIT) cw[S][r][q] = qc[q];
-            }
+        for (int q = 0; q < PW; ++q) {
+            bw[S][q] = qb[q];
+            if (EMIT) cw[S][q] = qc[q];
         }
+    };
+    // entry i of row r of a tile, from its panel words
+    auto word = [&](const Words16 (&wv)[PW], int r, int i) {
+        const int k = r * kNS + i;
+        return __uint_as_float(wv[k / 16][k % 16]);
     };
     // finish this wave's rows of a tile: sum the partials, skip, gate, store
     auto finish_rows = [&](int tile, auto slot) {
@@ -346,17 +348,13 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
         }
 #pragma unroll
         for (int r = 0; r < TT; ++r) {
-            float bv[kNS];
-            TL::widen(bw[S][r], bv);
             const float xb = xd[r].y;
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) h[i] = fmaf(e[r][i], h[i], xb * bv[i]);
+            for (int i = 0; i < kNS; ++i) h[i] = fmaf(e[r][i], h[i], xb * word(bw[S], r, i));
             if constexpr (EMIT) {
-                float cv[kNS];
-                TL::widen(cw[S][r], cv);
                 float acc = 0.0f;
 #pragma unroll
-                for (int i = 0; i < kNS; ++i) acc = fmaf(cv[i], h[i], acc);
+                for (int i = 0; i < kNS; ++i) acc = fmaf(word(cw[S], r, i), h[i], acc);
                 s_part[S][w][r][lane] = acc;
             } else {
                 dsum += xd[r].x;
@@ -530,6 +528,8 @@ template <int DT, bool HAS_D, bool HAS_Z>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
 {
     const unsigned nblk = unsigned((a.dim + kWave - 1) / kWave);
+    const int64_t words = a.batch * a.n_chunks * 2 * a.panel_rows * N;
+    panel_kernel<DT><<<dim3(unsigned((words + 255) / 256)), dim3(256), 0, s>>>(a);
     if (a.n_chunks > 1) {
         scan_kernel<DT, false, false, false>
             <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), dim3(kThreads), 0, s>>>(a);

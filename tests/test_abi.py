@@ -68,8 +68,18 @@ def test_auto_plan_invariants(lib, shape):
     bounds = [(c * T, min(c * T + T, l)) for c in range(K)]
     assert bounds[0][0] == 0 and bounds[-1][1] == l
     assert all(a1 == b0 for (_, a1), (b0, _) in zip(bounds, bounds[1:]))
-    ws = lib.ss_scan_workspace_bytes(b, l, d, n, 0)
-    assert ws == (0 if K == 1 else 4 * (K * b * d * n + (K - 1) * b * d))
+    check_workspace_size(lib.ss_scan_workspace_bytes(b, l, d, n, 0), b, l, d, n, T, K)
+
+
+def check_workspace_size(ws, b, l, d, n, T, K):
+    """The documented layout: carries and delta sums (K > 1), then from the next
+    256-byte boundary an fp32 B/C copy of every chunk, padded by at most a few
+    tiles of rows per chunk."""
+    front = 0 if K == 1 else 4 * (K * b * d * n + (K - 1) * b * d)
+    panel_min = 4 * b * K * 2 * n * min(T, l)
+    assert ws > 0
+    assert ws >= -(-front // 256) * 256 + panel_min
+    assert ws <= -(-front // 256) * 256 + panel_min + 4 * b * K * 2 * n * 64
 
 
 def test_forced_plan(lib):
@@ -149,9 +159,18 @@ def test_scan_workspace_checks(lib):
     st, T, K = plan(lib, 2, 512, 64, 16, 128)
     assert K == 4
     need = lib.ss_scan_workspace_bytes(2, 512, 64, 16, 128)
-    assert need == 4 * (4 * 2 * 64 * 16 + 3 * 2 * 64)
+    check_workspace_size(need, 2, 512, 64, 16, T, K)
     assert call_scan(lib, chunk=128, ws=None) == WORKSPACE
     assert call_scan(lib, chunk=128, ws_bytes=need - 1) == WORKSPACE
+    # a single-chunk plan needs a workspace too (the B/C copy)
+    st, T1, K1 = plan(lib, 2, 50, 64, 16, 0)
+    assert K1 == 1
+    need1 = lib.ss_scan_workspace_bytes(2, 50, 64, 16, 0)
+    check_workspace_size(need1, 2, 50, 64, 16, T1, K1)
+    assert call_scan(lib, seqlen=50, ws=None) == WORKSPACE
+    assert call_scan(lib, seqlen=50, ws_bytes=need1 - 1) == WORKSPACE
+    # workspace below 256-byte alignment
+    assert call_scan(lib, seqlen=50, ws=ctypes.c_void_p(BASE + 6 * GAP + 128)) == INVALID
 
 
 def call_step(lib, **kw):
