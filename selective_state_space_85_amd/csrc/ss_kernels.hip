@@ -280,7 +280,12 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
             s_xd[S][w * RPW + j][lane] = make_float2(dl, dl * x);
             if (EMIT) {
                 xf[S][j] = x;
-                if (HAS_Z) zf[S][j] = V::widen(rz[S][j]);
+                if (HAS_Z) {
+                    // widen z now: a raw value kept to the epilogue would outlive
+                    // its prefetch slot and force a wait on every row load in flight
+                    zf[S][j] = V::widen(rz[S][j]);
+                    __asm__ volatile("" : "+v"(zf[S][j]));
+                }
             }
         }
     };
@@ -326,9 +331,14 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
         float2 xd[TT];
 #pragma unroll
         for (int r = 0; r < TT; ++r) xd[r] = s_xd[S][r][lane];
-        // the next tile's scalar loads go out only after this tile's LDS reads
-        // have landed, so no later LDS wait has to drain them
-        __asm__ volatile("" ::"v"(xd[TT - 1].x) : "memory");
+        // the next tile's scalar loads go out only after all of this tile's LDS
+        // reads have landed (LDS and scalar loads share one counter, and scalar
+        // loads return out of order: a later LDS wait would drain them too)
+        static_assert(TT == 8, "the wait below names eight rows");
+        __asm__ volatile("" ::"v"(xd[0].x), "v"(xd[0].y), "v"(xd[1].x), "v"(xd[1].y), "v"(xd[2].x), "v"(xd[2].y),
+                         "v"(xd[3].x), "v"(xd[3].y), "v"(xd[4].x), "v"(xd[4].y), "v"(xd[5].x), "v"(xd[5].y),
+                         "v"(xd[6].x), "v"(xd[6].y), "v"(xd[7].x), "v"(xd[7].y)
+                         : "memory");
         issue_words(tile + 1, Slot<1 - S>{});
         // All delta*A products of the tile are formed before the first exp2 is
         // issued (the empty asm statements pin them in registers), so every
