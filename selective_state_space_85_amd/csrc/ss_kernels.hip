@@ -3,24 +3,28 @@
 // gate of section 3.4) and of the single-token recurrent update.
 //
 // Scan work decomposition
-//  * A workgroup of 4 waves owns 64 consecutive channels d of one batch row b
-//    (lane = channel) and one chunk of the sequence.  Wave w holds state
-//    entries n = 4w..4w+3 of every channel in registers, so B[b,t,n] and
-//    C[b,t,n] are the same for all lanes of a wave: they come in through
-//    scalar loads and are used as scalar operands.  Per element the wave
-//    issues one multiply (delta*A), one exp2, one multiply (delta*u*B), one
-//    fma (state) and one fma (C.h) -- no MFMA: nothing here is a dense
-//    contraction.
-//  * The sequence is processed in tiles of rows.  Per tile, each wave widens
-//    its share of the rows' u and delta once and publishes (delta, delta*u) in
-//    LDS for the other three waves; each wave leaves its partial C.h per row
-//    in LDS; each wave then finishes its share of rows (sum of the four
+//  * A workgroup of kGroups waves (8) owns 64 consecutive channels d of one
+//    batch row b (lane = channel) and one chunk of the sequence.  Wave w holds
+//    state entries n = kNS*w .. kNS*w+kNS-1 of every channel in registers, so
+//    B[b,t,n] and C[b,t,n] are the same for all lanes of a wave: they are
+//    scalar operands.  Per element the wave issues one multiply (delta*A), one
+//    exp2, one multiply (delta*u*B), one fma (state) and one fma (C.h) -- no
+//    MFMA: nothing here is a dense contraction.
+//  * B and C reach the waves through a panel: a pre-pass (panel_kernel) copies
+//    them to fp32 in the workspace, grouped per wave so that a wave's entries
+//    of consecutive rows are contiguous, zero-padded past the chunk end.  A
+//    tile of rows then costs one 16-word scalar load for B and one for C, with
+//    no widening or row clamping on the scalar unit.
+//  * The sequence is processed in tiles of kTileRows rows.  Per tile, each wave
+//    widens its share of the rows' u and delta once and publishes
+//    (delta, delta*u) in LDS for the other waves; each wave leaves its partial
+//    C.h per row in LDS; each wave then finishes its share of rows (sum of the
 //    partials, D skip, silu(z) gate, rounding, store).  LDS buffers alternate
 //    between even and odd tiles, so one barrier per tile suffices.
-//  * Prefetch: u/delta/z rows two tiles ahead (raw buffer loads, the channel
+//  * Prefetch: u/delta/z rows three tiles ahead (raw buffer loads, the channel
 //    as vector offset and the row as scalar offset, so stepping in t costs no
 //    vector instruction); the wave's B/C words one tile ahead, issued right
-//    after the tile's LDS reads so that no LDS wait has to drain them.
+//    after the tile's LDS reads have landed so that no LDS wait drains them.
 //  * The sequence can be cut into chunks (LTI chapter 3.1, section 3.1.5.2:
 //    the recurrence is a scan over an associative operator).  For K > 1:
 //      1. scan_kernel<aggregate> runs chunks 0..K-2 from a zero state and
