@@ -5,7 +5,9 @@ import this package.  The library path never does.
 
 * ``scan`` / ``step`` call the plain fp64 C loop in ``ss_oracle.c``
   (Mamba walk-through section 3.3 ``selective_scan`` plus the block's D skip and
-  silu(z) gate, section 3.4).
+  silu(z) gate, section 3.4).  Options: ``delta_bias`` / ``delta_softplus``
+  (step size softplus(delta + bias[d]), LTI chapter section 3.1.4.2) and ``zoh``
+  (zero-order-hold Bbar of the walk-through's section 2.2).
 * ``twin_scan`` (in ``twin.py``) is an independent NumPy statement of the same
   definition, used only to cross-check the C loop on tiny shapes.
 
@@ -27,6 +29,7 @@ _SRC = os.path.join(_HERE, "ss_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
+SOFTPLUS, ZOH = 1, 2  # option flags of oracle_scan / oracle_step
 _lib = None
 
 
@@ -47,10 +50,10 @@ class OracleLib:
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
         vp, i64, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        lib.oracle_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, i64,
+        lib.oracle_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, i64,
                                     vp, i64, vp, vp, vp, i64, vp, ip]
         lib.oracle_scan.restype = ctypes.c_int
-        lib.oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, vp]
+        lib.oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, vp, i64, vp]
         lib.oracle_step.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -89,12 +92,18 @@ def _c(a: Optional[np.ndarray], dt=None) -> Optional[np.ndarray]:
     return np.ascontiguousarray(a if dt is None else a.astype(dt, copy=False))
 
 
+def _flags(delta_softplus: bool, zoh: bool) -> int:
+    return (SOFTPLUS if delta_softplus else 0) | (ZOH if zoh else 0)
+
+
 def scan(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
          D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
          h0: Optional[np.ndarray] = None, lanes: Optional[Sequence[int]] = None,
-         record_t: Optional[Sequence[int]] = None, threads: int = 1, _lib=None) -> Dict[str, np.ndarray]:
+         record_t: Optional[Sequence[int]] = None, threads: int = 1, *,
+         delta_bias: Optional[np.ndarray] = None, delta_softplus: bool = False, zoh: bool = False,
+         _lib=None) -> Dict[str, np.ndarray]:
     """fp64 scan.  u, delta, z: (B,L,D); B, C: (B,L,N) in float32 or bf16 bits (uint16);
-    A (D,N) and D (D,) float32; h0 (B,D,N) any float (widened to double).
+    A (D,N), D (D,) and delta_bias (D,) float32; h0 (B,D,N) any float (widened to double).
 
     Returns ``y`` (B,L,D) -- or (n_lanes, L) when ``lanes`` (flat b*D+d) is given --
     ``h_last`` (B,D,N) / (n_lanes, N), and ``h_rec`` (n_lanes, len(record_t), N) with the
@@ -113,6 +122,7 @@ def scan(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.n
     u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
     A = _c(A, np.float32)
     D = _c(D, np.float32)
+    bias = _c(delta_bias, np.float32)
     h0 = _c(h0, np.float64)
     lane_arr = None if lanes is None else np.ascontiguousarray(np.asarray(lanes, dtype=np.int64))
     n_lanes = batch * dim if lane_arr is None else lane_arr.size
@@ -122,7 +132,7 @@ def scan(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.n
     h_last = np.empty((n_lanes, dstate), dtype=np.float64)
     h_rec = np.empty((n_lanes, max(n_rec, 1), dstate), dtype=np.float64)
     rc = lib.oracle_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                         dt, batch, seqlen, dim, dstate, _ptr(lane_arr), n_lanes,
+                         _ptr(bias), _flags(delta_softplus, zoh), dt, batch, seqlen, dim, dstate, _ptr(lane_arr), n_lanes,
                          _ptr(y), _ptr(h_last), _ptr(rec), n_rec,
                          _ptr(h_rec) if rec is not None else None, int(threads))
     if rc != 0:
@@ -139,7 +149,8 @@ def scan(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.n
 
 def step(h: np.ndarray, u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray,
          C: np.ndarray, D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
-         lanes: Optional[Sequence[int]] = None, _lib=None) -> np.ndarray:
+         lanes: Optional[Sequence[int]] = None, *, delta_bias: Optional[np.ndarray] = None,
+         delta_softplus: bool = False, zoh: bool = False, _lib=None) -> np.ndarray:
     """One recurrent token.  h: float64 (B,D,N), or (n_lanes, N) with ``lanes``; updated
     in place.  u, delta, z: (B,D); B, C: (B,N).  Returns y float64 (B,D) / (n_lanes,)."""
     lib = _lib or _load()
@@ -151,13 +162,14 @@ def step(h: np.ndarray, u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.n
     u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
     A = _c(A, np.float32)
     D = _c(D, np.float32)
+    bias = _c(delta_bias, np.float32)
     lane_arr = None if lanes is None else np.ascontiguousarray(np.asarray(lanes, dtype=np.int64))
     n_lanes = batch * dim if lane_arr is None else lane_arr.size
     if h.size != n_lanes * dstate:
         raise ValueError("h has %d values, expected %d" % (h.size, n_lanes * dstate))
     y = np.empty(n_lanes, dtype=np.float64)
     rc = lib.oracle_step(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                         dt, batch, dim, dstate, _ptr(lane_arr), n_lanes, _ptr(y))
+                         _ptr(bias), _flags(delta_softplus, zoh), dt, batch, dim, dstate, _ptr(lane_arr), n_lanes, _ptr(y))
     if rc != 0:
         raise ValueError("oracle_step rejected its arguments")
     return y.reshape(batch, dim) if lane_arr is None else y

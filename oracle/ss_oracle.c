@@ -19,11 +19,22 @@
  *       y *= z / (1 + exp(-z)),  z = Z[b,t,d]  (if Z: silu gate)
  *       out[b, t, d] = y
  *
+ * Two options change how delta and Bbar are formed (flags):
+ *  - ORACLE_SOFTPLUS, with an optional per-channel delta_bias: the step size
+ *    is softplus(delta + delta_bias[d]), softplus(v) = log(1 + e^v) (LTI
+ *    chapter, section 3.1.4.2: delta_t = Softplus(Parameter + projection of
+ *    x_t), the Parameter being one value per channel).  A bias without the
+ *    flag is added as is.
+ *  - ORACLE_ZOH: Bbar = (delta*A)^-1 (exp(delta*A) - 1) * delta*B, the
+ *    zero-order-hold form of the walk-through's section 2.2, elementwise for
+ *    the diagonal A; at delta*A = 0 it takes its limit delta*B.
+ *
  * Readings of the pages taken here (each also listed in the design notes):
  *  - Abar = exp(delta*A) (zero-order hold, section 2.2), Bbar = delta*B (the
- *    Euler form the section 3.3 code uses), so the input term is delta*B*x.
+ *    Euler form the section 3.3 code uses) unless ORACLE_ZOH, so the input
+ *    term is delta*B*x.
  *  - y reads the state after the update at t.
- *  - delta arrives already positive; no softplus is applied here.
+ *  - delta arrives already positive unless ORACLE_SOFTPLUS.
  *  - A is a fixed (D, N) array; only delta, B and C vary with t.
  *  - D skip is added before the gate.
  *
@@ -41,6 +52,8 @@
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
 #define ORACLE_MAX_N 1024
+#define ORACLE_SOFTPLUS 1
+#define ORACLE_ZOH 2
 
 static double widen(const void* p, int64_t i, int dtype)
 {
@@ -53,6 +66,30 @@ static double widen(const void* p, int64_t i, int dtype)
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* log(1 + e^v), written so that neither branch overflows or cancels */
+static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+
+/* the step size of lane d at one timestep: raw delta, plus the channel's
+ * bias, through softplus when asked */
+static double step_size(double raw, const float* delta_bias, int64_t d, int flags)
+{
+    double v = raw + (delta_bias ? (double)delta_bias[d] : 0.0);
+    return (flags & ORACLE_SOFTPLUS) ? softplus(v) : v;
+}
+
+/* Bbar[n] * x for step size delta, A[d,n] = a, B[b,t,n] = bm */
+static double input_term(double delta, double a, double bm, double x, int flags)
+{
+    double b_bar = delta * bm; /* Euler */
+    if (flags & ORACLE_ZOH) {
+        const double da = delta * a;
+        /* (delta*A)^-1 (exp(delta*A) - 1), continuous at delta*A = 0 */
+        const double phi = da == 0.0 ? 1.0 : expm1(da) / da;
+        b_bar = phi * (delta * bm);
+    }
+    return b_bar * x;
+}
+
 typedef struct {
     const void* u;
     const void* delta;
@@ -62,6 +99,8 @@ typedef struct {
     const float* Dskip;
     const void* z;
     const double* h0;
+    const float* delta_bias;
+    int flags;
     int dtype;
     int64_t batch, seqlen, dim, dstate;
     const int64_t* lanes;
@@ -87,12 +126,12 @@ static void scan_lane(const scan_job* j, int64_t li)
     for (int64_t t = 0; t < L; ++t) {
         const int64_t row = (b * L + t) * D + d;  /* (B, L, D) row-major */
         const int64_t srow = (b * L + t) * N;     /* (B, L, N) row-major */
-        const double delta = widen(j->delta, row, j->dtype);
+        const double delta = step_size(widen(j->delta, row, j->dtype), j->delta_bias, d, j->flags);
         const double x = widen(j->u, row, j->dtype);
         for (int64_t n = 0; n < N; ++n) {
-            const double a_bar = exp(delta * (double)j->A[d * N + n]);
-            const double b_bar = delta * widen(j->B, srow + n, j->dtype);
-            h[n] = a_bar * h[n] + b_bar * x;
+            const double a = (double)j->A[d * N + n];
+            const double a_bar = exp(delta * a);
+            h[n] = a_bar * h[n] + input_term(delta, a, widen(j->B, srow + n, j->dtype), x, j->flags);
         }
         double y = 0.0;
         for (int64_t n = 0; n < N; ++n) y += h[n] * widen(j->C, srow + n, j->dtype);
@@ -130,7 +169,8 @@ static void* scan_worker(void* arg)
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_scan(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                const float* Dskip, const void* z, const double* h0, int dtype,
+                const float* Dskip, const void* z, const double* h0,
+                const float* delta_bias, int flags, int dtype,
                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                 const int64_t* lanes, int64_t n_lanes,
                 double* y_out, double* h_last,
@@ -139,13 +179,14 @@ int oracle_scan(const void* u, const void* delta, const float* A, const void* B,
     if (!u || !delta || !A || !B || !C) return -1;
     if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > ORACLE_MAX_N) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (flags & ~(ORACLE_SOFTPLUS | ORACLE_ZOH)) return -1;
     if (!lanes) n_lanes = batch * dim;
     for (int64_t i = 0; lanes && i < n_lanes; ++i)
         if (lanes[i] < 0 || lanes[i] >= batch * dim) return -1;
     for (int64_t k = 1; rec_t && k < n_rec; ++k)
         if (rec_t[k] <= rec_t[k - 1]) return -1;
 
-    scan_job job = {u, delta, A, B, C, Dskip, z, h0, dtype, batch, seqlen, dim, dstate,
+    scan_job job = {u, delta, A, B, C, Dskip, z, h0, delta_bias, flags, dtype, batch, seqlen, dim, dstate,
                     lanes, n_lanes, y_out, h_last, rec_t, rec_t ? n_rec : 0, h_rec};
 
     if (nthreads <= 1 || n_lanes < 2) {
@@ -179,26 +220,28 @@ int oracle_scan(const void* u, const void* delta, const float* A, const void* B,
  * (B, D), B and C are (B, N), all in `dtype`; y_out (n_lanes) double.
  */
 int oracle_step(double* h, const void* u, const void* delta, const float* A, const void* B,
-                const void* C, const float* Dskip, const void* z, int dtype,
+                const void* C, const float* Dskip, const void* z,
+                const float* delta_bias, int flags, int dtype,
                 int64_t batch, int64_t dim, int64_t dstate,
                 const int64_t* lanes, int64_t n_lanes, double* y_out)
 {
     if (!h || !u || !delta || !A || !B || !C) return -1;
     if (batch <= 0 || dim <= 0 || dstate <= 0) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (flags & ~(ORACLE_SOFTPLUS | ORACLE_ZOH)) return -1;
     if (!lanes) n_lanes = batch * dim;
     for (int64_t li = 0; li < n_lanes; ++li) {
         const int64_t bd = lanes ? lanes[li] : li;
         if (bd < 0 || bd >= batch * dim) return -1;
         const int64_t b = bd / dim, d = bd % dim;
-        const double delta_v = widen(delta, bd, dtype);
+        const double delta_v = step_size(widen(delta, bd, dtype), delta_bias, d, flags);
         const double x = widen(u, bd, dtype);
         double* hl = &h[li * dstate];
         double y = 0.0;
         for (int64_t n = 0; n < dstate; ++n) {
-            const double a_bar = exp(delta_v * (double)A[d * dstate + n]);
-            const double b_bar = delta_v * widen(B, b * dstate + n, dtype);
-            hl[n] = a_bar * hl[n] + b_bar * x;
+            const double a = (double)A[d * dstate + n];
+            const double a_bar = exp(delta_v * a);
+            hl[n] = a_bar * hl[n] + input_term(delta_v, a, widen(B, b * dstate + n, dtype), x, flags);
         }
         for (int64_t n = 0; n < dstate; ++n) y += hl[n] * widen(C, b * dstate + n, dtype);
         if (Dskip) y += (double)Dskip[d] * x;

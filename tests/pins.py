@@ -15,6 +15,12 @@ Sources on the pages:
   parameters y = x * Kbar, Kbar = (C Bbar, C Abar Bbar, ..., C Abar^{L-1} Bbar).
 * LTI chapter, section 0.4.2: delta -> 0 keeps the state (Abar -> I), large
   delta with negative A resets it (Abar -> 0).
+* LTI chapter, section 3.1.4.2: delta_t = Softplus(per-channel parameter +
+  projection of x_t), softplus(v) = log(1 + e^v).
+* Mamba walk-through, section 2.2: zero-order hold,
+  Bbar = (delta A)^-1 (exp(delta A) - I) delta B; for a diagonal A it is exact
+  for inputs held constant over each step, so with u = 1 and a constant B the
+  state equals the continuous-time step response at every sample time.
 """
 from __future__ import annotations
 
@@ -344,8 +350,125 @@ def pin_twin(orc):
         y, h = twin_scan(**c)
         _close(out["y"], y, 1e-13, "twin y %s" % (shp,))
         _close(out["h_last"], h, 1e-13, "twin h %s" % (shp,))
+    # the options, against the twin's library routines (numpy logaddexp, scipy exprel)
+    for i, (softplus, zoh) in enumerate(((True, False), (False, True), (True, True))):
+        c = _rand_case(rng, 2, 21, 5, 16, dtype="bf16" if i == 2 else "f32", has_D=True, has_z=True,
+                       has_h0=True)
+        raw = rng.normal(-1.0, 1.5, c["u"].shape).astype(np.float32)
+        c["delta"] = f32_to_bf16_bits(raw) if c["u"].dtype == np.uint16 else raw
+        if not softplus:
+            c["delta"] = np.abs(c["delta"]) if c["u"].dtype != np.uint16 else c["delta"] & np.uint16(0x7FFF)
+        bias = rng.normal(0.0, 0.5, c["u"].shape[2]).astype(np.float32)
+        opts = dict(delta_bias=bias if softplus else None, delta_softplus=softplus, zoh=zoh)
+        out = orc.scan(**c, **opts)
+        y, h = twin_scan(**c, **opts)
+        _close(out["y"], y, 1e-12, "twin y, softplus=%s zoh=%s" % (softplus, zoh))
+        _close(out["h_last"], h, 1e-12, "twin h, softplus=%s zoh=%s" % (softplus, zoh))
+
+
+# ---------------------------------------------------------------------------
+# 12. zero-order hold = exact continuous-time step response
+#     h' = A h + B u with u = 1 and B constant: h(T) = e^{AT} h0 + (B/A)(e^{AT} - 1),
+#     T = delta_0 + ... + delta_t, whatever the step sizes; A = 0 integrates: h0 + B T
+# ---------------------------------------------------------------------------
+def pin_zoh_step_response(orc):
+    rng = np.random.default_rng(23)
+    nb, nl, nd, nn = 2, 40, 3, 4
+    A = -rng.uniform(0.2, 3.0, (nd, nn)).astype(np.float32)
+    A[0, 0] = 0.0
+    A[1, 1] = 0.3  # a growing mode obeys the same formula
+    delta = rng.uniform(0.01, 0.8, (nb, nl, nd)).astype(np.float32)
+    u = np.ones((nb, nl, nd), dtype=np.float32)
+    beta = rng.standard_normal((nb, nn)).astype(np.float32)
+    Bm = np.repeat(beta[:, None, :], nl, axis=1)
+    Cm = rng.standard_normal((nb, nl, nn)).astype(np.float32)
+    h0 = rng.standard_normal((nb, nd, nn)).astype(np.float32)
+    out = orc.scan(u, delta, A, Bm, Cm, h0=h0, zoh=True)
+    T = np.cumsum(delta.astype(np.float64), axis=1)[..., None]           # (B, L, D, 1)
+    a = A.astype(np.float64)[None, None]                                  # (1, 1, D, N)
+    at = a * T
+    safe = np.where(a == 0.0, 1.0, a)
+    growth = np.where(a == 0.0, T, np.expm1(at) / safe)                   # (e^{AT} - 1)/A, or T
+    h = np.exp(at) * h0.astype(np.float64)[:, None] + beta.astype(np.float64)[:, None, None, :] * growth
+    y = np.einsum("bldn,bln->bld", h, Cm.astype(np.float64))
+    _close(out["y"], y, 1e-11, "ZOH step response y")
+    _close(out["h_last"], h[:, -1], 1e-11, "ZOH step response h_last")
+
+
+# ---------------------------------------------------------------------------
+# 13. zero-order hold, one step from zero: the input term is exprel(delta A)
+#     times Euler's (scipy's exprel(x) = (e^x - 1)/x); a huge step with A < 0
+#     lands on the equilibrium -B u / A; A = 0 is Euler bit for bit
+# ---------------------------------------------------------------------------
+def pin_zoh_limits(orc):
+    import scipy.special
+
+    rng = np.random.default_rng(24)
+    c = _rand_case(rng, 2, 1, 6, 16)
+    zoh = orc.scan(**c, zoh=True)["h_last"]
+    euler = orc.scan(**c)["h_last"]
+    da = _f64(c["delta"])[:, 0, :, None] * c["A"].astype(np.float64)[None]
+    _close(zoh, scipy.special.exprel(da) * euler, 1e-14, "ZOH / Euler = exprel(delta A)")
+
+    c["delta"] = np.full_like(c["delta"], 1.0e4)
+    c["h0"] = rng.standard_normal((2, 6, 16)).astype(np.float32)
+    big = orc.scan(**c, zoh=True)["h_last"]
+    bu = _f64(c["B"])[:, 0, None, :] * _f64(c["u"])[:, 0, :, None]
+    _close(big, -bu / c["A"].astype(np.float64)[None], 1e-14, "ZOH huge step -> -B u / A")
+
+    c = _rand_case(rng, 2, 9, 4, 8, has_h0=True)
+    c["A"] = np.zeros_like(c["A"])
+    a0 = orc.scan(**c, zoh=True)
+    e0 = orc.scan(**c)
+    assert np.array_equal(a0["y"], e0["y"]) and np.array_equal(a0["h_last"], e0["h_last"]), "A = 0: ZOH is Euler"
+
+
+# ---------------------------------------------------------------------------
+# 14. step size softplus(delta + bias[d]), softplus(v) = log(1 + e^v):
+#     softplus(0) = ln 2 and 2^A = e^{ln2 A}; a per-channel bias; no overflow
+#     at +-1000; a bias without softplus is a plain shift
+# ---------------------------------------------------------------------------
+def pin_softplus_bias(orc):
+    rng = np.random.default_rng(25)
+    c = _rand_case(rng, 2, 1, 5, 16, has_h0=True)
+    h0 = c["h0"].astype(np.float64)
+    bu = _f64(c["B"])[:, 0, None, :] * _f64(c["u"])[:, 0, :, None]      # (B, D, N)
+    A = c["A"].astype(np.float64)[None]
+
+    c["delta"] = np.zeros_like(c["delta"])
+    got = orc.scan(**c, delta_softplus=True)["h_last"]
+    _close(got, np.exp2(A) * h0 + math.log(2.0) * bu, 1e-14, "softplus(0) = ln 2")
+
+    bias = np.array([-3.0, -0.5, 0.0, 0.75, 4.0], dtype=np.float32)
+    got = orc.scan(**c, delta_softplus=True, delta_bias=bias)["h_last"]
+    dl = np.logaddexp(0.0, bias.astype(np.float64))[None, :, None]         # log(1 + e^b) per channel
+    _close(got, np.exp(dl * A) * h0 + dl * bu, 1e-14, "softplus(bias[d])")
+
+    c["delta"] = np.full_like(c["delta"], 1000.0)
+    got = orc.scan(**c, delta_softplus=True)["h_last"]
+    _close(got, 1000.0 * bu, 1e-14, "softplus(1000) = 1000, e^{1000 A} = 0")
+    c["delta"] = np.full_like(c["delta"], -1000.0)
+    got = orc.scan(**c, delta_softplus=True)
+    assert np.array_equal(got["h_last"], h0), "softplus(-1000) = 0 keeps the state"
+
+    c["delta"] = np.full_like(c["delta"], 0.25)
+    shift = np.full(5, 0.5, dtype=np.float32)
+    got = orc.scan(**c, delta_bias=shift)["h_last"]
+    _close(got, np.exp(0.75 * A) * h0 + 0.75 * bu, 1e-14, "bias without softplus")
+
+    # the recurrent step takes the same options
+    st = _rand_case(rng, 3, 1, 4, 16, has_h0=True)
+    bias4 = rng.normal(0.0, 1.0, 4).astype(np.float32)
+    for opts in (dict(delta_softplus=True, delta_bias=bias4), dict(zoh=True),
+                 dict(delta_softplus=True, zoh=True)):
+        h = st["h0"].astype(np.float64).copy()
+        y = orc.step(h, st["u"][:, 0], st["delta"][:, 0], st["A"], st["B"][:, 0], st["C"][:, 0], **opts)
+        ref = orc.scan(**st, **opts)
+        _close(y, ref["y"][:, 0, :], 1e-15, "step == one scan step %s" % sorted(opts))
+        _close(h, ref["h_last"], 1e-15, "step state %s" % sorted(opts))
 
 
 ALL_PINS = [pin_hand_worked, pin_single_step_closed_form, pin_lti_convolution, pin_zero_input,
             pin_brute_force, pin_geometric, pin_delta_limits, pin_chaining,
-            pin_causality_linearity, pin_bookkeeping, pin_twin]
+            pin_causality_linearity, pin_bookkeeping, pin_twin, pin_zoh_step_response,
+            pin_zoh_limits, pin_softplus_bias]

@@ -16,14 +16,13 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
 
 # (name, exact snippet of the oracle source, replacement)
 MUTANTS = [
-    ("input term drops x", "h[n] = a_bar * h[n] + b_bar * x;", "h[n] = a_bar * h[n] + b_bar;"),
-    ("sign of the exponent", "exp(delta * (double)j->A[d * N + n])", "exp(-delta * (double)j->A[d * N + n])"),
+    ("input term drops x", "return b_bar * x;", "return b_bar;"),
+    ("sign of the exponent", "const double a_bar = exp(delta * a);", "const double a_bar = exp(-delta * a);"),
     ("A transposed", "(double)j->A[d * N + n]", "(double)j->A[n * D + d]"),
     ("C read from B", "widen(j->C, srow + n, j->dtype)", "widen(j->B, srow + n, j->dtype)"),
-    ("B one step late", "const double b_bar = delta * widen(j->B, srow + n, j->dtype);",
-     "const double b_bar = delta * widen(j->B, (t > 0 ? srow - N : srow) + n, j->dtype);"),
-    ("Bbar without delta", "const double b_bar = delta * widen(j->B, srow + n, j->dtype);",
-     "const double b_bar = widen(j->B, srow + n, j->dtype);"),
+    ("B one step late", "input_term(delta, a, widen(j->B, srow + n, j->dtype), x, j->flags)",
+     "input_term(delta, a, widen(j->B, (t > 0 ? srow - N : srow) + n, j->dtype), x, j->flags)"),
+    ("Bbar without delta", "double b_bar = delta * bm; /* Euler */", "double b_bar = bm; /* Euler */"),
     ("D skip without x", "y += (double)j->Dskip[d] * x;", "y += (double)j->Dskip[d];"),
     ("sigmoid gate instead of silu", "static double silu(double z) { return z / (1.0 + exp(-z)); }",
      "static double silu(double z) { return 1.0 / (1.0 + exp(-z)); }"),
@@ -31,14 +30,26 @@ MUTANTS = [
     ("lane index swapped", "const int64_t b = bd / D, d = bd % D;",
      "const int64_t b = bd % j->batch, d = bd / j->batch;"),
     ("y from the pre-update state",
-     "            h[n] = a_bar * h[n] + b_bar * x;\n        }\n        double y = 0.0;\n"
+     "            h[n] = a_bar * h[n] + input_term(delta, a, widen(j->B, srow + n, j->dtype), x, j->flags);\n"
+     "        }\n        double y = 0.0;\n"
      "        for (int64_t n = 0; n < N; ++n) y += h[n] * widen(j->C, srow + n, j->dtype);",
-     "            (void)0;\n        }\n        double y = 0.0;\n"
+     "            (void)a_bar;\n        }\n        double y = 0.0;\n"
      "        for (int64_t n = 0; n < N; ++n) y += h[n] * widen(j->C, srow + n, j->dtype);\n"
      "        for (int64_t n = 0; n < N; ++n) h[n] = exp(delta * (double)j->A[d * N + n]) * h[n]"
-     " + delta * widen(j->B, srow + n, j->dtype) * x;"),
-    ("step forgets the decay", "hl[n] = a_bar * hl[n] + b_bar * x;", "hl[n] = hl[n] + b_bar * x;"),
+     " + input_term(delta, (double)j->A[d * N + n], widen(j->B, srow + n, j->dtype), x, j->flags);"),
+    ("step forgets the decay", "hl[n] = a_bar * hl[n] + input_term(", "hl[n] = hl[n] + input_term("),
     ("state recorded one step late", "j->rec_t[next_rec] == t)", "j->rec_t[next_rec] == t - 1)"),
+    # the delta / Bbar options
+    ("ZOH ignored", "if (flags & ORACLE_ZOH) {", "if (0) {"),
+    ("ZOH with the exponent's sign flipped", "expm1(da) / da;", "expm1(-da) / da;"),
+    ("ZOH as a backward difference", "expm1(da) / da;", "-expm1(-da) / da;"),
+    ("ZOH drops delta", "b_bar = phi * (delta * bm);", "b_bar = phi * bm;"),
+    ("softplus drops its linear part", "return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
+     "return v > 0.0 ? log1p(exp(-v)) : log1p(exp(v));"),
+    ("softplus is exp", "return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));", "return exp(v);"),
+    ("bias subtracted", "double v = raw + (delta_bias", "double v = raw - (delta_bias"),
+    ("bias of channel 0 everywhere", "(double)delta_bias[d]", "(double)delta_bias[0]"),
+    ("softplus always on", "return (flags & ORACLE_SOFTPLUS) ? softplus(v) : v;", "return softplus(v);"),
 ]
 
 
