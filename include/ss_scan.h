@@ -56,6 +56,23 @@ typedef enum {
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
 /*
+ * Option bits of ss_scan_fwd_ex / ss_step_ex (0 = the plain ss_scan_fwd /
+ * ss_step behaviour):
+ *  SS_DELTA_SOFTPLUS  the step size is softplus(delta + delta_bias[d]),
+ *                     softplus(v) = log(1 + e^v) (LTI chapter, section
+ *                     3.1.4.2: softplus of a per-channel parameter plus a
+ *                     projection of the input).  Without it a given
+ *                     delta_bias is added as is.
+ *  SS_B_ZOH           the zero-order-hold input term of the walk-through's
+ *                     section 2.2, Bbar = (delta*A)^-1 (exp(delta*A) - 1) *
+ *                     delta*B, elementwise for the diagonal A and equal to
+ *                     delta*B where delta*A = 0; instead of the Euler term
+ *                     delta*B.
+ * Unknown bits return SS_ERR_UNSUPPORTED.
+ */
+typedef enum { SS_DELTA_SOFTPLUS = 1, SS_B_ZOH = 2 } ss_option;
+
+/*
  * ss_scan_plan -- how ss_scan_fwd splits the sequence axis.
  *
  * The scan is cut into n_chunks = ceil(seqlen / chunk_len) chunks; chunk c
@@ -122,10 +139,26 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
                       int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
 
 /*
+ * ss_scan_fwd_ex -- ss_scan_fwd with the step-size and input-term options:
+ *   delta_bias : (dim,) fp32, 4-byte aligned, or NULL (no bias); an input, so
+ *                y and h_last must not overlap it
+ *   options    : SS_DELTA_SOFTPLUS and/or SS_B_ZOH (see ss_option)
+ * Every other argument, the validation and the errors are as for ss_scan_fwd,
+ * which is ss_scan_fwd_ex with delta_bias = NULL and options = 0.
+ */
+ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* Dskip, const void* z, const float* h0,
+                         const float* delta_bias, uint32_t options,
+                         void* y, float* h_last,
+                         void* workspace, size_t workspace_bytes,
+                         int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
+
+/*
  * ss_step -- one token of the recurrent (constant-state) mode: the walk-
  * through's section 6 (O(1) state per generated token) and the interactive
- * demo page ("only h survives between steps").  The same update as one
- * timestep of ss_scan_fwd, applied in place to h:
+ * demo page (the state is all that is carried from one token to the next).
+ * The same update as one timestep of ss_scan_fwd, applied in place to h:
  *
  *   h     : (batch, dim, dstate) fp32, read and overwritten
  *   u, delta, z : (batch, dim)    dtype   (z NULL: no gate)
@@ -139,6 +172,17 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
 ss_status ss_step(float* h, const void* u, const void* delta, const float* A, const void* B,
                   const void* C, const float* Dskip, const void* z, void* y,
                   int64_t batch, int64_t dim, int64_t dstate, ss_dtype dtype, hipStream_t stream);
+
+/*
+ * ss_step_ex -- ss_step with delta_bias ((dim,) fp32 or NULL) and the options
+ * of ss_scan_fwd_ex; a token of ss_step_ex matches one timestep of
+ * ss_scan_fwd_ex with the same options.  ss_step is ss_step_ex with
+ * delta_bias = NULL and options = 0.
+ */
+ss_status ss_step_ex(float* h, const void* u, const void* delta, const float* A, const void* B,
+                     const void* C, const float* Dskip, const void* z,
+                     const float* delta_bias, uint32_t options, void* y,
+                     int64_t batch, int64_t dim, int64_t dstate, ss_dtype dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* ss_status_string(ss_status s);

@@ -215,8 +215,9 @@ int oracle_scan(const void* u, const void* delta, const float* A, const void* B,
 
 /*
  * oracle_step: one token of the recurrent mode (the walk-through's O(1)-state
- * inference, section 6; "only h survives between steps" on the interactive
- * demo page).  h (n_lanes, N) double is read and overwritten; u, delta, z are
+ * inference, section 6; on the interactive demo page the state is all that
+ * is carried from one token to the next).  h (n_lanes, N) double is read and
+ * overwritten; u, delta, z are
  * (B, D), B and C are (B, N), all in `dtype`; y_out (n_lanes) double.
  */
 int oracle_step(double* h, const void* u, const void* delta, const float* A, const void* B,

@@ -13,8 +13,9 @@ SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE, SS_ERR_HIP = ra
 SS_F32, SS_BF16 = 0, 1
 
 # Every function the header declares.
-EXPORTS = ("ss_scan_plan", "ss_scan_workspace_bytes", "ss_scan_fwd", "ss_step",
-           "ss_status_string", "ss_last_hip_error")
+EXPORTS = ("ss_scan_plan", "ss_scan_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_step",
+           "ss_step_ex", "ss_status_string", "ss_last_hip_error")
+SS_DELTA_SOFTPLUS, SS_B_ZOH = 1, 2  # ss_option bits
 
 _lib = None
 
@@ -48,8 +49,14 @@ def load() -> ctypes.CDLL:
     lib.ss_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                 i64, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.ss_scan_fwd.restype = ctypes.c_int
+    lib.ss_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp, sz,
+                                   i64, i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.ss_scan_fwd_ex.restype = ctypes.c_int
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.ss_step.restype = ctypes.c_int
+    lib.ss_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, i64, i64, i64,
+                               ctypes.c_int, vp]
+    lib.ss_step_ex.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_last_hip_error.argtypes = []

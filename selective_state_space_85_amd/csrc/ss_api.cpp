@@ -156,6 +156,16 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
                       void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
                       int64_t dstate, int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream)
 {
+    return ss_scan_fwd_ex(u, delta, A, B, C, Dskip, z, h0, nullptr, 0u, y, h_last, workspace, workspace_bytes,
+                          batch, seqlen, dim, dstate, chunk_len_request, dtype, stream);
+}
+
+ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                         uint32_t options, void* y, float* h_last, void* workspace, size_t workspace_bytes,
+                         int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t chunk_len_request,
+                         ss_dtype dtype, hipStream_t stream)
+{
     if (!u || !delta || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
     Sizes s;
     if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
@@ -163,6 +173,7 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
     if (!plan(batch, seqlen, dim, chunk_len_request, &T, &K)) return SS_ERR_INVALID_ARG;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
     if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
+    if (options & ~ssk::kOptAll) return SS_ERR_UNSUPPORTED;
     if (batch > kMaxGridYZ || K > kMaxGridYZ || batch * dim > INT32_MAX) return SS_ERR_UNSUPPORTED;
     WsLayout wl;
     if (!ws_layout(batch, seqlen, dim, dstate, T, K, &wl)) return SS_ERR_INVALID_ARG;
@@ -182,19 +193,21 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
     for (const void* p : vec_ptrs)
         if (p && !aligned(p, 16)) return SS_ERR_INVALID_ARG;
     if (Dskip && !aligned(Dskip, 4)) return SS_ERR_INVALID_ARG;
+    if (delta_bias && !aligned(delta_bias, 4)) return SS_ERR_INVALID_ARG;
 
     const int64_t e = static_cast<int64_t>(es);
     const Range r_u = span(u, s.rows * e), r_dl = span(delta, s.rows * e), r_z = span(z, s.rows * e);
     const Range r_B = span(B, s.srows * e), r_C = span(C, s.srows * e);
-    const Range r_A = span(A, s.an * 4), r_D = span(Dskip, dim * 4);
+    const Range r_A = span(A, s.an * 4), r_D = span(Dskip, dim * 4), r_bias = span(delta_bias, dim * 4);
     const Range r_h0 = span(h0, s.states * 4), r_hl = span(h_last, s.states * 4);
     const Range r_y = span(y, s.rows * e);
-    const Range inputs[] = {r_u, r_dl, r_z, r_B, r_C, r_A, r_D, r_h0};
+    const Range inputs[] = {r_u, r_dl, r_z, r_B, r_C, r_A, r_D, r_bias, r_h0};
+    constexpr int kH0 = 8;  // index of h0 in inputs
     for (const Range& r : inputs)
         if (overlap(r_y, r)) return SS_ERR_INVALID_ARG;
     if (overlap(r_y, r_hl)) return SS_ERR_INVALID_ARG;
     for (const Range& r : inputs) {
-        if (&r == &inputs[7] && h_last == h0) continue;  // exact in-place continuation is allowed
+        if (&r == &inputs[kH0] && h_last == h0) continue;  // exact in-place continuation is allowed
         if (overlap(r_hl, r)) return SS_ERR_INVALID_ARG;
     }
 
@@ -214,6 +227,8 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
     a.Dskip = Dskip;
     a.z = z;
     a.h0 = h0;
+    a.delta_bias = delta_bias;
+    a.options = options;
     a.y = y;
     a.h_last = h_last;
     a.ws_state = K > 1 ? static_cast<float*>(workspace) : nullptr;
@@ -234,11 +249,19 @@ ss_status ss_step(float* h, const void* u, const void* delta, const float* A, co
                   const float* Dskip, const void* z, void* y, int64_t batch, int64_t dim, int64_t dstate,
                   ss_dtype dtype, hipStream_t stream)
 {
+    return ss_step_ex(h, u, delta, A, B, C, Dskip, z, nullptr, 0u, y, batch, dim, dstate, dtype, stream);
+}
+
+ss_status ss_step_ex(float* h, const void* u, const void* delta, const float* A, const void* B, const void* C,
+                     const float* Dskip, const void* z, const float* delta_bias, uint32_t options, void* y,
+                     int64_t batch, int64_t dim, int64_t dstate, ss_dtype dtype, hipStream_t stream)
+{
     if (!h || !u || !delta || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
     Sizes s;
     if (!shape_sizes(batch, 1, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
     if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
+    if (options & ~ssk::kOptAll) return SS_ERR_UNSUPPORTED;
     int64_t threads;
     if (!mul(s.rows, 4, &threads) || ceil_div(threads, 256) > INT32_MAX) return SS_ERR_UNSUPPORTED;
 
@@ -248,12 +271,13 @@ ss_status ss_step(float* h, const void* u, const void* delta, const float* A, co
         if (p && !aligned(p, es)) return SS_ERR_INVALID_ARG;
     if (!aligned(h, 16) || !aligned(A, 16)) return SS_ERR_INVALID_ARG;
     if (Dskip && !aligned(Dskip, 4)) return SS_ERR_INVALID_ARG;
+    if (delta_bias && !aligned(delta_bias, 4)) return SS_ERR_INVALID_ARG;
 
     const int64_t e = static_cast<int64_t>(es);
     const Range r_h = span(h, s.states * 4), r_y = span(y, s.rows * e);
     const Range inputs[] = {span(u, s.rows * e), span(delta, s.rows * e), span(z, s.rows * e),
                             span(B, s.srows * e), span(C, s.srows * e), span(A, s.an * 4),
-                            span(Dskip, dim * 4)};
+                            span(Dskip, dim * 4), span(delta_bias, dim * 4)};
     if (overlap(r_h, r_y)) return SS_ERR_INVALID_ARG;
     for (const Range& r : inputs)
         if (overlap(r_h, r) || overlap(r_y, r)) return SS_ERR_INVALID_ARG;
@@ -267,6 +291,8 @@ ss_status ss_step(float* h, const void* u, const void* delta, const float* A, co
     a.C = C;
     a.Dskip = Dskip;
     a.z = z;
+    a.delta_bias = delta_bias;
+    a.options = options;
     a.y = y;
     a.batch = batch;
     a.dim = dim;

@@ -9,6 +9,11 @@ namespace ssk {
 
 constexpr int kDState = 16;  // the state width the kernels are built for
 
+// Option bits of a scan or step call (the same values as the C ABI's).
+constexpr uint32_t kOptSoftplus = 1u;  // step size = softplus(delta + bias[d])
+constexpr uint32_t kOptZoh = 2u;       // zero-order-hold input term
+constexpr uint32_t kOptAll = kOptSoftplus | kOptZoh;
+
 // Waves per scan workgroup; the 16 state entries are split evenly across them.
 #ifndef SS_SCAN_WAVES
 #define SS_SCAN_WAVES 8
@@ -44,6 +49,8 @@ struct ScanArgs {
     const float* Dskip;  // nullable
     const void* z;       // nullable
     const float* h0;     // nullable
+    const float* delta_bias;  // (dim,), nullable
+    uint32_t options;         // kOpt* bits
     void* y;
     float* h_last;       // nullable
     float* ws_state;     // (K, batch, dim, N) state slots, nullable when K == 1
@@ -65,6 +72,8 @@ struct StepArgs {
     const void* C;
     const float* Dskip;  // nullable
     const void* z;       // nullable
+    const float* delta_bias;  // (dim,), nullable
+    uint32_t options;         // kOpt* bits
     void* y;
     int64_t batch, dim;
 };

@@ -81,6 +81,38 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e)); }
 
+// softplus(v) = log(1 + e^v), as max(v, 0) + log1p(e^-|v|): no overflow, and
+// log1p keeps the small values of strongly negative v
+__device__ __forceinline__ float softplus(float v) { return fmaxf(v, 0.0f) + log1pf(exp2_hw(-fabsf(v) * kLog2e)); }
+
+// The step size of one (row, channel): the raw delta plus the channel's bias,
+// through softplus when the call asks for it (LTI chapter, section 3.1.4.2:
+// softplus of a per-channel parameter plus a projection of the input).
+template <int MODE>
+__device__ __forceinline__ float step_size(float raw, float bias)
+{
+    const float v = raw + bias;
+    return (MODE & kOptSoftplus) ? softplus(v) : v;
+}
+
+// Zero-order hold (Mamba walk-through, section 2.2): Bbar = (dA)^-1 (e^{dA} - 1) dB,
+// i.e. the Euler term delta*B times phi(x) = (e^x - 1)/x at x = delta*A.  Given
+// x2 = x * log2 e, e = 2^x2 (already formed for Abar) and inv_x = 1/x: where
+// e - 1 would cancel (|x| < 1/8) a degree-4 series, truncation below 5e-8;
+// elsewhere (e - 1) * inv_x.  phi(0) = 1 comes from the series, so an infinite
+// inv_x at delta = 0 or A = 0 is never used.
+constexpr float kZohSeriesBound = 0.18033688f;  // |x2| below which the series is used (|x| < 1/8)
+__device__ __forceinline__ float zoh_phi(float x2, float e, float inv_x)
+{
+    constexpr float c1 = 0.34657359f;    // ln2 / 2!
+    constexpr float c2 = 0.080075502f;   // ln2^2 / 3!
+    constexpr float c3 = 0.013876027f;   // ln2^3 / 4!
+    constexpr float c4 = 0.0019236258f;  // ln2^4 / 5!
+    const float series = fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, c4, c3), c2), c1), 1.0f);
+    const float direct = (e - 1.0f) * inv_x;
+    return fabsf(x2) < kZohSeriesBound ? series : direct;
+}
+
 // Scalar (wave-uniform) reads go through the constant address space so they
 // are issued as scalar loads.
 #define SS_CONST __attribute__((address_space(4)))
@@ -194,9 +226,10 @@ __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
 //       slot c+1 and its delta sum.
 // Host guarantees: chunk_len * dim * element size < 2^31.
 // ---------------------------------------------------------------------------
-template <int DT, bool EMIT, bool HAS_D, bool HAS_Z>
+template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
 {
+    constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using T = typename Elem<DT>::T;
     using V = Buf<DT>;
     using Raw = typename V::Raw;
@@ -205,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
     constexpr int PW = TT * kNS / 16;     // 16-word panel loads per tile and plane
 
     __shared__ float2 s_xd[2][TT][kWave];                       // (delta, delta*u) per row and channel
+    __shared__ float s_iv[ZOH ? 2 : 1][TT][kWave];              // 1/delta per row and channel (ZOH)
     __shared__ float s_part[EMIT ? 2 : 1][kGroups][TT][kWave];  // partial C.h per wave
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -236,9 +270,14 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
     const SS_CONST char* pC = pB + plane * 4;
 
     const int64_t sbase = bd * N + w * kNS;  // this lane's entries in a (B, D, N) state array
-    float A2[kNS];
+    float A2[kNS], iA[kNS];  // A * log2 e, and 1/A for the zero-order hold
 #pragma unroll
-    for (int i = 0; i < kNS; ++i) A2[i] = a.A[d * N + w * kNS + i] * kLog2e;
+    for (int i = 0; i < kNS; ++i) {
+        const float av = a.A[d * N + w * kNS + i];
+        A2[i] = av * kLog2e;
+        iA[i] = ZOH ? 1.0f / av : 0.0f;
+    }
+    const float bias = a.delta_bias ? a.delta_bias[d] : 0.0f;
 
     float h[kNS];
     const bool from_ws = EMIT && a.n_chunks > 1;
@@ -279,9 +318,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
             const bool in = tile * TT + w * RPW + j < len;
-            const float dl = in ? V::widen(rdl[S][j]) : 0.0f;
+            const float dl = in ? step_size<MODE>(V::widen(rdl[S][j]), bias) : 0.0f;
             const float x = V::widen(ru[S][j]);
             s_xd[S][w * RPW + j][lane] = make_float2(dl, dl * x);
+            if constexpr (ZOH) s_iv[S][w * RPW + j][lane] = __builtin_amdgcn_rcpf(dl);
             if (EMIT) {
                 xf[S][j] = x;
                 if (HAS_Z) {
@@ -339,32 +379,43 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
         // reads have landed (LDS and scalar loads share one counter, and scalar
         // loads return out of order: a later LDS wait would drain them too)
         static_assert(TT == 8, "the wait below names eight rows");
+        float iv[TT];  // 1/delta per row (zero-order hold only)
+#pragma unroll
+        for (int r = 0; r < TT; ++r) iv[r] = ZOH ? s_iv[ZOH ? S : 0][r][lane] : 0.0f;
         __asm__ volatile("" ::"v"(xd[0].x), "v"(xd[0].y), "v"(xd[1].x), "v"(xd[1].y), "v"(xd[2].x), "v"(xd[2].y),
                          "v"(xd[3].x), "v"(xd[3].y), "v"(xd[4].x), "v"(xd[4].y), "v"(xd[5].x), "v"(xd[5].y),
                          "v"(xd[6].x), "v"(xd[6].y), "v"(xd[7].x), "v"(xd[7].y)
                          : "memory");
+        if constexpr (ZOH)
+            __asm__ volatile("" ::"v"(iv[0]), "v"(iv[1]), "v"(iv[2]), "v"(iv[3]), "v"(iv[4]), "v"(iv[5]), "v"(iv[6]),
+                             "v"(iv[7])
+                             : "memory");
         issue_words(tile + 1, Slot<1 - S>{});
         // All delta*A products of the tile are formed before the first exp2 is
         // issued (the empty asm statements pin them in registers), so every
         // exp2 reads an operand produced many instructions earlier instead of
         // waiting on the multiply right before it.
-        float e[TT][kNS];
+        float x2[TT][kNS], e[TT][kNS];
 #pragma unroll
         for (int r = 0; r < TT; ++r) {
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) e[r][i] = xd[r].x * A2[i];
+            for (int i = 0; i < kNS; ++i) x2[r][i] = xd[r].x * A2[i];
         }
-        pin_rows(e);
+        pin_rows(x2);
 #pragma unroll
         for (int r = 0; r < TT; ++r) {
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) e[r][i] = exp2_hw(e[r][i]);
+            for (int i = 0; i < kNS; ++i) e[r][i] = exp2_hw(x2[r][i]);
         }
 #pragma unroll
         for (int r = 0; r < TT; ++r) {
             const float xb = xd[r].y;
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) h[i] = fmaf(e[r][i], h[i], xb * word(bw[S], r, i));
+            for (int i = 0; i < kNS; ++i) {
+                float in_term = xb * word(bw[S], r, i);  // delta*B*u (Euler)
+                if constexpr (ZOH) in_term *= zoh_phi(x2[r][i], e[r][i], iA[i] * iv[r]);
+                h[i] = fmaf(e[r][i], h[i], in_term);
+            }
             if constexpr (EMIT) {
                 float acc = 0.0f;
 #pragma unroll
@@ -490,7 +541,7 @@ __global__ __launch_bounds__(kWave) void carry_kernel(ScanArgs a)
 // entries (16-byte loads/stores of h), the quad's partial C.h summed with two
 // butterfly exchanges.  grid = ceil(batch*dim*4 / 256), block = 256.
 // ---------------------------------------------------------------------------
-template <int DT, bool HAS_D, bool HAS_Z>
+template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
 {
     using E = Elem<DT>;
@@ -512,9 +563,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
 
     float4 hv = *reinterpret_cast<const float4*>(a.h + bd * N + q * 4);
     const float4 av = *reinterpret_cast<const float4*>(a.A + d * N + q * 4);
-    const float dl = E::load(delta, bd);
+    const float dl = step_size<MODE>(E::load(delta, bd), a.delta_bias ? a.delta_bias[d] : 0.0f);
     const float x = E::load(u, bd);
     const float xb = dl * x;
+    const float inv_dl = (MODE & kOptZoh) ? __builtin_amdgcn_rcpf(dl) : 0.0f;
     const int64_t s0 = b * N + q * 4;
 
     float hs[4] = {hv.x, hv.y, hv.z, hv.w};
@@ -522,8 +574,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float abar = exp2_hw(dl * (as[i] * kLog2e));
-        hs[i] = fmaf(abar, hs[i], xb * E::load(Bm, s0 + i));
+        const float x2 = dl * (as[i] * kLog2e);
+        const float abar = exp2_hw(x2);
+        float in_term = xb * E::load(Bm, s0 + i);
+        if constexpr ((MODE & kOptZoh) != 0) in_term *= zoh_phi(x2, abar, (1.0f / as[i]) * inv_dl);
+        hs[i] = fmaf(abar, hs[i], in_term);
         part = fmaf(E::load(Cm, s0 + i), hs[i], part);
     }
     float acc = part + __shfl_xor(part, 1, 4);
@@ -538,49 +593,71 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     }
 }
 
-template <int DT, bool HAS_D, bool HAS_Z>
+template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
 {
     const unsigned nblk = unsigned((a.dim + kWave - 1) / kWave);
     const int64_t words = a.batch * a.n_chunks * 2 * a.panel_rows * N;
     panel_kernel<DT><<<dim3(unsigned((words + 255) / 256)), dim3(256), 0, s>>>(a);
     if (a.n_chunks > 1) {
-        scan_kernel<DT, false, false, false>
+        scan_kernel<DT, false, false, false, MODE>
             <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), dim3(kThreads), 0, s>>>(a);
         carry_kernel<<<dim3(unsigned(a.batch * a.dim)), dim3(kWave), 0, s>>>(a);
     }
-    scan_kernel<DT, true, HAS_D, HAS_Z>
+    scan_kernel<DT, true, HAS_D, HAS_Z, MODE>
         <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
-template <int DT, bool HAS_D, bool HAS_Z>
+template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 hipError_t launch_step_t(const StepArgs& a, hipStream_t s)
 {
     const int64_t threads = a.batch * a.dim * 4;
     const unsigned blocks = unsigned((threads + 255) / 256);
-    step_kernel<DT, HAS_D, HAS_Z><<<dim3(blocks), dim3(256), 0, s>>>(a);
+    step_kernel<DT, HAS_D, HAS_Z, MODE><<<dim3(blocks), dim3(256), 0, s>>>(a);
     return hipGetLastError();
+}
+
+template <int DT, int MODE>
+hipError_t dispatch_scan_mode(const ScanArgs& a, hipStream_t s)
+{
+    const bool hd = a.Dskip != nullptr, hz = a.z != nullptr;
+    if (hd && hz) return launch_scan_t<DT, true, true, MODE>(a, s);
+    if (hd) return launch_scan_t<DT, true, false, MODE>(a, s);
+    if (hz) return launch_scan_t<DT, false, true, MODE>(a, s);
+    return launch_scan_t<DT, false, false, MODE>(a, s);
 }
 
 template <int DT>
 hipError_t dispatch_scan(const ScanArgs& a, hipStream_t s)
 {
+    switch (a.options & kOptAll) {
+        case 0: return dispatch_scan_mode<DT, 0>(a, s);
+        case kOptSoftplus: return dispatch_scan_mode<DT, kOptSoftplus>(a, s);
+        case kOptZoh: return dispatch_scan_mode<DT, kOptZoh>(a, s);
+        default: return dispatch_scan_mode<DT, kOptSoftplus | kOptZoh>(a, s);
+    }
+}
+
+template <int DT, int MODE>
+hipError_t dispatch_step_mode(const StepArgs& a, hipStream_t s)
+{
     const bool hd = a.Dskip != nullptr, hz = a.z != nullptr;
-    if (hd && hz) return launch_scan_t<DT, true, true>(a, s);
-    if (hd) return launch_scan_t<DT, true, false>(a, s);
-    if (hz) return launch_scan_t<DT, false, true>(a, s);
-    return launch_scan_t<DT, false, false>(a, s);
+    if (hd && hz) return launch_step_t<DT, true, true, MODE>(a, s);
+    if (hd) return launch_step_t<DT, true, false, MODE>(a, s);
+    if (hz) return launch_step_t<DT, false, true, MODE>(a, s);
+    return launch_step_t<DT, false, false, MODE>(a, s);
 }
 
 template <int DT>
 hipError_t dispatch_step(const StepArgs& a, hipStream_t s)
 {
-    const bool hd = a.Dskip != nullptr, hz = a.z != nullptr;
-    if (hd && hz) return launch_step_t<DT, true, true>(a, s);
-    if (hd) return launch_step_t<DT, true, false>(a, s);
-    if (hz) return launch_step_t<DT, false, true>(a, s);
-    return launch_step_t<DT, false, false>(a, s);
+    switch (a.options & kOptAll) {
+        case 0: return dispatch_step_mode<DT, 0>(a, s);
+        case kOptSoftplus: return dispatch_step_mode<DT, kOptSoftplus>(a, s);
+        case kOptZoh: return dispatch_step_mode<DT, kOptZoh>(a, s);
+        default: return dispatch_step_mode<DT, kOptSoftplus | kOptZoh>(a, s);
+    }
 }
 
 }  // namespace

@@ -44,6 +44,10 @@ def scan_plan(batch: int, seqlen: int, dim: int, dstate: int, chunk_len: int = 0
     return T.value, K.value
 
 
+def _options(delta_softplus: bool, zoh: bool) -> int:
+    return (_lib.SS_DELTA_SOFTPLUS if delta_softplus else 0) | (_lib.SS_B_ZOH if zoh else 0)
+
+
 def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, chunk_len: int = 0) -> int:
     n = _lib.load().ss_scan_workspace_bytes(batch, seqlen, dim, dstate, chunk_len)
     if n == ctypes.c_size_t(-1).value:
@@ -55,12 +59,15 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
              h0: Optional[torch.Tensor] = None, *, return_last_state: bool = False,
              chunk_len: int = 0, out: Optional[torch.Tensor] = None,
-             h_last: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+             h_last: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False
              ) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
-    """Selective scan ``ss_scan_fwd`` on device tensors.
+    """Selective scan ``ss_scan_fwd_ex`` on device tensors.
 
     u, delta, z: (B, L, D); B, C: (B, L, N) -- all float32 or all bfloat16.
     A: (D, N) float32; D: (D,) float32; h0: (B, D, N) float32.
+    delta_bias (D,) float32 / delta_softplus: step size softplus(delta + bias[d]);
+    zoh: zero-order-hold input term instead of Euler's delta*B.
     Returns y (B, L, D) in the input dtype, and h_last (B, D, N) float32 if asked.
     ``out`` / ``h_last`` / ``workspace`` may be passed in to avoid allocation.
     """
@@ -85,6 +92,8 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
         _need(z, "z", (nb, nl, nd), dt, dev)
     if h0 is not None:
         _need(h0, "h0", (nb, nd, nn), torch.float32, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (nd,), torch.float32, dev)
     y = out if out is not None else torch.empty((nb, nl, nd), dtype=dt, device=dev)
     _need(y, "out", (nb, nl, nd), dt, dev)
     hl = h_last
@@ -98,10 +107,11 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     with torch.cuda.device(dev):
-        st = _lib.load().ss_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                     _ptr(h0), _ptr(y), _ptr(hl), _ptr(ws), ws_bytes,
-                                     nb, nl, nd, nn, chunk_len, _DTYPES[dt], _stream(dev))
-    _lib.check("ss_scan_fwd", st)
+        st = _lib.load().ss_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                        _ptr(h0), _ptr(delta_bias), _options(delta_softplus, zoh),
+                                        _ptr(y), _ptr(hl), _ptr(ws), ws_bytes,
+                                        nb, nl, nd, nn, chunk_len, _DTYPES[dt], _stream(dev))
+    _lib.check("ss_scan_fwd_ex", st)
     if return_last_state:
         return y, hl
     return y
@@ -109,10 +119,12 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
 
 def step(h: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
          C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
-         *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One recurrent token ``ss_step``: h (B, D, N) float32 is updated in place.
+         *, out: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+         delta_softplus: bool = False, zoh: bool = False) -> torch.Tensor:
+    """One recurrent token ``ss_step_ex``: h (B, D, N) float32 is updated in place.
 
     u, delta, z: (B, D); B, C: (B, N), float32 or bfloat16; A (D, N), D (D,) float32.
+    delta_bias / delta_softplus / zoh as for ``scan_fwd``.
     Returns y (B, D) in the input dtype.
     """
     if u.dim() != 2:
@@ -134,10 +146,13 @@ def step(h: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
         _need(D, "D", (nd,), torch.float32, dev)
     if z is not None:
         _need(z, "z", (nb, nd), dt, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (nd,), torch.float32, dev)
     y = out if out is not None else torch.empty((nb, nd), dtype=dt, device=dev)
     _need(y, "out", (nb, nd), dt, dev)
     with torch.cuda.device(dev):
-        st = _lib.load().ss_step(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                 _ptr(y), nb, nd, nn, _DTYPES[dt], _stream(dev))
-    _lib.check("ss_step", st)
+        st = _lib.load().ss_step_ex(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(z), _ptr(delta_bias), _options(delta_softplus, zoh), _ptr(y),
+                                    nb, nd, nn, _DTYPES[dt], _stream(dev))
+    _lib.check("ss_step_ex", st)
     return y

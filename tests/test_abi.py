@@ -192,3 +192,43 @@ def test_step_validation(lib):
     assert call_step(lib, y=ctypes.c_void_p(BASE + 64)) == INVALID           # y inside h
     assert call_step(lib, h=ctypes.c_void_p(BASE + 1 * GAP + 0)) == INVALID  # h on u
     assert call_step(lib, z=ctypes.c_void_p(BASE + 6 * GAP + 16)) == INVALID  # z inside y
+
+
+def call_scan_ex(lib, bias=None, options=0, **kw):
+    args = dict(u=addr(0), delta=addr(1), A=addr(2), B=addr(3), C=addr(4), D=None, z=None, h0=None,
+                y=addr(5), h_last=None, ws=addr(6), ws_bytes=1 << 40, batch=2, seqlen=512, dim=64,
+                dstate=16, chunk=0, dtype=BF16)
+    args.update(kw)
+    return lib.ss_scan_fwd_ex(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                              args["h0"], bias, options, args["y"], args["h_last"], args["ws"], args["ws_bytes"],
+                              args["batch"], args["seqlen"], args["dim"], args["dstate"], args["chunk"],
+                              args["dtype"], None)
+
+
+def call_step_ex(lib, bias=None, options=0, **kw):
+    args = dict(h=addr(0), u=addr(1), delta=addr(2), A=addr(3), B=addr(4), C=addr(5), D=None, z=None,
+                y=addr(6), batch=4, dim=64, dstate=16, dtype=BF16)
+    args.update(kw)
+    return lib.ss_step_ex(args["h"], args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"],
+                          args["z"], bias, options, args["y"], args["batch"], args["dim"], args["dstate"],
+                          args["dtype"], None)
+
+
+def test_options_validation(lib):
+    """Unknown option bits, a misaligned bias and a bias overlapping an output are
+    rejected on the host, by both extended entry points."""
+    for opt in (4, 8, 1 << 31, 3 | 4):
+        assert call_scan_ex(lib, options=opt) == UNSUPPORTED, opt
+        assert call_step_ex(lib, options=opt) == UNSUPPORTED, opt
+    odd = ctypes.c_void_p(BASE + 9 * GAP + 2)
+    assert call_scan_ex(lib, bias=odd, options=1) == INVALID
+    assert call_step_ex(lib, bias=odd, options=1) == INVALID
+    near = lambda i, off: ctypes.c_void_p(BASE + i * GAP + off)  # noqa: E731
+    assert call_scan_ex(lib, bias=near(5, 64), options=1) == INVALID                 # bias inside y
+    assert call_scan_ex(lib, bias=near(8, 0), h_last=near(8, 128)) == INVALID        # h_last over bias
+    assert call_step_ex(lib, bias=near(6, 0), options=3) == INVALID                  # bias on y
+    assert call_step_ex(lib, bias=near(0, 256)) == INVALID                           # bias inside h
+    # the same validation as the plain entry points for everything else
+    assert call_scan_ex(lib, dstate=8, options=1) == UNSUPPORTED
+    assert call_scan_ex(lib, ws=None, options=2) == WORKSPACE
+    assert call_step_ex(lib, u=None, options=2) == INVALID

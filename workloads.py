@@ -32,7 +32,7 @@ F32 = "f32"
 BF16 = "bf16"
 
 # tensor ids for the per-tensor streams
-_TID = {"u": 0, "delta": 1, "A": 2, "B": 3, "C": 4, "D": 5, "z": 6, "h0": 7}
+_TID = {"u": 0, "delta": 1, "A": 2, "B": 3, "C": 4, "D": 5, "z": 6, "h0": 7, "delta_bias": 8}
 
 _CHUNK = 1 << 22  # values per generation block (bounds the float32 temporaries)
 
@@ -161,6 +161,23 @@ def scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str = BF1
     out["D"] = _normal(_rng(seed, cfg_id, "D"), (dim,)) if has_D else None
     out["z"] = _store(_normal(_rng(seed, cfg_id, "z"), shp_x), dtype) if has_z else None
     out["h0"] = _normal(_rng(seed, cfg_id, "h0"), (batch, dim, dstate)) if has_h0 else None
+    return out
+
+
+def with_raw_delta(inp: Dict[str, Optional[np.ndarray]], *, raw_sigma: float = 0.5, dt_min: float = 1e-3,
+                   dt_max: float = 1e-1, seed: int = 0, cfg_id: int = 0) -> Dict[str, Optional[np.ndarray]]:
+    """Inputs for the softplus option: ``delta`` replaced by a raw pre-softplus value
+    N(0, raw_sigma) of the same shape and dtype, plus ``delta_bias`` (D,) float32 whose
+    softplus, log(1 + e^b), is a step size drawn log-uniformly from [dt_min, dt_max]
+    (the bias is stored as its inverse, log(e^dt - 1))."""
+    out = dict(inp)
+    dtype = BF16 if inp["u"].dtype == np.uint16 else F32
+    shp_x = inp["u"].shape
+    out["delta"] = _store(_normal(_rng(seed, cfg_id, "delta", 1), shp_x, 0.0, raw_sigma), dtype)
+    dim = shp_x[-1]
+    g = _rng(seed, cfg_id, "delta_bias")
+    dt = np.exp(g.uniform(np.log(dt_min), np.log(dt_max), dim))
+    out["delta_bias"] = np.log(np.expm1(dt)).astype(np.float32)
     return out
 
 
