@@ -11,9 +11,10 @@ HBM bytes per launch over its event-timed duration, against 8 TB/s), and the
 fp64 CPU oracle timed on a bounded sample of the same workload.
 
 Extra objects: ``decode_step`` (ss_step on the B=256, D=5120 recurrent-step
-workload), ``parity`` (timed output vs the oracle on sampled channels) and
+workload), ``parity`` (timed output vs the oracle on sampled channels),
 ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
-before every step).
+before every step) and ``options`` (the same layer with the softplus(delta +
+bias) step size and/or the zero-order-hold input term).
 """
 from __future__ import annotations
 
@@ -220,6 +221,33 @@ def main():
         rms = float(np.sqrt(np.mean(ref * ref)))
         err = float(np.max(np.abs(yl - ref) / np.maximum(np.abs(ref), rms)))
         result["parity"] = {"max_rel_err": err, "tol": 2e-2, "lanes": int(lanes.size)}
+
+        # the same layer with the step-size / input-term options
+        raw = wl.with_raw_delta(inp, seed=0, cfg_id=w.cfg_id)
+        dl_raw, bias = to_dev(raw["delta"]), to_dev(raw["delta_bias"])
+        opt_res = {}
+        for name, kw in (("softplus+bias", dict(delta_softplus=True)), ("zoh", dict(zoh=True)),
+                         ("softplus+bias+zoh", dict(delta_softplus=True, zoh=True))):
+            sp = kw.get("delta_softplus", False)
+
+            def ostep():
+                ss.scan_fwd(t["u"], dl_raw if sp else t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                            out=y, workspace=ws, delta_bias=bias if sp else None, **kw)
+
+            for _ in range(3):
+                ostep()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                ostep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            oms = e0.elapsed_time(e1) / 20
+            opt_res[name] = {"ms_per_step": oms, "elements/s": elements / (oms * 1e-3),
+                             "alg_GB/s": (alg_bytes + 4 * w.dim * sp) / (oms * 1e-3) / 1e9}
+        result["options"] = opt_res
 
         # recurrent step workload: one token for B=256, D=5120, state in place
         sw = wl.WORKLOADS["step"]

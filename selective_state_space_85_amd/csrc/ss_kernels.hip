@@ -81,9 +81,22 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e)); }
 
-// softplus(v) = log(1 + e^v), as max(v, 0) + log1p(e^-|v|): no overflow, and
-// log1p keeps the small values of strongly negative v
-__device__ __forceinline__ float softplus(float v) { return fmaxf(v, 0.0f) + log1pf(exp2_hw(-fabsf(v) * kLog2e)); }
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(t), t = e^-|v| in (0, 1]: no
+// overflow.  log1p(t) = log(w) + log(1 + r/w) with w = 1 + t rounded and r the
+// rounding error of w, which is exact (w - 1 is exact for w in [1, 2], and
+// t - (w - 1) is exact because both are within a factor of two or w - 1 = 0).
+// |r| <= 2^-24, so log(1 + r/w) = r/w to fp32 precision, and 2 - w stands in
+// for 1/w within 12.5% (a relative 3e-9 on the result).  Where w rounds to 1
+// the result is t itself.  Two hardware transcendentals (exp2, log2).
+constexpr float kLn2 = 0.69314718f;
+__device__ __forceinline__ float softplus(float v)
+{
+    const float t = exp2_hw(-fabsf(v) * kLog2e);
+    const float w = 1.0f + t;
+    const float r = t - (w - 1.0f);
+    const float l1p = fmaf(__builtin_amdgcn_logf(w), kLn2, r * (2.0f - w));
+    return fmaxf(v, 0.0f) + l1p;
+}
 
 // The step size of one (row, channel): the raw delta plus the channel's bias,
 // through softplus when the call asks for it (LTI chapter, section 3.1.4.2:
@@ -98,17 +111,17 @@ __device__ __forceinline__ float step_size(float raw, float bias)
 // Zero-order hold (Mamba walk-through, section 2.2): Bbar = (dA)^-1 (e^{dA} - 1) dB,
 // i.e. the Euler term delta*B times phi(x) = (e^x - 1)/x at x = delta*A.  Given
 // x2 = x * log2 e, e = 2^x2 (already formed for Abar) and inv_x = 1/x: where
-// e - 1 would cancel (|x| < 1/8) a degree-4 series, truncation below 5e-8;
+// e - 1 would cancel (|x| < 1/16) a degree-3 series;
 // elsewhere (e - 1) * inv_x.  phi(0) = 1 comes from the series, so an infinite
-// inv_x at delta = 0 or A = 0 is never used.
-constexpr float kZohSeriesBound = 0.18033688f;  // |x2| below which the series is used (|x| < 1/8)
+// inv_x at delta = 0 or A = 0 is never used.  Worst case about 1e-6 relative:
+// series truncation x^4/5! at the bound, or an ulp of e over |x| just above it.
+constexpr float kZohSeriesBound = 0.090168440f;  // |x2| below which the series is used (|x| < 1/16)
 __device__ __forceinline__ float zoh_phi(float x2, float e, float inv_x)
 {
-    constexpr float c1 = 0.34657359f;    // ln2 / 2!
-    constexpr float c2 = 0.080075502f;   // ln2^2 / 3!
-    constexpr float c3 = 0.013876027f;   // ln2^3 / 4!
-    constexpr float c4 = 0.0019236258f;  // ln2^4 / 5!
-    const float series = fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, c4, c3), c2), c1), 1.0f);
+    constexpr float c1 = 0.34657359f;   // ln2 / 2!
+    constexpr float c2 = 0.080075502f;  // ln2^2 / 3!
+    constexpr float c3 = 0.013876027f;  // ln2^3 / 4!
+    const float series = fmaf(x2, fmaf(x2, fmaf(x2, c3, c2), c1), 1.0f);
     const float direct = (e - 1.0f) * inv_x;
     return fabsf(x2) < kZohSeriesBound ? series : direct;
 }
