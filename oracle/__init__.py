@@ -8,6 +8,8 @@ import this package.  The library path never does.
   silu(z) gate, section 3.4).  Options: ``delta_bias`` / ``delta_softplus``
   (step size softplus(delta + bias[d]), LTI chapter section 3.1.4.2) and ``zoh``
   (zero-order-hold Bbar of the walk-through's section 2.2).
+* ``scan_bwd`` calls the fp64 backward in ``ss_oracle.c``: the chain rule taken
+  backward through the same recurrence, every state recomputed per lane.
 * ``twin_scan`` (in ``twin.py``) is an independent NumPy statement of the same
   definition, used only to cross-check the C loop on tiny shapes.
 
@@ -55,6 +57,9 @@ class OracleLib:
         lib.oracle_scan.restype = ctypes.c_int
         lib.oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, vp, i64, vp]
         lib.oracle_step.restype = ctypes.c_int
+        lib.oracle_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, i64,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip]
+        lib.oracle_scan_bwd.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -63,6 +68,9 @@ class OracleLib:
 
     def step(self, *args, **kwargs):
         return step(*args, _lib=self.lib, **kwargs)
+
+    def scan_bwd(self, *args, **kwargs):
+        return scan_bwd(*args, _lib=self.lib, **kwargs)
 
 
 def _load():
@@ -173,6 +181,59 @@ def step(h: np.ndarray, u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.n
     if rc != 0:
         raise ValueError("oracle_step rejected its arguments")
     return y.reshape(batch, dim) if lane_arr is None else y
+
+
+def scan_bwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
+             D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
+             h0: Optional[np.ndarray] = None, *, dy: np.ndarray, dh_last: Optional[np.ndarray] = None,
+             delta_bias: Optional[np.ndarray] = None, delta_softplus: bool = False, threads: int = 1,
+             _lib=None) -> Dict[str, np.ndarray]:
+    """fp64 gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input of
+    ``scan`` (same argument conventions; dy (B,L,D) and dh_last (B,D,N) any float).
+
+    Returns float64 ``du``, ``ddelta``, ``dz`` (B,L,D); ``dA`` (D,N); ``dB``, ``dC`` (B,L,N);
+    ``dD``, ``ddelta_bias`` (D,); ``dh0`` (B,D,N).  Gradients of absent inputs are absent
+    (``dz`` without z, ``dD`` without D, ``ddelta_bias`` without a bias).  ``ddelta`` is with
+    respect to delta as passed (the raw value under ``delta_softplus``).
+    """
+    lib = _lib or _load()
+    dt = _dtype_of(u)
+    batch, seqlen, dim = u.shape
+    dstate = A.shape[1]
+    for name, arr, shp in (("delta", delta, u.shape), ("B", B, (batch, seqlen, dstate)),
+                           ("C", C, (batch, seqlen, dstate))):
+        if tuple(arr.shape) != tuple(shp) or _dtype_of(arr) != dt:
+            raise ValueError("%s has shape %s dtype %s" % (name, arr.shape, arr.dtype))
+    u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
+    A = _c(A, np.float32)
+    D = _c(D, np.float32)
+    bias = _c(delta_bias, np.float32)
+    h0 = _c(h0, np.float64)
+    dy = _c(dy, np.float64)
+    dhl = _c(dh_last, np.float64)
+    if dy.shape != (batch, seqlen, dim):
+        raise ValueError("dy must be (B, L, D)")
+    out = {k: np.zeros((batch, seqlen, dim)) for k in ("du", "ddelta", "dz")}
+    out["dA"] = np.zeros((dim, dstate))
+    out["dB"] = np.zeros((batch, seqlen, dstate))
+    out["dC"] = np.zeros((batch, seqlen, dstate))
+    out["dD"] = np.zeros(dim)
+    out["ddelta_bias"] = np.zeros(dim)
+    out["dh0"] = np.zeros((batch, dim, dstate))
+    rc = lib.oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                             _ptr(bias), _flags(delta_softplus, False), dt, batch, seqlen, dim, dstate,
+                             _ptr(dy), _ptr(dhl), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]),
+                             _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                             _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_scan_bwd rejected its arguments")
+    if z is None:
+        del out["dz"]
+    if D is None:
+        del out["dD"]
+    if bias is None:
+        del out["ddelta_bias"]
+    return out
 
 
 def widen(a: np.ndarray) -> np.ndarray:

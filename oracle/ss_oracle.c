@@ -251,3 +251,216 @@ int oracle_step(double* h, const void* u, const void* delta, const float* A, con
     }
     return 0;
 }
+
+/*
+ * Backward of the scan: the gradients of
+ *   Loss = sum_{b,t,d} dy[b,t,d] * out[b,t,d] + sum_{b,d,n} dh_last[b,d,n] * h_last[b,d,n]
+ * with respect to every input of oracle_scan, by the chain rule taken backward
+ * through the forward recurrence (the backward that the walk-through's
+ * section 3.3 and the LTI chapter's section 3.1.5.3 say recomputes the states
+ * from the inputs instead of storing them):
+ *
+ *   per lane (b, d): run the forward once, keeping every state h_t, the step
+ *   sizes and the pre-gate outputs; then with g = dh_last (0 if absent), for
+ *   t = L-1 down to 0:
+ *     gate:   dz_t = dy_t * ypre_t * silu'(z_t);  dy_t <- dy_t * silu(z_t)
+ *     skip:   du_t += dy_t * D[d];  dD[d] += dy_t * u_t
+ *     output: dC[b,t,n] += dy_t * h_t[n];  g[n] += dy_t * C[b,t,n]
+ *     update h_t[n] = e[n] h_{t-1}[n] + delta_t B[b,t,n] u_t,  e[n] = exp(delta_t A[d,n]):
+ *             ddelta_t += g[n] (A[d,n] e[n] h_{t-1}[n] + B[b,t,n] u_t)
+ *             dA[d,n]  += g[n] delta_t e[n] h_{t-1}[n]
+ *             dB[b,t,n] += g[n] delta_t u_t;  du_t += g[n] delta_t B[b,t,n]
+ *             g[n] <- g[n] e[n]
+ *     step size: with softplus, d(raw)_t = ddelta_t * sigmoid(raw_t + bias[d]);
+ *             dbias[d] += d(raw)_t (a bias enters with derivative 1)
+ *   dh0 = g.
+ * silu'(z) = s (1 + z (1 - s)), s = sigmoid(z).  The zero-order-hold option is
+ * not covered (returns -1).
+ *
+ * dA, dD, dbias sum over batch rows and dB, dC over channels.  The lanes are
+ * cut into at most 64 fixed blocks, each block adds its lanes' terms in lane
+ * order into its own accumulators, and the blocks are added in block order:
+ * the result does not depend on the thread count.
+ */
+#define BWD_MAX_BLOCKS 64
+
+typedef struct {
+    const scan_job* f;
+    const double* dy;
+    const double* dh_last;
+    double *du, *ddelta, *dz, *dh0; /* per lane, written directly */
+    int64_t nblk;
+    double* acc; /* nblk blocks of [dA (D*N) | dD (D) | dbias (D) | dB (B*L*N) | dC (B*L*N)] */
+    int64_t acc_stride;
+} bwd_job;
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+static void bwd_lane(const bwd_job* j, int64_t bd, double* hs, double* acc)
+{
+    const scan_job* f = j->f;
+    const int64_t L = f->seqlen, D = f->dim, N = f->dstate;
+    const int64_t b = bd / D, d = bd % D;
+    double* dA = acc;
+    double* dD = dA + D * N;
+    double* dbias = dD + D;
+    double* dB = dbias + D;
+    double* dC = dB + f->batch * L * N;
+    double* dl = hs + (L + 1) * N; /* step sizes */
+    double* yp = dl + L;           /* pre-gate outputs */
+
+    for (int64_t n = 0; n < N; ++n) hs[n] = f->h0 ? f->h0[bd * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t row = (b * L + t) * D + d, srow = (b * L + t) * N;
+        const double delta = step_size(widen(f->delta, row, f->dtype), f->delta_bias, d, f->flags);
+        const double x = widen(f->u, row, f->dtype);
+        const double* hp = hs + t * N;
+        double* hn = hs + (t + 1) * N;
+        double y = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double a = (double)f->A[d * N + n];
+            hn[n] = exp(delta * a) * hp[n] + input_term(delta, a, widen(f->B, srow + n, f->dtype), x, f->flags);
+        }
+        for (int64_t n = 0; n < N; ++n) y += hn[n] * widen(f->C, srow + n, f->dtype);
+        if (f->Dskip) y += (double)f->Dskip[d] * x;
+        dl[t] = delta;
+        yp[t] = y;
+    }
+
+    double g[ORACLE_MAX_N];
+    for (int64_t n = 0; n < N; ++n) g[n] = j->dh_last ? j->dh_last[bd * N + n] : 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t row = (b * L + t) * D + d, srow = (b * L + t) * N;
+        const double x = widen(f->u, row, f->dtype);
+        const double delta = dl[t];
+        double dyt = j->dy[row];
+        double du = 0.0, dd = 0.0;
+        if (f->z) {
+            const double zz = widen(f->z, row, f->dtype), s = sigmoid(zz);
+            j->dz[row] = dyt * yp[t] * s * (1.0 + zz * (1.0 - s));
+            dyt *= zz * s;
+        }
+        if (f->Dskip) {
+            du += dyt * (double)f->Dskip[d];
+            dD[d] += dyt * x;
+        }
+        const double* hcur = hs + (t + 1) * N;
+        const double* hprev = hs + t * N;
+        for (int64_t n = 0; n < N; ++n) {
+            dC[srow + n] += dyt * hcur[n];
+            g[n] += dyt * widen(f->C, srow + n, f->dtype);
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            const double a = (double)f->A[d * N + n];
+            const double bm = widen(f->B, srow + n, f->dtype);
+            const double e = exp(delta * a);
+            dd += g[n] * (a * e * hprev[n] + bm * x);
+            dA[d * N + n] += g[n] * delta * e * hprev[n];
+            dB[srow + n] += g[n] * delta * x;
+            du += g[n] * delta * bm;
+            g[n] *= e;
+        }
+        if (f->flags & ORACLE_SOFTPLUS) {
+            const double v = widen(f->delta, row, f->dtype) + (f->delta_bias ? (double)f->delta_bias[d] : 0.0);
+            dd *= sigmoid(v);
+        }
+        if (f->delta_bias) dbias[d] += dd;
+        j->du[row] = du;
+        j->ddelta[row] = dd;
+    }
+    for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n];
+}
+
+typedef struct {
+    const bwd_job* job;
+    int first, step; /* blocks first, first + step, ... */
+    int failed;
+} bwd_worker_arg;
+
+static void* bwd_worker(void* arg)
+{
+    bwd_worker_arg* w = (bwd_worker_arg*)arg;
+    const bwd_job* j = w->job;
+    const scan_job* f = j->f;
+    const int64_t BD = f->batch * f->dim;
+    double* hs = (double*)malloc(sizeof(double) * (size_t)((f->seqlen + 1) * f->dstate + 2 * f->seqlen));
+    if (!hs) {
+        w->failed = 1;
+        return NULL;
+    }
+    for (int64_t k = w->first; k < j->nblk; k += w->step) {
+        double* acc = j->acc + k * j->acc_stride;
+        for (int64_t bd = BD * k / j->nblk; bd < BD * (k + 1) / j->nblk; ++bd) bwd_lane(j, bd, hs, acc);
+    }
+    free(hs);
+    return NULL;
+}
+
+/*
+ * oracle_scan_bwd: inputs as oracle_scan (all lanes), dy (B,L,D) and dh_last
+ * (B,D,N, or NULL) as double.  Outputs (double, none may be NULL):
+ * du, ddelta, dz (B,L,D) -- dz untouched without z; dA (D,N); dB, dC (B,L,N);
+ * dD (D) -- zeros without D; dbias (D) -- zeros without a bias; dh0 (B,D,N).
+ * ddelta is the gradient with respect to the delta argument as passed (the
+ * raw value when ORACLE_SOFTPLUS is set).  Returns 0, or -1 on a bad argument,
+ * an unsupported option (ORACLE_ZOH) or a failed allocation.
+ */
+int oracle_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                    const float* Dskip, const void* z, const double* h0,
+                    const float* delta_bias, int flags, int dtype,
+                    int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                    const double* dy, const double* dh_last,
+                    double* du, double* ddelta, double* dz, double* dA, double* dB, double* dC,
+                    double* dD, double* dbias, double* dh0, int nthreads)
+{
+    if (!u || !delta || !A || !B || !C || !dy) return -1;
+    if (!du || !ddelta || !dz || !dA || !dB || !dC || !dD || !dbias || !dh0) return -1;
+    if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > ORACLE_MAX_N) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (flags & ~ORACLE_SOFTPLUS) return -1;
+    const int64_t BD = batch * dim, L = seqlen, N = dstate, D = dim;
+
+    scan_job f = {u, delta, A, B, C, Dskip, z, h0, delta_bias, flags, dtype, batch, seqlen, dim, dstate,
+                  NULL, BD, NULL, NULL, NULL, 0, NULL};
+    bwd_job job = {&f, dy, dh_last, du, ddelta, dz, dh0, BD < BWD_MAX_BLOCKS ? BD : BWD_MAX_BLOCKS, NULL, 0};
+    job.acc_stride = D * N + 2 * D + 2 * batch * L * N;
+    job.acc = (double*)calloc((size_t)(job.nblk * job.acc_stride), sizeof(double));
+    if (!job.acc) return -1;
+
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > job.nblk) nthreads = (int)job.nblk;
+    pthread_t th[BWD_MAX_BLOCKS];
+    bwd_worker_arg wa[BWD_MAX_BLOCKS];
+    for (int i = 0; i < nthreads; ++i) {
+        wa[i].job = &job;
+        wa[i].first = i;
+        wa[i].step = nthreads;
+        wa[i].failed = 0;
+    }
+    if (nthreads == 1) {
+        bwd_worker(&wa[0]);
+    } else {
+        for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, bwd_worker, &wa[i]);
+        for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    }
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i)
+        if (wa[i].failed) rc = -1;
+
+    /* blocks added in block order */
+    memset(dA, 0, sizeof(double) * (size_t)(D * N));
+    memset(dD, 0, sizeof(double) * (size_t)D);
+    memset(dbias, 0, sizeof(double) * (size_t)D);
+    memset(dB, 0, sizeof(double) * (size_t)(batch * L * N));
+    memset(dC, 0, sizeof(double) * (size_t)(batch * L * N));
+    for (int64_t k = 0; k < job.nblk; ++k) {
+        const double* acc = job.acc + k * job.acc_stride;
+        for (int64_t i = 0; i < D * N; ++i) dA[i] += acc[i];
+        for (int64_t i = 0; i < D; ++i) dD[i] += acc[D * N + i];
+        for (int64_t i = 0; i < D; ++i) dbias[i] += acc[D * N + D + i];
+        for (int64_t i = 0; i < batch * L * N; ++i) dB[i] += acc[D * N + 2 * D + i];
+        for (int64_t i = 0; i < batch * L * N; ++i) dC[i] += acc[D * N + 2 * D + batch * L * N + i];
+    }
+    free(job.acc);
+    return rc;
+}

@@ -468,7 +468,103 @@ def pin_softplus_bias(orc):
         _close(h, ref["h_last"], 1e-15, "step state %s" % sorted(opts))
 
 
+# ---------------------------------------------------------------------------
+# 15. backward: every gradient element against torch's fp64 autograd of a torch
+#     statement of the forward (library reverse mode, no hand-derived adjoint)
+# ---------------------------------------------------------------------------
+def _torch_forward(c, softplus):
+    import torch
+
+    f64 = lambda a: None if a is None else torch.tensor(_f64(a), dtype=torch.float64, requires_grad=True)  # noqa: E731
+    t = {k: f64(c.get(k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0", "delta_bias")}
+    dl = t["delta"]
+    if t["delta_bias"] is not None:
+        dl = dl + t["delta_bias"][None, None, :]
+    if softplus:
+        dl = torch.logaddexp(torch.zeros_like(dl), dl)
+    nb, nl, nd = dl.shape
+    if t["h0"] is None:  # a zero initial state still has a gradient
+        t["h0"] = torch.zeros(nb, nd, t["A"].shape[1], dtype=torch.float64, requires_grad=True)
+    h = t["h0"]
+    ys = []
+    for s_ in range(nl):
+        h = torch.exp(dl[:, s_, :, None] * t["A"][None]) * h + \
+            (dl[:, s_, :, None] * t["B"][:, s_, None, :]) * t["u"][:, s_, :, None]
+        ys.append((h * t["C"][:, s_, None, :]).sum(-1))
+    y = torch.stack(ys, 1)
+    if t["D"] is not None:
+        y = y + t["D"][None, None, :] * t["u"]
+    if t["z"] is not None:
+        y = y * torch.nn.functional.silu(t["z"])
+    return t, y, h
+
+
+def pin_bwd_autograd(orc):
+    import torch
+
+    rng = np.random.default_rng(26)
+    cases = [((2, 11, 5, 8), dict(dtype="f32", has_D=True, has_z=True, has_h0=True), False, True),
+             ((1, 17, 3, 16), dict(dtype="bf16", has_D=True, has_z=False, has_h0=False), True, False),
+             ((3, 6, 4, 4), dict(dtype="f32", has_D=False, has_z=True, has_h0=True), True, True)]
+    for shp, kw, softplus, with_dh in cases:
+        c = _rand_case(rng, *shp, **kw)
+        if softplus:
+            raw = rng.normal(-1.0, 1.0, c["u"].shape).astype(np.float32)
+            c["delta"] = f32_to_bf16_bits(raw) if c["u"].dtype == np.uint16 else raw
+            c["delta_bias"] = rng.normal(0.0, 0.7, shp[2]).astype(np.float32)
+        dy = rng.standard_normal(shp[:3])
+        dhl = rng.standard_normal((shp[0], shp[2], shp[3])) if with_dh else None
+        got = orc.scan_bwd(**c, dy=dy, dh_last=dhl, delta_softplus=softplus)
+        t, y, h = _torch_forward(c, softplus)
+        loss = (y * torch.tensor(dy)).sum()
+        if with_dh:
+            loss = loss + (h * torch.tensor(dhl)).sum()
+        loss.backward()
+        names = {"du": "u", "ddelta": "delta", "dA": "A", "dB": "B", "dC": "C", "dD": "D", "dz": "z",
+                 "dh0": "h0", "ddelta_bias": "delta_bias"}
+        for gk, ik in names.items():
+            if t[ik] is None:
+                assert gk not in got, "%s present without %s" % (gk, ik)
+                continue
+            _close(got[gk], t[ik].grad.numpy(), 1e-11, "autograd %s %s" % (gk, shp))
+
+
+# ---------------------------------------------------------------------------
+# 16. backward: directional derivatives against fp64 central differences of
+#     the NumPy twin's forward (one random direction per input)
+# ---------------------------------------------------------------------------
+def pin_bwd_finite_differences(orc):
+    from oracle.twin import twin_scan
+
+    rng = np.random.default_rng(27)
+    c = _rand_case(rng, 2, 9, 3, 4, dtype="f32", has_D=True, has_z=True, has_h0=True)
+    raw = rng.normal(-0.5, 1.0, c["u"].shape).astype(np.float32)
+    c["delta"] = raw
+    c["delta_bias"] = rng.normal(0.0, 0.5, 3).astype(np.float32)
+    dy = rng.standard_normal((2, 9, 3))
+    dhl = rng.standard_normal((2, 3, 4))
+    grads = orc.scan_bwd(**c, dy=dy, dh_last=dhl, delta_softplus=True)
+
+    base = {k: (None if v is None else _f64(v)) for k, v in c.items()}
+
+    def loss(inp):
+        y, h = twin_scan(**inp, delta_softplus=True)
+        return float(np.sum(y * dy) + np.sum(h * dhl))
+
+    eps = 1e-6
+    for gk, ik in (("du", "u"), ("ddelta", "delta"), ("dA", "A"), ("dB", "B"), ("dC", "C"), ("dD", "D"),
+                   ("dz", "z"), ("dh0", "h0"), ("ddelta_bias", "delta_bias")):
+        v = rng.standard_normal(base[ik].shape)
+        plus = dict(base)
+        minus = dict(base)
+        plus[ik] = base[ik] + eps * v
+        minus[ik] = base[ik] - eps * v
+        fd = (loss(plus) - loss(minus)) / (2 * eps)
+        an = float(np.sum(grads[gk] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), "finite differences %s: %.9g vs %.9g" % (gk, an, fd)
+
+
 ALL_PINS = [pin_hand_worked, pin_single_step_closed_form, pin_lti_convolution, pin_zero_input,
             pin_brute_force, pin_geometric, pin_delta_limits, pin_chaining,
             pin_causality_linearity, pin_bookkeeping, pin_twin, pin_zoh_step_response,
-            pin_zoh_limits, pin_softplus_bias]
+            pin_zoh_limits, pin_softplus_bias, pin_bwd_autograd, pin_bwd_finite_differences]

@@ -27,8 +27,8 @@ MUTANTS = [
     ("sigmoid gate instead of silu", "static double silu(double z) { return z / (1.0 + exp(-z)); }",
      "static double silu(double z) { return 1.0 / (1.0 + exp(-z)); }"),
     ("h0 ignored", "h[n] = j->h0 ? j->h0[bd * N + n] : 0.0;", "h[n] = 0.0;"),
-    ("lane index swapped", "const int64_t b = bd / D, d = bd % D;",
-     "const int64_t b = bd % j->batch, d = bd / j->batch;"),
+    ("lane index swapped", "const int64_t bd = j->lanes ? j->lanes[li] : li;\n    const int64_t b = bd / D, d = bd % D;",
+     "const int64_t bd = j->lanes ? j->lanes[li] : li;\n    const int64_t b = bd % j->batch, d = bd / j->batch;"),
     ("y from the pre-update state",
      "            h[n] = a_bar * h[n] + input_term(delta, a, widen(j->B, srow + n, j->dtype), x, j->flags);\n"
      "        }\n        double y = 0.0;\n"
@@ -50,6 +50,18 @@ MUTANTS = [
     ("bias subtracted", "double v = raw + (delta_bias", "double v = raw - (delta_bias"),
     ("bias of channel 0 everywhere", "(double)delta_bias[d]", "(double)delta_bias[0]"),
     ("softplus always on", "return (flags & ORACLE_SOFTPLUS) ? softplus(v) : v;", "return softplus(v);"),
+    # the backward
+    ("adjoint not decayed", "            g[n] *= e;\n", "            (void)e;\n"),
+    ("dA without the decay factor", "dA[d * N + n] += g[n] * delta * e * hprev[n];",
+     "dA[d * N + n] += g[n] * delta * hprev[n];"),
+    ("dC from the previous state", "dC[srow + n] += dyt * hcur[n];", "dC[srow + n] += dyt * hprev[n];"),
+    ("dB without u", "dB[srow + n] += g[n] * delta * x;", "dB[srow + n] += g[n] * delta;"),
+    ("ddelta misses the decay path", "dd += g[n] * (a * e * hprev[n] + bm * x);", "dd += g[n] * (bm * x);"),
+    ("silu derivative wrong", "s * (1.0 + zz * (1.0 - s))", "s * (1.0 + zz * s)"),
+    ("skip uses the ungated gradient", "dD[d] += dyt * x;", "dD[d] += j->dy[row] * x;"),
+    ("softplus derivative dropped", "            dd *= sigmoid(v);\n", "            (void)v;\n"),
+    ("dh0 before the last decay", "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n];",
+     "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n] / exp(dl[0] * (double)f->A[d * N + n]);"),
 ]
 
 
