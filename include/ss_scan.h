@@ -184,6 +184,57 @@ ss_status ss_step_ex(float* h, const void* u, const void* delta, const float* A,
                      const float* delta_bias, uint32_t options, void* y,
                      int64_t batch, int64_t dim, int64_t dstate, ss_dtype dtype, hipStream_t stream);
 
+/*
+ * ss_scan_bwd_workspace_bytes -- device workspace ss_scan_bwd needs for this
+ * shape ((size_t)-1 for invalid sizes).  It holds the fp32 B/C panel, state
+ * checkpoints every 16 timesteps (ceil(seqlen/16) * batch * dim * dstate
+ * words), per-64-channel partial sums of dB and dC (2 * ceil(dim/64) * batch *
+ * seqlen * dstate words) and per-batch-row partial sums of dA, dD and the
+ * delta bias; its arrangement is internal to the library.
+ */
+size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * ss_scan_bwd -- gradients of the scan (reverse mode), recomputing the states
+ * from the inputs instead of storing them (the backward of the walk-through's
+ * section 3.3 and the LTI chapter's section 3.1.5.3).  With out = ss_scan_fwd_ex
+ * of the same inputs and options, it returns the gradients of
+ *     sum(dy * out) + sum(dh_last * h_last)
+ * with respect to every input:
+ *
+ *   forward inputs : as ss_scan_fwd_ex (options: SS_DELTA_SOFTPLUS only;
+ *                    SS_B_ZOH returns SS_ERR_UNSUPPORTED)
+ *   dy          : (batch, seqlen, dim)   dtype   gradient of out
+ *   dh_last     : (batch, dim, dstate)   fp32    gradient of h_last (NULL: zero)
+ *   du, ddelta  : (batch, seqlen, dim)   dtype   output; ddelta is with respect
+ *                                                to delta as passed (the raw
+ *                                                value under SS_DELTA_SOFTPLUS)
+ *   dz          : (batch, seqlen, dim)   dtype   output, required iff z is given
+ *   dA          : (dim, dstate)          fp32    output
+ *   dB, dC      : (batch, seqlen, dstate) dtype  output (sums over channels in
+ *                                                fp32, rounded once)
+ *   dD          : (dim,)                 fp32    output, required iff Dskip is given
+ *   ddelta_bias : (dim,)                 fp32    output, required iff delta_bias is given
+ *   dh0         : (batch, dim, dstate)   fp32    output, gradient of the initial
+ *                                                state (NULL: not written)
+ *   workspace   : ss_scan_bwd_workspace_bytes(...) bytes, 256-byte aligned
+ *
+ * Sums over channels, timesteps and batch rows are taken in a fixed order:
+ * the results are the same from run to run.  Outputs must not overlap the
+ * inputs or each other; the workspace overlaps nothing.  One batch row's
+ * (seqlen, dim) slab must stay below 2 GiB (SS_ERR_UNSUPPORTED otherwise).
+ * Alignment and the other errors are as for ss_scan_fwd.
+ */
+ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* Dskip, const void* z, const float* h0,
+                      const float* delta_bias, uint32_t options,
+                      const void* dy, const float* dh_last,
+                      void* du, void* ddelta, float* dA, void* dB, void* dC,
+                      float* dD, void* dz, float* ddelta_bias, float* dh0,
+                      void* workspace, size_t workspace_bytes,
+                      int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                      ss_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* ss_status_string(ss_status s);
 

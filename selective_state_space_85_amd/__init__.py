@@ -3,11 +3,14 @@
     from selective_state_space_85_amd import scan_fwd, step
     y = scan_fwd(u, delta, A, B, C, D=Dskip, z=z)          # (B, L, D)
     y_t = step(h, u_t, delta_t, A, B_t, C_t, D=Dskip, z=z_t)  # h (B, D, N) updated in place
+    grads = scan_bwd(u, delta, A, B, C, dy, D=Dskip, z=z)    # du, ddelta, dA, dB, dC, dD, dz, dh0
 
 The library itself is ``libssscan.so`` (``include/ss_scan.h``), built by
 ``selective_state_space_85_amd.build``.
 """
 from ._lib import LIB_PATH, SSError, load as load_library  # noqa: F401
-from .ops import scan_fwd, scan_plan, scan_workspace_bytes, step  # noqa: F401
+from .ops import (scan_bwd, scan_bwd_workspace_bytes, scan_fwd, scan_plan, scan_workspace_bytes,  # noqa: F401
+                  step)
 
-__all__ = ["scan_fwd", "step", "scan_plan", "scan_workspace_bytes", "load_library", "LIB_PATH", "SSError"]
+__all__ = ["scan_fwd", "scan_bwd", "step", "scan_plan", "scan_workspace_bytes", "scan_bwd_workspace_bytes",
+           "load_library", "LIB_PATH", "SSError"]

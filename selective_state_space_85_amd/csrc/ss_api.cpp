@@ -117,6 +117,45 @@ bool ws_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64
     return true;
 }
 
+// Backward workspace (fp32 words), each region from a 256-byte boundary:
+//   B/C panel (one chunk per batch row), checkpoints (J, B, N, D) with
+//   J = ceil(L / kBwdSub), dB and dC partials (nblk, B, L, N) each, dA
+//   partials (B, D, N), dD and dbias partials (B, D) each.
+struct BwdLayout {
+    int64_t panel_rows, n_sub, nblk;
+    int64_t off_panel, off_ckpt, off_pdB, off_pdC, off_pdA, off_pdD, off_pdbias;  // bytes
+    int64_t total;                                                               // bytes
+};
+
+bool bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, BwdLayout* w)
+{
+    w->panel_rows = ssk::panel_rows(seqlen);
+    w->n_sub = ceil_div(seqlen, ssk::kBwdSub);
+    w->nblk = ceil_div(dim, kWave);
+    int64_t words[7];
+    int64_t bl, tmp;
+    if (!mul(batch, seqlen, &bl)) return false;
+    if (!mul(batch, 2 * w->panel_rows, &tmp) || !mul(tmp, dstate, &words[0])) return false;
+    if (!mul(w->n_sub, batch, &tmp) || !mul(tmp, dstate, &tmp) || !mul(tmp, dim, &words[1])) return false;
+    if (!mul(w->nblk, bl, &tmp) || !mul(tmp, dstate, &words[2])) return false;
+    words[3] = words[2];
+    if (!mul(batch, dim, &tmp) || !mul(tmp, dstate, &words[4])) return false;
+    if (!mul(batch, dim, &words[5])) return false;
+    words[6] = words[5];
+    int64_t* offs[7] = {&w->off_panel, &w->off_ckpt, &w->off_pdB, &w->off_pdC, &w->off_pdA, &w->off_pdD,
+                        &w->off_pdbias};
+    int64_t at = 0;
+    for (int i = 0; i < 7; ++i) {
+        int64_t bytes;
+        if (__builtin_add_overflow(at, int64_t(255), &at)) return false;
+        at &= ~int64_t(255);
+        *offs[i] = at;
+        if (!mul(words[i], 4, &bytes) || __builtin_add_overflow(at, bytes, &at)) return false;
+    }
+    w->total = at;
+    return true;
+}
+
 ss_status hip_fail(hipError_t e)
 {
     g_last_hip_error = static_cast<int>(e);
@@ -297,6 +336,122 @@ ss_status ss_step_ex(float* h, const void* u, const void* delta, const float* A,
     a.batch = batch;
     a.dim = dim;
     const hipError_t err = ssk::launch_step(a, dtype == SS_F32 ? 0 : 1, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    return SS_OK;
+}
+
+size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate)
+{
+    Sizes s;
+    BwdLayout wl;
+    if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return static_cast<size_t>(-1);
+    if (!bwd_layout(batch, seqlen, dim, dstate, &wl)) return static_cast<size_t>(-1);
+    return static_cast<size_t>(wl.total);
+}
+
+ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                      uint32_t options, const void* dy, const float* dh_last, void* du, void* ddelta, float* dA,
+                      void* dB, void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0, void* workspace,
+                      size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                      ss_dtype dtype, hipStream_t stream)
+{
+    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SS_ERR_INVALID_ARG;
+    if ((Dskip && !dD) || (z && !dz) || (delta_bias && !ddelta_bias)) return SS_ERR_INVALID_ARG;
+    Sizes s;
+    if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
+    if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
+    if (options & ~ssk::kOptSoftplus) return SS_ERR_UNSUPPORTED;  // no zero-order hold in the backward
+    if (batch > kMaxGridYZ || batch * dim > INT32_MAX) return SS_ERR_UNSUPPORTED;
+    BwdLayout wl;
+    if (!bwd_layout(batch, seqlen, dim, dstate, &wl)) return SS_ERR_INVALID_ARG;
+    const uintptr_t es = dtype == SS_F32 ? 4 : 2;
+    int64_t row_bytes_all;  // one batch row's (L, D) slab is addressed with 32-bit buffer offsets
+    if (!mul(seqlen, dim, &row_bytes_all) || !mul(row_bytes_all, int64_t(es), &row_bytes_all) ||
+        row_bytes_all >= kMaxChunkBytes)
+        return SS_ERR_UNSUPPORTED;
+
+    const void* elem_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz};
+    for (const void* p : elem_ptrs)
+        if (p && !aligned(p, es)) return SS_ERR_INVALID_ARG;
+    if (!aligned(A, 16)) return SS_ERR_INVALID_ARG;
+    const void* f32_ptrs[] = {Dskip, h0, delta_bias, dh_last, dA, dD, ddelta_bias, dh0};
+    for (const void* p : f32_ptrs)
+        if (p && !aligned(p, 4)) return SS_ERR_INVALID_ARG;
+
+    const int64_t e = static_cast<int64_t>(es);
+    const Range inputs[] = {span(u, s.rows * e), span(delta, s.rows * e), span(z, s.rows * e),
+                            span(B, s.srows * e), span(C, s.srows * e), span(A, s.an * 4), span(Dskip, dim * 4),
+                            span(h0, s.states * 4), span(delta_bias, dim * 4), span(dy, s.rows * e),
+                            span(dh_last, s.states * 4)};
+    const Range outputs[] = {span(du, s.rows * e), span(ddelta, s.rows * e), span(dz, s.rows * e),
+                             span(dB, s.srows * e), span(dC, s.srows * e), span(dA, s.an * 4),
+                             span(dD, dim * 4), span(ddelta_bias, dim * 4), span(dh0, s.states * 4)};
+    // outputs overlap neither the inputs nor each other
+    for (size_t i = 0; i < sizeof(outputs) / sizeof(outputs[0]); ++i) {
+        for (const Range& r : inputs)
+            if (overlap(outputs[i], r)) return SS_ERR_INVALID_ARG;
+        for (size_t k = i + 1; k < sizeof(outputs) / sizeof(outputs[0]); ++k)
+            if (overlap(outputs[i], outputs[k])) return SS_ERR_INVALID_ARG;
+    }
+    if (!workspace || workspace_bytes < static_cast<size_t>(wl.total)) return SS_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SS_ERR_INVALID_ARG;
+    const Range r_ws = span(workspace, wl.total);
+    for (const Range& r : inputs)
+        if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
+    for (const Range& r : outputs)
+        if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
+    if (ceil_div(int64_t(batch) * 2 * wl.panel_rows * dstate, 256) > int64_t(UINT32_MAX)) return SS_ERR_UNSUPPORTED;
+
+    char* ws = static_cast<char*>(workspace);
+    ssk::ScanArgs pa{};
+    pa.B = B;
+    pa.C = C;
+    pa.ws_panel = reinterpret_cast<float*>(ws + wl.off_panel);
+    pa.panel_rows = wl.panel_rows;
+    pa.batch = batch;
+    pa.seqlen = seqlen;
+    pa.dim = dim;
+    pa.chunk_len = seqlen;
+    pa.n_chunks = 1;
+    hipError_t err = ssk::launch_panel(pa, dtype == SS_F32 ? 0 : 1, stream);
+    if (err != hipSuccess) return hip_fail(err);
+
+    ssk::BwdArgs a{};
+    a.u = u;
+    a.delta = delta;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.z = z;
+    a.h0 = h0;
+    a.delta_bias = delta_bias;
+    a.options = options;
+    a.dy = dy;
+    a.dh_last = dh_last;
+    a.du = du;
+    a.ddelta = ddelta;
+    a.dz = dz;
+    a.dh0 = dh0;
+    a.dB = dB;
+    a.dC = dC;
+    a.dA = dA;
+    a.dD = dD;
+    a.ddelta_bias = ddelta_bias;
+    a.panel = pa.ws_panel;
+    a.panel_rows = wl.panel_rows;
+    a.ckpt = reinterpret_cast<float*>(ws + wl.off_ckpt);
+    a.part_dB = reinterpret_cast<float*>(ws + wl.off_pdB);
+    a.part_dC = reinterpret_cast<float*>(ws + wl.off_pdC);
+    a.part_dA = reinterpret_cast<float*>(ws + wl.off_pdA);
+    a.part_dD = reinterpret_cast<float*>(ws + wl.off_pdD);
+    a.part_dbias = reinterpret_cast<float*>(ws + wl.off_pdbias);
+    a.batch = batch;
+    a.seqlen = seqlen;
+    a.dim = dim;
+    a.n_sub = wl.n_sub;
+    a.nblk = wl.nblk;
+    err = ssk::launch_bwd(a, dtype == SS_F32 ? 0 : 1, stream);
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;
 }

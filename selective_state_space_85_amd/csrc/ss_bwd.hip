@@ -1,0 +1,436 @@
+// gfx950 kernels of the selective scan's backward: the gradients of
+// sum(dy * y) + sum(dh_last * h_last) with respect to u, delta (raw under
+// softplus), A, B, C, D, z, the delta bias and h0.  The per-timestep states
+// are never stored: they are recomputed from checkpoints (the backward of the
+// Mamba walk-through's section 3.3 and of the LTI chapter's section 3.1.5.3,
+// which recomputes the states from the inputs instead of reading them back).
+//
+// For a lane (b, d) and state n, with e_t = exp(delta_t A) and the adjoint g
+// (the gradient with respect to h_t, accumulated from the last timestep down):
+//   g += dy'_t C_t                         dy' = dy * silu(z) (the gated gradient)
+//   dC_t += dy'_t h_t        (summed over channels d)
+//   ddelta_t += g (A e_t h_{t-1} + B_t u_t),  dA += g delta_t e_t h_{t-1}
+//   dB_t += g delta_t u_t    (summed over channels d),  du_t += g delta_t B_t
+//   g *= e_t
+// plus du_t += D dy'_t, dD += dy'_t u_t, dz_t = dy_t ypre_t silu'(z_t), the
+// softplus derivative sigmoid(raw + bias) on ddelta, dbias += ddelta, dh0 = g.
+//
+// Three launches after the B/C panel:
+//  1. prep_kernel runs the forward once, storing the state every kBwdSub rows
+//     (the checkpoints), the per-workgroup channel sums of dC, and dz;
+//  2. bwd_kernel walks the sub-blocks from the last to the first: it rebuilds
+//     the sub-block's states in registers from its checkpoint, then runs the
+//     adjoint down the sub-block, writing du and ddelta and the per-workgroup
+//     channel sums of dB, and keeping dA, dD, dbias per lane;
+//  3. bwd_reduce_kernel adds the per-workgroup and per-batch-row partial sums
+//     in a fixed order (the result does not depend on scheduling) and rounds
+//     dB, dC to the operand type.
+// The workgroup shape is the forward's: 64 channels of one batch row, the 16
+// state entries split over 8 waves (2 per wave), B and C as scalar operands.
+#include "ss_device.h"
+
+namespace ssk {
+namespace {
+
+constexpr int kSub = kBwdSub;             // rows per sub-block (checkpoint spacing)
+constexpr int kHalf = kSub / 2;           // the backward finishes a sub-block in two halves
+constexpr int kPW = kSub * kNS / 16;      // 16-word panel loads per sub-block and plane
+static_assert(kSub == 2 * kTileRows, "a sub-block is two panel tiles");
+static_assert(kHalf == kGroups, "each wave publishes and finishes one row of each half");
+static_assert((kSub * kNS) % 16 == 0, "panel rows of a sub-block come in 16-word loads");
+
+__device__ __forceinline__ float sigmoid(float v) { return __builtin_amdgcn_rcpf(1.0f + exp2_hw(-v * kLog2e)); }
+
+// The per-workgroup pieces both kernels share: channel, row streams, panel.
+template <int DT>
+struct Lane {
+    using T = typename Elem<DT>::T;
+    using V = Buf<DT>;
+    int lane, w;
+    bool active;
+    int64_t d, b;  // d clamped to a real channel for idle lanes
+    uint32_t row_bytes, voff;
+    const SS_CONST char* pB;  // this wave's B plane of the batch row's panel
+    const SS_CONST char* pC;
+
+    __device__ Lane(const BwdArgs& a)
+    {
+        lane = threadIdx.x & (kWave - 1);
+        w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        const int64_t d_raw = int64_t(blockIdx.x) * kWave + lane;
+        active = d_raw < a.dim;
+        d = active ? d_raw : a.dim - 1;
+        b = blockIdx.y;
+        row_bytes = uint32_t(a.dim) * V::kBytes;
+        voff = active ? uint32_t(d_raw) * V::kBytes : kIdleOffset;
+        const int64_t plane = a.panel_rows * kNS;
+        pB = (const SS_CONST char*)(a.panel + (b * kGroups + w) * 2 * plane);
+        pC = pB + plane * 4;
+    }
+    // a (B, L, D) stream of this batch row
+    __device__ __amdgpu_buffer_rsrc_t rsrc(const void* base, const BwdArgs& a) const
+    {
+        return make_rsrc(static_cast<const T*>(base) + b * a.seqlen * a.dim, uint32_t(a.seqlen) * row_bytes);
+    }
+    __device__ void words(int j, Words16 (&bw)[kPW], Words16 (&cw)[kPW]) const
+    {
+        const uint32_t off = uint32_t(j) * uint32_t(kSub * kNS * 4);
+        const SS_CONST Words16* qb = (const SS_CONST Words16*)(pB + off);
+        const SS_CONST Words16* qc = (const SS_CONST Words16*)(pC + off);
+#pragma unroll
+        for (int q = 0; q < kPW; ++q) {
+            bw[q] = qb[q];
+            cw[q] = qc[q];
+        }
+    }
+};
+
+__device__ __forceinline__ float word(const Words16 (&wv)[kPW], int r, int i)
+{
+    const int k = r * kNS + i;
+    return __uint_as_float(wv[k / 16][k % 16]);
+}
+
+// The rows a wave publishes (and, in the backward, finishes) in a sub-block:
+// row w of the first half and row w of the second.
+__device__ __forceinline__ int row_of(int w, int k) { return w + k * kHalf; }
+
+// Raw operand rows of a sub-block in flight, and the widened values a wave
+// keeps for its own rows.
+template <int DT>
+struct Rows {
+    using V = Buf<DT>;
+    typename V::Raw dl[2], x[2], dy[2], z[2];
+
+    template <bool HAS_Z>
+    __device__ void issue(const Lane<DT>& ln, int64_t L, int j, __amdgpu_buffer_rsrc_t r_dl,
+                          __amdgpu_buffer_rsrc_t r_u, __amdgpu_buffer_rsrc_t r_dy, __amdgpu_buffer_rsrc_t r_z)
+    {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t t = int64_t(j) * kSub + row_of(ln.w, k);
+            const uint32_t so = uint32_t(t < L ? t : L - 1) * ln.row_bytes;
+            dl[k] = V::load(r_dl, ln.voff, so);
+            x[k] = V::load(r_u, ln.voff, so);
+            dy[k] = V::load(r_dy, ln.voff, so);
+            if (HAS_Z) z[k] = V::load(r_z, ln.voff, so);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// prep_kernel: the forward once, from h0.  grid = (ceil(dim/64), batch),
+// block = 64 * kGroups.  Per sub-block j: store the state entering row
+// kSub*j, publish (delta, delta*u, dy') per row in LDS, advance the state over
+// the sub-block while summing dy'*h_t over the workgroup's channels (dC
+// partials), and with a gate finish dz = dy * ypre * silu'(z).
+// ---------------------------------------------------------------------------
+template <int DT, bool HAS_D, bool HAS_Z, int MODE>
+__global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
+{
+    using V = Buf<DT>;
+    __shared__ float4 s_row[kSub][kWave];                     // (delta, delta*u, dy', 0)
+    __shared__ float s_y[HAS_Z ? kGroups : 1][kSub][kWave];  // partial C.h per wave (for dz)
+
+    const Lane<DT> ln(a);
+    const int lane = ln.lane, w = ln.w;
+    const int64_t D = a.dim, L = a.seqlen, NB = a.batch, blk = blockIdx.x;
+    const auto r_u = ln.rsrc(a.u, a), r_dl = ln.rsrc(a.delta, a), r_dy = ln.rsrc(a.dy, a);
+    const auto r_z = ln.rsrc(HAS_Z ? a.z : a.u, a), r_dz = ln.rsrc(HAS_Z ? a.dz : a.u, a);
+
+    float A2[kNS], h[kNS];
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) {
+        A2[i] = a.A[ln.d * N + w * kNS + i] * kLog2e;
+        h[i] = (a.h0 && ln.active) ? a.h0[(ln.b * D + ln.d) * N + w * kNS + i] : 0.0f;
+    }
+    const float bias = a.delta_bias ? a.delta_bias[ln.d] : 0.0f;
+    const float dskip = HAS_D ? a.Dskip[ln.d] : 0.0f;
+
+    Rows<DT> rows;
+    rows.template issue<HAS_Z>(ln, L, 0, r_dl, r_u, r_dy, r_z);
+    float xf[2], dyf[2], zf[2];
+    Words16 bw[kPW], cw[kPW];
+
+    for (int j = 0; j < int(a.n_sub); ++j) {
+        if (ln.active) {
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) a.ckpt[((int64_t(j) * NB + ln.b) * N + w * kNS + i) * D + ln.d] = h[i];
+        }
+        ln.words(j, bw, cw);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = row_of(w, k);
+            const bool in = ln.active && int64_t(j) * kSub + r < L;
+            const float dl = in ? step_size<MODE>(V::widen(rows.dl[k]), bias) : 0.0f;
+            const float x = V::widen(rows.x[k]);
+            const float dyv = in ? V::widen(rows.dy[k]) : 0.0f;
+            const float zv = HAS_Z ? V::widen(rows.z[k]) : 0.0f;
+            const float dyp = HAS_Z ? dyv * silu(zv) : dyv;
+            s_row[r][lane] = make_float4(dl, dl * x, dyp, 0.0f);
+            xf[k] = x;
+            dyf[k] = dyv;
+            zf[k] = zv;
+        }
+        if (j + 1 < int(a.n_sub)) rows.template issue<HAS_Z>(ln, L, j + 1, r_dl, r_u, r_dy, r_z);
+        __syncthreads();
+
+#pragma unroll
+        for (int r = 0; r < kSub; ++r) {
+            const float4 rv = s_row[r][lane];
+            const int64_t t = int64_t(j) * kSub + r;
+            float ypart = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) {
+                const float e = exp2_hw(rv.x * A2[i]);
+                h[i] = fmaf(e, h[i], rv.y * word(bw, r, i));
+                const float dc = wave_sum_to_lane63(rv.z * h[i]);
+                if (lane == kWave - 1 && t < L) a.part_dC[((blk * NB + ln.b) * L + t) * N + w * kNS + i] = dc;
+                if (HAS_Z) ypart = fmaf(word(cw, r, i), h[i], ypart);
+            }
+            if constexpr (HAS_Z) s_y[w][r][lane] = ypart;
+        }
+        __syncthreads();
+
+        if constexpr (HAS_Z) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int r = row_of(w, k);
+                const int64_t t = int64_t(j) * kSub + r;
+                if (t < L) {
+                    float y = s_y[0][r][lane];
+#pragma unroll
+                    for (int g = 1; g < kGroups; ++g) y += s_y[g][r][lane];
+                    if (HAS_D) y = fmaf(dskip, xf[k], y);
+                    const float s = sigmoid(zf[k]);
+                    V::store(r_dz, ln.voff, uint32_t(t) * ln.row_bytes, dyf[k] * y * s * fmaf(zf[k], 1.0f - s, 1.0f));
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_kernel: the adjoint, sub-block by sub-block from the last.  grid =
+// (ceil(dim/64), batch), block = 64 * kGroups.  Per sub-block: publish the
+// rows, rebuild the states from the checkpoint, then for each half (last
+// first) run the adjoint down its rows -- per-wave partial sums over the
+// wave's state entries of g.B and g.h_{t-1}.e.A go to LDS, the channel sums
+// of g*delta*u (dB) to the partial buffer -- and finish one row per wave:
+// du, ddelta, and the per-lane dD and dbias terms.
+// ---------------------------------------------------------------------------
+template <int DT, bool HAS_D, bool HAS_Z, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
+{
+    using V = Buf<DT>;
+    __shared__ float4 s_row[kSub][kWave];        // (delta, delta*u, dy', 0)
+    __shared__ float2 s_par[kGroups][kHalf][kWave];  // per wave (sum g.B, sum g.h.e.A) of one half
+
+    const Lane<DT> ln(a);
+    const int lane = ln.lane, w = ln.w;
+    const int64_t D = a.dim, L = a.seqlen, NB = a.batch, blk = blockIdx.x;
+    const auto r_u = ln.rsrc(a.u, a), r_dl = ln.rsrc(a.delta, a), r_dy = ln.rsrc(a.dy, a);
+    const auto r_z = ln.rsrc(HAS_Z ? a.z : a.u, a);
+    const auto r_du = ln.rsrc(a.du, a), r_ddl = ln.rsrc(a.ddelta, a);
+
+    float A2[kNS], Av[kNS], g[kNS], dA_acc[kNS];
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) {
+        Av[i] = a.A[ln.d * N + w * kNS + i];
+        A2[i] = Av[i] * kLog2e;
+        g[i] = (a.dh_last && ln.active) ? a.dh_last[(ln.b * D + ln.d) * N + w * kNS + i] : 0.0f;
+        dA_acc[i] = 0.0f;
+    }
+    const float bias = a.delta_bias ? a.delta_bias[ln.d] : 0.0f;
+    const float dskip = HAS_D ? a.Dskip[ln.d] : 0.0f;
+    float dD_acc = 0.0f, dbias_acc = 0.0f;
+
+    Rows<DT> rows;
+    rows.template issue<HAS_Z>(ln, L, int(a.n_sub) - 1, r_dl, r_u, r_dy, r_z);
+    float xf[2], dlf[2], sgf[2], dypf[2];
+    Words16 bw[kPW], cw[kPW];
+
+    for (int j = int(a.n_sub) - 1; j >= 0; --j) {
+        ln.words(j, bw, cw);
+        float hprev[kNS];
+#pragma unroll
+        for (int i = 0; i < kNS; ++i)
+            hprev[i] = ln.active ? a.ckpt[((int64_t(j) * NB + ln.b) * N + w * kNS + i) * D + ln.d] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = row_of(w, k);
+            const bool in = ln.active && int64_t(j) * kSub + r < L;
+            const float v = V::widen(rows.dl[k]) + bias;
+            const float dl = in ? ((MODE & kOptSoftplus) ? softplus(v) : v) : 0.0f;
+            const float x = V::widen(rows.x[k]);
+            const float dyv = in ? V::widen(rows.dy[k]) : 0.0f;
+            const float dyp = HAS_Z ? dyv * silu(V::widen(rows.z[k])) : dyv;
+            s_row[r][lane] = make_float4(dl, dl * x, dyp, 0.0f);
+            xf[k] = x;
+            dlf[k] = dl;
+            sgf[k] = (MODE & kOptSoftplus) ? sigmoid(v) : 1.0f;
+            dypf[k] = dyp;
+        }
+        if (j > 0) rows.template issue<HAS_Z>(ln, L, j - 1, r_dl, r_u, r_dy, r_z);
+        __syncthreads();
+
+        // the sub-block's states, rebuilt from its checkpoint
+        float hh[kSub][kNS];
+#pragma unroll
+        for (int r = 0; r < kSub; ++r) {
+            const float4 rv = s_row[r][lane];
+#pragma unroll
+            for (int i = 0; i < kNS; ++i)
+                hh[r][i] = fmaf(exp2_hw(rv.x * A2[i]), r ? hh[r - 1][i] : hprev[i], rv.y * word(bw, r, i));
+        }
+
+#pragma unroll
+        for (int half = 1; half >= 0; --half) {
+#pragma unroll
+            for (int rr = kHalf - 1; rr >= 0; --rr) {
+                const int r = half * kHalf + rr;
+                const int64_t t = int64_t(j) * kSub + r;
+                const float4 rv = s_row[r][lane];
+                float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kNS; ++i) {
+                    g[i] = fmaf(rv.z, word(cw, r, i), g[i]);
+                    const float hp = r ? hh[r - 1][i] : hprev[i];
+                    const float e = exp2_hw(rv.x * A2[i]);
+                    const float t1 = g[i] * hp * e;
+                    dA_acc[i] = fmaf(t1, rv.x, dA_acc[i]);
+                    s2 = fmaf(t1, Av[i], s2);
+                    s1 = fmaf(g[i], word(bw, r, i), s1);
+                    const float db = wave_sum_to_lane63(g[i] * rv.y);
+                    if (lane == kWave - 1 && t < L) a.part_dB[((blk * NB + ln.b) * L + t) * N + w * kNS + i] = db;
+                    g[i] *= e;
+                }
+                s_par[w][rr][lane] = make_float2(s1, s2);
+            }
+            __syncthreads();
+            {
+                const int r = row_of(w, half);
+                const int64_t t = int64_t(j) * kSub + r;
+                if (ln.active && t < L) {
+                    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < kGroups; ++q) {
+                        const float2 p = s_par[q][w][lane];
+                        s1 += p.x;
+                        s2 += p.y;
+                    }
+                    float du = dlf[half] * s1;
+                    if (HAS_D) {
+                        du = fmaf(dskip, dypf[half], du);
+                        dD_acc = fmaf(dypf[half], xf[half], dD_acc);
+                    }
+                    const float ddl = fmaf(xf[half], s1, s2) * sgf[half];
+                    dbias_acc += ddl;
+                    V::store(r_du, ln.voff, uint32_t(t) * ln.row_bytes, du);
+                    V::store(r_ddl, ln.voff, uint32_t(t) * ln.row_bytes, ddl);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    const int64_t bd = ln.b * D + ln.d;
+    if (ln.active) {
+#pragma unroll
+        for (int i = 0; i < kNS; ++i) {
+            if (a.dh0) a.dh0[bd * N + w * kNS + i] = g[i];
+            a.part_dA[bd * N + w * kNS + i] = dA_acc[i];
+        }
+    }
+    // dD and dbias: the eight waves' per-lane terms, added in wave order
+    s_par[w][0][lane] = make_float2(dD_acc, dbias_acc);
+    __syncthreads();
+    if (w == 0 && ln.active) {
+        float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            const float2 p = s_par[q][0][lane];
+            sd += p.x;
+            sb += p.y;
+        }
+        a.part_dD[bd] = sd;
+        a.part_dbias[bd] = sb;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_reduce_kernel: fixed-order sums of the partials.  blockIdx.y selects the
+// job: 0 = dB, dC over the channel blocks (rounded to the operand type);
+// 1 = dA over batch rows; 2 = dD and dbias over batch rows.  block = 256.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    const int64_t k = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t BLN = a.batch * a.seqlen * N;
+    if (blockIdx.y == 0) {
+        if (k >= BLN) return;
+        float sb = 0.0f, sc = 0.0f;
+        for (int64_t q = 0; q < a.nblk; ++q) {
+            sb += a.part_dB[q * BLN + k];
+            sc += a.part_dC[q * BLN + k];
+        }
+        E::store(static_cast<T*>(a.dB), k, sb);
+        E::store(static_cast<T*>(a.dC), k, sc);
+    } else if (blockIdx.y == 1) {
+        const int64_t DN = a.dim * N;
+        if (k >= DN) return;
+        float s = 0.0f;
+        for (int64_t q = 0; q < a.batch; ++q) s += a.part_dA[q * DN + k];
+        a.dA[k] = s;
+    } else {
+        if (k >= a.dim) return;
+        float sd = 0.0f, sb = 0.0f;
+        for (int64_t q = 0; q < a.batch; ++q) {
+            sd += a.part_dD[q * a.dim + k];
+            sb += a.part_dbias[q * a.dim + k];
+        }
+        if (a.Dskip) a.dD[k] = sd;
+        if (a.delta_bias) a.ddelta_bias[k] = sb;
+    }
+}
+
+template <int DT, bool HAS_D, bool HAS_Z, int MODE>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s)
+{
+    const dim3 grid(unsigned(a.nblk), unsigned(a.batch));
+    prep_kernel<DT, HAS_D, HAS_Z, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
+    bwd_kernel<DT, HAS_D, HAS_Z, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
+    int64_t most = a.batch * a.seqlen * N;
+    if (a.dim * N > most) most = a.dim * N;
+    bwd_reduce_kernel<DT><<<dim3(unsigned((most + 255) / 256), 3), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DT, int MODE>
+hipError_t dispatch_bwd_mode(const BwdArgs& a, hipStream_t s)
+{
+    const bool hd = a.Dskip != nullptr, hz = a.z != nullptr;
+    if (hd && hz) return launch_bwd_t<DT, true, true, MODE>(a, s);
+    if (hd) return launch_bwd_t<DT, true, false, MODE>(a, s);
+    if (hz) return launch_bwd_t<DT, false, true, MODE>(a, s);
+    return launch_bwd_t<DT, false, false, MODE>(a, s);
+}
+
+template <int DT>
+hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s)
+{
+    return (a.options & kOptSoftplus) ? dispatch_bwd_mode<DT, kOptSoftplus>(a, s) : dispatch_bwd_mode<DT, 0>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    return dtype == 0 ? dispatch_bwd<0>(a, stream) : dispatch_bwd<1>(a, stream);
+}
+
+}  // namespace ssk

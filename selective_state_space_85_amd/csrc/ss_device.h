@@ -1,0 +1,191 @@
+// Device-side helpers shared by the forward (ss_kernels.hip) and backward
+// (ss_bwd.hip) kernels: work geometry, operand access, the step size and the
+// pointwise functions.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "ss_internal.h"
+
+namespace ssk {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int N = kDState;
+constexpr int kWave = 64;
+constexpr int kGroups = kScanWaves;  // waves per scan workgroup = state groups
+constexpr int kNS = N / kGroups;  // state entries per wave
+constexpr int kThreads = kWave * kGroups;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in one instruction,
+// v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<0> {  // fp32 operands
+    using T = float;
+    static __device__ __forceinline__ float load(const T* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = v; }
+};
+template <>
+struct Elem<1> {  // bf16 operands, fp32 arithmetic
+    using T = uint16_t;
+    static __device__ __forceinline__ float load(const T* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e)); }
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(t), t = e^-|v| in (0, 1]: no
+// overflow.  log1p(t) = log(w) + log(1 + r/w) with w = 1 + t rounded and r the
+// rounding error of w, which is exact (w - 1 is exact for w in [1, 2], and
+// t - (w - 1) is exact because both are within a factor of two or w - 1 = 0).
+// |r| <= 2^-24, so log(1 + r/w) = r/w to fp32 precision, and 2 - w stands in
+// for 1/w within 12.5% (a relative 3e-9 on the result).  Where w rounds to 1
+// the result is t itself.  Two hardware transcendentals (exp2, log2).
+constexpr float kLn2 = 0.69314718f;
+__device__ __forceinline__ float softplus(float v)
+{
+    const float t = exp2_hw(-fabsf(v) * kLog2e);
+    const float w = 1.0f + t;
+    const float r = t - (w - 1.0f);
+    const float l1p = fmaf(__builtin_amdgcn_logf(w), kLn2, r * (2.0f - w));
+    return fmaxf(v, 0.0f) + l1p;
+}
+
+// The step size of one (row, channel): the raw delta plus the channel's bias,
+// through softplus when the call asks for it (LTI chapter, section 3.1.4.2:
+// softplus of a per-channel parameter plus a projection of the input).
+template <int MODE>
+__device__ __forceinline__ float step_size(float raw, float bias)
+{
+    const float v = raw + bias;
+    return (MODE & kOptSoftplus) ? softplus(v) : v;
+}
+
+// Zero-order hold (Mamba walk-through, section 2.2): Bbar = (dA)^-1 (e^{dA} - 1) dB,
+// i.e. the Euler term delta*B times phi(x) = (e^x - 1)/x at x = delta*A.  Given
+// x2 = x * log2 e, e = 2^x2 (already formed for Abar) and inv_x = 1/x: where
+// e - 1 would cancel (|x| < 1/16) a degree-3 series;
+// elsewhere (e - 1) * inv_x.  phi(0) = 1 comes from the series, so an infinite
+// inv_x at delta = 0 or A = 0 is never used.  Worst case about 1e-6 relative:
+// series truncation x^4/5! at the bound, or an ulp of e over |x| just above it.
+constexpr float kZohSeriesBound = 0.090168440f;  // |x2| below which the series is used (|x| < 1/16)
+__device__ __forceinline__ float zoh_phi(float x2, float e, float inv_x)
+{
+    constexpr float c1 = 0.34657359f;   // ln2 / 2!
+    constexpr float c2 = 0.080075502f;  // ln2^2 / 3!
+    constexpr float c3 = 0.013876027f;  // ln2^3 / 4!
+    const float series = fmaf(x2, fmaf(x2, fmaf(x2, c3, c2), c1), 1.0f);
+    const float direct = (e - 1.0f) * inv_x;
+    return fabsf(x2) < kZohSeriesBound ? series : direct;
+}
+
+// Scalar (wave-uniform) reads go through the constant address space so they
+// are issued as scalar loads.
+#define SS_CONST __attribute__((address_space(4)))
+
+// Raw buffer access for the (B, L, D) row streams.  The resource is based at
+// the chunk's first row; the lane's channel is the vector offset and the row a
+// scalar offset.  Lanes past the last channel get an out-of-range vector
+// offset: their loads read 0 and their stores are dropped by the range check.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw (untyped) buffer, gfx9 family
+constexpr uint32_t kIdleOffset = 0x80000000u;
+
+template <int DT>
+struct Buf;
+template <>
+struct Buf<0> {
+    static constexpr uint32_t kBytes = 4;
+    using Raw = uint32_t;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float widen(Raw v) { return __uint_as_float(v); }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
+};
+template <>
+struct Buf<1> {
+    static constexpr uint32_t kBytes = 2;
+    using Raw = uint16_t;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float widen(Raw v) { return __uint_as_float(uint32_t(v) << 16); }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, voff, soff, 0);
+    }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), int(kRsrcWord3));
+}
+
+// Sixteen 32-bit words: one scalar load of a wave's B (or C) entries for
+// 16 / kNS consecutive rows of the fp32 panel.
+typedef uint32_t Words16 __attribute__((ext_vector_type(16)));
+
+template <int V>
+using Slot = std::integral_constant<int, V>;
+
+// An empty asm statement that reads and rewrites a whole group of values: all of
+// them are computed before it and nothing that consumes them moves above it.
+template <int R, int C>
+__device__ __forceinline__ void pin_rows(float (&v)[R][C])
+{
+    static_assert(C == 4 || C == 2 || C == 8, "row width");
+#pragma unroll
+    for (int r = 0; r + 1 < R; r += 2) {
+        if constexpr (C == 4)
+            __asm__ volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r][2]), "+v"(v[r][3]), "+v"(v[r + 1][0]),
+                             "+v"(v[r + 1][1]), "+v"(v[r + 1][2]), "+v"(v[r + 1][3]));
+        else if constexpr (C == 2)
+            __asm__ volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r + 1][0]), "+v"(v[r + 1][1]));
+        else
+            __asm__ volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r][2]), "+v"(v[r][3]), "+v"(v[r][4]),
+                             "+v"(v[r][5]), "+v"(v[r][6]), "+v"(v[r][7]));
+    }
+}
+
+// DPP controls: row shifts by 1/2/4/8 lanes within rows of 16, and the
+// broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Sum of v over the 64 lanes of the wave, left in lane 63 (other lanes hold
+// partial sums).  Prefix sums within each row of 16 lanes, then the row totals
+// carried up by the two broadcasts; lanes a shift or a row mask leaves out
+// add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float add_from(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_to_lane63(float v)
+{
+    v = add_from<kDppRowShr1, 0xf>(v);
+    v = add_from<kDppRowShr2, 0xf>(v);
+    v = add_from<kDppRowShr4, 0xf>(v);
+    v = add_from<kDppRowShr8, 0xf>(v);
+    v = add_from<kDppRowBcast15, 0xa>(v);
+    return add_from<kDppRowBcast31, 0xc>(v);
+}
+
+}  // namespace
+}  // namespace ssk

@@ -78,8 +78,51 @@ struct StepArgs {
     int64_t batch, dim;
 };
 
+// Backward: rows per sub-block, which is also the spacing of the state
+// checkpoints the backward recomputes from.
+constexpr int kBwdSub = 16;
+
+struct BwdArgs {
+    // forward inputs
+    const void* u;
+    const void* delta;
+    const float* A;
+    const float* Dskip;       // nullable
+    const void* z;            // nullable
+    const float* h0;          // nullable
+    const float* delta_bias;  // nullable
+    uint32_t options;         // kOptSoftplus only
+    // incoming gradients
+    const void* dy;           // (batch, seqlen, dim), dtype
+    const float* dh_last;     // (batch, dim, N), nullable
+    // gradients
+    void* du;
+    void* ddelta;
+    void* dz;                 // written when z is given
+    float* dh0;               // nullable
+    void* dB;
+    void* dC;
+    float* dA;
+    float* dD;                // written when Dskip is given
+    float* ddelta_bias;       // written when delta_bias is given
+    // workspace
+    const float* panel;       // the fp32 B/C panel, one chunk per batch row
+    int64_t panel_rows;
+    float* ckpt;              // (n_sub, batch, N, dim): state entering row kBwdSub*j
+    float* part_dB;           // (nblk, batch, seqlen, N): per-workgroup sums over its channels
+    float* part_dC;
+    float* part_dA;           // (batch, dim, N): per-batch-row sums over time
+    float* part_dD;           // (batch, dim)
+    float* part_dbias;        // (batch, dim)
+    int64_t batch, seqlen, dim, n_sub, nblk;
+};
+
 // Each returns the hipError_t of its launches (hipSuccess when all were enqueued).
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, int dtype, hipStream_t stream);
+// the B/C panel alone (a.B, a.C, a.ws_panel, a.panel_rows, a.batch, a.seqlen,
+// a.chunk_len, a.n_chunks)
+hipError_t launch_panel(const ScanArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace ssk

@@ -7,7 +7,7 @@ C entry points (``ss_scan_fwd`` -> ``scan_fwd``, ``ss_step`` -> ``step``).
 from __future__ import annotations
 
 import ctypes
-from typing import Optional, Tuple, Union
+from typing import Dict, Optional, Tuple, Union
 
 import torch
 
@@ -156,3 +156,70 @@ def step(h: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
                                     nb, nd, nn, _DTYPES[dt], _stream(dev))
     _lib.check("ss_step_ex", st)
     return y
+
+
+def scan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int) -> int:
+    n = _lib.load().ss_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid scan shape")
+    return int(n)
+
+
+def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             h0: Optional[torch.Tensor] = None, *, dh_last: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+             want_dh0: bool = True, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Gradients of sum(dy * y) + sum(dh_last * h_last) for ``scan_fwd`` with the same inputs
+    (``ss_scan_bwd``).  dy (B, L, D) in the input dtype; dh_last (B, D, N) float32 or None.
+
+    Returns a dict: du, ddelta, dz (B, L, D) and dB, dC (B, L, N) in the input dtype; dA (D, N),
+    dD (D,), ddelta_bias (D,), dh0 (B, D, N) float32.  Gradients of absent inputs are absent;
+    dh0 only if ``want_dh0``.  ddelta is with respect to delta as passed (raw under softplus).
+    """
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, seqlen, dim)")
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("scan_bwd runs on the GPU; u is on %s" % dev)
+    dt = u.dtype
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    nb, nl, nd = u.shape
+    nn = A.shape[-1]
+    for t, name, shp, tdt in ((u, "u", (nb, nl, nd), dt), (delta, "delta", (nb, nl, nd), dt),
+                              (A, "A", (nd, nn), torch.float32), (B, "B", (nb, nl, nn), dt),
+                              (C, "C", (nb, nl, nn), dt), (dy, "dy", (nb, nl, nd), dt)):
+        _need(t, name, shp, tdt, dev)
+    for t, name, shp, tdt in ((D, "D", (nd,), torch.float32), (z, "z", (nb, nl, nd), dt),
+                              (h0, "h0", (nb, nd, nn), torch.float32),
+                              (dh_last, "dh_last", (nb, nd, nn), torch.float32),
+                              (delta_bias, "delta_bias", (nd,), torch.float32)):
+        if t is not None:
+            _need(t, name, shp, tdt, dev)
+    g = {"du": torch.empty((nb, nl, nd), dtype=dt, device=dev),
+         "ddelta": torch.empty((nb, nl, nd), dtype=dt, device=dev),
+         "dA": torch.empty((nd, nn), dtype=torch.float32, device=dev),
+         "dB": torch.empty((nb, nl, nn), dtype=dt, device=dev),
+         "dC": torch.empty((nb, nl, nn), dtype=dt, device=dev)}
+    if D is not None:
+        g["dD"] = torch.empty((nd,), dtype=torch.float32, device=dev)
+    if z is not None:
+        g["dz"] = torch.empty((nb, nl, nd), dtype=dt, device=dev)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty((nd,), dtype=torch.float32, device=dev)
+    if want_dh0:
+        g["dh0"] = torch.empty((nb, nd, nn), dtype=torch.float32, device=dev)
+    need = scan_bwd_workspace_bytes(nb, nl, nd, nn)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = ws.numel() * ws.element_size()
+    opts = _options(delta_softplus, False)
+    with torch.cuda.device(dev):
+        st = _lib.load().ss_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                     _ptr(delta_bias), opts, _ptr(dy), _ptr(dh_last),
+                                     _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                     _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                                     _ptr(g.get("dh0")), _ptr(ws), ws_bytes, nb, nl, nd, nn, _DTYPES[dt],
+                                     _stream(dev))
+    _lib.check("ss_scan_bwd", st)
+    return g

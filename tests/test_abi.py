@@ -232,3 +232,55 @@ def test_options_validation(lib):
     assert call_scan_ex(lib, dstate=8, options=1) == UNSUPPORTED
     assert call_scan_ex(lib, ws=None, options=2) == WORKSPACE
     assert call_step_ex(lib, u=None, options=2) == INVALID
+
+
+def call_bwd(lib, **kw):
+    args = dict(u=addr(0), delta=addr(1), A=addr(2), B=addr(3), C=addr(4), D=None, z=None, h0=None, bias=None,
+                options=0, dy=addr(5), dh_last=None, du=addr(6), ddelta=addr(7), dA=addr(8), dB=addr(9),
+                dC=addr(10), dD=None, dz=None, dbias=None, dh0=None, ws=addr(11), ws_bytes=1 << 40, batch=2,
+                seqlen=512, dim=64, dstate=16, dtype=BF16)
+    args.update(kw)
+    return lib.ss_scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                           args["h0"], args["bias"], args["options"], args["dy"], args["dh_last"], args["du"],
+                           args["ddelta"], args["dA"], args["dB"], args["dC"], args["dD"], args["dz"],
+                           args["dbias"], args["dh0"], args["ws"], args["ws_bytes"], args["batch"], args["seqlen"],
+                           args["dim"], args["dstate"], args["dtype"], None)
+
+
+def test_bwd_workspace_size(lib):
+    b, l, d, n = 2, 300, 100, 16
+    ws = lib.ss_scan_bwd_workspace_bytes(b, l, d, n)
+    sub = -(-l // 16)
+    nblk = -(-d // 64)
+    ckpt = 4 * sub * b * n * d
+    parts = 4 * (2 * nblk * b * l * n + b * d * n + 2 * b * d)
+    panel = 4 * b * 2 * n * l
+    assert ckpt + parts + panel <= ws <= ckpt + parts + panel + 7 * 256 + 4 * b * 2 * n * 64
+    assert lib.ss_scan_bwd_workspace_bytes(0, l, d, n) == ctypes.c_size_t(-1).value
+
+
+def test_bwd_validation(lib):
+    """Every rejection happens on the host, before anything is enqueued."""
+    for name in ("u", "delta", "A", "B", "C", "dy", "du", "ddelta", "dA", "dB", "dC"):
+        assert call_bwd(lib, **{name: None}) == INVALID, name
+    # a gradient output is required for each optional input given
+    assert call_bwd(lib, D=addr(12)) == INVALID
+    assert call_bwd(lib, z=addr(12)) == INVALID
+    assert call_bwd(lib, bias=addr(12)) == INVALID
+    assert call_bwd(lib, options=2) == UNSUPPORTED            # no zero-order hold in the backward
+    assert call_bwd(lib, options=4) == UNSUPPORTED
+    assert call_bwd(lib, dstate=8) == UNSUPPORTED
+    assert call_bwd(lib, batch=70000, seqlen=1, dim=1) == UNSUPPORTED
+    assert call_bwd(lib, seqlen=2 ** 20, dim=2 ** 10) == UNSUPPORTED  # a batch row's slab >= 2 GiB
+    assert call_bwd(lib, ws=None) == WORKSPACE
+    assert call_bwd(lib, ws_bytes=1000) == WORKSPACE
+    assert call_bwd(lib, ws=ctypes.c_void_p(BASE + 11 * GAP + 64)) == INVALID
+    odd = ctypes.c_void_p(BASE + 13 * GAP + 1)
+    for name in ("dy", "du", "ddelta", "dB", "dC"):
+        assert call_bwd(lib, **{name: odd}) == INVALID, name
+    near = lambda i, off: ctypes.c_void_p(BASE + i * GAP + off)  # noqa: E731
+    assert call_bwd(lib, du=near(0, 512)) == INVALID          # du inside u
+    assert call_bwd(lib, dB=near(5, 0)) == INVALID            # dB on dy
+    assert call_bwd(lib, dC=near(9, 256)) == INVALID          # dC inside dB
+    assert call_bwd(lib, dh0=near(8, 64)) == INVALID          # dh0 inside dA
+    assert call_bwd(lib, ws=near(6, 0)) == INVALID            # workspace on du

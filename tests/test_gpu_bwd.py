@@ -1,0 +1,119 @@
+"""GPU parity of ss_scan_bwd (gradients of the scan) against the fp64 oracle backward.
+
+The oracle's backward is pinned by torch autograd and by finite differences
+(tests/pins.py).  Tolerances are the forward's: max relative error (gpu_util.rel_err)
+<= 1e-4 with fp32 operands, <= 2e-2 with bf16 operands (their gradients are rounded
+to bf16 once; dA, dD, the bias gradient and dh0 stay fp32).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import TOL, dev, host64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+GRADS = ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0")
+
+
+def ss():
+    import selective_state_space_85_amd as m
+
+    return m
+
+
+def make_case(batch, seqlen, dim, dtype, *, has_D, has_z, has_h0, softplus, seed, with_dh=True):
+    inp = wl.scan_inputs(batch, seqlen, dim, 16, dtype, has_D=has_D, has_z=has_z, has_h0=has_h0, seed=seed)
+    if softplus:
+        inp = wl.with_raw_delta(inp, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    dy = rng.standard_normal((batch, seqlen, dim)).astype(np.float32)
+    if dtype == wl.BF16:
+        dy = wl.f32_to_bf16_bits(dy)
+    dhl = rng.standard_normal((batch, dim, 16)).astype(np.float32) if with_dh else None
+    return inp, dy, dhl
+
+
+def gpu_grads(inp, dy, dhl, softplus):
+    t = {k: dev(v) for k, v in inp.items()}
+    g = ss().scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dev(dy), D=t.get("D"), z=t.get("z"),
+                      h0=t.get("h0"), dh_last=dev(dhl), delta_bias=t.get("delta_bias"), delta_softplus=softplus)
+    torch.cuda.synchronize()
+    return g
+
+
+def check(inp, dy, dhl, softplus, what, threads=1):
+    g = gpu_grads(inp, dy, dhl, softplus)
+    dyw = oracle.widen(dy)
+    ref = oracle.scan_bwd(**inp, dy=dyw, dh_last=dhl, delta_softplus=softplus, threads=threads)
+    tol = TOL["bf16" if inp["u"].dtype == np.uint16 else "f32"]
+    msg = []
+    for k in GRADS:
+        if k not in ref:
+            assert k not in g or k == "dh0", "%s: unexpected gradient %s" % (what, k)
+            continue
+        got = host64(g[k])
+        assert np.all(np.isfinite(got)), "%s: %s not finite" % (what, k)
+        e = rel_err(got, ref[k])
+        msg.append("%s %.1e" % (k, e))
+        assert e <= tol, "%s: %s error %.3e > %.0e" % (what, k, e, tol)
+    say("  %s: %s" % (what, ", ".join(msg)))
+    return g
+
+
+CASES = [
+    # (batch, seqlen, dim, dtype, has_D, has_z, has_h0, softplus, with_dh)
+    (1, 64, 64, wl.F32, True, True, True, False, True),
+    (2, 100, 100, wl.F32, True, True, True, False, True),      # ragged rows and channels
+    (2, 16, 64, wl.F32, False, False, False, False, False),    # plain scan, no dh_last
+    (3, 37, 130, wl.F32, True, False, True, True, True),       # softplus + bias
+    (1, 1, 1, wl.F32, True, True, True, True, True),           # one step, one channel
+    (2, 33, 70, wl.BF16, True, True, False, False, True),
+    (1, 257, 192, wl.BF16, True, True, True, True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["B%dL%dD%d-%s%s%s%s%s" % (c[0], c[1], c[2], c[3], "-D" * c[4], "-z" * c[5],
+                                                                    "-h0" * c[6], "-sp" * c[7]) for c in CASES])
+def test_bwd_small(case):
+    b, l, d, dt, has_D, has_z, has_h0, sp, with_dh = case
+    inp, dy, dhl = make_case(b, l, d, dt, has_D=has_D, has_z=has_z, has_h0=has_h0, softplus=sp, seed=40 + l,
+                             with_dh=with_dh)
+    say("backward B%d L%d D%d %s" % (b, l, d, dt))
+    check(inp, dy, dhl, sp, "B%d L%d D%d %s" % (b, l, d, dt))
+
+
+def test_bwd_deterministic():
+    """Fixed-order sums: two calls give the same bits."""
+    inp, dy, dhl = make_case(2, 200, 200, wl.F32, has_D=True, has_z=True, has_h0=True, softplus=True, seed=51)
+    say("backward determinism")
+    g1 = gpu_grads(inp, dy, dhl, True)
+    g2 = gpu_grads(inp, dy, dhl, True)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_bwd_zero_dy_gives_zero_gradients():
+    """dy = 0 and no dh_last: every gradient is exactly zero."""
+    inp, dy, _ = make_case(2, 50, 96, wl.BF16, has_D=True, has_z=True, has_h0=True, softplus=True, seed=52)
+    dy = np.zeros_like(dy)
+    say("backward with dy = 0")
+    g = gpu_grads(inp, dy, None, True)
+    for k, v in g.items():
+        assert torch.count_nonzero(v).item() == 0, k
+
+
+def test_bwd_large_layer():
+    """The large-layer shape (B8 L2048 D5120, bf16, D skip and gate), every output
+    element against the full oracle backward."""
+    w = wl.WORKLOADS["large"]
+    inp = wl.workload_inputs(w)
+    rng = np.random.default_rng(53)
+    dy = wl.f32_to_bf16_bits(rng.standard_normal((w.batch, w.seqlen, w.dim)).astype(np.float32))
+    say("backward on the large layer")
+    check(inp, dy, None, False, "large layer", threads=THREADS)
