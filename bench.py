@@ -13,8 +13,9 @@ fp64 CPU oracle timed on a bounded sample of the same workload.
 Extra objects: ``decode_step`` (ss_step on the B=256, D=5120 recurrent-step
 workload), ``parity`` (timed output vs the oracle on sampled channels),
 ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
-before every step) and ``options`` (the same layer with the softplus(delta +
-bias) step size and/or the zero-order-hold input term).
+before every step), ``options`` (the same layer with the softplus(delta +
+bias) step size and/or the zero-order-hold input term) and ``backward``
+(ss_scan_bwd on the same layer: all input gradients from dy).
 """
 from __future__ import annotations
 
@@ -248,6 +249,31 @@ def main():
             opt_res[name] = {"ms_per_step": oms, "elements/s": elements / (oms * 1e-3),
                              "alg_GB/s": (alg_bytes + 4 * w.dim * sp) / (oms * 1e-3) / 1e9}
         result["options"] = opt_res
+
+        # the backward on the same layer
+        dy_t = torch.randn(w.batch, w.seqlen, w.dim, device=device, generator=torch.Generator(device).manual_seed(5)
+                           ).to(torch.bfloat16)
+        bws = torch.empty(ss.scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate), dtype=torch.uint8,
+                          device=device)
+
+        def bstep():
+            ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=bws)
+
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / 10
+        result["backward"] = {"ms_per_step": bms, "elements/s": elements / (bms * 1e-3),
+                              "vs_forward": bms / ms_step, "workspace_bytes": bws.numel(),
+                              "note": "panel + prep (forward with checkpoints, dC, dz) + adjoint + reduce"}
+        del bws
 
         # recurrent step workload: one token for B=256, D=5120, state in place
         sw = wl.WORKLOADS["step"]

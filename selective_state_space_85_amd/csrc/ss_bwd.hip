@@ -34,10 +34,9 @@ namespace {
 
 constexpr int kSub = kBwdSub;             // rows per sub-block (checkpoint spacing)
 constexpr int kHalf = kSub / 2;           // the backward finishes a sub-block in two halves
-constexpr int kPW = kSub * kNS / 16;      // 16-word panel loads per sub-block and plane
 static_assert(kSub == 2 * kTileRows, "a sub-block is two panel tiles");
 static_assert(kHalf == kGroups, "each wave publishes and finishes one row of each half");
-static_assert((kSub * kNS) % 16 == 0, "panel rows of a sub-block come in 16-word loads");
+static_assert(kHalf * kNS == 16, "one 16-word scalar load holds a wave's entries of a half's rows");
 
 __device__ __forceinline__ float sigmoid(float v) { return __builtin_amdgcn_rcpf(1.0f + exp2_hw(-v * kLog2e)); }
 
@@ -72,24 +71,19 @@ struct Lane {
     {
         return make_rsrc(static_cast<const T*>(base) + b * a.seqlen * a.dim, uint32_t(a.seqlen) * row_bytes);
     }
-    __device__ void words(int j, Words16 (&bw)[kPW], Words16 (&cw)[kPW]) const
+    // this wave's B (or C) entries of the 8 rows of half `half` of sub-block j
+    __device__ Words16 words_B(int j, int half) const
     {
-        const uint32_t off = uint32_t(j) * uint32_t(kSub * kNS * 4);
-        const SS_CONST Words16* qb = (const SS_CONST Words16*)(pB + off);
-        const SS_CONST Words16* qc = (const SS_CONST Words16*)(pC + off);
-#pragma unroll
-        for (int q = 0; q < kPW; ++q) {
-            bw[q] = qb[q];
-            cw[q] = qc[q];
-        }
+        return *(const SS_CONST Words16*)(pB + uint32_t(j * kSub + half * kHalf) * uint32_t(kNS * 4));
+    }
+    __device__ Words16 words_C(int j, int half) const
+    {
+        return *(const SS_CONST Words16*)(pC + uint32_t(j * kSub + half * kHalf) * uint32_t(kNS * 4));
     }
 };
 
-__device__ __forceinline__ float word(const Words16 (&wv)[kPW], int r, int i)
-{
-    const int k = r * kNS + i;
-    return __uint_as_float(wv[k / 16][k % 16]);
-}
+// entry i of row rr (0..7) of a half, from its 16 words
+__device__ __forceinline__ float word(const Words16& wv, int rr, int i) { return __uint_as_float(wv[rr * kNS + i]); }
 
 // The rows a wave publishes (and, in the backward, finishes) in a sub-block:
 // row w of the first half and row w of the second.
@@ -150,14 +144,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
     Rows<DT> rows;
     rows.template issue<HAS_Z>(ln, L, 0, r_dl, r_u, r_dy, r_z);
     float xf[2], dyf[2], zf[2];
-    Words16 bw[kPW], cw[kPW];
 
     for (int j = 0; j < int(a.n_sub); ++j) {
         if (ln.active) {
 #pragma unroll
             for (int i = 0; i < kNS; ++i) a.ckpt[((int64_t(j) * NB + ln.b) * N + w * kNS + i) * D + ln.d] = h[i];
         }
-        ln.words(j, bw, cw);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int r = row_of(w, k);
@@ -176,19 +168,30 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
         __syncthreads();
 
 #pragma unroll
-        for (int r = 0; r < kSub; ++r) {
-            const float4 rv = s_row[r][lane];
-            const int64_t t = int64_t(j) * kSub + r;
-            float ypart = 0.0f;
+        for (int tile = 0; tile < 2; ++tile) {
+            const Words16 bw = ln.words_B(j, tile);
+            Words16 cw;
+            if constexpr (HAS_Z) cw = ln.words_C(j, tile);
+            float dc[16];  // dy' * h_t for the tile's 8 rows and the wave's 2 entries
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) {
-                const float e = exp2_hw(rv.x * A2[i]);
-                h[i] = fmaf(e, h[i], rv.y * word(bw, r, i));
-                const float dc = wave_sum_to_lane63(rv.z * h[i]);
-                if (lane == kWave - 1 && t < L) a.part_dC[((blk * NB + ln.b) * L + t) * N + w * kNS + i] = dc;
-                if (HAS_Z) ypart = fmaf(word(cw, r, i), h[i], ypart);
+            for (int rr = 0; rr < kHalf; ++rr) {
+                const int r = tile * kHalf + rr;
+                const float4 rv = s_row[r][lane];
+                float ypart = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kNS; ++i) {
+                    const float e = exp2_hw(rv.x * A2[i]);
+                    h[i] = fmaf(e, h[i], rv.y * word(bw, rr, i));
+                    dc[rr * kNS + i] = rv.z * h[i];
+                    if constexpr (HAS_Z) ypart = fmaf(word(cw, rr, i), h[i], ypart);
+                }
+                if constexpr (HAS_Z) s_y[w][r][lane] = ypart;
             }
-            if constexpr (HAS_Z) s_y[w][r][lane] = ypart;
+            // channel sums; lane l holds entry l/4 = (row, state) of the tile
+            const float tot = sum16_across_lanes(dc);
+            const int k = lane >> 2;
+            const int64_t t = int64_t(j) * kSub + tile * kHalf + (k >> 1);
+            if ((lane & 3) == 0 && t < L) a.part_dC[((blk * NB + ln.b) * L + t) * N + w * kNS + (k & 1)] = tot;
         }
         __syncthreads();
 
@@ -248,10 +251,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
     Rows<DT> rows;
     rows.template issue<HAS_Z>(ln, L, int(a.n_sub) - 1, r_dl, r_u, r_dy, r_z);
     float xf[2], dlf[2], sgf[2], dypf[2];
-    Words16 bw[kPW], cw[kPW];
 
     for (int j = int(a.n_sub) - 1; j >= 0; --j) {
-        ln.words(j, bw, cw);
         float hprev[kNS];
 #pragma unroll
         for (int i = 0; i < kNS; ++i)
@@ -277,35 +278,47 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
         // the sub-block's states, rebuilt from its checkpoint
         float hh[kSub][kNS];
 #pragma unroll
-        for (int r = 0; r < kSub; ++r) {
-            const float4 rv = s_row[r][lane];
+        for (int half = 0; half < 2; ++half) {
+            const Words16 bw = ln.words_B(j, half);
 #pragma unroll
-            for (int i = 0; i < kNS; ++i)
-                hh[r][i] = fmaf(exp2_hw(rv.x * A2[i]), r ? hh[r - 1][i] : hprev[i], rv.y * word(bw, r, i));
+            for (int rr = 0; rr < kHalf; ++rr) {
+                const int r = half * kHalf + rr;
+                const float4 rv = s_row[r][lane];
+#pragma unroll
+                for (int i = 0; i < kNS; ++i)
+                    hh[r][i] = fmaf(exp2_hw(rv.x * A2[i]), r ? hh[r - 1][i] : hprev[i], rv.y * word(bw, rr, i));
+            }
         }
 
 #pragma unroll
         for (int half = 1; half >= 0; --half) {
+            const Words16 bw = ln.words_B(j, half), cw = ln.words_C(j, half);
+            float db[16];  // g * delta * u for the half's 8 rows and the wave's 2 entries
 #pragma unroll
             for (int rr = kHalf - 1; rr >= 0; --rr) {
                 const int r = half * kHalf + rr;
-                const int64_t t = int64_t(j) * kSub + r;
                 const float4 rv = s_row[r][lane];
                 float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
                 for (int i = 0; i < kNS; ++i) {
-                    g[i] = fmaf(rv.z, word(cw, r, i), g[i]);
+                    g[i] = fmaf(rv.z, word(cw, rr, i), g[i]);
                     const float hp = r ? hh[r - 1][i] : hprev[i];
                     const float e = exp2_hw(rv.x * A2[i]);
                     const float t1 = g[i] * hp * e;
                     dA_acc[i] = fmaf(t1, rv.x, dA_acc[i]);
                     s2 = fmaf(t1, Av[i], s2);
-                    s1 = fmaf(g[i], word(bw, r, i), s1);
-                    const float db = wave_sum_to_lane63(g[i] * rv.y);
-                    if (lane == kWave - 1 && t < L) a.part_dB[((blk * NB + ln.b) * L + t) * N + w * kNS + i] = db;
+                    s1 = fmaf(g[i], word(bw, rr, i), s1);
+                    db[rr * kNS + i] = g[i] * rv.y;
                     g[i] *= e;
                 }
                 s_par[w][rr][lane] = make_float2(s1, s2);
+            }
+            {
+                // channel sums; lane l holds entry l/4 = (row, state) of the half
+                const float tot = sum16_across_lanes(db);
+                const int k = lane >> 2;
+                const int64_t t = int64_t(j) * kSub + half * kHalf + (k >> 1);
+                if ((lane & 3) == 0 && t < L) a.part_dB[((blk * NB + ln.b) * L + t) * N + w * kNS + (k & 1)] = tot;
             }
             __syncthreads();
             {

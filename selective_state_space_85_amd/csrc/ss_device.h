@@ -187,5 +187,51 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v)
     return add_from<kDppRowBcast31, 0xc>(v);
 }
 
+// Channel sums of 16 per-lane values at once: afterwards every lane l holds
+// the sum over the wave's 64 lanes of v[l / 4].  A butterfly that halves the
+// number of live vectors at each step, pairing vector p with vector p + m:
+//   swap of the 32-lane halves (v_permlane32_swap): vector p holds value p in
+//     lanes 0-31 and value p + 8 in lanes 32-63, each a sum over two lanes;
+//   swap of odd and even 16-lane rows (v_permlane16_swap): value p + 4*(l/16);
+//   within each row, the two 8-lane halves (row rotation by 8): value
+//     p + 2*((l/8)&1) + 4*(l/16);
+//   within each 8 lanes, the two quarters (half-row mirror): value l/4;
+//   and a sum over each quad (quad permutations 1,0,3,2 and 2,3,0,1).
+// 38 instructions for 16 sums, where one DPP tree per value costs 6 each.
+constexpr int kDppRowRor8 = 0x128, kDppRowHalfMirror = 0x141, kDppQuadSwap1 = 0xB1, kDppQuadSwap2 = 0x4E;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float sum16_across_lanes(const float (&v)[16])
+{
+    const int lane = threadIdx.x & 63;
+    float w[8], x[4], y[2];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[p]), __float_as_uint(v[p + 8]), false, false);
+        w[p] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[p]), __float_as_uint(w[p + 4]), false, false);
+        x[p] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+    const bool hi8 = (lane & 8) != 0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const float keep = hi8 ? x[p + 2] : x[p];
+        const float give = hi8 ? x[p] : x[p + 2];
+        y[p] = keep + dpp<kDppRowRor8>(give);
+    }
+    const bool hi4 = (lane & 4) != 0;
+    float z = (hi4 ? y[1] : y[0]) + dpp<kDppRowHalfMirror>(hi4 ? y[0] : y[1]);
+    z += dpp<kDppQuadSwap1>(z);
+    return z + dpp<kDppQuadSwap2>(z);
+}
+
 }  // namespace
 }  // namespace ssk
