@@ -10,6 +10,8 @@ import this package.  The library path never does.
   (zero-order-hold Bbar of the walk-through's section 2.2).
 * ``scan_bwd`` calls the fp64 backward in ``ss_oracle.c``: the chain rule taken
   backward through the same recurrence, every state recomputed per lane.
+* ``conv1d_silu`` calls the fp64 causal depthwise convolution + SiLU of the Mamba
+  block (walk-through section 3.4) that produces the scan's u.
 * ``twin_scan`` (in ``twin.py``) is an independent NumPy statement of the same
   definition, used only to cross-check the C loop on tiny shapes.
 
@@ -60,6 +62,8 @@ class OracleLib:
         lib.oracle_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, i64,
                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip]
         lib.oracle_scan_bwd.restype = ctypes.c_int
+        lib.oracle_conv1d_silu.argtypes = [vp, i64, vp, vp, ip, i64, i64, i64, i64, vp]
+        lib.oracle_conv1d_silu.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -71,6 +75,9 @@ class OracleLib:
 
     def scan_bwd(self, *args, **kwargs):
         return scan_bwd(*args, _lib=self.lib, **kwargs)
+
+    def conv1d_silu(self, *args, **kwargs):
+        return conv1d_silu(*args, _lib=self.lib, **kwargs)
 
 
 def _load():
@@ -234,6 +241,29 @@ def scan_bwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: 
     if bias is None:
         del out["ddelta_bias"]
     return out
+
+
+def conv1d_silu(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray] = None, *, dim: Optional[int] = None,
+                _lib=None) -> np.ndarray:
+    """fp64 causal depthwise convolution + SiLU.  x: (B, L, S) float32 or bf16 bits with the
+    channels in its first ``dim`` columns (default S: all of them; e.g. the x half of a
+    (B, L, 2D) projection with dim = D); weight (dim, width), bias (dim,) float32.
+    Returns u (B, L, dim) float64."""
+    lib = _lib or _load()
+    dt = _dtype_of(x)
+    x = _c(x)
+    batch, seqlen, stride = x.shape
+    dim = stride if dim is None else int(dim)
+    weight = _c(weight, np.float32)
+    width = weight.shape[1]
+    if weight.shape != (dim, width):
+        raise ValueError("weight must be (dim, width)")
+    bias = _c(bias, np.float32)
+    u = np.empty((batch, seqlen, dim), dtype=np.float64)
+    rc = lib.oracle_conv1d_silu(_ptr(x), stride, _ptr(weight), _ptr(bias), dt, batch, seqlen, dim, width, _ptr(u))
+    if rc != 0:
+        raise ValueError("oracle_conv1d_silu rejected its arguments")
+    return u
 
 
 def widen(a: np.ndarray) -> np.ndarray:

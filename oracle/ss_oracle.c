@@ -464,3 +464,33 @@ int oracle_scan_bwd(const void* u, const void* delta, const float* A, const void
     free(job.acc);
     return rc;
 }
+
+/*
+ * oracle_conv1d_silu: the Mamba block's causal depthwise convolution and
+ * SiLU that produce the scan's input u (walk-through, section 3.4: a Conv1d
+ * with one filter per channel, padding width-1 and only the first L outputs
+ * kept, then silu):
+ *   u[b,t,d] = silu(bias[d] + sum_{k=0}^{width-1} w[d,k] * x[b, t-width+1+k, d]),
+ * with x = 0 before t = 0.  x rows are x_row_stride elements apart (x may be
+ * the first half of a (B, L, 2D) projection read in place); w is (D, width)
+ * fp32, bias (D) fp32 or NULL.  u_out (B, L, D) double.  Returns 0 or -1.
+ */
+int oracle_conv1d_silu(const void* x, int64_t x_row_stride, const float* w, const float* bias, int dtype,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t width, double* u_out)
+{
+    if (!x || !w || !u_out) return -1;
+    if (batch <= 0 || seqlen <= 0 || dim <= 0 || width <= 0 || x_row_stride < dim) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t t = 0; t < seqlen; ++t)
+            for (int64_t d = 0; d < dim; ++d) {
+                double acc = bias ? (double)bias[d] : 0.0;
+                for (int64_t k = 0; k < width; ++k) {
+                    const int64_t s = t - width + 1 + k;
+                    if (s < 0) continue;
+                    acc += (double)w[d * width + k] * widen(x, (b * seqlen + s) * x_row_stride + d, dtype);
+                }
+                u_out[(b * seqlen + t) * dim + d] = silu(acc);
+            }
+    return 0;
+}

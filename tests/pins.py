@@ -564,7 +564,61 @@ def pin_bwd_finite_differences(orc):
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), "finite differences %s: %.9g vs %.9g" % (gk, an, fd)
 
 
+# ---------------------------------------------------------------------------
+# 17. causal depthwise convolution + SiLU (walk-through section 3.4): against
+#     torch's fp64 grouped conv1d with the block's padding and truncation; the
+#     impulse response; causality; the x half of a (B, L, 2D) projection read
+#     in place
+# ---------------------------------------------------------------------------
+def pin_conv1d_silu(orc):
+    import torch
+
+    rng = np.random.default_rng(28)
+    for (nb, nl, nd, width, dtype) in ((2, 40, 7, 4, "f32"), (1, 33, 16, 3, "bf16"), (3, 5, 4, 6, "f32")):
+        x = rng.standard_normal((nb, nl, nd)).astype(np.float32)
+        if dtype == "bf16":
+            x = f32_to_bf16_bits(x)
+        wt = rng.standard_normal((nd, width)).astype(np.float32)
+        bias = rng.standard_normal(nd).astype(np.float32)
+        got = orc.conv1d_silu(x, wt, bias)
+        xt = torch.tensor(_f64(x)).transpose(1, 2)                       # (B, D, L)
+        ref = torch.nn.functional.conv1d(xt, torch.tensor(wt, dtype=torch.float64)[:, None, :],
+                                         torch.tensor(bias, dtype=torch.float64), padding=width - 1,
+                                         groups=nd)[:, :, :nl]
+        ref = torch.nn.functional.silu(ref).transpose(1, 2).numpy()
+        _close(got, ref, 1e-13, "conv1d vs torch (%d,%d,%d,w%d)" % (nb, nl, nd, width))
+        # no bias = bias of zeros
+        _close(orc.conv1d_silu(x, wt), orc.conv1d_silu(x, wt, np.zeros(nd, np.float32)), 0.0, "no bias")
+
+    # impulse at t0 in channel 1: silu(bias + w[1, width-1-(t-t0)]) for t0 <= t < t0+width, silu(bias) elsewhere
+    nl, nd, width, t0 = 20, 3, 4, 6
+    x = np.zeros((1, nl, nd), np.float32)
+    x[0, t0, 1] = 1.0
+    wt = rng.standard_normal((nd, width)).astype(np.float32)
+    bias = rng.standard_normal(nd).astype(np.float32)
+    got = orc.conv1d_silu(x, wt, bias)[0, :, 1]
+    pre = np.full(nl, float(bias[1]))
+    for t in range(t0, t0 + width):
+        pre[t] += float(wt[1, width - 1 - (t - t0)])
+    _close(got, _silu(pre), 1e-15, "conv1d impulse response")
+
+    # causality: changing x at t1 leaves u before t1 bit-identical
+    x = rng.standard_normal((2, 30, 5)).astype(np.float32)
+    wt = rng.standard_normal((5, 4)).astype(np.float32)
+    a = orc.conv1d_silu(x, wt)
+    x2 = x.copy()
+    x2[:, 17:, :] += 1.0
+    b = orc.conv1d_silu(x2, wt)
+    assert np.array_equal(a[:, :17], b[:, :17]) and not np.array_equal(a[:, 17:], b[:, 17:]), "conv1d causality"
+
+    # the x half of xz (B, L, 2D) read in place equals the contiguous copy
+    xz = f32_to_bf16_bits(rng.standard_normal((2, 12, 10)).astype(np.float32))
+    wt = rng.standard_normal((5, 4)).astype(np.float32)
+    assert np.array_equal(orc.conv1d_silu(xz, wt, dim=5), orc.conv1d_silu(np.ascontiguousarray(xz[:, :, :5]), wt)), \
+        "conv1d strided rows"
+
+
 ALL_PINS = [pin_hand_worked, pin_single_step_closed_form, pin_lti_convolution, pin_zero_input,
             pin_brute_force, pin_geometric, pin_delta_limits, pin_chaining,
             pin_causality_linearity, pin_bookkeeping, pin_twin, pin_zoh_step_response,
-            pin_zoh_limits, pin_softplus_bias, pin_bwd_autograd, pin_bwd_finite_differences]
+            pin_zoh_limits, pin_softplus_bias, pin_bwd_autograd, pin_bwd_finite_differences, pin_conv1d_silu]

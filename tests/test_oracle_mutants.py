@@ -60,6 +60,16 @@ MUTANTS = [
     ("silu derivative wrong", "s * (1.0 + zz * (1.0 - s))", "s * (1.0 + zz * s)"),
     ("skip uses the ungated gradient", "dD[d] += dyt * x;", "dD[d] += j->dy[row] * x;"),
     ("softplus derivative dropped", "            dd *= sigmoid(v);\n", "            (void)v;\n"),
+    # the convolution
+    ("conv taps reversed", "acc += (double)w[d * width + k] * widen(x, (b * seqlen + s) * x_row_stride + d, dtype);",
+     "acc += (double)w[d * width + (width - 1 - k)] * widen(x, (b * seqlen + s) * x_row_stride + d, dtype);"),
+    ("conv drops its oldest tap", "for (int64_t k = 0; k < width; ++k) {\n                    const int64_t s",
+     "for (int64_t k = 1; k < width; ++k) {\n                    const int64_t s"),
+    ("conv without its bias", "double acc = bias ? (double)bias[d] : 0.0;", "double acc = 0.0;"),
+    ("conv output not through silu", "u_out[(b * seqlen + t) * dim + d] = silu(acc);",
+     "u_out[(b * seqlen + t) * dim + d] = acc;"),
+    ("conv rows read contiguous", "widen(x, (b * seqlen + s) * x_row_stride + d, dtype)",
+     "widen(x, (b * seqlen + s) * dim + d, dtype)"),
     ("dh0 before the last decay", "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n];",
      "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n] / exp(dl[0] * (double)f->A[d * N + n]);"),
 ]
