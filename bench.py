@@ -14,8 +14,10 @@ Extra objects: ``decode_step`` (ss_step on the B=256, D=5120 recurrent-step
 workload), ``parity`` (timed output vs the oracle on sampled channels),
 ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
 before every step), ``options`` (the same layer with the softplus(delta +
-bias) step size and/or the zero-order-hold input term) and ``backward``
-(ss_scan_bwd on the same layer: all input gradients from dy).
+bias) step size and/or the zero-order-hold input term), ``backward``
+(ss_scan_bwd on the same layer: all input gradients from dy) and ``conv1d``
+(ss_conv1d_silu producing the layer's u from the x half of a (B, L, 2D)
+in-projection output, with its HBM roofline).
 """
 from __future__ import annotations
 
@@ -274,6 +276,33 @@ def main():
                               "vs_forward": bms / ms_step, "workspace_bytes": bws.numel(),
                               "note": "panel + prep (forward with checkpoints, dC, dz) + adjoint + reduce"}
         del bws
+
+        # the block's causal depthwise convolution + SiLU producing u (x read in place from xz)
+        xz = torch.randn(w.batch, w.seqlen, 2 * w.dim, device=device,
+                         generator=torch.Generator(device).manual_seed(6)).to(torch.bfloat16)
+        cw = torch.randn(w.dim, 4, device=device, generator=torch.Generator(device).manual_seed(7)) * 0.5
+        cb = torch.randn(w.dim, device=device, generator=torch.Generator(device).manual_seed(8))
+        cu = torch.empty(w.batch, w.seqlen, w.dim, dtype=torch.bfloat16, device=device)
+
+        def cstep():
+            ss.conv1d_silu(xz[..., :w.dim], cw, cb, out=cu)
+
+        for _ in range(3):
+            cstep()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            cstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / 20
+        cbytes = 2 * 2 * w.batch * w.seqlen * w.dim + 4 * w.dim * 5  # x read + u written (bf16), weights, bias
+        cgbs = cbytes / (cms * 1e-3) / 1e9
+        result["conv1d"] = {"workload": "B=8 L=2048 D=5120 bf16, width 4, x = first half of xz (B, L, 2D)",
+                            "ms": cms, "alg_bytes": cbytes, "alg_GB/s": cgbs, "frac_of_8TB/s": cgbs / HBM_PEAK_GBS}
+        del xz, cu
 
         # recurrent step workload: one token for B=256, D=5120, state in place
         sw = wl.WORKLOADS["step"]

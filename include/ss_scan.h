@@ -235,6 +235,27 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                       ss_dtype dtype, hipStream_t stream);
 
+/*
+ * ss_conv1d_silu -- the Mamba block's causal depthwise convolution and SiLU
+ * that produce the scan's input u (walk-through, section 3.4: a Conv1d with
+ * one filter of `width` taps per channel, padding width-1, only the first L
+ * outputs kept, then silu):
+ *   u[b,t,d] = silu(bias[d] + sum_{k<width} weight[d,k] * x[b, t-width+1+k, d]),
+ * with x = 0 before t = 0.
+ *
+ *   x      : (batch, seqlen, dim) dtype, rows x_row_stride (>= dim) elements
+ *            apart: the x half of the in-projection output xz (batch, seqlen,
+ *            2*dim) is read in place with x_row_stride = 2*dim
+ *   weight : (dim, width) fp32;  bias : (dim,) fp32 or NULL (no bias)
+ *   u      : (batch, seqlen, dim) dtype, contiguous; must not overlap x,
+ *            weight or bias
+ *   width  : 2, 3 or 4 (SS_ERR_UNSUPPORTED otherwise)
+ * x and u are aligned to their element size; weight and bias to 4 bytes.
+ */
+ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weight, const float* bias,
+                         void* u, int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                         ss_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* ss_status_string(ss_status s);
 

@@ -456,6 +456,37 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
     return SS_OK;
 }
 
+ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weight, const float* bias, void* u,
+                         int64_t batch, int64_t seqlen, int64_t dim, int64_t width, ss_dtype dtype,
+                         hipStream_t stream)
+{
+    if (!x || !weight || !u) return SS_ERR_INVALID_ARG;
+    if (batch <= 0 || seqlen <= 0 || dim <= 0 || width <= 0 || x_row_stride < dim) return SS_ERR_INVALID_ARG;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
+    if (width < 2 || width > 4) return SS_ERR_UNSUPPORTED;
+    const int64_t es = dtype == SS_F32 ? 4 : 2;
+    int64_t bl, u_elems, x_elems, u_bytes, x_bytes;
+    if (!mul(batch, seqlen, &bl) || !mul(bl, dim, &u_elems) || !mul(u_elems, es, &u_bytes)) return SS_ERR_INVALID_ARG;
+    // x spans (batch*seqlen - 1) strides plus one row of dim elements
+    if (!mul(bl - 1, x_row_stride, &x_elems) || __builtin_add_overflow(x_elems, dim, &x_elems) ||
+        !mul(x_elems, es, &x_bytes))
+        return SS_ERR_INVALID_ARG;
+    if (batch > kMaxGridYZ || ceil_div(seqlen, ssk::kConvRows) > kMaxGridYZ) return SS_ERR_UNSUPPORTED;
+    if (!aligned(x, uintptr_t(es)) || !aligned(u, uintptr_t(es))) return SS_ERR_INVALID_ARG;
+    if (!aligned(weight, 4) || (bias && !aligned(bias, 4))) return SS_ERR_INVALID_ARG;
+    const Range r_u = span(u, u_bytes);
+    if (overlap(r_u, span(x, x_bytes)) || overlap(r_u, span(weight, dim * width * 4)) ||
+        overlap(r_u, span(bias, dim * 4)))
+        return SS_ERR_INVALID_ARG;
+    // 8-byte accesses when every row start is 8-byte aligned
+    const int vec = int(8 / es);
+    const bool vec_ok = dim % vec == 0 && x_row_stride % vec == 0 && aligned(x, 8) && aligned(u, 8);
+    ssk::ConvArgs a{x, x_row_stride, weight, bias, u, batch, seqlen, dim, width};
+    const hipError_t err = ssk::launch_conv(a, dtype == SS_F32 ? 0 : 1, vec_ok ? vec : 1, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    return SS_OK;
+}
+
 const char* ss_status_string(ss_status st)
 {
     switch (st) {

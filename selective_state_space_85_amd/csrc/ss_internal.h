@@ -117,6 +117,18 @@ struct BwdArgs {
     int64_t batch, seqlen, dim, n_sub, nblk;
 };
 
+// Causal depthwise convolution + SiLU: rows of output per thread run.
+constexpr int64_t kConvRows = 64;
+
+struct ConvArgs {
+    const void* x;     // rows of x_stride elements
+    int64_t x_stride;
+    const float* w;    // (dim, width)
+    const float* bias; // (dim,), nullable
+    void* u;           // (batch, seqlen, dim)
+    int64_t batch, seqlen, dim, width;
+};
+
 // Each returns the hipError_t of its launches (hipSuccess when all were enqueued).
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, int dtype, hipStream_t stream);
@@ -124,5 +136,7 @@ hipError_t launch_step(const StepArgs& a, int dtype, hipStream_t stream);
 // a.chunk_len, a.n_chunks)
 hipError_t launch_panel(const ScanArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
+// vec: channels per thread, 1, or 4 (bf16) / 2 (fp32) when the host has checked alignment
+hipError_t launch_conv(const ConvArgs& a, int dtype, int vec, hipStream_t stream);
 
 }  // namespace ssk

@@ -223,3 +223,33 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
                                      _stream(dev))
     _lib.check("ss_scan_bwd", st)
     return g
+
+
+def conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal depthwise convolution + SiLU ``ss_conv1d_silu``: u (B, L, D) from x (B, L, D),
+    weight (D, width) float32, bias (D,) float32.  x may be a column slice with unit inner
+    stride, e.g. ``xz[..., :D]`` of a contiguous (B, L, 2D) projection, read in place."""
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, dim)")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("conv1d_silu runs on the GPU; x is on %s" % dev)
+    dt = x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    nb, nl, nd = x.shape
+    if x.stride(2) != 1 or x.stride(0) != nl * x.stride(1):
+        raise ValueError("x rows must be evenly strided with unit channel stride")
+    if weight.dim() != 2 or weight.shape[0] != nd:
+        raise ValueError("weight must be (dim, width)")
+    _need(weight, "weight", tuple(weight.shape), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (nd,), torch.float32, dev)
+    u = out if out is not None else torch.empty((nb, nl, nd), dtype=dt, device=dev)
+    _need(u, "out", (nb, nl, nd), dt, dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().ss_conv1d_silu(_ptr(x), x.stride(1), _ptr(weight), _ptr(bias), _ptr(u), nb, nl, nd,
+                                        weight.shape[1], _DTYPES[dt], _stream(dev))
+    _lib.check("ss_conv1d_silu", st)
+    return u

@@ -284,3 +284,32 @@ def test_bwd_validation(lib):
     assert call_bwd(lib, dC=near(9, 256)) == INVALID          # dC inside dB
     assert call_bwd(lib, dh0=near(8, 64)) == INVALID          # dh0 inside dA
     assert call_bwd(lib, ws=near(6, 0)) == INVALID            # workspace on du
+
+
+def call_conv(lib, **kw):
+    args = dict(x=addr(0), stride=64, w=addr(1), bias=None, u=addr(2), batch=2, seqlen=100, dim=64, width=4,
+                dtype=BF16)
+    args.update(kw)
+    return lib.ss_conv1d_silu(args["x"], args["stride"], args["w"], args["bias"], args["u"], args["batch"],
+                              args["seqlen"], args["dim"], args["width"], args["dtype"], None)
+
+
+def test_conv_validation(lib):
+    for name in ("x", "w", "u"):
+        assert call_conv(lib, **{name: None}) == INVALID, name
+    for name in ("batch", "seqlen", "dim", "width"):
+        assert call_conv(lib, **{name: 0}) == INVALID, name
+    assert call_conv(lib, stride=63) == INVALID               # rows narrower than dim
+    assert call_conv(lib, width=1) == UNSUPPORTED
+    assert call_conv(lib, width=5) == UNSUPPORTED
+    assert call_conv(lib, dtype=3) == UNSUPPORTED
+    assert call_conv(lib, batch=70000) == UNSUPPORTED
+    odd = ctypes.c_void_p(BASE + 9 * GAP + 1)
+    assert call_conv(lib, x=odd) == INVALID
+    assert call_conv(lib, u=odd) == INVALID
+    assert call_conv(lib, w=ctypes.c_void_p(BASE + 9 * GAP + 2)) == INVALID
+    near = lambda i, off: ctypes.c_void_p(BASE + i * GAP + off)  # noqa: E731
+    assert call_conv(lib, u=near(0, 1000)) == INVALID         # u inside x
+    last_row = (2 * 100 - 1) * 128 * 2                          # byte offset of x's last row at stride 128
+    assert call_conv(lib, u=near(0, last_row + 100), stride=128) == INVALID  # u on the last strided x row
+    assert call_conv(lib, bias=near(2, 8)) == INVALID         # bias inside u
