@@ -12,6 +12,8 @@ import this package.  The library path never does.
   backward through the same recurrence, every state recomputed per lane.
 * ``conv1d_silu`` calls the fp64 causal depthwise convolution + SiLU of the Mamba
   block (walk-through section 3.4) that produces the scan's u.
+* ``ssd`` calls the fp64 multi-head recurrence of Mamba-2 (walk-through sections 4.1
+  and 5.2): an (N, P) state per head, scalar decay exp(dt A) per head.
 * ``twin_scan`` (in ``twin.py``) is an independent NumPy statement of the same
   definition, used only to cross-check the C loop on tiny shapes.
 
@@ -64,6 +66,8 @@ class OracleLib:
         lib.oracle_scan_bwd.restype = ctypes.c_int
         lib.oracle_conv1d_silu.argtypes = [vp, i64, vp, vp, ip, i64, i64, i64, i64, vp]
         lib.oracle_conv1d_silu.restype = ctypes.c_int
+        lib.oracle_ssd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, i64, i64, vp, i64, vp, vp]
+        lib.oracle_ssd.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -78,6 +82,9 @@ class OracleLib:
 
     def conv1d_silu(self, *args, **kwargs):
         return conv1d_silu(*args, _lib=self.lib, **kwargs)
+
+    def ssd(self, *args, **kwargs):
+        return ssd(*args, _lib=self.lib, **kwargs)
 
 
 def _load():
@@ -264,6 +271,38 @@ def conv1d_silu(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray] = 
     if rc != 0:
         raise ValueError("oracle_conv1d_silu rejected its arguments")
     return u
+
+
+def ssd(x: np.ndarray, dt: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
+        D: Optional[np.ndarray] = None, h0: Optional[np.ndarray] = None,
+        heads: Optional[Sequence[int]] = None, _lib=None) -> Dict[str, np.ndarray]:
+    """fp64 multi-head recurrence.  x (B, L, H, P), dt (B, L, H), B, C (B, L, N) in float32 or
+    bf16 bits; A, D (H,) float32; h0 (B, H, N, P) any float.  Returns ``y`` (B, L, H, P) and
+    ``h_last`` (B, H, N, P) -- or (n, L, P) / (n, N, P) for ``heads`` = flat b*H + h."""
+    lib = _lib or _load()
+    dtp = _dtype_of(x)
+    batch, seqlen, nh, hdim = x.shape
+    dstate = B.shape[2]
+    for name, arr, shp in (("dt", dt, (batch, seqlen, nh)), ("B", B, (batch, seqlen, dstate)),
+                           ("C", C, (batch, seqlen, dstate))):
+        if tuple(arr.shape) != shp or _dtype_of(arr) != dtp:
+            raise ValueError("%s has shape %s dtype %s" % (name, arr.shape, arr.dtype))
+    x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
+    A = _c(A, np.float32)
+    D = _c(D, np.float32)
+    h0 = _c(h0, np.float64)
+    sel = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    n = batch * nh if sel is None else sel.size
+    y = np.empty((n, seqlen, hdim))
+    hl = np.empty((n, dstate, hdim))
+    rc = lib.oracle_ssd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), dtp, batch, seqlen, nh,
+                        hdim, dstate, _ptr(sel), n, _ptr(y), _ptr(hl))
+    if rc != 0:
+        raise ValueError("oracle_ssd rejected its arguments")
+    if sel is None:
+        return {"y": y.reshape(batch, nh, seqlen, hdim).transpose(0, 2, 1, 3).copy(),
+                "h_last": hl.reshape(batch, nh, dstate, hdim)}
+    return {"y": y, "h_last": hl}
 
 
 def widen(a: np.ndarray) -> np.ndarray:

@@ -494,3 +494,59 @@ int oracle_conv1d_silu(const void* x, int64_t x_row_stride, const float* w, cons
             }
     return 0;
 }
+
+/*
+ * oracle_ssd: the multi-head state-space recurrence of Mamba-2 (walk-through,
+ * section 4.1: h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t, with a state per
+ * head; section 5.2: heads of headdim channels and d_state up to 128-256).
+ * Per batch row b and head h the state S is (N, P):
+ *   S_t = exp(dt[b,t,h] * A[h]) S_{t-1} + dt[b,t,h] * B[b,t,:] (outer) x[b,t,h,:]
+ *   y[b,t,h,:] = S_t^T C[b,t,:] + D[h] x[b,t,h,:]
+ * A_t = exp(dt A) with a scalar A per head and the input term dt*B*x are
+ * the discretisation of section 2.2 (the same as oracle_scan's) applied per
+ * head; B and C are shared by all heads.  x, y (B, L, H, P); dt (B, L, H);
+ * B, C (B, L, N), all in `dtype`; A, D (H) fp32 (D may be NULL); h0 (B, H, N,
+ * P) double or NULL.  Outputs (double): y_out (B, L, H, P), h_last (B, H, N,
+ * P), either may be NULL.  heads: NULL for all (b, h) pairs in order, or a
+ * list of flat b*H + h (then y_out is (n, L, P) and h_last (n, N, P)).
+ * Returns 0 or -1.
+ */
+int oracle_ssd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+               const double* h0, int dtype, int64_t batch, int64_t seqlen, int64_t heads, int64_t hdim,
+               int64_t dstate, const int64_t* sel, int64_t n_sel, double* y_out, double* h_last)
+{
+    if (!x || !dt || !A || !B || !C) return -1;
+    if (batch <= 0 || seqlen <= 0 || heads <= 0 || hdim <= 0 || dstate <= 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    const int64_t L = seqlen, H = heads, P = hdim, N = dstate;
+    if (!sel) n_sel = batch * H;
+    double* S = (double*)malloc(sizeof(double) * (size_t)(N * P));
+    if (!S) return -1;
+    for (int64_t k = 0; k < n_sel; ++k) {
+        const int64_t bh = sel ? sel[k] : k;
+        if (bh < 0 || bh >= batch * H) {
+            free(S);
+            return -1;
+        }
+        const int64_t b = bh / H, h = bh % H;
+        for (int64_t i = 0; i < N * P; ++i) S[i] = h0 ? h0[bh * N * P + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double d = widen(dt, (b * L + t) * H + h, dtype);
+            const double a = exp(d * (double)A[h]);
+            const int64_t xrow = ((b * L + t) * H + h) * P, srow = (b * L + t) * N;
+            for (int64_t n = 0; n < N; ++n) {
+                const double bn = widen(B, srow + n, dtype);
+                for (int64_t p = 0; p < P; ++p) S[n * P + p] = a * S[n * P + p] + d * bn * widen(x, xrow + p, dtype);
+            }
+            for (int64_t p = 0; p < P; ++p) {
+                double y = 0.0;
+                for (int64_t n = 0; n < N; ++n) y += S[n * P + p] * widen(C, srow + n, dtype);
+                if (D) y += (double)D[h] * widen(x, xrow + p, dtype);
+                if (y_out) y_out[(k * L + t) * P + p] = y;
+            }
+        }
+        if (h_last) memcpy(&h_last[k * N * P], S, sizeof(double) * (size_t)(N * P));
+    }
+    free(S);
+    return 0;
+}

@@ -618,7 +618,77 @@ def pin_conv1d_silu(orc):
         "conv1d strided rows"
 
 
+# ---------------------------------------------------------------------------
+# 18. multi-head recurrence (walk-through section 4.1): its dual, the causal
+#     structured matrix applied to the inputs,
+#       y_t = sum_{s<=t} (C_t . B_s) exp(A sum_{s<r<=t} dt_r) dt_s x_s + exp(A sum_{r<=t} dt_r) C_t . h0 + D x_t,
+#     materialised as an L x L matrix per head; and its reduction to the
+#     selective scan (every head channel is a scan channel with A broadcast over
+#     the state entries and the head's dt); chaining
+# ---------------------------------------------------------------------------
+def _ssd_case(rng, nb, nl, nh, hp, ns, dtype="f32", has_D=True, has_h0=True):
+    def cast(a):
+        a = np.asarray(a, dtype=np.float32)
+        return f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+    x = cast(rng.standard_normal((nb, nl, nh, hp)))
+    dt = cast(np.log1p(np.exp(rng.normal(-1.5, 0.8, (nb, nl, nh)))))
+    A = -np.exp(rng.uniform(-1.0, 1.0, nh)).astype(np.float32)
+    B = cast(rng.standard_normal((nb, nl, ns)))
+    C = cast(rng.standard_normal((nb, nl, ns)))
+    D = rng.standard_normal(nh).astype(np.float32) if has_D else None
+    h0 = rng.standard_normal((nb, nh, ns, hp)).astype(np.float32) if has_h0 else None
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, h0=h0)
+
+
+def pin_ssd_dual_form(orc):
+    rng = np.random.default_rng(29)
+    for (nb, nl, nh, hp, ns, dtype) in ((2, 13, 3, 4, 5, "f32"), (1, 21, 2, 8, 16, "bf16")):
+        c = _ssd_case(rng, nb, nl, nh, hp, ns, dtype)
+        got = orc.ssd(**c)
+        x, dt, B, C = _f64(c["x"]), _f64(c["dt"]), _f64(c["B"]), _f64(c["C"])
+        A = c["A"].astype(np.float64)
+        y = np.zeros((nb, nl, nh, hp))
+        for b in range(nb):
+            for h in range(nh):
+                cum = np.cumsum(dt[b, :, h])                      # sum_{r<=t} dt_r
+                seg = cum[:, None] - cum[None, :]                 # sum_{s<r<=t} dt_r
+                Lmat = np.where(np.tril(np.ones((nl, nl))) > 0, np.exp(A[h] * seg), 0.0)
+                M = Lmat * (C[b] @ B[b].T)                        # (T o M) of the dual form
+                y[b, :, h] = M @ (dt[b, :, h, None] * x[b, :, h])
+                y[b, :, h] += np.exp(A[h] * cum)[:, None] * (C[b] @ c["h0"][b, h].astype(np.float64))
+                y[b, :, h] += c["D"][h] * x[b, :, h]
+        _close(got["y"], y, 1e-12, "SSD dual form (%d,%d,%d,%d,%d)" % (nb, nl, nh, hp, ns))
+
+
+def pin_ssd_reduces_to_scan(orc):
+    rng = np.random.default_rng(30)
+    nb, nl, nh, hp, ns = 2, 17, 3, 4, 16
+    c = _ssd_case(rng, nb, nl, nh, hp, ns)
+    got = orc.ssd(**c)
+    d = nh * hp
+    u = c["x"].reshape(nb, nl, d)
+    delta = np.repeat(c["dt"], hp, axis=2)                            # channel h*P + p takes dt of head h
+    A = np.repeat(c["A"], hp)[:, None] * np.ones((1, ns), np.float32)
+    Dskip = np.repeat(c["D"], hp)
+    h0 = c["h0"].transpose(0, 1, 3, 2).reshape(nb, d, ns)             # (B, H, N, P) -> (B, H*P, N)
+    ref = orc.scan(u, delta, A.astype(np.float32), c["B"], c["C"], D=Dskip, h0=h0)
+    _close(got["y"].reshape(nb, nl, d), ref["y"], 1e-13, "SSD as a selective scan")
+    _close(got["h_last"].transpose(0, 1, 3, 2).reshape(nb, d, ns), ref["h_last"], 1e-13, "SSD state as scan state")
+    # chaining: the first 9 steps then the rest from their state
+    first = {k: (v[:, :9] if k in ("x", "dt", "B", "C") else v) for k, v in c.items()}
+    rest = {k: (v[:, 9:] if k in ("x", "dt", "B", "C") else v) for k, v in c.items()}
+    a = orc.ssd(**first)
+    rest["h0"] = a["h_last"]
+    b = orc.ssd(**rest)
+    assert np.array_equal(np.concatenate([a["y"], b["y"]], axis=1), got["y"]), "SSD chaining"
+    sel = [1, 4, 5]
+    part = orc.ssd(**c, heads=sel)
+    assert np.array_equal(part["y"], got["y"].transpose(0, 2, 1, 3).reshape(nb * nh, nl, hp)[sel]), "SSD head subset"
+
+
 ALL_PINS = [pin_hand_worked, pin_single_step_closed_form, pin_lti_convolution, pin_zero_input,
             pin_brute_force, pin_geometric, pin_delta_limits, pin_chaining,
             pin_causality_linearity, pin_bookkeeping, pin_twin, pin_zoh_step_response,
-            pin_zoh_limits, pin_softplus_bias, pin_bwd_autograd, pin_bwd_finite_differences, pin_conv1d_silu]
+            pin_zoh_limits, pin_softplus_bias, pin_bwd_autograd, pin_bwd_finite_differences, pin_conv1d_silu,
+            pin_ssd_dual_form, pin_ssd_reduces_to_scan]

@@ -70,6 +70,15 @@ MUTANTS = [
      "u_out[(b * seqlen + t) * dim + d] = acc;"),
     ("conv rows read contiguous", "widen(x, (b * seqlen + s) * x_row_stride + d, dtype)",
      "widen(x, (b * seqlen + s) * dim + d, dtype)"),
+    # the multi-head recurrence
+    ("SSD decay sign flipped", "const double a = exp(d * (double)A[h]);", "const double a = exp(-d * (double)A[h]);"),
+    ("SSD input without dt", "S[n * P + p] = a * S[n * P + p] + d * bn * widen(x, xrow + p, dtype);",
+     "S[n * P + p] = a * S[n * P + p] + bn * widen(x, xrow + p, dtype);"),
+    ("SSD output reads B", "y += S[n * P + p] * widen(C, srow + n, dtype);", "y += S[n * P + p] * widen(B, srow + n, dtype);"),
+    ("SSD state transposed", "y += S[n * P + p] * widen(C, srow + n, dtype);",
+     "y += S[(p % N) * P + (n % P)] * widen(C, srow + n, dtype);"),
+    ("SSD dt of head 0", "const double d = widen(dt, (b * L + t) * H + h, dtype);",
+     "const double d = widen(dt, (b * L + t) * H, dtype);"),
     ("dh0 before the last decay", "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n];",
      "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n] / exp(dl[0] * (double)f->A[d * N + n]);"),
 ]
