@@ -256,6 +256,32 @@ ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weigh
                          void* u, int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
                          ss_dtype dtype, hipStream_t stream);
 
+/*
+ * ss_ssd_fwd -- the multi-head state-space recurrence of Mamba-2 (walk-through,
+ * section 4.1: h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t with a state per
+ * head, and its dual form, a causal structured matrix applied to the inputs;
+ * section 5.2: heads of 64 channels, d_state 64-256).  Per batch row b and
+ * head h, with an (dstate x headdim) state S and a scalar decay per head:
+ *   S_t = exp(dt[b,t,h] A[h]) S_{t-1} + dt[b,t,h] B[b,t,:] x[b,t,h,:]^T
+ *   y[b,t,h,:] = S_t^T C[b,t,:] + D[h] x[b,t,h,:]
+ * (the discretisation of ss_scan_fwd applied per head; B and C shared by all
+ * heads).  Computed chunk by chunk on the matrix cores: bf16 products with
+ * fp32 accumulation, the state kept in fp32.
+ *
+ *   x, y   : (batch, seqlen, heads, headdim)  bf16, 16-byte aligned
+ *   dt     : (batch, seqlen, heads)           bf16 (positive step sizes)
+ *   A      : (heads,) fp32;  D : (heads,) fp32 or NULL
+ *   B, C   : (batch, seqlen, dstate)          bf16, 16-byte aligned
+ *   h0     : (batch, heads, dstate, headdim)  fp32 or NULL (zero state)
+ *   h_last : (batch, heads, dstate, headdim)  fp32 output or NULL
+ * Supported: dtype SS_BF16, headdim 64, dstate 64 or 128 (SS_ERR_UNSUPPORTED
+ * otherwise).  y and h_last must not overlap the inputs or each other.
+ */
+ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                     const float* D, const float* h0, void* y, float* h_last,
+                     int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                     ss_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* ss_status_string(ss_status s);
 

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libssscan.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("ss_kernels.hip", "ss_bwd.hip", "ss_conv.hip", "ss_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("ss_kernels.hip", "ss_bwd.hip", "ss_conv.hip", "ss_ssd.hip", "ss_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 (v_pk_*_f32) is switched off for all device code.

@@ -487,6 +487,40 @@ ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weigh
     return SS_OK;
 }
 
+ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                     const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen, int64_t heads,
+                     int64_t headdim, int64_t dstate, ss_dtype dtype, hipStream_t stream)
+{
+    if (!x || !dt || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
+    if (batch <= 0 || seqlen <= 0 || heads <= 0 || headdim <= 0 || dstate <= 0) return SS_ERR_INVALID_ARG;
+    if (dtype != SS_BF16 && dtype != SS_F32) return SS_ERR_UNSUPPORTED;
+    if (dtype != SS_BF16 || headdim != 64 || (dstate != 64 && dstate != 128)) return SS_ERR_UNSUPPORTED;
+    if (batch > kMaxGridYZ || heads > INT32_MAX) return SS_ERR_UNSUPPORTED;
+    int64_t bl, xe, se, he, hs;
+    if (!mul(batch, seqlen, &bl) || !mul(bl, heads, &he) || !mul(he, headdim, &xe) || !mul(xe, 2, &xe))
+        return SS_ERR_INVALID_ARG;
+    if (!mul(bl, dstate, &se) || !mul(se, 2, &se) || !mul(he, 2, &he)) return SS_ERR_INVALID_ARG;
+    if (!mul(batch, heads, &hs) || !mul(hs, dstate, &hs) || !mul(hs, headdim, &hs) || !mul(hs, 4, &hs))
+        return SS_ERR_INVALID_ARG;
+    const void* v16[] = {x, B, C, y};
+    for (const void* p : v16)
+        if (!aligned(p, 16)) return SS_ERR_INVALID_ARG;
+    if (!aligned(dt, 2)) return SS_ERR_INVALID_ARG;
+    const void* f32[] = {A, D, h0, h_last};
+    for (const void* p : f32)
+        if (p && !aligned(p, 4)) return SS_ERR_INVALID_ARG;
+    const Range inputs[] = {span(x, xe), span(dt, he), span(A, heads * 4), span(B, se), span(C, se),
+                            span(D, heads * 4), span(h0, hs)};
+    const Range r_y = span(y, xe), r_hl = span(h_last, hs);
+    if (overlap(r_y, r_hl)) return SS_ERR_INVALID_ARG;
+    for (const Range& r : inputs)
+        if (overlap(r_y, r) || overlap(r_hl, r)) return SS_ERR_INVALID_ARG;
+    ssk::SsdArgs a{x, dt, A, B, C, D, h0, y, h_last, batch, seqlen, heads, dstate};
+    const hipError_t err = ssk::launch_ssd(a, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    return SS_OK;
+}
+
 const char* ss_status_string(ss_status st)
 {
     switch (st) {

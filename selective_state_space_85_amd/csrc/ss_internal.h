@@ -129,6 +129,20 @@ struct ConvArgs {
     int64_t batch, seqlen, dim, width;
 };
 
+// Multi-head state-space recurrence (bf16 operands, 64 channels per head).
+struct SsdArgs {
+    const void* x;     // (batch, seqlen, heads, 64)
+    const void* dt;    // (batch, seqlen, heads)
+    const float* A;    // (heads,)
+    const void* B;     // (batch, seqlen, dstate)
+    const void* C;     // (batch, seqlen, dstate)
+    const float* D;    // (heads,), nullable
+    const float* h0;   // (batch, heads, dstate, 64), nullable
+    void* y;           // (batch, seqlen, heads, 64)
+    float* h_last;     // (batch, heads, dstate, 64), nullable
+    int64_t batch, seqlen, heads, dstate;
+};
+
 // Each returns the hipError_t of its launches (hipSuccess when all were enqueued).
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, int dtype, hipStream_t stream);
@@ -138,5 +152,6 @@ hipError_t launch_panel(const ScanArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
 // vec: channels per thread, 1, or 4 (bf16) / 2 (fp32) when the host has checked alignment
 hipError_t launch_conv(const ConvArgs& a, int dtype, int vec, hipStream_t stream);
+hipError_t launch_ssd(const SsdArgs& a, hipStream_t stream);
 
 }  // namespace ssk

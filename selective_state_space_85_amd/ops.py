@@ -253,3 +253,38 @@ def conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
                                         weight.shape[1], _DTYPES[dt], _stream(dev))
     _lib.check("ss_conv1d_silu", st)
     return u
+
+
+def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+            D: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None, *,
+            return_last_state: bool = False, out: Optional[torch.Tensor] = None
+            ) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+    """Multi-head state-space recurrence ``ss_ssd_fwd`` (bf16, 64 channels per head).
+
+    x (B, L, H, 64), dt (B, L, H), B and C (B, L, N) bfloat16 with N 64 or 128; A, D (H,)
+    float32; h0 (B, H, N, 64) float32.  Returns y (B, L, H, 64) bfloat16 and, if asked,
+    h_last (B, H, N, 64) float32."""
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, heads, headdim)")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd runs on the GPU; x is on %s" % dev)
+    nb, nl, nh, hp = x.shape
+    ns = B.shape[-1]
+    dt_ = x.dtype
+    for t, name, shp, tdt in ((x, "x", (nb, nl, nh, hp), dt_), (dt, "dt", (nb, nl, nh), dt_),
+                              (A, "A", (nh,), torch.float32), (B, "B", (nb, nl, ns), dt_),
+                              (C, "C", (nb, nl, ns), dt_)):
+        _need(t, name, shp, tdt, dev)
+    if D is not None:
+        _need(D, "D", (nh,), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (nb, nh, ns, hp), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", (nb, nl, nh, hp), dt_, dev)
+    hl = torch.empty((nb, nh, ns, hp), dtype=torch.float32, device=dev) if return_last_state else None
+    with torch.cuda.device(dev):
+        st = _lib.load().ss_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+                                    _ptr(hl), nb, nl, nh, hp, ns, _DTYPES.get(dt_, 99), _stream(dev))
+    _lib.check("ss_ssd_fwd", st)
+    return (y, hl) if return_last_state else y

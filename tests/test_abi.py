@@ -313,3 +313,30 @@ def test_conv_validation(lib):
     last_row = (2 * 100 - 1) * 128 * 2                          # byte offset of x's last row at stride 128
     assert call_conv(lib, u=near(0, last_row + 100), stride=128) == INVALID  # u on the last strided x row
     assert call_conv(lib, bias=near(2, 8)) == INVALID         # bias inside u
+
+
+def call_ssd(lib, **kw):
+    args = dict(x=addr(0), dt=addr(1), A=addr(2), B=addr(3), C=addr(4), D=None, h0=None, y=addr(5), hl=None,
+                batch=2, seqlen=100, heads=4, hdim=64, dstate=128, dtype=BF16)
+    args.update(kw)
+    return lib.ss_ssd_fwd(args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"], args["h0"], args["y"],
+                          args["hl"], args["batch"], args["seqlen"], args["heads"], args["hdim"], args["dstate"],
+                          args["dtype"], None)
+
+
+def test_ssd_validation(lib):
+    for name in ("x", "dt", "A", "B", "C", "y"):
+        assert call_ssd(lib, **{name: None}) == INVALID, name
+    for name in ("batch", "seqlen", "heads", "hdim", "dstate"):
+        assert call_ssd(lib, **{name: 0}) == INVALID, name
+    assert call_ssd(lib, dtype=F32) == UNSUPPORTED
+    assert call_ssd(lib, hdim=32) == UNSUPPORTED
+    assert call_ssd(lib, dstate=256) == UNSUPPORTED
+    assert call_ssd(lib, batch=70000) == UNSUPPORTED
+    eight = ctypes.c_void_p(BASE + 9 * GAP + 8)
+    for name in ("x", "B", "C", "y"):
+        assert call_ssd(lib, **{name: eight}) == INVALID, name
+    near = lambda i, off: ctypes.c_void_p(BASE + i * GAP + off)  # noqa: E731
+    assert call_ssd(lib, y=near(0, 4096)) == INVALID            # y inside x
+    assert call_ssd(lib, hl=near(3, 64)) == INVALID             # h_last inside B
+    assert call_ssd(lib, hl=near(5, 1024)) == INVALID           # h_last inside y

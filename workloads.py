@@ -32,7 +32,8 @@ F32 = "f32"
 BF16 = "bf16"
 
 # tensor ids for the per-tensor streams
-_TID = {"u": 0, "delta": 1, "A": 2, "B": 3, "C": 4, "D": 5, "z": 6, "h0": 7, "delta_bias": 8}
+_TID = {"u": 0, "delta": 1, "A": 2, "B": 3, "C": 4, "D": 5, "z": 6, "h0": 7, "delta_bias": 8,
+        "x": 9, "dt": 10}
 
 _CHUNK = 1 << 22  # values per generation block (bounds the float32 temporaries)
 
@@ -179,6 +180,29 @@ def with_raw_delta(inp: Dict[str, Optional[np.ndarray]], *, raw_sigma: float = 0
     dt = np.exp(g.uniform(np.log(dt_min), np.log(dt_max), dim))
     out["delta_bias"] = np.log(np.expm1(dt)).astype(np.float32)
     return out
+
+
+def ssd_inputs(batch: int, seqlen: int, heads: int, hdim: int, dstate: int, *, has_D: bool = True,
+               has_h0: bool = False, seed: int = 0, cfg_id: int = 0) -> Dict[str, Optional[np.ndarray]]:
+    """Inputs of the multi-head recurrence, bf16 bits for x (B,L,H,P), dt (B,L,H), B and C
+    (B,L,N); fp32 A (H,) = -U(1, 16), D (H,) ~ N(0,1), h0 (B,H,N,P) ~ N(0,1).
+    dt = softplus(N(-2, 1)) as for the scan; x, B, C ~ N(0, 1)."""
+    out: Dict[str, Optional[np.ndarray]] = {}
+    out["x"] = _store(_normal(_rng(seed, cfg_id, "x"), (batch, seqlen, heads, hdim)), BF16)
+    out["dt"] = _store(_softplus_normal(_rng(seed, cfg_id, "dt"), (batch, seqlen, heads), -2.0, 1.0), BF16)
+    out["A"] = (-_rng(seed, cfg_id, "A").uniform(1.0, 16.0, heads)).astype(np.float32)
+    out["B"] = _store(_normal(_rng(seed, cfg_id, "B"), (batch, seqlen, dstate)), BF16)
+    out["C"] = _store(_normal(_rng(seed, cfg_id, "C"), (batch, seqlen, dstate)), BF16)
+    out["D"] = _normal(_rng(seed, cfg_id, "D"), (heads,)) if has_D else None
+    out["h0"] = _normal(_rng(seed, cfg_id, "h0"), (batch, heads, dstate, hdim)) if has_h0 else None
+    return out
+
+
+def algorithmic_bytes_ssd(batch: int, seqlen: int, heads: int, hdim: int, dstate: int, has_D: bool = True) -> int:
+    """HBM bytes the multi-head recurrence must move: x read and y written (bf16), dt, B and C
+    read (bf16), A and D (fp32)."""
+    rows = batch * seqlen
+    return 2 * 2 * rows * heads * hdim + 2 * rows * heads + 2 * 2 * rows * dstate + 4 * heads * (1 + int(has_D))
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[np.ndarray]]:
