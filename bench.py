@@ -15,9 +15,11 @@ workload), ``parity`` (timed output vs the oracle on sampled channels),
 ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
 before every step), ``options`` (the same layer with the softplus(delta +
 bias) step size and/or the zero-order-hold input term), ``backward``
-(ss_scan_bwd on the same layer: all input gradients from dy) and ``conv1d``
+(ss_scan_bwd on the same layer: all input gradients from dy), ``conv1d``
 (ss_conv1d_silu producing the layer's u from the x half of a (B, L, 2D)
-in-projection output, with its HBM roofline).
+in-projection output, with its HBM roofline) and ``ssd`` (ss_ssd_fwd, the
+multi-head recurrence on the matrix cores, B=8 L=2048, 64 heads of 64
+channels, dstate 128).
 """
 from __future__ import annotations
 
@@ -303,6 +305,36 @@ def main():
         result["conv1d"] = {"workload": "B=8 L=2048 D=5120 bf16, width 4, x = first half of xz (B, L, 2D)",
                             "ms": cms, "alg_bytes": cbytes, "alg_GB/s": cgbs, "frac_of_8TB/s": cgbs / HBM_PEAK_GBS}
         del xz, cu
+
+        # the multi-head (Mamba-2) recurrence on the matrix cores
+        sb, sl, sh, sn = 8, 2048, 64, 128
+        si = wl.ssd_inputs(sb, sl, sh, 64, sn, seed=0)
+        stt = {k: to_dev(v) for k, v in si.items() if v is not None}
+        sy = torch.empty_like(stt["x"])
+
+        def sstep():
+            ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy)
+
+        for _ in range(3):
+            sstep()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            sstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / 20
+        sbytes = wl.algorithmic_bytes_ssd(sb, sl, sh, 64, sn)
+        # executed bf16 MFMA 32x32x16 per 64-row chunk and head: 24 (C B^T, upper block skipped)
+        # + 64 (C S_in, hi + lo) + 24 (M X, hi + lo, upper half skipped) + 64 (state, hi + lo)
+        sflops = 176 * 32 * 32 * 16 * 2 * (sl // 64) * sb * sh
+        result["ssd"] = {"workload": "B=8 L=2048 H=64 headdim=64 dstate=128 bf16, D skip",
+                         "ms": sms, "alg_bytes": sbytes, "alg_GB/s": sbytes / (sms * 1e-3) / 1e9,
+                         "frac_of_8TB/s": sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "mfma_TFLOP/s": sflops / (sms * 1e-3) / 1e12, "frac_of_2.5PF": sflops / (sms * 1e-3) / 2.5e15}
+        del stt, sy
 
         # recurrent step workload: one token for B=256, D=5120, state in place
         sw = wl.WORKLOADS["step"]
