@@ -274,8 +274,10 @@ ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weigh
  *   B, C   : (batch, seqlen, dstate)          bf16, 16-byte aligned
  *   h0     : (batch, heads, dstate, headdim)  fp32 or NULL (zero state)
  *   h_last : (batch, heads, dstate, headdim)  fp32 output or NULL
- * Supported: dtype SS_BF16, headdim 64, dstate 64 or 128 (SS_ERR_UNSUPPORTED
- * otherwise).  y and h_last must not overlap the inputs or each other.
+ * Supported: dtype SS_BF16, headdim 64, dstate 64 or 128, and one batch row of
+ * x (seqlen*heads*headdim*2 bytes) and of B (seqlen*dstate*2 bytes) below
+ * 2 GiB (SS_ERR_UNSUPPORTED otherwise).  y and h_last must not overlap the
+ * inputs or each other.
  */
 ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
                      const float* D, const float* h0, void* y, float* h_last,

@@ -496,6 +496,9 @@ ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* 
     if (dtype != SS_BF16 && dtype != SS_F32) return SS_ERR_UNSUPPORTED;
     if (dtype != SS_BF16 || headdim != 64 || (dstate != 64 && dstate != 128)) return SS_ERR_UNSUPPORTED;
     if (batch > kMaxGridYZ || heads > INT32_MAX) return SS_ERR_UNSUPPORTED;
+    // the kernel addresses one batch row of x, y (and B, C) with 32-bit byte offsets
+    const int64_t row_bytes = 2 * (heads * headdim > dstate ? heads * headdim : dstate);
+    if (seqlen > (int64_t(1) << 31) / row_bytes - 1) return SS_ERR_UNSUPPORTED;
     int64_t bl, xe, se, he, hs;
     if (!mul(batch, seqlen, &bl) || !mul(bl, heads, &he) || !mul(he, headdim, &xe) || !mul(xe, 2, &xe))
         return SS_ERR_INVALID_ARG;

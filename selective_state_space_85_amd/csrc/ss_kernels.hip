@@ -305,7 +305,19 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
     issue_words(0, Slot<0>{});
     __syncthreads();
 
+    // Two or three workgroups share a CU, and the wave arbiter favours older
+    // waves: left alone, the first workgroup finishes far ahead of the last and
+    // the CU ends its run with a single latency-bound workgroup.  Lowering a
+    // wave's priority at each quarter of the chunk lets the laggards catch up,
+    // so the workgroups of a CU stay within a quarter of each other.
+    const int quarter = (ntiles / 4) & ~1;
+    __builtin_amdgcn_s_setprio(3);
     for (int k = 0; k < ntiles; k += 2) {
+        if (quarter > 0) {
+            if (k == quarter) __builtin_amdgcn_s_setprio(2);
+            else if (k == 2 * quarter) __builtin_amdgcn_s_setprio(1);
+            else if (k == 3 * quarter) __builtin_amdgcn_s_setprio(0);
+        }
         step(k, Slot<0>{});
         step(k + 1, Slot<1>{});
     }

@@ -11,147 +11,208 @@
 // (b, h) walks the sequence in chunks of 64 rows with the state in MFMA
 // accumulator registers (fp32) -- it never reaches memory between chunks.  Per
 // chunk, with cs_t = sum of dt_r A over the chunk's rows up to t:
-//   G      = C B^T                                   (64 x 64, over dstate)
+//   G^T    = B C^T                                   (s x t, over dstate)
 //   M[t,s] = G[t,s] exp(cs_t - cs_s) dt_s  for s <= t, else 0
-//   Y      = M X + diag(exp(cs_t)) C S_in  (+ D x)   (the dual form inside the
-//                                                     chunk, the carried state)
-//   S_out^T = exp(cs_end) S_in^T + X^T diag(w) B,  w_s = exp(cs_end - cs_s) dt_s
-// Every operand that is a product (M, w*B) or the fp32 state goes to the
+//   Y^T    = X^T M^T + S_in^T C^T diag(exp(cs_t))  (+ D x)    (the dual form
+//            inside the chunk, plus the carried state)
+//   S_out  = exp(cs_end) S_in + B^T (w X),  w_s = exp(cs_end - cs_s) dt_s
+// Every operand that is a product (M, w*x) or the fp32 state goes to the
 // matrix cores as two bf16 parts, hi + lo (lo = the rounding error of hi), so
 // each such product keeps ~16 more bits: rounding these operands once to bf16
 // costs up to ~1% of y per operand on slowly decaying heads.
-// C is loaded straight into registers in the MFMA operand layout; B by row
-// (state index contiguous), x transposed (row index contiguous), M by row and
-// the state's two bf16 parts transposed are staged in LDS.  Blocks above the
-// diagonal of M are zero and skipped.
+//
+// Data movement.  Every LDS matrix is row-major and written with 8- or
+// 16-byte stores: x and B as they arrive, M and the state copy straight from
+// the accumulator layout.  An MFMA operand is 8 consecutive values along the
+// contraction index: where that index runs along a row it is one 16-byte
+// read, where it runs down a column (x and w*x over s, B over s) it comes
+// from two LDS transpose reads.  Y is formed transposed (p x t), so each lane
+// ends up with 4 consecutive channels of one row and stores them as 8 bytes.
+// C goes from memory straight into registers in the operand layout.  The next
+// chunk's x, B, C and dt are loaded into registers while the current chunk
+// computes, through range-checked buffer loads: rows past the sequence read
+// 0 and their y stores are dropped, so the ragged last chunk needs no
+// branches.  Blocks above the diagonal of M are zero and skipped.
 #include "ss_device.h"
 
 namespace ssk {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQ = 64;            // rows per chunk
 constexpr int kP = 64;            // channels per head
 constexpr int kSsdThreads = 256;  // 4 waves
 constexpr int kPad = 8;           // bf16 padding per LDS row (keeps 16-byte alignment)
+constexpr int kXP = kP + kPad;    // row pitch of x, M and w*x in LDS
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+// 8 bf16 along a row: one 16-byte LDS read
+__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-__device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
-
-// Accumulator layout of a 32x32 MFMA block: lane l, register r holds row
-// 8*(r/4) + 4*(l/32) + r%4 and column l%32.
-__device__ __forceinline__ int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi)
-__device__ __forceinline__ void store_split(uint16_t& hi, uint16_t& lo, float v)
+// 8 bf16 down a column: operand[i] = Mx[8*(lane/32) + i][lane%32] of the
+// row-major LDS block that starts at `base`, row pitch `pitch` elements.
+// Within each group of 16 lanes the transpose read gives lane i, as its
+// element k, element i%4 of the 4-vector that lane 4k + i/4 addresses.  So
+// lane j of the group addresses row j/4, columns 4*(j%4).. of a 4 x 16 block
+// and lane i receives rows 0..3 of column i; two reads cover the 8 rows.
+__device__ __forceinline__ bf16x8 lds_col8(const uint16_t* base, int pitch, int lane)
 {
-    const uint16_t h = f32_to_bf16_bits(v);
-    hi = h;
-    lo = f32_to_bf16_bits(v - __uint_as_float(uint32_t(h) << 16));
+    typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+    const int j = lane & 15, g = lane >> 4;
+    const uint16_t* p = base + (8 * (g >> 1) + (j >> 2)) * pitch + 16 * (g & 1) + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p + 4 * pitch));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
-// M rows are 64 bf16 (128 bytes) with no padding; its 8-element groups are
-// permuted per row (group g of row t at g ^ (t & 7)) so that the 32 rows a
-// 16-byte operand read touches fall on different banks.
-__device__ __forceinline__ int mcol(int t, int s) { return s ^ ((t & 7) << 3); }
+// the bf16 in the low 16 bits of `bits`, widened
+__device__ __forceinline__ float bf(uint32_t bits) { return __uint_as_float(bits << 16); }
+// ... in the high 16 bits
+__device__ __forceinline__ float bf_hi(uint32_t bits) { return __uint_as_float(bits & 0xffff0000u); }
+
+// two values rounded to bf16 (nearest even) in one conversion: a in the low
+// half, b in the high half
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi), for four values, each
+// part packed as 4 bf16 (8 bytes)
+__device__ __forceinline__ void split4(const float (&v)[4], u32x2& hi, u32x2& lo)
+{
+    const uint32_t h01 = pack_bf16(v[0], v[1]), h23 = pack_bf16(v[2], v[3]);
+    hi = u32x2{h01, h23};
+    lo = u32x2{pack_bf16(v[0] - bf(h01), v[1] - bf_hi(h01)), pack_bf16(v[2] - bf(h23), v[3] - bf_hi(h23))};
+}
 
 // grid = (heads, batch), block = 256.  Host guarantees bf16 operands, headdim
-// 64, dstate NS, 16-byte alignment of x, y, B, C.
+// 64, dstate NS, 16-byte alignment of x, y, B, C, and byte extents of one
+// batch row of x (seqlen*heads*128) and of B (seqlen*NS*2) below 2^31.
 template <int NS, bool HAS_D>
-__global__ __launch_bounds__(kSsdThreads) void ssd_kernel(SsdArgs a)
+__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))) void ssd_kernel(SsdArgs a)
 {
-    constexpr int kNB = NS / 32;               // 32-wide state blocks
-    constexpr int kSB = (kP / 32) * kNB;       // state blocks of S^T (p x n)
-    constexpr int kSPW = kSB / 4;              // state blocks per wave
-    static_assert(kSPW >= 1, "dstate 64 or 128");
+    constexpr int kNB = NS / 32;                    // 32-row blocks of the state (index n)
+    constexpr int kSPW = kNB * 2 / 4;               // state blocks (n block, p block) per wave
+    constexpr int kBP = NS + kPad;                  // row pitch of B and of the state copy in LDS
+    constexpr int kVB = kQ * NS / 8 / kSsdThreads;  // 16-byte pieces of B per thread and chunk
+    constexpr int kVX = kQ * kP / 8 / kSsdThreads;  // ... of x
+    constexpr int kKS = NS / 16;                    // MFMA steps over dstate
+    static_assert(kSPW >= 1 && kVB >= 1 && kVX >= 1, "dstate 64 or 128");
 
-    __shared__ __align__(16) uint16_t sB[kQ][NS + kPad];   // B chunk (s, n)
-    __shared__ __align__(16) uint16_t sXT[kP][kQ + kPad];  // x chunk transposed (p, s)
-    __shared__ __align__(16) uint16_t sMh[kQ][kQ];         // masked decay matrix (t, s), hi part (swizzled)
-    __shared__ __align__(16) uint16_t sMl[kQ][kQ];         // ... and lo part
-    __shared__ __align__(16) uint16_t sSh[kP][NS + kPad];  // state transposed (p, n), hi part
-    __shared__ __align__(16) uint16_t sSl[kP][NS + kPad];  // ... and lo part
-    __shared__ float s_cs[kQ], s_dt[kQ], s_ecs[kQ], s_w[kQ];
-    __shared__ float s_end;
+    __shared__ __align__(16) uint16_t sB[kQ][kBP];     // B chunk (s, n)
+    __shared__ __align__(16) uint16_t sX[kQ][kXP];     // x chunk (s, p)
+    __shared__ __align__(16) uint16_t sU[2][kQ][kXP];  // M (t, s) hi/lo, then w*x (s, p) hi/lo
+    __shared__ __align__(16) uint16_t sS[2][kP][kBP];  // state^T (p, n) hi/lo
+    __shared__ __align__(16) float s_cs[kQ];           // cs_t * log2 e
+    __shared__ __align__(16) float s_lc[kQ];           // cs_s * log2 e - log2(dt_s)  (+inf where dt_s = 0)
+    __shared__ float s_w[kQ];
+    __shared__ float s_end;  // exp(cs_end)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
     const int64_t h = blockIdx.x, b = blockIdx.y;
     const int64_t L = a.seqlen, H = a.heads;
-    const float Ah = a.A[h];
+    const float A2 = a.A[h] * kLog2e;
     const float Dh = HAS_D ? a.D[h] : 0.0f;
-    const uint16_t* __restrict__ X = static_cast<const uint16_t*>(a.x);
-    const uint16_t* __restrict__ DT = static_cast<const uint16_t*>(a.dt);
-    const uint16_t* __restrict__ Bg = static_cast<const uint16_t*>(a.B);
-    const uint16_t* __restrict__ Cg = static_cast<const uint16_t*>(a.C);
-    uint16_t* __restrict__ Y = static_cast<uint16_t*>(a.y);
 
-    // state blocks of this wave: block k -> (p block, n block)
+    // range-checked views of this (b, h): row t of x and y at t*H*128 bytes, of
+    // dt at t*H*2, of B and C at t*NS*2.  All offsets go in the vector operand.
+    const uint32_t x_row = uint32_t(H) * kP * 2, dt_row = uint32_t(H) * 2, bc_row = NS * 2;
+    const uint32_t x_ext = uint32_t(((L - 1) * H + 1) * kP * 2), dt_ext = uint32_t(((L - 1) * H + 1) * 2);
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(static_cast<const uint16_t*>(a.x) + (b * L * H + h) * kP, x_ext);
+    const __amdgpu_buffer_rsrc_t rY = make_rsrc(static_cast<uint16_t*>(a.y) + (b * L * H + h) * kP, x_ext);
+    const __amdgpu_buffer_rsrc_t rDT = make_rsrc(static_cast<const uint16_t*>(a.dt) + b * L * H + h, dt_ext);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const uint16_t*>(a.B) + b * L * NS, uint32_t(L) * bc_row);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<const uint16_t*>(a.C) + b * L * NS, uint32_t(L) * bc_row);
+
+    // this wave's blocks: G^T block (s block gs, t block tb), Y^T block (p block
+    // yp, t block tb), state blocks (n block, p block) number w*kSPW + j
+    const int tb = w & 1, gs = w >> 1, yp = w >> 1;
+    const bool has_g = gs <= tb;  // the G^T block with s > t throughout is zero
+
+    // ---- operands of a chunk in flight (issued one chunk ahead) ----
+    u32x4 pB[kVB], pX[kVX], pC[kKS];
+    uint32_t pdt = 0;
+    auto issue = [&](uint32_t t0) {
+#pragma unroll
+        for (int i = 0; i < kVB; ++i) {
+            const int v = tid + kSsdThreads * i, r = v / (NS / 8), c8 = (v % (NS / 8)) * 8;
+            pB[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, (t0 + r) * bc_row + c8 * 2, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kVX; ++i) {
+            const int v = tid + kSsdThreads * i, s = v / (kP / 8), p8 = (v % (kP / 8)) * 8;
+            pX[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, (t0 + s) * x_row + p8 * 2, 0, 0);
+        }
+        // C rows of this wave's t block in the MFMA operand layout (row l%32,
+        // entries 16*ks + 8*(l/32) .. +8)
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+            pC[ks] = __builtin_amdgcn_raw_buffer_load_b128(rC, (t0 + 32 * tb + l32) * bc_row + (16 * ks + 8 * hl) * 2,
+                                                           0, 0);
+        if (w == 0) pdt = __builtin_amdgcn_raw_buffer_load_b16(rDT, (t0 + lane) * dt_row, 0, 0);
+    };
+
+    // ---- initial state: accumulators (n x p blocks) and the LDS copy ----
     f32x16 acc_s[kSPW];
 #pragma unroll
     for (int j = 0; j < kSPW; ++j) {
-        const int blk = w * kSPW + j, pb = blk / kNB, nb = blk % kNB;
+        const int blk = w * kSPW + j, nb = blk % kNB, pb = blk / kNB;
+        const int p = 32 * pb + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int p = 32 * pb + acc_row(lane, r), n = 32 * nb + (lane & 31);
-            const float v = a.h0 ? a.h0[((b * H + h) * NS + n) * kP + p] : 0.0f;
-            acc_s[j][r] = v;
-            store_split(sSh[p][n], sSl[p][n], v);
+        for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = 32 * nb + 8 * q + 4 * hl + e;
+                v[e] = a.h0 ? a.h0[((b * H + h) * NS + n) * kP + p] : 0.0f;
+                acc_s[j][4 * q + e] = v[e];
+            }
+            u32x2 hi, lo;
+            split4(v, hi, lo);
+            *reinterpret_cast<u32x2*>(&sS[0][p][32 * nb + 8 * q + 4 * hl]) = hi;
+            *reinterpret_cast<u32x2*>(&sS[1][p][32 * nb + 8 * q + 4 * hl]) = lo;
         }
     }
 
-    const int bm = w >> 1, bn = w & 1;  // this wave's 32x32 block of G, M and Y
+    issue(0);
     const int64_t n_chunks = (L + kQ - 1) / kQ;
     for (int64_t c = 0; c < n_chunks; ++c) {
-        const int64_t t0 = c * kQ;
-        const int rows = int(L - t0 < kQ ? L - t0 : kQ);
+        const uint32_t t0 = uint32_t(c * kQ);
 
-        // ---- stage the chunk ----
-        // B and C: rows x NS bf16, 16-byte vectors
-        constexpr int kVecRow = NS / 8;
+        // ---- A: stage the chunk, start the next one's loads ----
 #pragma unroll
-        for (int i = 0; i < (kQ * kVecRow) / kSsdThreads; ++i) {
-            const int v = tid + kSsdThreads * i, r = v / kVecRow, c8 = (v % kVecRow) * 8;
-            uint4 qb = make_uint4(0, 0, 0, 0);
-            if (r < rows) qb = *reinterpret_cast<const uint4*>(Bg + (b * L + t0 + r) * NS + c8);
-            *reinterpret_cast<uint4*>(&sB[r][c8]) = qb;
+        for (int i = 0; i < kVB; ++i) {
+            const int v = tid + kSsdThreads * i, r = v / (NS / 8), c8 = (v % (NS / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&sB[r][c8]) = pB[i];
         }
-        // C: this wave's 32 rows, straight into the A-operand layout (row l%32,
-        // entries 16*ks + 8*(l/32) .. +8)
-        bf16x8 ca[NS / 16];
-        {
-            const int r = 32 * (w >> 1) + (lane & 31);
 #pragma unroll
-            for (int ks = 0; ks < NS / 16; ++ks) {
-                uint4 q = make_uint4(0, 0, 0, 0);
-                if (r < rows) q = *reinterpret_cast<const uint4*>(Cg + (b * L + t0 + r) * NS + 16 * ks + 8 * (lane >> 5));
-                ca[ks] = __builtin_bit_cast(bf16x8, q);
-            }
-        }
-        // x: rows x 64 bf16 (rows strided by H*64), written transposed
-#pragma unroll
-        for (int i = 0; i < (kQ * kP / 8) / kSsdThreads; ++i) {
+        for (int i = 0; i < kVX; ++i) {
             const int v = tid + kSsdThreads * i, s = v / (kP / 8), p8 = (v % (kP / 8)) * 8;
-            uint4 q = make_uint4(0, 0, 0, 0);
-            if (s < rows) q = *reinterpret_cast<const uint4*>(X + ((b * L + t0 + s) * H + h) * kP + p8);
-            const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sXT[p8 + 2 * k][s] = uint16_t(wd[k] & 0xffffu);
-                sXT[p8 + 2 * k + 1][s] = uint16_t(wd[k] >> 16);
-            }
+            *reinterpret_cast<u32x4*>(&sX[s][p8]) = pX[i];
         }
-        // dt*A prefix over the chunk (wave 0): inclusive scan across the 64 lanes
+        bf16x8 ca[kKS];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) ca[ks] = __builtin_bit_cast(bf16x8, pC[ks]);
+        // dt*A prefix over the chunk (wave 0): inclusive scan across the 64
+        // lanes, in log2 units; rows past the sequence have dt = 0
         if (w == 0) {
-            const float dt = lane < rows ? bf(DT[(b * L + t0 + lane) * H + h]) : 0.0f;
-            float v = dt * Ah;
+            const float dt = bf(pdt);
+            float v = dt * A2;
             v = add_from<kDppRowShr1, 0xf>(v);
             v = add_from<kDppRowShr2, 0xf>(v);
             v = add_from<kDppRowShr4, 0xf>(v);
@@ -160,108 +221,140 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_kernel(SsdArgs a)
             v = add_from<kDppRowBcast31, 0xc>(v);
             const float end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kQ - 1));
             s_cs[lane] = v;
-            s_dt[lane] = dt;
-            s_ecs[lane] = exp2_hw(v * kLog2e);
-            s_w[lane] = exp2_hw((end - v) * kLog2e) * dt;
-            if (lane == 0) s_end = exp2_hw(end * kLog2e);
+            s_lc[lane] = v - __builtin_amdgcn_logf(dt);
+            s_w[lane] = exp2_hw(end - v) * dt;
+            if (lane == 0) s_end = exp2_hw(end);
         }
+        if (c + 1 < n_chunks) issue(t0 + kQ);
         __syncthreads();
 
-        // ---- G = C B^T -> M (masked, decayed); Y = exp(cs_t) C S_in ----
-        f32x16 acc_y;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_y[r] = 0.0f;
-        {
-            const bool upper = bm == 0 && bn == 1;  // t < 32 <= s: M is zero there
+        // ---- B: G^T = B C^T -> M (LDS); Y^T = S_in^T C^T, scaled by exp(cs_t) ----
+        const int t = 32 * tb + l32;  // this lane's column of G^T and Y^T
+        const float cs_t = s_cs[t];
+        if (has_g) {
             f32x16 acc_g;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_g[r] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < NS / 16; ++ks) {
-                const int k0 = 16 * ks + 8 * (lane >> 5);
-                if (!upper) acc_g = mfma(ca[ks], lds_b128(&sB[32 * bn + (lane & 31)][k0]), acc_g);
-                acc_y = mfma(ca[ks], lds_b128(&sSh[32 * bn + (lane & 31)][k0]), acc_y);
-                acc_y = mfma(ca[ks], lds_b128(&sSl[32 * bn + (lane & 31)][k0]), acc_y);
-            }
-            const int s = 32 * bn + (lane & 31);
-            const float cs_s = s_cs[s], dt_s = s_dt[s];
+            for (int ks = 0; ks < kKS; ++ks)
+                acc_g = mfma(lds_row8(&sB[32 * gs + l32][16 * ks + 8 * hl]), ca[ks], acc_g);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * bm + acc_row(lane, r);
-                const float m = (!upper && s <= t) ? acc_g[r] * exp2_hw((s_cs[t] - cs_s) * kLog2e) * dt_s : 0.0f;
-                store_split(sMh[t][mcol(t, s)], sMl[t][mcol(t, s)], m);
-                acc_y[r] *= s_ecs[t];
+            for (int q = 0; q < 4; ++q) {
+                const int s0 = 32 * gs + 8 * q + 4 * hl;  // rows s0..s0+3 of G^T in this lane
+                // exp(cs_t - cs_s) dt_s = exp2(cs_t*log2 e - s_lc[s])
+                const float4 lc = *reinterpret_cast<const float4*>(&s_lc[s0]);
+                const float lcv[4] = {lc.x, lc.y, lc.z, lc.w};
+                float m[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = (s0 + e <= t) ? acc_g[4 * q + e] * exp2_hw(cs_t - lcv[e]) : 0.0f;
+                u32x2 hi, lo;
+                split4(m, hi, lo);
+                *reinterpret_cast<u32x2*>(&sU[0][t][s0]) = hi;
+                *reinterpret_cast<u32x2*>(&sU[1][t][s0]) = lo;
             }
+        }
+        f32x16 acc_y;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_y[r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+            acc_y = mfma(lds_row8(&sS[0][32 * yp + l32][16 * ks + 8 * hl]), ca[ks], acc_y);
+            acc_y = mfma(lds_row8(&sS[1][32 * yp + l32][16 * ks + 8 * hl]), ca[ks], acc_y);
+        }
+        {
+            const float e_t = exp2_hw(cs_t);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_y[r] *= e_t;
         }
         __syncthreads();
 
-        // ---- Y += M X, + D x; store ----
+        // ---- C: Y^T += X^T M^T, + D x; store ----
         {
-            const int ks_end = bm == 0 ? 2 : 4;  // M[t][s] = 0 for s > t
+            const int ks_end = tb == 0 ? 2 : 4;  // M[t][s] = 0 for s > t
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 if (ks < ks_end) {
-                    const int k0 = 16 * ks + 8 * (lane >> 5);
-                    const int t = 32 * bm + (lane & 31);
-                    const bf16x8 xb = lds_b128(&sXT[32 * bn + (lane & 31)][k0]);
-                    acc_y = mfma(lds_b128(&sMh[t][mcol(t, k0)]), xb, acc_y);
-                    acc_y = mfma(lds_b128(&sMl[t][mcol(t, k0)]), xb, acc_y);
+                    const bf16x8 xa = lds_col8(&sX[16 * ks][32 * yp], kXP, lane);
+                    acc_y = mfma(xa, lds_row8(&sU[0][t][16 * ks + 8 * hl]), acc_y);
+                    acc_y = mfma(xa, lds_row8(&sU[1][t][16 * ks + 8 * hl]), acc_y);
                 }
             }
-            const int p = 32 * bn + (lane & 31);
+            const uint32_t yrow = (t0 + t) * x_row;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * bm + acc_row(lane, r);
-                float yv = acc_y[r];
-                if (HAS_D) yv = fmaf(Dh, bf(sXT[p][t]), yv);
-                if (t < rows) Y[((b * L + t0 + t) * H + h) * kP + p] = f32_to_bf16_bits(yv);
+            for (int q = 0; q < 4; ++q) {
+                const int p0 = 32 * yp + 8 * q + 4 * hl;  // channels p0..p0+3 of row t in this lane
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc_y[4 * q + e];
+                if (HAS_D) {
+                    const u32x2 xr = *reinterpret_cast<const u32x2*>(&sX[t][p0]);
+                    v[0] = fmaf(Dh, bf(xr[0]), v[0]);
+                    v[1] = fmaf(Dh, bf_hi(xr[0]), v[1]);
+                    v[2] = fmaf(Dh, bf(xr[1]), v[2]);
+                    v[3] = fmaf(Dh, bf_hi(xr[1]), v[3]);
+                }
+                const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(o, rY, yrow + p0 * 2, 0, 0);
             }
         }
-        // ---- S^T = exp(cs_end) S^T + X^T diag(w) B ----
+        __syncthreads();  // M is consumed; its space takes w*x
+
+        // ---- D: w*x (s, p) in two bf16 parts ----
+#pragma unroll
+        for (int i = 0; i < kVX; ++i) {
+            const int v = tid + kSsdThreads * i, s = v / (kP / 8), p8 = (v % (kP / 8)) * 8;
+            const u32x4 xr = *reinterpret_cast<const u32x4*>(&sX[s][p8]);
+            const float ws = s_w[s];
+            float first[4], second[4];  // w*x of elements 0..3 and 4..7
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                first[2 * k] = ws * bf(xr[k]);
+                first[2 * k + 1] = ws * bf_hi(xr[k]);
+                second[2 * k] = ws * bf(xr[k + 2]);
+                second[2 * k + 1] = ws * bf_hi(xr[k + 2]);
+            }
+            u32x2 h0, l0, h1, l1;
+            split4(first, h0, l0);
+            split4(second, h1, l1);
+            *reinterpret_cast<u32x4*>(&sU[0][s][p8]) = u32x4{h0[0], h0[1], h1[0], h1[1]};
+            *reinterpret_cast<u32x4*>(&sU[1][s][p8]) = u32x4{l0[0], l0[1], l1[0], l1[1]};
+        }
+        __syncthreads();
+
+        // ---- E: S = exp(cs_end) S + B^T (w x); new LDS copy of S^T ----
         const float decay = s_end;
 #pragma unroll
         for (int j = 0; j < kSPW; ++j) {
-            const int blk = w * kSPW + j, pb = blk / kNB, nb = blk % kNB;
+            const int blk = w * kSPW + j, nb = blk % kNB, pb = blk / kNB;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_s[j][r] *= decay;
 #pragma unroll
             for (int ks = 0; ks < kQ / 16; ++ks) {
-                const int k0 = 16 * ks + 8 * (lane >> 5);
-                const int n = 32 * nb + (lane & 31);
-                // w*B in two bf16 parts (hi + lo): the state keeps ~16 more bits of it
-                bf16x8 bw_hi, bw_lo;
+                const bf16x8 bt = lds_col8(&sB[16 * ks][32 * nb], kBP, lane);
+                acc_s[j] = mfma(bt, lds_col8(&sU[0][16 * ks][32 * pb], kXP, lane), acc_s[j]);
+                acc_s[j] = mfma(bt, lds_col8(&sU[1][16 * ks][32 * pb], kXP, lane), acc_s[j]);
+            }
+            const int p = 32 * pb + l32;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float v = bf(sB[k0 + i][n]) * s_w[k0 + i];
-                    bw_hi[i] = (__bf16)v;
-                    bw_lo[i] = (__bf16)(v - (float)bw_hi[i]);
-                }
-                const bf16x8 xa = lds_b128(&sXT[32 * pb + (lane & 31)][k0]);
-                acc_s[j] = mfma(xa, bw_hi, acc_s[j]);
-                acc_s[j] = mfma(xa, bw_lo, acc_s[j]);
+            for (int q = 0; q < 4; ++q) {
+                const float v[4] = {acc_s[j][4 * q], acc_s[j][4 * q + 1], acc_s[j][4 * q + 2], acc_s[j][4 * q + 3]};
+                u32x2 hi, lo;
+                split4(v, hi, lo);
+                *reinterpret_cast<u32x2*>(&sS[0][p][32 * nb + 8 * q + 4 * hl]) = hi;
+                *reinterpret_cast<u32x2*>(&sS[1][p][32 * nb + 8 * q + 4 * hl]) = lo;
             }
         }
-        __syncthreads();  // every wave is done with sB, sXT, sM and the old state parts
-#pragma unroll
-        for (int j = 0; j < kSPW; ++j) {
-            const int blk = w * kSPW + j, pb = blk / kNB, nb = blk % kNB;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int p = 32 * pb + acc_row(lane, r), n = 32 * nb + (lane & 31);
-                store_split(sSh[p][n], sSl[p][n], acc_s[j][r]);
-            }
-        }
-        // the next chunk's staging writes sB/sXT (not the state parts) before its
-        // first barrier, and the state parts are read only after that barrier
+        __syncthreads();  // B and w*x consumed; the new state copy is complete
     }
 
     if (a.h_last) {
 #pragma unroll
         for (int j = 0; j < kSPW; ++j) {
-            const int blk = w * kSPW + j, pb = blk / kNB, nb = blk % kNB;
+            const int blk = w * kSPW + j, nb = blk % kNB, pb = blk / kNB;
+            const int p = 32 * pb + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int p = 32 * pb + acc_row(lane, r), n = 32 * nb + (lane & 31);
+                const int n = 32 * nb + 8 * (r >> 2) + 4 * hl + (r & 3);
                 a.h_last[((b * H + h) * NS + n) * kP + p] = acc_s[j][r];
             }
         }

@@ -333,6 +333,10 @@ def test_ssd_validation(lib):
     assert call_ssd(lib, hdim=32) == UNSUPPORTED
     assert call_ssd(lib, dstate=256) == UNSUPPORTED
     assert call_ssd(lib, batch=70000) == UNSUPPORTED
+    # one batch row of x must stay below 2 GiB (32-bit offsets): 64 heads of 64
+    # channels allow 262143 rows
+    assert call_ssd(lib, seqlen=262144, heads=64) == UNSUPPORTED
+    assert call_ssd(lib, seqlen=8388608, heads=1, dstate=128) == UNSUPPORTED  # B's row: 256 bytes
     eight = ctypes.c_void_p(BASE + 9 * GAP + 8)
     for name in ("x", "B", "C", "y"):
         assert call_ssd(lib, **{name: eight}) == INVALID, name
