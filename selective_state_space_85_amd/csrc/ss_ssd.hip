@@ -147,7 +147,16 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
     // ---- operands of a chunk in flight (issued one chunk ahead) ----
     u32x4 pB[kVB], pX[kVX], pC[kKS];
     uint32_t pdt = 0;
+    // Issue order matters: a wait for one load also waits for every older
+    // one, so dt (needed first) goes out first and x/B last.
     auto issue = [&](uint32_t t0) {
+        if (w == 0) pdt = __builtin_amdgcn_raw_buffer_load_b16(rDT, (t0 + lane) * dt_row, 0, 0);
+        // C rows of this wave's t block in the MFMA operand layout (row l%32,
+        // entries 16*ks + 8*(l/32) .. +8)
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+            pC[ks] = __builtin_amdgcn_raw_buffer_load_b128(rC, (t0 + 32 * tb + l32) * bc_row + (16 * ks + 8 * hl) * 2,
+                                                           0, 0);
 #pragma unroll
         for (int i = 0; i < kVB; ++i) {
             const int v = tid + kSsdThreads * i, r = v / (NS / 8), c8 = (v % (NS / 8)) * 8;
@@ -158,13 +167,6 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
             const int v = tid + kSsdThreads * i, s = v / (kP / 8), p8 = (v % (kP / 8)) * 8;
             pX[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, (t0 + s) * x_row + p8 * 2, 0, 0);
         }
-        // C rows of this wave's t block in the MFMA operand layout (row l%32,
-        // entries 16*ks + 8*(l/32) .. +8)
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks)
-            pC[ks] = __builtin_amdgcn_raw_buffer_load_b128(rC, (t0 + 32 * tb + l32) * bc_row + (16 * ks + 8 * hl) * 2,
-                                                           0, 0);
-        if (w == 0) pdt = __builtin_amdgcn_raw_buffer_load_b16(rDT, (t0 + lane) * dt_row, 0, 0);
     };
 
     // ---- initial state: accumulators (n x p blocks) and the LDS copy ----
@@ -235,36 +237,43 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
             f32x16 acc_g;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_g[r] = 0.0f;
+            bf16x8 gb[kKS];
 #pragma unroll
-            for (int ks = 0; ks < kKS; ++ks)
-                acc_g = mfma(lds_row8(&sB[32 * gs + l32][16 * ks + 8 * hl]), ca[ks], acc_g);
+            for (int ks = 0; ks < kKS; ++ks) gb[ks] = lds_row8(&sB[32 * gs + l32][16 * ks + 8 * hl]);
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks) acc_g = mfma(gb[ks], ca[ks], acc_g);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int s0 = 32 * gs + 8 * q + 4 * hl;  // rows s0..s0+3 of G^T in this lane
                 // exp(cs_t - cs_s) dt_s = exp2(cs_t*log2 e - s_lc[s])
                 const float4 lc = *reinterpret_cast<const float4*>(&s_lc[s0]);
                 const float lcv[4] = {lc.x, lc.y, lc.z, lc.w};
+                // computed for every s and masked with a bitwise and (no
+                // branches; above the diagonal the product may be inf or NaN)
                 float m[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) m[e] = (s0 + e <= t) ? acc_g[4 * q + e] * exp2_hw(cs_t - lcv[e]) : 0.0f;
+                for (int e = 0; e < 4; ++e) {
+                    const float v = acc_g[4 * q + e] * exp2_hw(cs_t - lcv[e]);
+                    m[e] = __uint_as_float(__float_as_uint(v) & (s0 + e <= t ? 0xffffffffu : 0u));
+                }
                 u32x2 hi, lo;
                 split4(m, hi, lo);
                 *reinterpret_cast<u32x2*>(&sU[0][t][s0]) = hi;
                 *reinterpret_cast<u32x2*>(&sU[1][t][s0]) = lo;
             }
         }
-        f32x16 acc_y;
+        f32x16 acc_y, acc_l;  // the hi and lo parts of the state: two independent chains
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_y[r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc_y[r] = acc_l[r] = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
             acc_y = mfma(lds_row8(&sS[0][32 * yp + l32][16 * ks + 8 * hl]), ca[ks], acc_y);
-            acc_y = mfma(lds_row8(&sS[1][32 * yp + l32][16 * ks + 8 * hl]), ca[ks], acc_y);
+            acc_l = mfma(lds_row8(&sS[1][32 * yp + l32][16 * ks + 8 * hl]), ca[ks], acc_l);
         }
         {
             const float e_t = exp2_hw(cs_t);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc_y[r] *= e_t;
+            for (int r = 0; r < 16; ++r) acc_y[r] = (acc_y[r] + acc_l[r]) * e_t;
         }
         __syncthreads();
 
@@ -272,11 +281,13 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
         {
             const int ks_end = tb == 0 ? 2 : 4;  // M[t][s] = 0 for s > t
 #pragma unroll
+            for (int r = 0; r < 16; ++r) acc_l[r] = 0.0f;
+#pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 if (ks < ks_end) {
                     const bf16x8 xa = lds_col8(&sX[16 * ks][32 * yp], kXP, lane);
                     acc_y = mfma(xa, lds_row8(&sU[0][t][16 * ks + 8 * hl]), acc_y);
-                    acc_y = mfma(xa, lds_row8(&sU[1][t][16 * ks + 8 * hl]), acc_y);
+                    acc_l = mfma(xa, lds_row8(&sU[1][t][16 * ks + 8 * hl]), acc_l);
                 }
             }
             const uint32_t yrow = (t0 + t) * x_row;
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 const int p0 = 32 * yp + 8 * q + 4 * hl;  // channels p0..p0+3 of row t in this lane
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc_y[4 * q + e];
+                for (int e = 0; e < 4; ++e) v[e] = acc_y[4 * q + e] + acc_l[4 * q + e];
                 if (HAS_D) {
                     const u32x2 xr = *reinterpret_cast<const u32x2*>(&sX[t][p0]);
                     v[0] = fmaf(Dh, bf(xr[0]), v[0]);
@@ -323,17 +334,30 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
         // ---- E: S = exp(cs_end) S + B^T (w x); new LDS copy of S^T ----
         const float decay = s_end;
+        // a wave's state blocks share their p block, so the w*x operands of a
+        // step serve all of them
+        const int spb = (w * kSPW) / kNB;
+        static_assert(kNB % kSPW == 0, "a wave's state blocks lie in one p block");
 #pragma unroll
         for (int j = 0; j < kSPW; ++j) {
-            const int blk = w * kSPW + j, nb = blk % kNB, pb = blk / kNB;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_s[j][r] *= decay;
+        }
 #pragma unroll
-            for (int ks = 0; ks < kQ / 16; ++ks) {
+        for (int ks = 0; ks < kQ / 16; ++ks) {
+            const bf16x8 xh = lds_col8(&sU[0][16 * ks][32 * spb], kXP, lane);
+            const bf16x8 xl = lds_col8(&sU[1][16 * ks][32 * spb], kXP, lane);
+#pragma unroll
+            for (int j = 0; j < kSPW; ++j) {
+                const int nb = (w * kSPW + j) % kNB;
                 const bf16x8 bt = lds_col8(&sB[16 * ks][32 * nb], kBP, lane);
-                acc_s[j] = mfma(bt, lds_col8(&sU[0][16 * ks][32 * pb], kXP, lane), acc_s[j]);
-                acc_s[j] = mfma(bt, lds_col8(&sU[1][16 * ks][32 * pb], kXP, lane), acc_s[j]);
+                acc_s[j] = mfma(bt, xh, acc_s[j]);
+                acc_s[j] = mfma(bt, xl, acc_s[j]);
             }
+        }
+#pragma unroll
+        for (int j = 0; j < kSPW; ++j) {
+            const int nb = (w * kSPW + j) % kNB, pb = spb;
             const int p = 32 * pb + l32;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
