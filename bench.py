@@ -85,6 +85,23 @@ def read_traffic(src_hash: str):
         return None
 
 
+def alu_cobound(w, ms_step):
+    """The vector-ALU ceiling of the same step, from unit counts and clock.
+
+    Per scan element the recurrence needs 4 fp32 vector operations (delta*A,
+    delta*u*B, the state fma, the C.h fma) and one exp2; the exp2 issues at half
+    the fma rate on gfx950 (measured: 8.7 vs 4 cycles per wave64 instruction),
+    so it costs 2 issue slots.  Per (b, t, d) row: delta*u (1), the D skip (1),
+    silu(z) (3 operations + exp2 + reciprocal = 7 slots) and the bf16 rounding
+    (1).  Peak: 256 CUs x 64 fp32 lanes x 2.4 GHz, no packed fp32."""
+    per_row = 1 + (1 if w.has_D else 0) + (7 if w.has_z else 0) + 1
+    slots = 6.0 + per_row / w.dstate
+    peak_slots = 256 * 64 * 2.4e9
+    floor_ms = w.elements * slots / peak_slots * 1e3
+    return {"bound": "alu", "slots_per_element": slots, "peak_lane_slots_per_s": peak_slots,
+            "floor_ms": floor_ms, "frac": floor_ms / ms_step}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -174,7 +191,8 @@ def main():
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "kernel": "ss_scan_fwd: scan_kernel (emit)%s" % (" + aggregate + carry" if K > 1 else ""),
-                     "kernel_source_hash": src_hash},
+                     "kernel_source_hash": src_hash,
+                     "co_bound": alu_cobound(w, ms_step)},
     }
 
     if args.copy_reference:
