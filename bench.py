@@ -11,7 +11,9 @@ HBM bytes per launch over its event-timed duration, against 8 TB/s), and the
 fp64 CPU oracle timed on a bounded sample of the same workload.
 
 Extra objects: ``decode_step`` (ss_step on the B=256, D=5120 recurrent-step
-workload), ``parity`` (timed output vs the oracle on sampled channels),
+workload), ``decode_graph`` (single-sequence decode, B=1: 64 chained ss_step
+calls launched one by one against the same loop captured once in a hipGraph
+and replayed), ``parity`` (timed output vs the oracle on sampled channels),
 ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
 before every step), ``options`` (the same layer with the softplus(delta +
 bias) step size and/or the zero-order-hold input term), ``backward``
@@ -394,6 +396,47 @@ def main():
                                  "alg_GB/s": sb / (us * 1e-6) / 1e9, "note": "chained, state warm in cache",
                                  "cold_us_per_token": us_cold, "cold_alg_GB/s": sb / (us_cold * 1e-6) / 1e9,
                                  "cold_frac_of_8TB/s": sb / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del st, y5, h5
+
+        # single-sequence decode (B=1): launch-bound, so the token loop is captured
+        # once in a hipGraph and replayed, against the same loop launched eagerly
+        n_tok, gd = 64, 5120
+        gi = wl.scan_inputs(1, n_tok, gd, 16, wl.BF16, has_D=True, has_z=True, has_h0=True, seed=77)
+        gt = {k: to_dev(v) for k, v in gi.items()}
+        gcol = {k: [gt[k][:, s].contiguous() for s in range(n_tok)] for k in ("u", "delta", "B", "C", "z")}
+        gh = gt["h0"].clone()
+        gy = torch.empty(n_tok, 1, gd, dtype=torch.bfloat16, device=device)
+
+        def gloop():
+            for s_ in range(n_tok):
+                ss.step(gh, gcol["u"][s_], gcol["delta"][s_], gt["A"], gcol["B"][s_], gcol["C"][s_], D=gt["D"],
+                        z=gcol["z"][s_], out=gy[s_])
+
+        def per_token(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            e0.record(torch.cuda.current_stream())
+            for _ in range(reps):
+                fn()
+            e1.record(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * n_tok)
+
+        us_eager = per_token(gloop)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            gloop()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gloop()
+        torch.cuda.synchronize()
+        us_graph = per_token(graph.replay)
+        result["decode_graph"] = {"workload": "recurrent step B=1 D=5120 N=16, bf16, D skip + gate, %d tokens "
+                                              "per hipGraph" % n_tok,
+                                  "eager_us_per_token": us_eager, "graph_us_per_token": us_graph}
+        del graph, gt, gcol, gy, gh
 
     if not args.no_cpu_baseline:
         import oracle

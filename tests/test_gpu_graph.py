@@ -1,0 +1,168 @@
+"""Entry points under HIP graph capture (torch.cuda.CUDAGraph on ROCm is a hipGraph).
+
+Every entry point enqueues kernels on the caller's stream and nothing else: no
+allocation, no memset, no copy, no synchronisation.  So a serving loop can be
+captured once and replayed, which takes the per-launch host cost out of
+launch-bound work such as one-token decode.  Each test captures a call (or a
+loop of calls), then replays the graph several times with eager work of its
+own and synchronisations in between, after filling the graph's outputs with
+NaN, and checks every replay bit for bit against the eager result of the same
+call; the eager result is checked against the fp64 oracle as elsewhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import TOL, dev, host64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+def ss():
+    import selective_state_space_85_amd as m
+
+    return m
+
+
+def capture(fn):
+    """Warm fn up on a side stream, then capture one call of it; returns (graph, outputs)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = fn()
+    torch.cuda.synchronize()
+    return g, outs
+
+
+def replay_and_check(g, outs, expect, before=None, between=None):
+    for rep in range(REPLAYS):
+        for t in outs:
+            t.fill_(float("nan"))
+        if before is not None:
+            before()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(outs, expect)):
+            assert torch.equal(t, e), "replay %d, output %d differs from the eager call" % (rep, i)
+        if between is not None:
+            between()
+            torch.cuda.synchronize()
+
+
+def test_graph_decode_loop():
+    """24 chained ss_step calls (bf16, D skip, gate, ragged channel count) in one graph."""
+    b, steps, d = 3, 24, 300
+    inp = wl.scan_inputs(b, steps, d, 16, wl.BF16, has_D=True, has_z=True, has_h0=True, seed=910)
+    m = ss()
+    t = {k: dev(v) for k, v in inp.items()}
+    cols = {k: [t[k][:, s].contiguous() for s in range(steps)] for k in ("u", "delta", "B", "C", "z")}
+    h0 = t["h0"].contiguous()
+    say("graph decode loop: B%d D%d, %d tokens" % (b, d, steps))
+
+    def loop(h, ys):
+        for s in range(steps):
+            m.step(h, cols["u"][s], cols["delta"][s], t["A"], cols["B"][s], cols["C"][s], D=t["D"],
+                   z=cols["z"][s], out=ys[s])
+
+    h_e = h0.clone()
+    y_e = torch.empty(steps, b, d, dtype=torch.bfloat16, device="cuda")
+    loop(h_e, y_e)
+    torch.cuda.synchronize()
+    ref = oracle.scan(**inp)
+    assert rel_err(host64(y_e.permute(1, 0, 2)), ref["y"]) <= TOL["bf16"]
+    assert rel_err(host64(h_e), ref["h_last"]) <= TOL["bf16"]
+
+    h_g = h0.clone()
+    y_g = torch.empty_like(y_e)
+    g, _ = capture(lambda: loop(h_g, y_g))
+    h_x, y_x = h0.clone(), torch.empty_like(y_e)  # eager work between replays
+    replay_and_check(g, [y_g, h_g], [y_e, h_e], before=lambda: h_g.copy_(h0),
+                     between=lambda: (h_x.copy_(h0), loop(h_x, y_x)))
+
+
+def test_graph_chunked_scan():
+    """The chunked forward (panel, aggregate, carry and emit launches) in one graph."""
+    b, l, d, chunk = 2, 700, 130, 64
+    inp = wl.scan_inputs(b, l, d, 16, wl.F32, has_D=True, has_z=True, has_h0=True, seed=911)
+    m = ss()
+    t = {k: dev(v) for k, v in inp.items()}
+    T, K = m.scan_plan(b, l, d, 16, chunk)
+    assert K > 1
+    ws = torch.empty(m.scan_workspace_bytes(b, l, d, 16, chunk), dtype=torch.uint8, device="cuda")
+    say("graph chunked scan: B%d L%d D%d T=%d K=%d" % (b, l, d, T, K))
+
+    def call(y, hl):
+        return m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], h0=t["h0"],
+                          chunk_len=chunk, out=y, h_last=hl, workspace=ws, return_last_state=True)
+
+    y_e, hl_e = torch.empty_like(t["u"]), torch.empty_like(t["h0"])
+    call(y_e, hl_e)
+    torch.cuda.synchronize()
+    ref = oracle.scan(**inp)
+    assert rel_err(host64(y_e), ref["y"]) <= TOL["f32"]
+    assert rel_err(host64(hl_e), ref["h_last"]) <= TOL["f32"]
+
+    y_g, hl_g = torch.empty_like(y_e), torch.empty_like(hl_e)
+    g, _ = capture(lambda: call(y_g, hl_g))
+    y_x, hl_x = torch.empty_like(y_e), torch.empty_like(hl_e)
+    replay_and_check(g, [y_g, hl_g], [y_e, hl_e], between=lambda: call(y_x, hl_x))
+
+
+def test_graph_backward():
+    """The backward's four launches in one graph; outputs come from the graph's pool."""
+    b, l, d = 1, 100, 70
+    inp = wl.scan_inputs(b, l, d, 16, wl.F32, has_D=True, has_z=True, has_h0=True, seed=912)
+    rng = np.random.default_rng(913)
+    dy = rng.standard_normal((b, l, d)).astype(np.float32)
+    m = ss()
+    t = {k: dev(v) for k, v in inp.items()}
+    dy_t = dev(dy)
+    ws = torch.empty(m.scan_bwd_workspace_bytes(b, l, d, 16), dtype=torch.uint8, device="cuda")
+    say("graph backward: B%d L%d D%d" % (b, l, d))
+
+    def grads():
+        return m.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], h0=t["h0"],
+                          workspace=ws)
+
+    g_e = grads()
+    torch.cuda.synchronize()
+    names = sorted(g_e)
+    ref = oracle.scan_bwd(**inp, dy=oracle.widen(dy))
+    for k, r in ref.items():
+        assert rel_err(host64(g_e[k]), r) <= TOL["f32"], k
+    eager = [g_e[k].clone() for k in names]
+    call = lambda: [g[k] for g in [grads()] for k in names]  # noqa: E731
+    graph, outs = capture(call)
+    replay_and_check(graph, outs, eager, between=call)
+
+
+def test_graph_ssd():
+    """The multi-head recurrence in a graph."""
+    b, l, h, n = 1, 200, 2, 64
+    inp = wl.ssd_inputs(b, l, h, 64, n, has_D=True, has_h0=True, seed=914)
+    m = ss()
+    t = {k: dev(v) for k, v in inp.items()}
+    say("graph ssd: B%d L%d H%d N%d" % (b, l, h, n))
+
+    def call(y):  # h_last comes from the caller's allocator (the graph's pool when captured)
+        return m.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], h0=t["h0"], out=y,
+                         return_last_state=True)
+
+    y_e, hl_e = call(torch.empty_like(t["x"]))
+    torch.cuda.synchronize()
+    ref = oracle.ssd(**inp)
+    assert rel_err(host64(y_e), ref["y"]) <= TOL["bf16"]
+    assert rel_err(host64(hl_e), ref["h_last"]) <= TOL["bf16"]
+    y_g = torch.empty_like(y_e)
+    g, outs = capture(lambda: call(y_g))
+    y_x = torch.empty_like(y_e)
+    replay_and_check(g, list(outs), [y_e, hl_e], between=lambda: call(y_x))
