@@ -17,7 +17,9 @@ and replayed), ``parity`` (timed output vs the oracle on sampled channels),
 ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
 before every step), ``options`` (the same layer with the softplus(delta +
 bias) step size and/or the zero-order-hold input term), ``backward``
-(ss_scan_bwd on the same layer: all input gradients from dy), ``conv1d``
+(ss_scan_bwd on the same layer: all input gradients from dy; and the training
+path, ss_scan_fwd_ckpt keeping every 16th state and ss_scan_bwd_ckpt reusing
+them), ``conv1d``
 (ss_conv1d_silu producing the layer's u from the x half of a (B, L, 2D)
 in-projection output, with its HBM roofline) and ``ssd`` (ss_ssd_fwd, the
 multi-head recurrence on the matrix cores, B=8 L=2048, 64 heads of 64
@@ -294,10 +296,41 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / 10
-        result["backward"] = {"ms_per_step": bms, "elements/s": elements / (bms * 1e-3),
-                              "vs_forward": bms / ms_step, "workspace_bytes": bws.numel(),
-                              "note": "panel + prep (forward with checkpoints, dC, dz) + adjoint + reduce"}
         del bws
+
+        # training path: the forward keeps every 16th state, the backward reuses them
+        ck = torch.empty(ss.scan_ckpt_shape(w.batch, w.seqlen, w.dim, w.dstate), device=device)
+        cws = torch.empty(ss.scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate, with_ckpt=True),
+                          dtype=torch.uint8, device=device)
+        yk = torch.empty_like(t["u"])
+
+        def fkstep():
+            ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=yk, workspace=ws,
+                        ckpt=ck)
+
+        def bkstep():
+            ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=cws, ckpt=ck)
+
+        def timed(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        fk_ms, bk_ms = timed(fkstep), timed(bkstep)
+        result["backward"] = {"ms_per_step": bms, "elements/s": elements / (bms * 1e-3),
+                              "vs_forward": bms / ms_step, "note": "panel + checkpoint pass + adjoint + reduce",
+                              "training": {"fwd_ckpt_ms": fk_ms, "bwd_from_ckpt_ms": bk_ms,
+                                           "fwd_plus_bwd_ms": fk_ms + bk_ms,
+                                           "fwd_plus_standalone_bwd_ms": ms_step + bms,
+                                           "ckpt_bytes": ck.numel() * 4,
+                                           "note": "ss_scan_fwd_ckpt keeps the state every 16 rows; "
+                                                   "ss_scan_bwd_ckpt skips the checkpoint pass"}}
+        del ck, cws, yk
 
         # the block's causal depthwise convolution + SiLU producing u (x read in place from xz)
         xz = torch.randn(w.batch, w.seqlen, 2 * w.dim, device=device,

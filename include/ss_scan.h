@@ -155,6 +155,34 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
                          int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
 
 /*
+ * ss_scan_ckpt_bytes -- size of the state checkpoints of a (batch, seqlen,
+ * dim, dstate) scan: ceil(seqlen/16) * batch * dim * dstate fp32 words, in
+ * bytes ((size_t)-1 for invalid sizes).
+ *
+ * ss_scan_fwd_ckpt -- ss_scan_fwd_ex that also keeps the states the backward
+ * needs, so that ss_scan_bwd_ckpt can reuse them instead of recomputing them
+ * (the walk-through's section 3.3 recomputes the per-timestep states in the
+ * backward; here only every 16th is kept, the way the chunked forward keeps
+ * only its chunk carries, LTI chapter section 3.1.5.2):
+ *   ckpt : (ceil(seqlen/16), batch, dstate, dim) fp32 output, 16-byte aligned;
+ *          ckpt[j, b, n, d] = the state h[n] of lane (b, d) entering timestep
+ *          16*j, i.e. after timestep 16*j - 1 (h0, or zero, for j = 0)
+ * ckpt must not overlap any input, y, h_last or the workspace.  With more than
+ * one chunk the chunk length must be a multiple of 16 (SS_ERR_UNSUPPORTED
+ * otherwise).  Every other argument, the validation and the errors are as for
+ * ss_scan_fwd_ex; y and h_last are the same as ss_scan_fwd_ex's.
+ */
+size_t ss_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+ss_status ss_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, const float* h0,
+                           const float* delta_bias, uint32_t options,
+                           void* y, float* h_last, float* ckpt,
+                           void* workspace, size_t workspace_bytes,
+                           int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
+
+/*
  * ss_step -- one token of the recurrent (constant-state) mode: the walk-
  * through's section 6 (O(1) state per generated token) and the interactive
  * demo page (the state is all that is carried from one token to the next).
@@ -234,6 +262,33 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
                       void* workspace, size_t workspace_bytes,
                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                       ss_dtype dtype, hipStream_t stream);
+
+/*
+ * ss_scan_bwd_ckpt -- ss_scan_bwd from the checkpoints of a forward pass:
+ *   ckpt : (ceil(seqlen/16), batch, dstate, dim) fp32, 16-byte aligned, as
+ *          written by ss_scan_fwd_ckpt for the same inputs, h0 and options;
+ *          read only.  Any other contents give the gradients of a scan whose
+ *          state entering every 16th timestep is ckpt's.
+ *   workspace : ss_scan_bwd_ckpt_workspace_bytes(...) bytes, 256-byte aligned
+ *          (the checkpoint region of ss_scan_bwd's workspace is not needed)
+ * The pass that recomputes the checkpoints is skipped.  With ss_scan_fwd_ckpt's
+ * checkpoints of a one-chunk forward the results are ss_scan_bwd's bit for
+ * bit; a chunked forward's checkpoints come from its chunk carries and differ
+ * from the sequential ones by rounding only.  ckpt is an input: outputs
+ * and the workspace must not overlap it.  Every other argument, the
+ * validation and the errors are as for ss_scan_bwd.
+ */
+size_t ss_scan_bwd_ckpt_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+ss_status ss_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, const float* h0,
+                           const float* delta_bias, uint32_t options,
+                           const void* dy, const float* dh_last, const float* ckpt,
+                           void* du, void* ddelta, float* dA, void* dB, void* dC,
+                           float* dD, void* dz, float* ddelta_bias, float* dh0,
+                           void* workspace, size_t workspace_bytes,
+                           int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           ss_dtype dtype, hipStream_t stream);
 
 /*
  * ss_conv1d_silu -- the Mamba block's causal depthwise convolution and SiLU

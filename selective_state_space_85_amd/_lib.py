@@ -13,9 +13,10 @@ SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE, SS_ERR_HIP = ra
 SS_F32, SS_BF16 = 0, 1
 
 # Every function the header declares.
-EXPORTS = ("ss_scan_plan", "ss_scan_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_step",
-           "ss_step_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_bwd", "ss_conv1d_silu", "ss_ssd_fwd", "ss_status_string",
-           "ss_last_hip_error")
+EXPORTS = ("ss_scan_plan", "ss_scan_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_ckpt_bytes",
+           "ss_scan_fwd_ckpt", "ss_step", "ss_step_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_bwd",
+           "ss_scan_bwd_ckpt_workspace_bytes", "ss_scan_bwd_ckpt", "ss_conv1d_silu", "ss_ssd_fwd",
+           "ss_status_string", "ss_last_hip_error")
 SS_DELTA_SOFTPLUS, SS_B_ZOH = 1, 2  # ss_option bits
 
 _lib = None
@@ -62,6 +63,16 @@ def load() -> ctypes.CDLL:
     lib.ss_scan_bwd_workspace_bytes.restype = sz
     lib.ss_scan_bwd.argtypes = [vp] * 9 + [ctypes.c_uint32] + [vp] * 12 + [sz, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.ss_scan_bwd.restype = ctypes.c_int
+    lib.ss_scan_ckpt_bytes.argtypes = [i64, i64, i64, i64]
+    lib.ss_scan_ckpt_bytes.restype = sz
+    lib.ss_scan_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp, vp, sz,
+                                     i64, i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.ss_scan_fwd_ckpt.restype = ctypes.c_int
+    lib.ss_scan_bwd_ckpt_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.ss_scan_bwd_ckpt_workspace_bytes.restype = sz
+    lib.ss_scan_bwd_ckpt.argtypes = [vp] * 9 + [ctypes.c_uint32] + [vp] * 13 + [sz, i64, i64, i64, i64, ctypes.c_int,
+                                                                               vp]
+    lib.ss_scan_bwd_ckpt.restype = ctypes.c_int
     lib.ss_conv1d_silu.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.ss_conv1d_silu.restype = ctypes.c_int
     lib.ss_ssd_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_int, vp]

@@ -127,7 +127,9 @@ struct BwdLayout {
     int64_t total;                                                               // bytes
 };
 
-bool bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, BwdLayout* w)
+// ckpt_region: false when the caller supplies the checkpoints (the region is
+// then empty).
+bool bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, BwdLayout* w, bool ckpt_region = true)
 {
     w->panel_rows = ssk::panel_rows(seqlen);
     w->n_sub = ceil_div(seqlen, ssk::kBwdSub);
@@ -137,6 +139,7 @@ bool bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, BwdL
     if (!mul(batch, seqlen, &bl)) return false;
     if (!mul(batch, 2 * w->panel_rows, &tmp) || !mul(tmp, dstate, &words[0])) return false;
     if (!mul(w->n_sub, batch, &tmp) || !mul(tmp, dstate, &tmp) || !mul(tmp, dim, &words[1])) return false;
+    if (!ckpt_region) words[1] = 0;
     if (!mul(w->nblk, bl, &tmp) || !mul(tmp, dstate, &words[2])) return false;
     words[3] = words[2];
     if (!mul(batch, dim, &tmp) || !mul(tmp, dstate, &words[4])) return false;
@@ -161,6 +164,21 @@ ss_status hip_fail(hipError_t e)
     g_last_hip_error = static_cast<int>(e);
     return SS_ERR_HIP;
 }
+
+// ss_scan_bwd with optional caller checkpoints (see ss_scan_bwd_ckpt)
+ss_status scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                        uint32_t options, const void* dy, const float* dh_last, void* du, void* ddelta, float* dA,
+                        void* dB, void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0, const float* ckpt,
+                        void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+                        int64_t dstate, ss_dtype dtype, hipStream_t stream);
+
+// ss_scan_fwd_ex with an optional checkpoint output (see ss_scan_fwd_ckpt)
+ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                        uint32_t options, void* y, float* h_last, float* ckpt, void* workspace,
+                        size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                        int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
 
 }  // namespace
 
@@ -205,6 +223,41 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
                          int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t chunk_len_request,
                          ss_dtype dtype, hipStream_t stream)
 {
+    return scan_fwd_impl(u, delta, A, B, C, Dskip, z, h0, delta_bias, options, y, h_last, nullptr, workspace,
+                         workspace_bytes, batch, seqlen, dim, dstate, chunk_len_request, dtype, stream);
+}
+
+size_t ss_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate)
+{
+    Sizes s;
+    int64_t bytes;
+    if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return static_cast<size_t>(-1);
+    if (!mul(ceil_div(seqlen, ssk::kBwdSub), s.states, &bytes) || !mul(bytes, 4, &bytes))
+        return static_cast<size_t>(-1);
+    return static_cast<size_t>(bytes);
+}
+
+ss_status ss_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                           uint32_t options, void* y, float* h_last, float* ckpt, void* workspace,
+                           size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream)
+{
+    if (!ckpt) return SS_ERR_INVALID_ARG;
+    return scan_fwd_impl(u, delta, A, B, C, Dskip, z, h0, delta_bias, options, y, h_last, ckpt, workspace,
+                         workspace_bytes, batch, seqlen, dim, dstate, chunk_len_request, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                        uint32_t options, void* y, float* h_last, float* ckpt, void* workspace,
+                        size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                        int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream)
+{
     if (!u || !delta || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
     Sizes s;
     if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
@@ -214,6 +267,8 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
     if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
     if (options & ~ssk::kOptAll) return SS_ERR_UNSUPPORTED;
     if (batch > kMaxGridYZ || K > kMaxGridYZ || batch * dim > INT32_MAX) return SS_ERR_UNSUPPORTED;
+    // checkpoints fall every kBwdSub rows: every chunk must start on one
+    if (ckpt && K > 1 && T % ssk::kBwdSub != 0) return SS_ERR_UNSUPPORTED;
     WsLayout wl;
     if (!ws_layout(batch, seqlen, dim, dstate, T, K, &wl)) return SS_ERR_INVALID_ARG;
     // the panel kernel runs one thread per word in a one-dimensional grid
@@ -245,6 +300,14 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
     for (const Range& r : inputs)
         if (overlap(r_y, r)) return SS_ERR_INVALID_ARG;
     if (overlap(r_y, r_hl)) return SS_ERR_INVALID_ARG;
+    Range r_ck = span(nullptr, 0);
+    if (ckpt) {
+        if (!aligned(ckpt, 16)) return SS_ERR_INVALID_ARG;
+        r_ck = span(ckpt, static_cast<int64_t>(ss_scan_ckpt_bytes(batch, seqlen, dim, dstate)));
+        for (const Range& r : inputs)
+            if (overlap(r_ck, r)) return SS_ERR_INVALID_ARG;
+        if (overlap(r_ck, r_y) || overlap(r_ck, r_hl)) return SS_ERR_INVALID_ARG;
+    }
     for (const Range& r : inputs) {
         if (&r == &inputs[kH0] && h_last == h0) continue;  // exact in-place continuation is allowed
         if (overlap(r_hl, r)) return SS_ERR_INVALID_ARG;
@@ -255,7 +318,7 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
     const Range r_ws = span(workspace, need);
     for (const Range& r : inputs)
         if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
-    if (overlap(r_ws, r_y) || overlap(r_ws, r_hl)) return SS_ERR_INVALID_ARG;
+    if (overlap(r_ws, r_y) || overlap(r_ws, r_hl) || overlap(r_ws, r_ck)) return SS_ERR_INVALID_ARG;
 
     ssk::ScanArgs a;
     a.u = u;
@@ -274,6 +337,7 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
     a.ws_dsum = K > 1 ? static_cast<float*>(workspace) + K * batch * dim * dstate : nullptr;
     a.ws_panel = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.panel_offset);
     a.panel_rows = wl.panel_rows;
+    a.ckpt = ckpt;
     a.batch = batch;
     a.seqlen = seqlen;
     a.dim = dim;
@@ -283,6 +347,10 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 ss_status ss_step(float* h, const void* u, const void* delta, const float* A, const void* B, const void* C,
                   const float* Dskip, const void* z, void* y, int64_t batch, int64_t dim, int64_t dstate,
@@ -349,12 +417,50 @@ size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, i
     return static_cast<size_t>(wl.total);
 }
 
+size_t ss_scan_bwd_ckpt_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate)
+{
+    Sizes s;
+    BwdLayout wl;
+    if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return static_cast<size_t>(-1);
+    if (!bwd_layout(batch, seqlen, dim, dstate, &wl, false)) return static_cast<size_t>(-1);
+    return static_cast<size_t>(wl.total);
+}
+
 ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                       const float* Dskip, const void* z, const float* h0, const float* delta_bias,
                       uint32_t options, const void* dy, const float* dh_last, void* du, void* ddelta, float* dA,
                       void* dB, void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0, void* workspace,
                       size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                       ss_dtype dtype, hipStream_t stream)
+{
+    return scan_bwd_impl(u, delta, A, B, C, Dskip, z, h0, delta_bias, options, dy, dh_last, du, ddelta, dA, dB,
+                         dC, dD, dz, ddelta_bias, dh0, nullptr, workspace, workspace_bytes, batch, seqlen, dim,
+                         dstate, dtype, stream);
+}
+
+ss_status ss_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                           uint32_t options, const void* dy, const float* dh_last, const float* ckpt, void* du,
+                           void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                           float* dh0, void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
+                           int64_t dim, int64_t dstate, ss_dtype dtype, hipStream_t stream)
+{
+    if (!ckpt) return SS_ERR_INVALID_ARG;
+    return scan_bwd_impl(u, delta, A, B, C, Dskip, z, h0, delta_bias, options, dy, dh_last, du, ddelta, dA, dB,
+                         dC, dD, dz, ddelta_bias, dh0, ckpt, workspace, workspace_bytes, batch, seqlen, dim,
+                         dstate, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+ss_status scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* Dskip, const void* z, const float* h0, const float* delta_bias,
+                        uint32_t options, const void* dy, const float* dh_last, void* du, void* ddelta, float* dA,
+                        void* dB, void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0, const float* ckpt,
+                        void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+                        int64_t dstate, ss_dtype dtype, hipStream_t stream)
 {
     if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SS_ERR_INVALID_ARG;
     if ((Dskip && !dD) || (z && !dz) || (delta_bias && !ddelta_bias)) return SS_ERR_INVALID_ARG;
@@ -365,7 +471,7 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
     if (options & ~ssk::kOptSoftplus) return SS_ERR_UNSUPPORTED;  // no zero-order hold in the backward
     if (batch > kMaxGridYZ || batch * dim > INT32_MAX) return SS_ERR_UNSUPPORTED;
     BwdLayout wl;
-    if (!bwd_layout(batch, seqlen, dim, dstate, &wl)) return SS_ERR_INVALID_ARG;
+    if (!bwd_layout(batch, seqlen, dim, dstate, &wl, ckpt == nullptr)) return SS_ERR_INVALID_ARG;
     const uintptr_t es = dtype == SS_F32 ? 4 : 2;
     int64_t row_bytes_all;  // one batch row's (L, D) slab is addressed with 32-bit buffer offsets
     if (!mul(seqlen, dim, &row_bytes_all) || !mul(row_bytes_all, int64_t(es), &row_bytes_all) ||
@@ -381,10 +487,12 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
         if (p && !aligned(p, 4)) return SS_ERR_INVALID_ARG;
 
     const int64_t e = static_cast<int64_t>(es);
+    if (ckpt && !aligned(ckpt, 16)) return SS_ERR_INVALID_ARG;
+    const int64_t ckpt_bytes = ckpt ? static_cast<int64_t>(ss_scan_ckpt_bytes(batch, seqlen, dim, dstate)) : 0;
     const Range inputs[] = {span(u, s.rows * e), span(delta, s.rows * e), span(z, s.rows * e),
                             span(B, s.srows * e), span(C, s.srows * e), span(A, s.an * 4), span(Dskip, dim * 4),
                             span(h0, s.states * 4), span(delta_bias, dim * 4), span(dy, s.rows * e),
-                            span(dh_last, s.states * 4)};
+                            span(dh_last, s.states * 4), span(ckpt, ckpt_bytes)};
     const Range outputs[] = {span(du, s.rows * e), span(ddelta, s.rows * e), span(dz, s.rows * e),
                              span(dB, s.srows * e), span(dC, s.srows * e), span(dA, s.an * 4),
                              span(dD, dim * 4), span(ddelta_bias, dim * 4), span(dh0, s.states * 4)};
@@ -440,7 +548,9 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
     a.ddelta_bias = ddelta_bias;
     a.panel = pa.ws_panel;
     a.panel_rows = wl.panel_rows;
-    a.ckpt = reinterpret_cast<float*>(ws + wl.off_ckpt);
+    // the kernels only read caller checkpoints (prep_kernel, the writer, is not launched)
+    a.ckpt = ckpt ? const_cast<float*>(ckpt) : reinterpret_cast<float*>(ws + wl.off_ckpt);
+    a.ckpt_given = ckpt != nullptr;
     a.part_dB = reinterpret_cast<float*>(ws + wl.off_pdB);
     a.part_dC = reinterpret_cast<float*>(ws + wl.off_pdC);
     a.part_dA = reinterpret_cast<float*>(ws + wl.off_pdA);
@@ -455,6 +565,10 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weight, const float* bias, void* u,
                          int64_t batch, int64_t seqlen, int64_t dim, int64_t width, ss_dtype dtype,

@@ -16,12 +16,16 @@
 // softplus derivative sigmoid(raw + bias) on ddelta, dbias += ddelta, dh0 = g.
 //
 // Three launches after the B/C panel:
-//  1. prep_kernel runs the forward once, storing the state every kBwdSub rows
-//     (the checkpoints), the per-workgroup channel sums of dC, and dz;
+//  1. prep_kernel runs the recurrence once and stores the state every kBwdSub
+//     rows (the checkpoints).  It is skipped when the caller passes the
+//     checkpoints of its forward pass (ss_scan_fwd_ckpt writes them), which
+//     reuses the forward's states the way the chunked forward reuses its
+//     chunk carries;
 //  2. bwd_kernel walks the sub-blocks from the last to the first: it rebuilds
 //     the sub-block's states in registers from its checkpoint, then runs the
-//     adjoint down the sub-block, writing du and ddelta and the per-workgroup
-//     channel sums of dB, and keeping dA, dD, dbias per lane;
+//     adjoint down the sub-block, writing du, ddelta and dz and the
+//     per-workgroup channel sums of dB and dC, and keeping dA, dD, dbias per
+//     lane;
 //  3. bwd_reduce_kernel adds the per-workgroup and per-batch-row partial sums
 //     in a fixed order (the result does not depend on scheduling) and rounds
 //     dB, dC to the operand type.
@@ -113,24 +117,21 @@ struct Rows {
 };
 
 // ---------------------------------------------------------------------------
-// prep_kernel: the forward once, from h0.  grid = (ceil(dim/64), batch),
-// block = 64 * kGroups.  Per sub-block j: store the state entering row
-// kSub*j, publish (delta, delta*u, dy') per row in LDS, advance the state over
-// the sub-block while summing dy'*h_t over the workgroup's channels (dC
-// partials), and with a gate finish dz = dy * ypre * silu'(z).
+// prep_kernel: the recurrence once, from h0, storing the state entering every
+// sub-block (the checkpoints).  grid = (ceil(dim/64), batch), block = 64 *
+// kGroups.  Per sub-block: store the state, publish (delta, delta*u) per row in
+// LDS, advance the state over the sub-block's 16 rows.
 // ---------------------------------------------------------------------------
-template <int DT, bool HAS_D, bool HAS_Z, int MODE>
+template <int DT, int MODE>
 __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
 {
     using V = Buf<DT>;
-    __shared__ float4 s_row[kSub][kWave];                     // (delta, delta*u, dy', 0)
-    __shared__ float s_y[HAS_Z ? kGroups : 1][kSub][kWave];  // partial C.h per wave (for dz)
+    __shared__ float2 s_row[2][kSub][kWave];  // (delta, delta*u), by sub-block parity
 
     const Lane<DT> ln(a);
     const int lane = ln.lane, w = ln.w;
-    const int64_t D = a.dim, L = a.seqlen, NB = a.batch, blk = blockIdx.x;
-    const auto r_u = ln.rsrc(a.u, a), r_dl = ln.rsrc(a.delta, a), r_dy = ln.rsrc(a.dy, a);
-    const auto r_z = ln.rsrc(HAS_Z ? a.z : a.u, a), r_dz = ln.rsrc(HAS_Z ? a.dz : a.u, a);
+    const int64_t D = a.dim, L = a.seqlen, NB = a.batch;
+    const auto r_u = ln.rsrc(a.u, a), r_dl = ln.rsrc(a.delta, a);
 
     float A2[kNS], h[kNS];
 #pragma unroll
@@ -139,13 +140,21 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
         h[i] = (a.h0 && ln.active) ? a.h0[(ln.b * D + ln.d) * N + w * kNS + i] : 0.0f;
     }
     const float bias = a.delta_bias ? a.delta_bias[ln.d] : 0.0f;
-    const float dskip = HAS_D ? a.Dskip[ln.d] : 0.0f;
 
-    Rows<DT> rows;
-    rows.template issue<HAS_Z>(ln, L, 0, r_dl, r_u, r_dy, r_z);
-    float xf[2], dyf[2], zf[2];
-
+    // this wave's two rows of sub-block j (row w of each half), raw
+    typename V::Raw rdl[2], rx[2];
+    auto issue = [&](int j) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t t = int64_t(j) * kSub + row_of(w, k);
+            const uint32_t so = uint32_t(t < L ? t : L - 1) * ln.row_bytes;
+            rdl[k] = V::load(r_dl, ln.voff, so);
+            rx[k] = V::load(r_u, ln.voff, so);
+        }
+    };
+    issue(0);
     for (int j = 0; j < int(a.n_sub); ++j) {
+        const int par = j & 1;
         if (ln.active) {
 #pragma unroll
             for (int i = 0; i < kNS; ++i) a.ckpt[((int64_t(j) * NB + ln.b) * N + w * kNS + i) * D + ln.d] = h[i];
@@ -154,60 +163,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
         for (int k = 0; k < 2; ++k) {
             const int r = row_of(w, k);
             const bool in = ln.active && int64_t(j) * kSub + r < L;
-            const float dl = in ? step_size<MODE>(V::widen(rows.dl[k]), bias) : 0.0f;
-            const float x = V::widen(rows.x[k]);
-            const float dyv = in ? V::widen(rows.dy[k]) : 0.0f;
-            const float zv = HAS_Z ? V::widen(rows.z[k]) : 0.0f;
-            const float dyp = HAS_Z ? dyv * silu(zv) : dyv;
-            s_row[r][lane] = make_float4(dl, dl * x, dyp, 0.0f);
-            xf[k] = x;
-            dyf[k] = dyv;
-            zf[k] = zv;
+            const float dl = in ? step_size<MODE>(V::widen(rdl[k]), bias) : 0.0f;
+            s_row[par][r][lane] = make_float2(dl, dl * V::widen(rx[k]));
         }
-        if (j + 1 < int(a.n_sub)) rows.template issue<HAS_Z>(ln, L, j + 1, r_dl, r_u, r_dy, r_z);
+        if (j + 1 < int(a.n_sub)) issue(j + 1);
+        // one barrier per sub-block: the next one writes the other parity
         __syncthreads();
-
 #pragma unroll
-        for (int tile = 0; tile < 2; ++tile) {
-            const Words16 bw = ln.words_B(j, tile);
-            Words16 cw;
-            if constexpr (HAS_Z) cw = ln.words_C(j, tile);
-            float dc[16];  // dy' * h_t for the tile's 8 rows and the wave's 2 entries
+        for (int half = 0; half < 2; ++half) {
+            const Words16 bw = ln.words_B(j, half);
 #pragma unroll
             for (int rr = 0; rr < kHalf; ++rr) {
-                const int r = tile * kHalf + rr;
-                const float4 rv = s_row[r][lane];
-                float ypart = 0.0f;
+                const float2 rv = s_row[par][half * kHalf + rr][lane];
 #pragma unroll
-                for (int i = 0; i < kNS; ++i) {
-                    const float e = exp2_hw(rv.x * A2[i]);
-                    h[i] = fmaf(e, h[i], rv.y * word(bw, rr, i));
-                    dc[rr * kNS + i] = rv.z * h[i];
-                    if constexpr (HAS_Z) ypart = fmaf(word(cw, rr, i), h[i], ypart);
-                }
-                if constexpr (HAS_Z) s_y[w][r][lane] = ypart;
-            }
-            // channel sums; lane l holds entry l/4 = (row, state) of the tile
-            const float tot = sum16_across_lanes(dc);
-            const int k = lane >> 2;
-            const int64_t t = int64_t(j) * kSub + tile * kHalf + (k >> 1);
-            if ((lane & 3) == 0 && t < L) a.part_dC[((blk * NB + ln.b) * L + t) * N + w * kNS + (k & 1)] = tot;
-        }
-        __syncthreads();
-
-        if constexpr (HAS_Z) {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int r = row_of(w, k);
-                const int64_t t = int64_t(j) * kSub + r;
-                if (t < L) {
-                    float y = s_y[0][r][lane];
-#pragma unroll
-                    for (int g = 1; g < kGroups; ++g) y += s_y[g][r][lane];
-                    if (HAS_D) y = fmaf(dskip, xf[k], y);
-                    const float s = sigmoid(zf[k]);
-                    V::store(r_dz, ln.voff, uint32_t(t) * ln.row_bytes, dyf[k] * y * s * fmaf(zf[k], 1.0f - s, 1.0f));
-                }
+                for (int i = 0; i < kNS; ++i) h[i] = fmaf(exp2_hw(rv.x * A2[i]), h[i], rv.y * word(bw, rr, i));
             }
         }
     }
@@ -219,15 +188,18 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
 // rows, rebuild the states from the checkpoint, then for each half (last
 // first) run the adjoint down its rows -- per-wave partial sums over the
 // wave's state entries of g.B and g.h_{t-1}.e.A go to LDS, the channel sums
-// of g*delta*u (dB) to the partial buffer -- and finish one row per wave:
-// du, ddelta, and the per-lane dD and dbias terms.
+// of g*delta*u (dB) to the partial buffer -- then, from the rebuilt states,
+// the channel sums of dy'*h_t (dC) and, with a gate, the per-wave partial
+// C.h_t; and finish one row per wave: du, ddelta, dz, and the per-lane dD and
+// dbias terms.
 // ---------------------------------------------------------------------------
 template <int DT, bool HAS_D, bool HAS_Z, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void bwd_kernel(BwdArgs a)
 {
     using V = Buf<DT>;
     __shared__ float4 s_row[kSub][kWave];        // (delta, delta*u, dy', 0)
     __shared__ float2 s_par[kGroups][kHalf][kWave];  // per wave (sum g.B, sum g.h.e.A) of one half
+    __shared__ float s_yp[HAS_Z ? kGroups : 1][kHalf][kWave];  // per wave C.h_t of one half (for dz)
 
     const Lane<DT> ln(a);
     const int lane = ln.lane, w = ln.w;
@@ -235,6 +207,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
     const auto r_u = ln.rsrc(a.u, a), r_dl = ln.rsrc(a.delta, a), r_dy = ln.rsrc(a.dy, a);
     const auto r_z = ln.rsrc(HAS_Z ? a.z : a.u, a);
     const auto r_du = ln.rsrc(a.du, a), r_ddl = ln.rsrc(a.ddelta, a);
+    const auto r_dz = ln.rsrc(HAS_Z ? a.dz : a.du, a);
 
     float A2[kNS], Av[kNS], g[kNS], dA_acc[kNS];
 #pragma unroll
@@ -250,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
 
     Rows<DT> rows;
     rows.template issue<HAS_Z>(ln, L, int(a.n_sub) - 1, r_dl, r_u, r_dy, r_z);
-    float xf[2], dlf[2], sgf[2], dypf[2];
+    float xf[2], dlf[2], sgf[2], dypf[2], dzf[2];  // dzf: dy * silu'(z), dz without ypre
 
     for (int j = int(a.n_sub) - 1; j >= 0; --j) {
         float hprev[kNS];
@@ -265,12 +238,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
             const float dl = in ? ((MODE & kOptSoftplus) ? softplus(v) : v) : 0.0f;
             const float x = V::widen(rows.x[k]);
             const float dyv = in ? V::widen(rows.dy[k]) : 0.0f;
-            const float dyp = HAS_Z ? dyv * silu(V::widen(rows.z[k])) : dyv;
+            const float zv = HAS_Z ? V::widen(rows.z[k]) : 0.0f;
+            const float dyp = HAS_Z ? dyv * silu(zv) : dyv;
             s_row[r][lane] = make_float4(dl, dl * x, dyp, 0.0f);
             xf[k] = x;
             dlf[k] = dl;
             sgf[k] = (MODE & kOptSoftplus) ? sigmoid(v) : 1.0f;
             dypf[k] = dyp;
+            if (HAS_Z) {
+                const float sz = sigmoid(zv);
+                dzf[k] = dyv * sz * fmaf(zv, 1.0f - sz, 1.0f);
+            }
         }
         if (j > 0) rows.template issue<HAS_Z>(ln, L, j - 1, r_dl, r_u, r_dy, r_z);
         __syncthreads();
@@ -293,32 +271,46 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
 #pragma unroll
         for (int half = 1; half >= 0; --half) {
             const Words16 bw = ln.words_B(j, half), cw = ln.words_C(j, half);
-            float db[16];  // g * delta * u for the half's 8 rows and the wave's 2 entries
+            // the half's rows in two quarters of 4, last first: per quarter the
+            // channel sums of g*delta*u (dB) and dy'*h_t (dC) over its 8
+            // (row, state) values, taken as soon as the quarter is done so that
+            // few of them and of the states are live at once
 #pragma unroll
-            for (int rr = kHalf - 1; rr >= 0; --rr) {
-                const int r = half * kHalf + rr;
-                const float4 rv = s_row[r][lane];
-                float s1 = 0.0f, s2 = 0.0f;
+            for (int qt = 1; qt >= 0; --qt) {
+                float db[8], dc[8];
 #pragma unroll
-                for (int i = 0; i < kNS; ++i) {
-                    g[i] = fmaf(rv.z, word(cw, rr, i), g[i]);
-                    const float hp = r ? hh[r - 1][i] : hprev[i];
-                    const float e = exp2_hw(rv.x * A2[i]);
-                    const float t1 = g[i] * hp * e;
-                    dA_acc[i] = fmaf(t1, rv.x, dA_acc[i]);
-                    s2 = fmaf(t1, Av[i], s2);
-                    s1 = fmaf(g[i], word(bw, rr, i), s1);
-                    db[rr * kNS + i] = g[i] * rv.y;
-                    g[i] *= e;
+                for (int rq = 3; rq >= 0; --rq) {
+                    const int rr = 4 * qt + rq, r = half * kHalf + rr;
+                    const float4 rv = s_row[r][lane];
+                    float s1 = 0.0f, s2 = 0.0f, yp = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < kNS; ++i) {
+                        // h_t is last needed here: dC, and C.h_t for dz
+                        dc[rq * kNS + i] = rv.z * hh[r][i];
+                        if (HAS_Z) yp = fmaf(word(cw, rr, i), hh[r][i], yp);
+                        g[i] = fmaf(rv.z, word(cw, rr, i), g[i]);
+                        const float hp = r ? hh[r - 1][i] : hprev[i];
+                        // g e is both a factor of g h_{t-1} e and the next row's g
+                        const float ge = g[i] * exp2_hw(rv.x * A2[i]);
+                        const float t1 = ge * hp;
+                        dA_acc[i] = fmaf(t1, rv.x, dA_acc[i]);
+                        s2 = fmaf(t1, Av[i], s2);
+                        s1 = fmaf(g[i], word(bw, rr, i), s1);
+                        db[rq * kNS + i] = g[i] * rv.y;
+                        g[i] = ge;
+                    }
+                    s_par[w][rr][lane] = make_float2(s1, s2);
+                    if (HAS_Z) s_yp[w][rr][lane] = yp;
                 }
-                s_par[w][rr][lane] = make_float2(s1, s2);
-            }
-            {
-                // channel sums; lane l holds entry l/4 = (row, state) of the half
-                const float tot = sum16_across_lanes(db);
-                const int k = lane >> 2;
-                const int64_t t = int64_t(j) * kSub + half * kHalf + (k >> 1);
-                if ((lane & 3) == 0 && t < L) a.part_dB[((blk * NB + ln.b) * L + t) * N + w * kNS + (k & 1)] = tot;
+                // lane l holds the sums of value l/8 = (row, state) of the quarter
+                const float tb = sum8_across_lanes(db), tc = sum8_across_lanes(dc);
+                const int k = lane >> 3;
+                const int64_t t = int64_t(j) * kSub + half * kHalf + 4 * qt + (k >> 1);
+                if ((lane & 7) == 0 && t < L) {
+                    const int64_t at = ((blk * NB + ln.b) * L + t) * N + w * kNS + (k & 1);
+                    a.part_dB[at] = tb;
+                    a.part_dC[at] = tc;
+                }
             }
             __syncthreads();
             {
@@ -341,6 +333,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a)
                     dbias_acc += ddl;
                     V::store(r_du, ln.voff, uint32_t(t) * ln.row_bytes, du);
                     V::store(r_ddl, ln.voff, uint32_t(t) * ln.row_bytes, ddl);
+                    if constexpr (HAS_Z) {
+                        // dz = dy * ypre * silu'(z), ypre = C.h_t + D u
+                        float y = s_yp[0][w][lane];
+#pragma unroll
+                        for (int q = 1; q < kGroups; ++q) y += s_yp[q][w][lane];
+                        if (HAS_D) y = fmaf(dskip, xf[half], y);
+                        V::store(r_dz, ln.voff, uint32_t(t) * ln.row_bytes, dzf[half] * y);
+                    }
                 }
             }
             __syncthreads();
@@ -414,7 +414,7 @@ template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s)
 {
     const dim3 grid(unsigned(a.nblk), unsigned(a.batch));
-    prep_kernel<DT, HAS_D, HAS_Z, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
+    if (!a.ckpt_given) prep_kernel<DT, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
     bwd_kernel<DT, HAS_D, HAS_Z, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
     int64_t most = a.batch * a.seqlen * N;
     if (a.dim * N > most) most = a.dim * N;

@@ -233,5 +233,32 @@ __device__ __forceinline__ float sum16_across_lanes(const float (&v)[16])
     return z + dpp<kDppQuadSwap2>(z);
 }
 
+// The same for 8 values: afterwards every lane l holds the sum over the
+// wave's 64 lanes of v[l / 8].  Swap of the 32-lane halves (vector p: value p
+// in lanes 0-31, p + 4 in lanes 32-63), swap of odd and even 16-lane rows
+// (value p + 2*((l/16)&1) + 4*(l/32)), the two 8-lane halves of each row
+// (row rotation by 8: value l/8), then a sum over each 8 lanes (half-row
+// mirror, quad permutations).  18 instructions for 8 sums.
+__device__ __forceinline__ float sum8_across_lanes(const float (&v)[8])
+{
+    const int lane = threadIdx.x & 63;
+    float w[4], x[2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[p]), __float_as_uint(v[p + 4]), false, false);
+        w[p] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[p]), __float_as_uint(w[p + 2]), false, false);
+        x[p] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+    const bool hi8 = (lane & 8) != 0;
+    float z = (hi8 ? x[1] : x[0]) + dpp<kDppRowRor8>(hi8 ? x[0] : x[1]);
+    z += dpp<kDppRowHalfMirror>(z);
+    z += dpp<kDppQuadSwap1>(z);
+    return z + dpp<kDppQuadSwap2>(z);
+}
+
 }  // namespace
 }  // namespace ssk

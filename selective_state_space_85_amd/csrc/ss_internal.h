@@ -59,6 +59,10 @@ struct ScanArgs {
     // regrouped so that a wave's entries of consecutive rows are contiguous
     float* ws_panel;
     int64_t panel_rows;
+    // (ceil(seqlen / kBwdSub), batch, N, dim) fp32: the state entering every
+    // kBwdSub-th row, written by the emit pass when not null (chunk_len is then
+    // a multiple of kBwdSub or n_chunks is 1)
+    float* ckpt;
     int64_t batch, seqlen, dim;
     int64_t chunk_len, n_chunks;
 };
@@ -109,6 +113,7 @@ struct BwdArgs {
     const float* panel;       // the fp32 B/C panel, one chunk per batch row
     int64_t panel_rows;
     float* ckpt;              // (n_sub, batch, N, dim): state entering row kBwdSub*j
+    bool ckpt_given;          // ckpt holds the forward's checkpoints: no recompute pass
     float* part_dB;           // (nblk, batch, seqlen, N): per-workgroup sums over its channels
     float* part_dC;
     float* part_dA;           // (batch, dim, N): per-batch-row sums over time

@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
     // the CU ends its run with a single latency-bound workgroup.  Lowering a
     // wave's priority at each quarter of the chunk lets the laggards catch up,
     // so the workgroups of a CU stay within a quarter of each other.
+    static_assert(2 * kTileRows == kBwdSub, "checkpoints fall at the start of every tile pair");
     const int quarter = (ntiles / 4) & ~1;
     __builtin_amdgcn_s_setprio(3);
     for (int k = 0; k < ntiles; k += 2) {
@@ -317,6 +318,12 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
             if (k == quarter) __builtin_amdgcn_s_setprio(2);
             else if (k == 2 * quarter) __builtin_amdgcn_s_setprio(1);
             else if (k == 3 * quarter) __builtin_amdgcn_s_setprio(0);
+        }
+        if (EMIT && a.ckpt && active && k * TT < len) {
+            // the state entering row t0 + k*TT, a multiple of kBwdSub (k is even)
+            float* dst = a.ckpt + (((t0 + k * TT) / kBwdSub * a.batch + b) * N + w * kNS) * D + d;
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) dst[int64_t(i) * D] = h[i];
         }
         step(k, Slot<0>{});
         step(k + 1, Slot<1>{});

@@ -60,9 +60,11 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              h0: Optional[torch.Tensor] = None, *, return_last_state: bool = False,
              chunk_len: int = 0, out: Optional[torch.Tensor] = None,
              h_last: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False
-             ) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
-    """Selective scan ``ss_scan_fwd_ex`` on device tensors.
+             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False,
+             ckpt: Optional[torch.Tensor] = None) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+    """Selective scan ``ss_scan_fwd_ex`` on device tensors; with ``ckpt`` (a float32 tensor of
+    ``scan_ckpt_shape(B, L, D, N)``) it is ``ss_scan_fwd_ckpt``, which also writes there the
+    state entering every 16th timestep for ``scan_bwd(..., ckpt=ckpt)``.
 
     u, delta, z: (B, L, D); B, C: (B, L, N) -- all float32 or all bfloat16.
     A: (D, N) float32; D: (D,) float32; h0: (B, D, N) float32.
@@ -101,17 +103,27 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
         hl = torch.empty((nb, nd, nn), dtype=torch.float32, device=dev)
     if hl is not None:
         _need(hl, "h_last", (nb, nd, nn), torch.float32, dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", scan_ckpt_shape(nb, nl, nd, nn), torch.float32, dev)
     need = scan_workspace_bytes(nb, nl, nd, nn, chunk_len)
     ws = workspace
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    lib = _lib.load()
     with torch.cuda.device(dev):
-        st = _lib.load().ss_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                        _ptr(h0), _ptr(delta_bias), _options(delta_softplus, zoh),
-                                        _ptr(y), _ptr(hl), _ptr(ws), ws_bytes,
-                                        nb, nl, nd, nn, chunk_len, _DTYPES[dt], _stream(dev))
-    _lib.check("ss_scan_fwd_ex", st)
+        if ckpt is None:
+            name = "ss_scan_fwd_ex"
+            st = lib.ss_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                    _ptr(delta_bias), _options(delta_softplus, zoh), _ptr(y), _ptr(hl),
+                                    _ptr(ws), ws_bytes, nb, nl, nd, nn, chunk_len, _DTYPES[dt], _stream(dev))
+        else:
+            name = "ss_scan_fwd_ckpt"
+            st = lib.ss_scan_fwd_ckpt(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(h0), _ptr(delta_bias), _options(delta_softplus, zoh), _ptr(y), _ptr(hl),
+                                      _ptr(ckpt), _ptr(ws), ws_bytes, nb, nl, nd, nn, chunk_len, _DTYPES[dt],
+                                      _stream(dev))
+    _lib.check(name, st)
     if return_last_state:
         return y, hl
     return y
@@ -158,8 +170,20 @@ def step(h: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
     return y
 
 
-def scan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int) -> int:
-    n = _lib.load().ss_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate)
+def scan_ckpt_shape(batch: int, seqlen: int, dim: int, dstate: int) -> Tuple[int, int, int, int]:
+    """Shape of the float32 state checkpoints (``ss_scan_ckpt_bytes``): one state every 16
+    timesteps, laid out (ceil(L/16), B, N, D)."""
+    n = _lib.load().ss_scan_ckpt_bytes(batch, seqlen, dim, dstate)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid scan shape")
+    return (-(-seqlen // 16), batch, dstate, dim)
+
+
+def scan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, with_ckpt: bool = False) -> int:
+    """Workspace of ``ss_scan_bwd`` (or, with_ckpt, of ``ss_scan_bwd_ckpt``)."""
+    lib = _lib.load()
+    fn = lib.ss_scan_bwd_ckpt_workspace_bytes if with_ckpt else lib.ss_scan_bwd_workspace_bytes
+    n = fn(batch, seqlen, dim, dstate)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid scan shape")
     return int(n)
@@ -169,9 +193,12 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
              h0: Optional[torch.Tensor] = None, *, dh_last: Optional[torch.Tensor] = None,
              delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
-             want_dh0: bool = True, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+             want_dh0: bool = True, workspace: Optional[torch.Tensor] = None,
+             ckpt: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """Gradients of sum(dy * y) + sum(dh_last * h_last) for ``scan_fwd`` with the same inputs
     (``ss_scan_bwd``).  dy (B, L, D) in the input dtype; dh_last (B, D, N) float32 or None.
+    With ``ckpt`` (the checkpoints ``scan_fwd(..., ckpt=ckpt)`` wrote) it is ``ss_scan_bwd_ckpt``,
+    which reuses them instead of recomputing the states' checkpoints.
 
     Returns a dict: du, ddelta, dz (B, L, D) and dB, dC (B, L, N) in the input dtype; dA (D, N),
     dD (D,), ddelta_bias (D,), dh0 (B, D, N) float32.  Gradients of absent inputs are absent;
@@ -210,18 +237,27 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
         g["ddelta_bias"] = torch.empty((nd,), dtype=torch.float32, device=dev)
     if want_dh0:
         g["dh0"] = torch.empty((nb, nd, nn), dtype=torch.float32, device=dev)
-    need = scan_bwd_workspace_bytes(nb, nl, nd, nn)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", scan_ckpt_shape(nb, nl, nd, nn), torch.float32, dev)
+    need = scan_bwd_workspace_bytes(nb, nl, nd, nn, with_ckpt=ckpt is not None)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = ws.numel() * ws.element_size()
     opts = _options(delta_softplus, False)
+    grads = (_ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+             _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")))
+    lib = _lib.load()
     with torch.cuda.device(dev):
-        st = _lib.load().ss_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                                     _ptr(delta_bias), opts, _ptr(dy), _ptr(dh_last),
-                                     _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
-                                     _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
-                                     _ptr(g.get("dh0")), _ptr(ws), ws_bytes, nb, nl, nd, nn, _DTYPES[dt],
-                                     _stream(dev))
-    _lib.check("ss_scan_bwd", st)
+        if ckpt is None:
+            name = "ss_scan_bwd"
+            st = lib.ss_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                 _ptr(delta_bias), opts, _ptr(dy), _ptr(dh_last), *grads, _ptr(ws), ws_bytes,
+                                 nb, nl, nd, nn, _DTYPES[dt], _stream(dev))
+        else:
+            name = "ss_scan_bwd_ckpt"
+            st = lib.ss_scan_bwd_ckpt(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(delta_bias), opts, _ptr(dy), _ptr(dh_last), _ptr(ckpt), *grads,
+                                      _ptr(ws), ws_bytes, nb, nl, nd, nn, _DTYPES[dt], _stream(dev))
+    _lib.check(name, st)
     return g
 
 

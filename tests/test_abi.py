@@ -286,6 +286,63 @@ def test_bwd_validation(lib):
     assert call_bwd(lib, ws=near(6, 0)) == INVALID            # workspace on du
 
 
+def call_fwd_ckpt(lib, ckpt=addr(7), bias=None, options=0, **kw):
+    args = dict(u=addr(0), delta=addr(1), A=addr(2), B=addr(3), C=addr(4), D=None, z=None, h0=None,
+                y=addr(5), h_last=None, ws=addr(6), ws_bytes=1 << 40, batch=2, seqlen=512, dim=64,
+                dstate=16, chunk=0, dtype=BF16)
+    args.update(kw)
+    return lib.ss_scan_fwd_ckpt(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                                args["h0"], bias, options, args["y"], args["h_last"], ckpt, args["ws"],
+                                args["ws_bytes"], args["batch"], args["seqlen"], args["dim"], args["dstate"],
+                                args["chunk"], args["dtype"], None)
+
+
+def call_bwd_ckpt(lib, ckpt=addr(14), **kw):
+    args = dict(u=addr(0), delta=addr(1), A=addr(2), B=addr(3), C=addr(4), D=None, z=None, h0=None, bias=None,
+                options=0, dy=addr(5), dh_last=None, du=addr(6), ddelta=addr(7), dA=addr(8), dB=addr(9),
+                dC=addr(10), dD=None, dz=None, dbias=None, dh0=None, ws=addr(11), ws_bytes=1 << 40, batch=2,
+                seqlen=512, dim=64, dstate=16, dtype=BF16)
+    args.update(kw)
+    return lib.ss_scan_bwd_ckpt(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                                args["h0"], args["bias"], args["options"], args["dy"], args["dh_last"], ckpt,
+                                args["du"], args["ddelta"], args["dA"], args["dB"], args["dC"], args["dD"],
+                                args["dz"], args["dbias"], args["dh0"], args["ws"], args["ws_bytes"], args["batch"],
+                                args["seqlen"], args["dim"], args["dstate"], args["dtype"], None)
+
+
+def test_ckpt_sizes(lib):
+    b, l, d, n = 2, 300, 100, 16
+    ck = lib.ss_scan_ckpt_bytes(b, l, d, n)
+    assert ck == 4 * (-(-l // 16)) * b * d * n
+    assert lib.ss_scan_ckpt_bytes(b, 0, d, n) == ctypes.c_size_t(-1).value
+    full = lib.ss_scan_bwd_workspace_bytes(b, l, d, n)
+    without = lib.ss_scan_bwd_ckpt_workspace_bytes(b, l, d, n)
+    # the same layout without the checkpoint region (its start is rounded to 256 bytes)
+    assert ck <= full - without <= ck + 255
+    assert lib.ss_scan_bwd_ckpt_workspace_bytes(b, l, 0, n) == ctypes.c_size_t(-1).value
+
+
+def test_ckpt_validation(lib):
+    """The checkpoint entry points reject on the host, before anything is enqueued."""
+    near = lambda i, off: ctypes.c_void_p(BASE + i * GAP + off)  # noqa: E731
+    assert call_fwd_ckpt(lib, ckpt=None) == INVALID
+    assert call_fwd_ckpt(lib, ckpt=near(7, 4)) == INVALID        # not 16-byte aligned
+    assert call_fwd_ckpt(lib, ckpt=near(5, 64)) == INVALID       # inside y
+    assert call_fwd_ckpt(lib, ckpt=near(1, 0)) == INVALID        # on delta
+    assert call_fwd_ckpt(lib, ckpt=near(6, 256)) == INVALID      # inside the workspace
+    assert call_fwd_ckpt(lib, chunk=8) == UNSUPPORTED            # chunks must start on a checkpoint row
+    assert call_fwd_ckpt(lib, dstate=8) == UNSUPPORTED
+    assert call_fwd_ckpt(lib, y=None) == INVALID
+    assert call_bwd_ckpt(lib, ckpt=None) == INVALID
+    assert call_bwd_ckpt(lib, ckpt=near(14, 8)) == INVALID       # not 16-byte aligned
+    assert call_bwd_ckpt(lib, du=near(14, 0)) == INVALID         # an output on the checkpoints
+    assert call_bwd_ckpt(lib, ws=near(14, 256)) == INVALID       # the workspace on the checkpoints
+    assert call_bwd_ckpt(lib, options=2) == UNSUPPORTED          # no zero-order hold in the backward
+    need = lib.ss_scan_bwd_ckpt_workspace_bytes(2, 512, 64, 16)
+    assert call_bwd_ckpt(lib, ws_bytes=need - 1) == WORKSPACE
+    assert call_bwd_ckpt(lib, dy=None) == INVALID
+
+
 def call_conv(lib, **kw):
     args = dict(x=addr(0), stride=64, w=addr(1), bias=None, u=addr(2), batch=2, seqlen=100, dim=64, width=4,
                 dtype=BF16)

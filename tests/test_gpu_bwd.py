@@ -117,3 +117,91 @@ def test_bwd_large_layer():
     dy = wl.f32_to_bf16_bits(rng.standard_normal((w.batch, w.seqlen, w.dim)).astype(np.float32))
     say("backward on the large layer")
     check(inp, dy, None, False, "large layer", threads=THREADS)
+
+
+# --- the training path: the forward keeps every 16th state, the backward reuses them ---
+
+def fwd_with_ckpt(inp, softplus, chunk_len=0):
+    m = ss()
+    t = {k: dev(v) for k, v in inp.items()}
+    b, l, d = inp["u"].shape
+    ck = torch.full(m.scan_ckpt_shape(b, l, d, 16), float("nan"), dtype=torch.float32, device="cuda")
+    y = m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t.get("D"), z=t.get("z"), h0=t.get("h0"),
+                   delta_bias=t.get("delta_bias"), delta_softplus=softplus, chunk_len=chunk_len, ckpt=ck)
+    y_plain = m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t.get("D"), z=t.get("z"), h0=t.get("h0"),
+                         delta_bias=t.get("delta_bias"), delta_softplus=softplus, chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_plain), "y of the checkpointing forward differs"
+    return ck
+
+
+def check_ckpt_states(inp, ck, softplus, tol):
+    """ckpt[j] = the oracle's state entering timestep 16 j (h0, or zero, for j = 0)."""
+    b, l, d = inp["u"].shape
+    n_sub = -(-l // 16)
+    ref = oracle.scan(**inp, lanes=np.arange(b * d), record_t=[16 * j - 1 for j in range(1, n_sub)],
+                      delta_softplus=softplus)
+    got = host64(ck)                                     # (J, B, N, D)
+    got = got.transpose(1, 3, 0, 2).reshape(b * d, n_sub, 16)  # (lanes, J, N)
+    h0 = np.zeros((b * d, 16)) if inp.get("h0") is None else inp["h0"].astype(np.float64).reshape(b * d, 16)
+    assert np.array_equal(got[:, 0], h0)
+    if n_sub > 1:
+        e = rel_err(got[:, 1:], ref["h_rec"])
+        say("  checkpoints: max rel err %.2e" % e)
+        assert e <= tol
+
+
+CKPT_CASES = [
+    # (batch, seqlen, dim, dtype, has_D, has_z, has_h0, softplus, chunk_len request)
+    (2, 100, 70, wl.F32, True, True, True, False, 100),    # ragged rows and channels, one chunk
+    (1, 200, 64, wl.F32, True, False, True, True, 32),     # softplus + bias, seven chunks of 32
+    (2, 300, 70, wl.F32, True, True, True, False, 0),      # the library's own chunking
+    (2, 33, 130, wl.BF16, True, True, False, False, 33),
+    (1, 16, 64, wl.F32, False, False, False, False, 16),   # exactly one sub-block
+]
+
+
+@pytest.mark.parametrize("case", CKPT_CASES, ids=["B%dL%dD%d-%s-T%d" % (c[0], c[1], c[2], c[3], c[8])
+                                                  for c in CKPT_CASES])
+def test_bwd_from_forward_checkpoints(case):
+    """ss_scan_fwd_ckpt's checkpoints are the oracle's states; ss_scan_bwd_ckpt from them matches the
+    oracle's gradients, and equals ss_scan_bwd bit for bit after a one-chunk forward (a chunked
+    forward's checkpoints come from its chunk carries, equal up to rounding)."""
+    b, l, d, dt, has_D, has_z, has_h0, sp, chunk = case
+    inp, dy, dhl = make_case(b, l, d, dt, has_D=has_D, has_z=has_z, has_h0=has_h0, softplus=sp, seed=60 + l)
+    tol = TOL["bf16" if dt == wl.BF16 else "f32"]
+    say("checkpointed backward B%d L%d D%d %s chunk %d" % (b, l, d, dt, chunk))
+    ck = fwd_with_ckpt(inp, sp, chunk)
+    check_ckpt_states(inp, ck, sp, tol)
+    t = {k: dev(v) for k, v in inp.items()}
+    g = ss().scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dev(dy), D=t.get("D"), z=t.get("z"),
+                      h0=t.get("h0"), dh_last=dev(dhl), delta_bias=t.get("delta_bias"), delta_softplus=sp, ckpt=ck)
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(**inp, dy=oracle.widen(dy), dh_last=dhl, delta_softplus=sp)
+    for k, r in ref.items():
+        e = rel_err(host64(g[k]), r)
+        assert e <= tol, "%s error %.3e" % (k, e)
+    if ss().scan_plan(b, l, d, 16, chunk)[1] == 1:
+        g_plain = gpu_grads(inp, dy, dhl, sp)
+        for k in g:
+            assert torch.equal(g[k], g_plain[k]), "%s differs from ss_scan_bwd" % k
+
+
+def test_bwd_from_checkpoints_large_layer():
+    """The large layer: the checkpointing forward and the backward from its checkpoints give
+    ss_scan_fwd's y and ss_scan_bwd's gradients bit for bit (those two are checked against
+    the oracle on every element above)."""
+    w = wl.WORKLOADS["large"]
+    inp = wl.workload_inputs(w)
+    rng = np.random.default_rng(53)
+    dy = dev(wl.f32_to_bf16_bits(rng.standard_normal((w.batch, w.seqlen, w.dim)).astype(np.float32)))
+    say("checkpointed backward on the large layer")
+    assert ss().scan_plan(w.batch, w.seqlen, w.dim, w.dstate)[1] == 1
+    ck = fwd_with_ckpt(inp, False)
+    t = {k: dev(v) for k, v in inp.items()}
+    args = (t["u"], t["delta"], t["A"], t["B"], t["C"], dy)
+    g_ck = ss().scan_bwd(*args, D=t.get("D"), z=t.get("z"), ckpt=ck)
+    g = ss().scan_bwd(*args, D=t.get("D"), z=t.get("z"))
+    torch.cuda.synchronize()
+    for k in g:
+        assert torch.equal(g[k], g_ck[k]), k
