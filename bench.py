@@ -16,7 +16,9 @@ calls launched one by one against the same loop captured once in a hipGraph
 and replayed), ``parity`` (timed output vs the oracle on sampled channels),
 ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
 before every step), ``options`` (the same layer with the softplus(delta +
-bias) step size and/or the zero-order-hold input term), ``backward``
+bias) step size and/or the zero-order-hold input term), ``configs``
+(the small-model layer and the long context at their own shapes; the long
+context runs the chunked plan: aggregate, carry and emit passes), ``backward``
 (ss_scan_bwd on the same layer: all input gradients from dy; and the training
 path, ss_scan_fwd_ckpt keeping every 16th state and ss_scan_bwd_ckpt reusing
 them), ``conv1d``
@@ -331,6 +333,43 @@ def main():
                                            "note": "ss_scan_fwd_ckpt keeps the state every 16 rows; "
                                                    "ss_scan_bwd_ckpt skips the checkpoint pass"}}
         del ck, cws, yk
+
+        # the other scan configurations at their own shapes: the small-model layer and the
+        # long context, whose automatic plan cuts the sequence into chunks (aggregate pass,
+        # carry pass, emit pass).  Inputs drawn on the device with the configurations'
+        # distributions.
+        cfgs = {}
+        for name in ("small", "long"):
+            cw_ = wl.WORKLOADS[name]
+            gen = torch.Generator(device).manual_seed(100 + cw_.cfg_id)
+            shp = (cw_.batch, cw_.seqlen, cw_.dim)
+            tdt = torch.bfloat16 if cw_.dtype == wl.BF16 else torch.float32
+            cu_ = torch.randn(shp, device=device, generator=gen).to(tdt)
+            cd_ = torch.nn.functional.softplus(torch.randn(shp, device=device, generator=gen) * cw_.delta_sigma
+                                               + cw_.delta_mu).to(tdt)
+            cB_ = torch.randn(cw_.batch, cw_.seqlen, cw_.dstate, device=device, generator=gen).to(tdt)
+            cC_ = torch.randn(cw_.batch, cw_.seqlen, cw_.dstate, device=device, generator=gen).to(tdt)
+            cA_ = to_dev(wl.make_A(cw_.dim, cw_.dstate, cw_.a_perturbed, cfg_id=cw_.cfg_id))
+            cD_ = torch.randn(cw_.dim, device=device, generator=gen) if cw_.has_D else None
+            cz_ = torch.randn(shp, device=device, generator=gen).to(tdt) if cw_.has_z else None
+            cy_ = torch.empty_like(cu_)
+            cT, cK = ss.scan_plan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate)
+            cws = torch.empty(max(ss.scan_workspace_bytes(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate), 1),
+                              dtype=torch.uint8, device=device)
+
+            def cstep_():
+                ss.scan_fwd(cu_, cd_, cA_, cB_, cC_, D=cD_, z=cz_, out=cy_, workspace=cws)
+
+            cms = timed(cstep_)
+            cel = cw_.batch * cw_.seqlen * cw_.dim * cw_.dstate
+            cby = wl.algorithmic_bytes_scan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate, cw_.dtype, cw_.has_D,
+                                            cw_.has_z)
+            cfgs[name] = {"workload": "%s: B=%d L=%d D=%d N=%d, %s" % (cw_.note, cw_.batch, cw_.seqlen, cw_.dim,
+                                                                      cw_.dstate, cw_.dtype),
+                          "chunk_len": cT, "n_chunks": cK, "ms_per_call": cms, "elements/s": cel / (cms * 1e-3),
+                          "alg_GB/s": cby / (cms * 1e-3) / 1e9, "frac_of_8TB/s": cby / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del cu_, cd_, cB_, cC_, cz_, cy_, cws
+        result["configs"] = cfgs
 
         # the block's causal depthwise convolution + SiLU producing u (x read in place from xz)
         xz = torch.randn(w.batch, w.seqlen, 2 * w.dim, device=device,

@@ -12,9 +12,19 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kWave = 64;
-constexpr int64_t kWavesPerBlock = ssk::kScanWaves;  // a scan workgroup: 64 channels, the states split over its waves
-constexpr int64_t kMinAutoChunk = 64;   // the automatic plan never cuts finer
-constexpr int64_t kTargetWaves = 2048;  // ~2 waves per SIMD on 256 CUs x 4 SIMDs
+constexpr int64_t kMinAutoChunk = 64;  // the automatic plan never cuts finer
+// The automatic plan, in scan workgroups (64 channels of one batch row and one
+// chunk each) against the 256 CUs of an MI355X.  Cutting the sequence costs an
+// extra aggregate pass over all but the last chunk, so a shape whose one-chunk
+// launch already has kSingleChunkBlocks workgroups (about 0.8 per CU) stays
+// whole; below that the chunk length halves until the emit launch has
+// kTargetBlocks (three per CU).  Measured at L = 2048 (one chunk against the
+// best cut): 128 workgroups 180 against 125 us, 160: 196 / 157, 192: 185 / 171,
+// 240: 201 / 226, 480: 256 / 376, 640 (the large layer): 380 / 475.  The long
+// context (32 per chunk) at 8 / 16 / 32 / 64 chunks takes 2.75 / 1.89 / 1.60 /
+// 1.53 ms; the small-model layer (48) at 8 / 16 / 32 chunks 73 / 59 / 69 us.
+constexpr int64_t kSingleChunkBlocks = 208;
+constexpr int64_t kTargetBlocks = 768;
 constexpr int64_t kMaxGridYZ = 65535;
 // A chunk's (B, L, D) slab is addressed with 32-bit buffer offsets, and idle
 // lanes use offsets at and above 2^31: one chunk of rows must stay below 2^31
@@ -59,10 +69,10 @@ bool shape_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, Siz
     return true;
 }
 
-// Plan: chunk length and count.  Automatic plans start from one chunk and
-// halve the chunk length (staying a power of two, never below kMinAutoChunk)
-// until the emit launch has at least kTargetWaves waves (4 per 64 channels
-// per chunk).
+// Plan: chunk length and count.  Automatic plans start from one chunk; a
+// shape with fewer than kSingleChunkBlocks workgroups then halves the chunk
+// length (staying a power of two, never below kMinAutoChunk) until the emit
+// launch has at least kTargetBlocks workgroups.
 bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* T, int64_t* K)
 {
     if (request < 0) return false;
@@ -70,12 +80,14 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
     if (t == 0) {
         t = 1;
         while (t < seqlen) t <<= 1;
-        int64_t lane_blocks;
-        if (!mul(batch, ceil_div(dim, kWave) * kWavesPerBlock, &lane_blocks)) lane_blocks = INT64_MAX;
-        while (t > kMinAutoChunk) {
-            int64_t waves;
-            if (!mul(lane_blocks, ceil_div(seqlen, t), &waves) || waves >= kTargetWaves) break;
-            t >>= 1;
+        int64_t blocks;  // workgroups of a one-chunk launch
+        if (!mul(batch, ceil_div(dim, kWave), &blocks)) blocks = INT64_MAX;
+        if (blocks < kSingleChunkBlocks) {
+            while (t > kMinAutoChunk) {
+                int64_t launched;
+                if (!mul(blocks, ceil_div(seqlen, t), &launched) || launched >= kTargetBlocks) break;
+                t >>= 1;
+            }
         }
         int64_t bytes;
         while (t > 1 && (!mul(t, dim, &bytes) || !mul(bytes, 4, &bytes) || bytes >= kMaxChunkBytes)) t >>= 1;
