@@ -82,6 +82,19 @@ def check_workspace_size(ws, b, l, d, n, T, K):
     assert ws <= -(-front // 256) * 256 + panel_min + 4 * b * K * 2 * n * 64
 
 
+def test_auto_plan_choices(lib):
+    """The automatic plan keeps a shape whole when its one-chunk launch has at least 208
+    workgroups (64 channels of one batch row each), and otherwise cuts the sequence until
+    the emit launch has 768, in powers of two, never below 64 rows."""
+    assert plan(lib, 8, 2048, 5120, 16) == (OK, 2048, 1)       # large layer: 640 workgroups
+    assert plan(lib, 2, 2048, 1536, 16) == (OK, 128, 16)       # small-model layer: 48 -> 768
+    assert plan(lib, 1, 131072, 2048, 16) == (OK, 4096, 32)    # long context: 32 -> 1024
+    assert plan(lib, 1, 256, 64, 16) == (OK, 64, 4)            # tiny: stops at 64 rows
+    assert plan(lib, 1, 2048, 64 * 208, 16) == (OK, 2048, 1)   # 208 workgroups: whole
+    assert plan(lib, 1, 2048, 64 * 207, 16) == (OK, 512, 4)    # 207: 4 chunks give 828
+    assert plan(lib, 3, 2048, 4096, 16) == (OK, 512, 4)        # 192 -> 768 exactly
+
+
 def test_forced_plan(lib):
     assert plan(lib, 1, 256, 64, 16, 64) == (OK, 64, 4)
     assert plan(lib, 1, 1000, 64, 16, 256) == (OK, 256, 4)
