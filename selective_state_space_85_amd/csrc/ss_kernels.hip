@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
 //       slot c+1 and its delta sum.
 // Host guarantees: chunk_len * dim * element size < 2^31.
 // ---------------------------------------------------------------------------
-template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE>
+template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
 {
     constexpr bool ZOH = (MODE & kOptZoh) != 0;
@@ -311,6 +311,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
     // wave's priority at each quarter of the chunk lets the laggards catch up,
     // so the workgroups of a CU stay within a quarter of each other.
     static_assert(2 * kTileRows == kBwdSub, "checkpoints fall at the start of every tile pair");
+    // checkpoints (a separate instantiation: the plain kernel has no scalar
+    // registers to spare): this lane's entries of the one at row t0 + k*TT,
+    // advanced by one checkpoint per tile pair
+    float* ck_row = nullptr;
+    int64_t ck_step = 0;
+    if constexpr (CKPT) {
+        ck_row = a.ckpt + ((t0 / kBwdSub * a.batch + b) * N + w * kNS) * D + d;
+        ck_step = a.batch * N * D;
+    }
     const int quarter = (ntiles / 4) & ~1;
     __builtin_amdgcn_s_setprio(3);
     for (int k = 0; k < ntiles; k += 2) {
@@ -319,11 +328,13 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
             else if (k == 2 * quarter) __builtin_amdgcn_s_setprio(1);
             else if (k == 3 * quarter) __builtin_amdgcn_s_setprio(0);
         }
-        if (EMIT && a.ckpt && active && k * TT < len) {
+        if constexpr (CKPT) {
             // the state entering row t0 + k*TT, a multiple of kBwdSub (k is even)
-            float* dst = a.ckpt + (((t0 + k * TT) / kBwdSub * a.batch + b) * N + w * kNS) * D + d;
+            if (active && k * TT < len) {
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) dst[int64_t(i) * D] = h[i];
+                for (int i = 0; i < kNS; ++i) ck_row[int64_t(i) * D] = h[i];
+            }
+            ck_row += ck_step;
         }
         step(k, Slot<0>{});
         step(k + 1, Slot<1>{});
@@ -479,8 +490,11 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
             <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), dim3(kThreads), 0, s>>>(a);
         carry_kernel<<<dim3(unsigned(a.batch * a.dim)), dim3(kWave), 0, s>>>(a);
     }
-    scan_kernel<DT, true, HAS_D, HAS_Z, MODE>
-        <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), dim3(kThreads), 0, s>>>(a);
+    const dim3 grid(nblk, unsigned(a.batch), unsigned(a.n_chunks));
+    if (a.ckpt)
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, true><<<grid, dim3(kThreads), 0, s>>>(a);
+    else
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
