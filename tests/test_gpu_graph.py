@@ -166,3 +166,40 @@ def test_graph_ssd():
     g, outs = capture(lambda: call(y_g))
     y_x = torch.empty_like(y_e)
     replay_and_check(g, list(outs), [y_e, hl_e], between=lambda: call(y_x))
+
+
+def test_graph_training_step():
+    """The training pair in one graph: the forward keeping checkpoints, then the backward
+    reusing them (panel, emit with checkpoint stores, panel, adjoint, reduce)."""
+    b, l, d = 2, 160, 96
+    inp = wl.scan_inputs(b, l, d, 16, wl.BF16, has_D=True, has_z=True, has_h0=True, seed=915)
+    rng = np.random.default_rng(916)
+    dy = wl.f32_to_bf16_bits(rng.standard_normal((b, l, d)).astype(np.float32))
+    m = ss()
+    t = {k: dev(v) for k, v in inp.items()}
+    dy_t = dev(dy)
+    ck = torch.empty(m.scan_ckpt_shape(b, l, d, 16), dtype=torch.float32, device="cuda")
+    ws_f = torch.empty(m.scan_workspace_bytes(b, l, d, 16, l), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(m.scan_bwd_workspace_bytes(b, l, d, 16, with_ckpt=True), dtype=torch.uint8, device="cuda")
+    say("graph training step: B%d L%d D%d" % (b, l, d))
+
+    def step():
+        y = m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], h0=t["h0"], chunk_len=l,
+                       workspace=ws_f, ckpt=ck)
+        g = m.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], h0=t["h0"],
+                       workspace=ws_b, ckpt=ck)
+        return [y] + [g[k] for k in sorted(g)]
+
+    first = step()
+    torch.cuda.synchronize()
+    y_ref = oracle.scan(**inp)["y"]
+    assert rel_err(host64(first[0]), y_ref) <= TOL["bf16"]
+    g_ref = oracle.scan_bwd(**inp, dy=oracle.widen(dy))
+    g_names = sorted(m.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"],
+                                h0=t["h0"], workspace=ws_b, ckpt=ck))
+    for k, got in zip(g_names, first[1:]):
+        if k in g_ref:
+            assert rel_err(host64(got), g_ref[k]) <= TOL["bf16"], k
+    eager = [e.clone() for e in first]
+    graph, outs = capture(step)
+    replay_and_check(graph, outs, eager, between=step)
