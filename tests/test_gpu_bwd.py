@@ -205,3 +205,24 @@ def test_bwd_from_checkpoints_large_layer():
     torch.cuda.synchronize()
     for k in g:
         assert torch.equal(g[k], g_ck[k]), k
+
+
+def test_fwd_ckpt_zoh_states():
+    """The checkpointing forward under the zero-order-hold option keeps that recurrence's
+    states (its backward is not built: ss_scan_bwd_ckpt rejects the option)."""
+    inp, _, _ = make_case(2, 90, 80, wl.F32, has_D=True, has_z=True, has_h0=True, softplus=True, seed=77)
+    m = ss()
+    t = {k: dev(v) for k, v in inp.items()}
+    b, l, d = inp["u"].shape
+    ck = torch.full(m.scan_ckpt_shape(b, l, d, 16), float("nan"), dtype=torch.float32, device="cuda")
+    say("checkpointing forward with ZOH + softplus, B%d L%d D%d" % (b, l, d))
+    y = m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], h0=t["h0"],
+                   delta_bias=t["delta_bias"], delta_softplus=True, zoh=True, chunk_len=32, ckpt=ck)
+    torch.cuda.synchronize()
+    n_sub = -(-l // 16)
+    ref = oracle.scan(**inp, lanes=np.arange(b * d), record_t=[16 * j - 1 for j in range(1, n_sub)],
+                      delta_softplus=True, zoh=True)
+    assert rel_err(host64(y), oracle.scan(**inp, delta_softplus=True, zoh=True)["y"]) <= TOL["f32"]
+    got = host64(ck).transpose(1, 3, 0, 2).reshape(b * d, n_sub, 16)
+    assert np.array_equal(got[:, 0], inp["h0"].astype(np.float64).reshape(b * d, 16))
+    assert rel_err(got[:, 1:], ref["h_rec"]) <= TOL["f32"]
