@@ -168,36 +168,16 @@ __device__ __forceinline__ void pin_rows(float (&v)[R][C])
 constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
 constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
 
-// Sum of v over the 64 lanes of the wave, left in lane 63 (other lanes hold
-// partial sums).  Prefix sums within each row of 16 lanes, then the row totals
-// carried up by the two broadcasts; lanes a shift or a row mask leaves out
-// add 0.
+// v plus the value CTRL brings from another lane (a DPP row shift or row
+// broadcast); lanes the shift or ROW_MASK leaves out add 0.  Chained over row
+// shifts 1, 2, 4, 8 and the broadcasts of lanes 15 and 31 it forms an
+// inclusive prefix sum across the wave.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float add_from(float v)
 {
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
 }
-__device__ __forceinline__ float wave_sum_to_lane63(float v)
-{
-    v = add_from<kDppRowShr1, 0xf>(v);
-    v = add_from<kDppRowShr2, 0xf>(v);
-    v = add_from<kDppRowShr4, 0xf>(v);
-    v = add_from<kDppRowShr8, 0xf>(v);
-    v = add_from<kDppRowBcast15, 0xa>(v);
-    return add_from<kDppRowBcast31, 0xc>(v);
-}
 
-// Channel sums of 16 per-lane values at once: afterwards every lane l holds
-// the sum over the wave's 64 lanes of v[l / 4].  A butterfly that halves the
-// number of live vectors at each step, pairing vector p with vector p + m:
-//   swap of the 32-lane halves (v_permlane32_swap): vector p holds value p in
-//     lanes 0-31 and value p + 8 in lanes 32-63, each a sum over two lanes;
-//   swap of odd and even 16-lane rows (v_permlane16_swap): value p + 4*(l/16);
-//   within each row, the two 8-lane halves (row rotation by 8): value
-//     p + 2*((l/8)&1) + 4*(l/16);
-//   within each 8 lanes, the two quarters (half-row mirror): value l/4;
-//   and a sum over each quad (quad permutations 1,0,3,2 and 2,3,0,1).
-// 38 instructions for 16 sums, where one DPP tree per value costs 6 each.
 constexpr int kDppRowRor8 = 0x128, kDppRowHalfMirror = 0x141, kDppQuadSwap1 = 0xB1, kDppQuadSwap2 = 0x4E;
 
 template <int CTRL>
@@ -206,39 +186,17 @@ __device__ __forceinline__ float dpp(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float sum16_across_lanes(const float (&v)[16])
-{
-    const int lane = threadIdx.x & 63;
-    float w[8], x[4], y[2];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[p]), __float_as_uint(v[p + 8]), false, false);
-        w[p] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[p]), __float_as_uint(w[p + 4]), false, false);
-        x[p] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    }
-    const bool hi8 = (lane & 8) != 0;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const float keep = hi8 ? x[p + 2] : x[p];
-        const float give = hi8 ? x[p] : x[p + 2];
-        y[p] = keep + dpp<kDppRowRor8>(give);
-    }
-    const bool hi4 = (lane & 4) != 0;
-    float z = (hi4 ? y[1] : y[0]) + dpp<kDppRowHalfMirror>(hi4 ? y[0] : y[1]);
-    z += dpp<kDppQuadSwap1>(z);
-    return z + dpp<kDppQuadSwap2>(z);
-}
-
-// The same for 8 values: afterwards every lane l holds the sum over the
-// wave's 64 lanes of v[l / 8].  Swap of the 32-lane halves (vector p: value p
-// in lanes 0-31, p + 4 in lanes 32-63), swap of odd and even 16-lane rows
-// (value p + 2*((l/16)&1) + 4*(l/32)), the two 8-lane halves of each row
-// (row rotation by 8: value l/8), then a sum over each 8 lanes (half-row
-// mirror, quad permutations).  18 instructions for 8 sums.
+// Channel sums of 8 per-lane values at once: afterwards every lane l holds
+// the sum over the wave's 64 lanes of v[l / 8].  A butterfly that halves the
+// number of live vectors at each step, pairing vector p with vector p + m:
+//   swap of the 32-lane halves (v_permlane32_swap): vector p holds value p in
+//     lanes 0-31 and value p + 4 in lanes 32-63, each a sum over two lanes;
+//   swap of odd and even 16-lane rows (v_permlane16_swap): value
+//     p + 2*((l/16)&1) + 4*(l/32);
+//   within each row, the two 8-lane halves (row rotation by 8): value l/8;
+//   then a sum over each 8 lanes (half-row mirror, quad permutations 1,0,3,2
+//   and 2,3,0,1).
+// 18 instructions for 8 sums, where one DPP tree per value costs 6 each.
 __device__ __forceinline__ float sum8_across_lanes(const float (&v)[8])
 {
     const int lane = threadIdx.x & 63;
