@@ -111,7 +111,7 @@ def alu_cobound(w, ms_step):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the scan would shard over batch and channels with no exchange). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
