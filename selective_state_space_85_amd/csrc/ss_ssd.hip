@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
     __shared__ __align__(16) uint16_t sS[2][kP][kBP];  // state^T (p, n) hi/lo
     __shared__ __align__(16) float s_cs[kQ];           // cs_t * log2 e
     __shared__ __align__(16) float s_lc[kQ];           // cs_s * log2 e - log2(dt_s)  (+inf where dt_s = 0)
-    __shared__ float s_w[kQ];
+    __shared__ __align__(16) float s_w[kQ];
     __shared__ float s_end;  // exp(cs_end)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -308,52 +308,56 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 __builtin_amdgcn_raw_buffer_store_b64(o, rY, yrow + p0 * 2, 0, 0);
             }
         }
-        __syncthreads();  // M is consumed; its space takes w*x
-
-        // ---- D: w*x (s, p) in two bf16 parts ----
-#pragma unroll
-        for (int i = 0; i < kVX; ++i) {
-            const int v = tid + kSsdThreads * i, s = v / (kP / 8), p8 = (v % (kP / 8)) * 8;
-            const u32x4 xr = *reinterpret_cast<const u32x4*>(&sX[s][p8]);
-            const float ws = s_w[s];
-            float first[4], second[4];  // w*x of elements 0..3 and 4..7
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                first[2 * k] = ws * bf(xr[k]);
-                first[2 * k + 1] = ws * bf_hi(xr[k]);
-                second[2 * k] = ws * bf(xr[k + 2]);
-                second[2 * k + 1] = ws * bf_hi(xr[k + 2]);
-            }
-            u32x2 h0, l0, h1, l1;
-            split4(first, h0, l0);
-            split4(second, h1, l1);
-            *reinterpret_cast<u32x4*>(&sU[0][s][p8]) = u32x4{h0[0], h0[1], h1[0], h1[1]};
-            *reinterpret_cast<u32x4*>(&sU[1][s][p8]) = u32x4{l0[0], l0[1], l1[0], l1[1]};
-        }
-        __syncthreads();
-
         // ---- E: S = exp(cs_end) S + B^T (w x); new LDS copy of S^T ----
+        // No barrier since phase C: this phase reads x, B and w (staged before
+        // the first barrier) and writes the state copy, which C does not read.
         const float decay = s_end;
         // a wave's state blocks share their p block, so the w*x operands of a
         // step serve all of them
         const int spb = (w * kSPW) / kNB;
         static_assert(kNB % kSPW == 0, "a wave's state blocks lie in one p block");
+        // the lo parts accumulate in chains of their own, added once at the end,
+        // so that each block's MFMAs form two independent chains
+        f32x16 acc_lo[kSPW];
 #pragma unroll
         for (int j = 0; j < kSPW; ++j) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc_s[j][r] *= decay;
+            for (int r = 0; r < 16; ++r) {
+                acc_s[j][r] *= decay;
+                acc_lo[j][r] = 0.0f;
+            }
         }
 #pragma unroll
         for (int ks = 0; ks < kQ / 16; ++ks) {
-            const bf16x8 xh = lds_col8(&sU[0][16 * ks][32 * spb], kXP, lane);
-            const bf16x8 xl = lds_col8(&sU[1][16 * ks][32 * spb], kXP, lane);
+            // the w*x operand, formed in registers: rows s = 16ks + 8(l/32) + i
+            // of x (a transpose read) times w_s, in two bf16 parts
+            bf16x8 xh, xl;
+            {
+                const bf16x8 xv = lds_col8(&sX[16 * ks][32 * spb], kXP, lane);
+                const float4 w0 = *reinterpret_cast<const float4*>(&s_w[16 * ks + 8 * hl]);
+                const float4 w1 = *reinterpret_cast<const float4*>(&s_w[16 * ks + 8 * hl + 4]);
+                const float first[4] = {w0.x * float(xv[0]), w0.y * float(xv[1]), w0.z * float(xv[2]),
+                                        w0.w * float(xv[3])};
+                const float second[4] = {w1.x * float(xv[4]), w1.y * float(xv[5]), w1.z * float(xv[6]),
+                                         w1.w * float(xv[7])};
+                u32x2 h0, l0, h1, l1;
+                split4(first, h0, l0);
+                split4(second, h1, l1);
+                xh = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
+                xl = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
+            }
 #pragma unroll
             for (int j = 0; j < kSPW; ++j) {
                 const int nb = (w * kSPW + j) % kNB;
                 const bf16x8 bt = lds_col8(&sB[16 * ks][32 * nb], kBP, lane);
                 acc_s[j] = mfma(bt, xh, acc_s[j]);
-                acc_s[j] = mfma(bt, xl, acc_s[j]);
+                acc_lo[j] = mfma(bt, xl, acc_lo[j]);
             }
+        }
+#pragma unroll
+        for (int j = 0; j < kSPW; ++j) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_s[j][r] += acc_lo[j][r];
         }
 #pragma unroll
         for (int j = 0; j < kSPW; ++j) {
