@@ -25,8 +25,9 @@
 // 16-byte stores: x and B as they arrive, M and the state copy straight from
 // the accumulator layout.  An MFMA operand is 8 consecutive values along the
 // contraction index: where that index runs along a row it is one 16-byte
-// read, where it runs down a column (x and w*x over s, B over s) it comes
-// from two LDS transpose reads.  Y is formed transposed (p x t), so each lane
+// read, where it runs down a column (x over s, B over s) it comes
+// from two LDS transpose reads; the state update's w*x operand is such a read
+// of x scaled by w in registers.  Y is formed transposed (p x t), so each lane
 // ends up with 4 consecutive channels of one row and stores them as 8 bytes.
 // C goes from memory straight into registers in the operand layout.  The next
 // chunk's x, B, C and dt are loaded into registers while the current chunk
@@ -49,7 +50,7 @@ constexpr int kQ = 64;            // rows per chunk
 constexpr int kP = 64;            // channels per head
 constexpr int kSsdThreads = 256;  // 4 waves
 constexpr int kPad = 8;           // bf16 padding per LDS row (keeps 16-byte alignment)
-constexpr int kXP = kP + kPad;    // row pitch of x, M and w*x in LDS
+constexpr int kXP = kP + kPad;    // row pitch of x and M in LDS
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c)
 {
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
     __shared__ __align__(16) uint16_t sB[kQ][kBP];     // B chunk (s, n)
     __shared__ __align__(16) uint16_t sX[kQ][kXP];     // x chunk (s, p)
-    __shared__ __align__(16) uint16_t sU[2][kQ][kXP];  // M (t, s) hi/lo, then w*x (s, p) hi/lo
+    __shared__ __align__(16) uint16_t sU[2][kQ][kXP];  // M (t, s) hi/lo
     __shared__ __align__(16) uint16_t sS[2][kP][kBP];  // state^T (p, n) hi/lo
     __shared__ __align__(16) float s_cs[kQ];           // cs_t * log2 e
     __shared__ __align__(16) float s_lc[kQ];           // cs_s * log2 e - log2(dt_s)  (+inf where dt_s = 0)
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 *reinterpret_cast<u32x2*>(&sS[1][p][32 * nb + 8 * q + 4 * hl]) = lo;
             }
         }
-        __syncthreads();  // B and w*x consumed; the new state copy is complete
+        __syncthreads();  // x and B consumed; the new state copy is complete
     }
 
     if (a.h_last) {
