@@ -200,10 +200,10 @@ def step(h: np.ndarray, u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.n
 def scan_bwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
              D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
              h0: Optional[np.ndarray] = None, *, dy: np.ndarray, dh_last: Optional[np.ndarray] = None,
-             delta_bias: Optional[np.ndarray] = None, delta_softplus: bool = False, threads: int = 1,
-             _lib=None) -> Dict[str, np.ndarray]:
+             delta_bias: Optional[np.ndarray] = None, delta_softplus: bool = False, zoh: bool = False,
+             threads: int = 1, _lib=None) -> Dict[str, np.ndarray]:
     """fp64 gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input of
-    ``scan`` (same argument conventions; dy (B,L,D) and dh_last (B,D,N) any float).
+    ``scan`` (same argument conventions and options; dy (B,L,D) and dh_last (B,D,N) any float).
 
     Returns float64 ``du``, ``ddelta``, ``dz`` (B,L,D); ``dA`` (D,N); ``dB``, ``dC`` (B,L,N);
     ``dD``, ``ddelta_bias`` (D,); ``dh0`` (B,D,N).  Gradients of absent inputs are absent
@@ -235,7 +235,7 @@ def scan_bwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: 
     out["ddelta_bias"] = np.zeros(dim)
     out["dh0"] = np.zeros((batch, dim, dstate))
     rc = lib.oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                             _ptr(bias), _flags(delta_softplus, False), dt, batch, seqlen, dim, dstate,
+                             _ptr(bias), _flags(delta_softplus, zoh), dt, batch, seqlen, dim, dstate,
                              _ptr(dy), _ptr(dhl), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]),
                              _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
                              _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), int(threads))

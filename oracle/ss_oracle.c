@@ -266,16 +266,16 @@ int oracle_step(double* h, const void* u, const void* delta, const float* A, con
  *     gate:   dz_t = dy_t * ypre_t * silu'(z_t);  dy_t <- dy_t * silu(z_t)
  *     skip:   du_t += dy_t * D[d];  dD[d] += dy_t * u_t
  *     output: dC[b,t,n] += dy_t * h_t[n];  g[n] += dy_t * C[b,t,n]
- *     update h_t[n] = e[n] h_{t-1}[n] + delta_t B[b,t,n] u_t,  e[n] = exp(delta_t A[d,n]):
- *             ddelta_t += g[n] (A[d,n] e[n] h_{t-1}[n] + B[b,t,n] u_t)
- *             dA[d,n]  += g[n] delta_t e[n] h_{t-1}[n]
- *             dB[b,t,n] += g[n] delta_t u_t;  du_t += g[n] delta_t B[b,t,n]
+ *     update h_t[n] = e[n] h_{t-1}[n] + beta[n] B[b,t,n] u_t,  e[n] = exp(delta_t A[d,n]),
+ *             beta[n] the input coefficient (see input_coef):
+ *             ddelta_t += g[n] (A[d,n] e[n] h_{t-1}[n] + dbeta/ddelta B[b,t,n] u_t)
+ *             dA[d,n]  += g[n] (delta_t e[n] h_{t-1}[n] + dbeta/dA B[b,t,n] u_t)
+ *             dB[b,t,n] += g[n] beta[n] u_t;  du_t += g[n] beta[n] B[b,t,n]
  *             g[n] <- g[n] e[n]
  *     step size: with softplus, d(raw)_t = ddelta_t * sigmoid(raw_t + bias[d]);
  *             dbias[d] += d(raw)_t (a bias enters with derivative 1)
  *   dh0 = g.
- * silu'(z) = s (1 + z (1 - s)), s = sigmoid(z).  The zero-order-hold option is
- * not covered (returns -1).
+ * silu'(z) = s (1 + z (1 - s)), s = sigmoid(z).
  *
  * dA, dD, dbias sum over batch rows and dB, dC over channels.  The lanes are
  * cut into at most 64 fixed blocks, each block adds its lanes' terms in lane
@@ -295,6 +295,45 @@ typedef struct {
 } bwd_job;
 
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/*
+ * The input coefficient beta, Bbar = beta * B, and its partial derivatives,
+ * for step size delta and A[d,n] = a (the discretisations of the
+ * walk-through's section 2.2):
+ *  - Euler: beta = delta; dbeta/ddelta = 1, dbeta/da = 0.
+ *  - zero-order hold: beta = (e^x - 1) / a = delta phi(x), x = delta a,
+ *    phi(x) = (e^x - 1) / x (1 at x = 0).  Then dbeta/ddelta = e^x (also at
+ *    a = 0, where beta = delta), and dbeta/da = delta^2 psi(x) with
+ *    psi(x) = phi'(x) = (x e^x - e^x + 1) / x^2, psi(0) = 1/2.  Near 0 the
+ *    closed form cancels, so psi comes from its Taylor series
+ *    sum_k (k + 1) x^k / (k + 2)! (the series of e^x, shifted twice).
+ */
+static void input_coef(double delta, double a, int flags, double* beta, double* dbeta_ddelta, double* dbeta_da)
+{
+    if (!(flags & ORACLE_ZOH)) {
+        *beta = delta;
+        *dbeta_ddelta = 1.0;
+        *dbeta_da = 0.0;
+        return;
+    }
+    const double x = delta * a;
+    const double phi = x == 0.0 ? 1.0 : expm1(x) / x;
+    double psi;
+    if (fabs(x) < 0.01) {
+        double xk = 1.0, fact = 2.0; /* x^k and (k + 2)! */
+        psi = 0.0;
+        for (int k = 0; k < 10; ++k) {
+            psi += (double)(k + 1) * xk / fact;
+            xk *= x;
+            fact *= (double)(k + 3);
+        }
+    } else {
+        psi = (x * exp(x) - expm1(x)) / (x * x);
+    }
+    *beta = phi * delta;
+    *dbeta_ddelta = exp(x);
+    *dbeta_da = delta * delta * psi;
+}
 
 static void bwd_lane(const bwd_job* j, int64_t bd, double* hs, double* acc)
 {
@@ -354,10 +393,12 @@ static void bwd_lane(const bwd_job* j, int64_t bd, double* hs, double* acc)
             const double a = (double)f->A[d * N + n];
             const double bm = widen(f->B, srow + n, f->dtype);
             const double e = exp(delta * a);
-            dd += g[n] * (a * e * hprev[n] + bm * x);
-            dA[d * N + n] += g[n] * delta * e * hprev[n];
-            dB[srow + n] += g[n] * delta * x;
-            du += g[n] * delta * bm;
+            double beta, dbeta_dd, dbeta_da;
+            input_coef(delta, a, f->flags, &beta, &dbeta_dd, &dbeta_da);
+            dd += g[n] * (a * e * hprev[n] + dbeta_dd * bm * x);
+            dA[d * N + n] += g[n] * (delta * e * hprev[n] + dbeta_da * bm * x);
+            dB[srow + n] += g[n] * beta * x;
+            du += g[n] * beta * bm;
             g[n] *= e;
         }
         if (f->flags & ORACLE_SOFTPLUS) {
@@ -403,7 +444,7 @@ static void* bwd_worker(void* arg)
  * dD (D) -- zeros without D; dbias (D) -- zeros without a bias; dh0 (B,D,N).
  * ddelta is the gradient with respect to the delta argument as passed (the
  * raw value when ORACLE_SOFTPLUS is set).  Returns 0, or -1 on a bad argument,
- * an unsupported option (ORACLE_ZOH) or a failed allocation.
+ * an unknown option or a failed allocation.
  */
 int oracle_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                     const float* Dskip, const void* z, const double* h0,
@@ -417,7 +458,7 @@ int oracle_scan_bwd(const void* u, const void* delta, const float* A, const void
     if (!du || !ddelta || !dz || !dA || !dB || !dC || !dD || !dbias || !dh0) return -1;
     if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > ORACLE_MAX_N) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
-    if (flags & ~ORACLE_SOFTPLUS) return -1;
+    if (flags & ~(ORACLE_SOFTPLUS | ORACLE_ZOH)) return -1;
     const int64_t BD = batch * dim, L = seqlen, N = dstate, D = dim;
 
     scan_job f = {u, delta, A, B, C, Dskip, z, h0, delta_bias, flags, dtype, batch, seqlen, dim, dstate,

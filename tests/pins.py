@@ -472,7 +472,7 @@ def pin_softplus_bias(orc):
 # 15. backward: every gradient element against torch's fp64 autograd of a torch
 #     statement of the forward (library reverse mode, no hand-derived adjoint)
 # ---------------------------------------------------------------------------
-def _torch_forward(c, softplus):
+def _torch_forward(c, softplus, zoh=False):
     import torch
 
     f64 = lambda a: None if a is None else torch.tensor(_f64(a), dtype=torch.float64, requires_grad=True)  # noqa: E731
@@ -488,8 +488,11 @@ def _torch_forward(c, softplus):
     h = t["h0"]
     ys = []
     for s_ in range(nl):
-        h = torch.exp(dl[:, s_, :, None] * t["A"][None]) * h + \
-            (dl[:, s_, :, None] * t["B"][:, s_, None, :]) * t["u"][:, s_, :, None]
+        da = dl[:, s_, :, None] * t["A"][None]
+        bbar = dl[:, s_, :, None] * t["B"][:, s_, None, :]
+        if zoh:  # (delta A)^-1 (exp(delta A) - 1) delta B; the cases keep delta A away from 0
+            bbar = torch.expm1(da) / da * bbar
+        h = torch.exp(da) * h + bbar * t["u"][:, s_, :, None]
         ys.append((h * t["C"][:, s_, None, :]).sum(-1))
     y = torch.stack(ys, 1)
     if t["D"] is not None:
@@ -503,19 +506,25 @@ def pin_bwd_autograd(orc):
     import torch
 
     rng = np.random.default_rng(26)
-    cases = [((2, 11, 5, 8), dict(dtype="f32", has_D=True, has_z=True, has_h0=True), False, True),
-             ((1, 17, 3, 16), dict(dtype="bf16", has_D=True, has_z=False, has_h0=False), True, False),
-             ((3, 6, 4, 4), dict(dtype="f32", has_D=False, has_z=True, has_h0=True), True, True)]
-    for shp, kw, softplus, with_dh in cases:
+    cases = [((2, 11, 5, 8), dict(dtype="f32", has_D=True, has_z=True, has_h0=True), False, True, False),
+             ((1, 17, 3, 16), dict(dtype="bf16", has_D=True, has_z=False, has_h0=False), True, False, False),
+             ((3, 6, 4, 4), dict(dtype="f32", has_D=False, has_z=True, has_h0=True), True, True, False),
+             # zero-order hold: step sizes from 1e-5 to 3, so that delta*A falls on both sides of
+             # the oracle's switch from the series of psi to its closed form
+             ((2, 13, 4, 8), dict(dtype="f32", has_D=True, has_z=True, has_h0=True), False, True, True),
+             ((1, 9, 3, 4), dict(dtype="f32", has_D=False, has_z=False, has_h0=True), True, False, True)]
+    for shp, kw, softplus, with_dh, zoh in cases:
         c = _rand_case(rng, *shp, **kw)
+        if zoh and not softplus:
+            c["delta"] = np.exp(rng.uniform(np.log(1e-5), np.log(3.0), c["u"].shape)).astype(np.float32)
         if softplus:
             raw = rng.normal(-1.0, 1.0, c["u"].shape).astype(np.float32)
             c["delta"] = f32_to_bf16_bits(raw) if c["u"].dtype == np.uint16 else raw
             c["delta_bias"] = rng.normal(0.0, 0.7, shp[2]).astype(np.float32)
         dy = rng.standard_normal(shp[:3])
         dhl = rng.standard_normal((shp[0], shp[2], shp[3])) if with_dh else None
-        got = orc.scan_bwd(**c, dy=dy, dh_last=dhl, delta_softplus=softplus)
-        t, y, h = _torch_forward(c, softplus)
+        got = orc.scan_bwd(**c, dy=dy, dh_last=dhl, delta_softplus=softplus, zoh=zoh)
+        t, y, h = _torch_forward(c, softplus, zoh)
         loss = (y * torch.tensor(dy)).sum()
         if with_dh:
             loss = loss + (h * torch.tensor(dhl)).sum()
@@ -526,42 +535,56 @@ def pin_bwd_autograd(orc):
             if t[ik] is None:
                 assert gk not in got, "%s present without %s" % (gk, ik)
                 continue
-            _close(got[gk], t[ik].grad.numpy(), 1e-11, "autograd %s %s" % (gk, shp))
+            _close(got[gk], t[ik].grad.numpy(), 1e-11, "autograd %s %s zoh=%s" % (gk, shp, zoh))
 
 
 # ---------------------------------------------------------------------------
 # 16. backward: directional derivatives against fp64 central differences of
-#     the NumPy twin's forward (one random direction per input)
+#     the NumPy twin's forward (one random direction per input), Euler and
+#     zero-order hold
 # ---------------------------------------------------------------------------
 def pin_bwd_finite_differences(orc):
     from oracle.twin import twin_scan
 
     rng = np.random.default_rng(27)
-    c = _rand_case(rng, 2, 9, 3, 4, dtype="f32", has_D=True, has_z=True, has_h0=True)
-    raw = rng.normal(-0.5, 1.0, c["u"].shape).astype(np.float32)
-    c["delta"] = raw
-    c["delta_bias"] = rng.normal(0.0, 0.5, 3).astype(np.float32)
-    dy = rng.standard_normal((2, 9, 3))
-    dhl = rng.standard_normal((2, 3, 4))
-    grads = orc.scan_bwd(**c, dy=dy, dh_last=dhl, delta_softplus=True)
+    for zoh in (False, True):
+        c = _rand_case(rng, 2, 9, 3, 4, dtype="f32", has_D=True, has_z=True, has_h0=True)
+        raw = rng.normal(-0.5, 1.0, c["u"].shape).astype(np.float32)
+        if zoh:  # some step sizes near 0 (the series side of psi) and a channel with A = 0
+            raw[:, ::3, :] = -12.0
+            c["A"][1, :] = 0.0
+        c["delta"] = raw
+        c["delta_bias"] = rng.normal(0.0, 0.5, 3).astype(np.float32)
+        dy = rng.standard_normal((2, 9, 3))
+        dhl = rng.standard_normal((2, 3, 4))
+        grads = orc.scan_bwd(**c, dy=dy, dh_last=dhl, delta_softplus=True, zoh=zoh)
 
-    base = {k: (None if v is None else _f64(v)) for k, v in c.items()}
+        base = {k: (None if v is None else _f64(v)) for k, v in c.items()}
 
-    def loss(inp):
-        y, h = twin_scan(**inp, delta_softplus=True)
-        return float(np.sum(y * dy) + np.sum(h * dhl))
+        def loss(inp):
+            y, h = twin_scan(**inp, delta_softplus=True, zoh=zoh)
+            return float(np.sum(y * dy) + np.sum(h * dhl))
 
-    eps = 1e-6
-    for gk, ik in (("du", "u"), ("ddelta", "delta"), ("dA", "A"), ("dB", "B"), ("dC", "C"), ("dD", "D"),
-                   ("dz", "z"), ("dh0", "h0"), ("ddelta_bias", "delta_bias")):
-        v = rng.standard_normal(base[ik].shape)
-        plus = dict(base)
-        minus = dict(base)
-        plus[ik] = base[ik] + eps * v
-        minus[ik] = base[ik] - eps * v
-        fd = (loss(plus) - loss(minus)) / (2 * eps)
-        an = float(np.sum(grads[gk] * v))
-        assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), "finite differences %s: %.9g vs %.9g" % (gk, an, fd)
+        eps = 1e-6
+        for gk, ik in (("du", "u"), ("ddelta", "delta"), ("dA", "A"), ("dB", "B"), ("dC", "C"), ("dD", "D"),
+                       ("dz", "z"), ("dh0", "h0"), ("ddelta_bias", "delta_bias")):
+            v = rng.standard_normal(base[ik].shape)
+            plus = dict(base)
+            minus = dict(base)
+            plus[ik] = base[ik] + eps * v
+            minus[ik] = base[ik] - eps * v
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = float(np.sum(grads[gk] * v))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
+                "finite differences %s zoh=%s: %.9g vs %.9g" % (gk, zoh, an, fd)
+        if zoh:  # the A = 0 channel's dA alone, where the closed form of dBbar/dA is 0/0
+            v = np.zeros_like(base["A"])
+            v[1, :] = rng.standard_normal(4)
+            plus, minus = dict(base), dict(base)
+            plus["A"], minus["A"] = base["A"] + eps * v, base["A"] - eps * v
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = float(np.sum(grads["dA"] * v))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), "finite differences dA at A = 0: %.9g vs %.9g" % (an, fd)
 
 
 # ---------------------------------------------------------------------------

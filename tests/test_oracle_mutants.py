@@ -52,11 +52,21 @@ MUTANTS = [
     ("softplus always on", "return (flags & ORACLE_SOFTPLUS) ? softplus(v) : v;", "return softplus(v);"),
     # the backward
     ("adjoint not decayed", "            g[n] *= e;\n", "            (void)e;\n"),
-    ("dA without the decay factor", "dA[d * N + n] += g[n] * delta * e * hprev[n];",
-     "dA[d * N + n] += g[n] * delta * hprev[n];"),
+    ("dA without the decay factor", "dA[d * N + n] += g[n] * (delta * e * hprev[n]",
+     "dA[d * N + n] += g[n] * (delta * hprev[n]"),
     ("dC from the previous state", "dC[srow + n] += dyt * hcur[n];", "dC[srow + n] += dyt * hprev[n];"),
-    ("dB without u", "dB[srow + n] += g[n] * delta * x;", "dB[srow + n] += g[n] * delta;"),
-    ("ddelta misses the decay path", "dd += g[n] * (a * e * hprev[n] + bm * x);", "dd += g[n] * (bm * x);"),
+    ("dB without u", "dB[srow + n] += g[n] * beta * x;", "dB[srow + n] += g[n] * beta;"),
+    ("ddelta misses the decay path", "dd += g[n] * (a * e * hprev[n] + dbeta_dd * bm * x);",
+     "dd += g[n] * (dbeta_dd * bm * x);"),
+    # the backward of the zero-order hold
+    ("ZOH: dBbar/ddelta taken as 1", "*dbeta_ddelta = exp(x);", "*dbeta_ddelta = 1.0;"),
+    ("ZOH: dBbar/dA dropped", "*dbeta_da = delta * delta * psi;", "*dbeta_da = 0.0;"),
+    ("ZOH: dBbar/dA with one delta", "*dbeta_da = delta * delta * psi;", "*dbeta_da = delta * psi;"),
+    ("ZOH: psi series without (k + 1)", "psi += (double)(k + 1) * xk / fact;", "psi += xk / fact;"),
+    ("ZOH: psi closed form sign", "psi = (x * exp(x) - expm1(x)) / (x * x);",
+     "psi = (x * exp(x) + expm1(x)) / (x * x);"),
+    ("ZOH: dB with the Euler coefficient", "dB[srow + n] += g[n] * beta * x;", "dB[srow + n] += g[n] * delta * x;"),
+    ("ZOH: du with the Euler coefficient", "du += g[n] * beta * bm;", "du += g[n] * delta * bm;"),
     ("silu derivative wrong", "s * (1.0 + zz * (1.0 - s))", "s * (1.0 + zz * s)"),
     ("skip uses the ungated gradient", "dD[d] += dyt * x;", "dD[d] += j->dy[row] * x;"),
     ("softplus derivative dropped", "            dd *= sigmoid(v);\n", "            (void)v;\n"),
