@@ -324,6 +324,17 @@ def main():
             return e0.elapsed_time(e1) / reps
 
         fk_ms, bk_ms = timed(fkstep), timed(bkstep)
+
+        # the same training pair under the zero-order-hold input term
+        def fzstep():
+            ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=yk, workspace=ws,
+                        ckpt=ck, zoh=True)
+
+        def bzstep():
+            ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=cws, ckpt=ck,
+                        zoh=True)
+
+        fz_ms, bz_ms = timed(fzstep), timed(bzstep)
         result["backward"] = {"ms_per_step": bms, "elements/s": elements / (bms * 1e-3),
                               "vs_forward": bms / ms_step, "note": "panel + checkpoint pass + adjoint + reduce",
                               "training": {"fwd_ckpt_ms": fk_ms, "bwd_from_ckpt_ms": bk_ms,
@@ -331,7 +342,9 @@ def main():
                                            "fwd_plus_standalone_bwd_ms": ms_step + bms,
                                            "ckpt_bytes": ck.numel() * 4,
                                            "note": "ss_scan_fwd_ckpt keeps the state every 16 rows; "
-                                                   "ss_scan_bwd_ckpt skips the checkpoint pass"}}
+                                                   "ss_scan_bwd_ckpt skips the checkpoint pass"},
+                              "training_zoh": {"fwd_ckpt_ms": fz_ms, "bwd_from_ckpt_ms": bz_ms,
+                                               "fwd_plus_bwd_ms": fz_ms + bz_ms}}
         del ck, cws, yk
 
         # the other scan configurations at their own shapes: the small-model layer and the

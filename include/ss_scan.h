@@ -230,8 +230,10 @@ size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, i
  *     sum(dy * out) + sum(dh_last * h_last)
  * with respect to every input:
  *
- *   forward inputs : as ss_scan_fwd_ex (options: SS_DELTA_SOFTPLUS only;
- *                    SS_B_ZOH returns SS_ERR_UNSUPPORTED)
+ *   forward inputs : as ss_scan_fwd_ex, options included (SS_DELTA_SOFTPLUS,
+ *                    SS_B_ZOH: the input coefficient beta = (e^{delta A} - 1)/A
+ *                    has dbeta/ddelta = e^{delta A} and dbeta/dA =
+ *                    delta^2 psi(delta A), psi(x) = (x e^x - e^x + 1)/x^2)
  *   dy          : (batch, seqlen, dim)   dtype   gradient of out
  *   dh_last     : (batch, dim, dstate)   fp32    gradient of h_last (NULL: zero)
  *   du, ddelta  : (batch, seqlen, dim)   dtype   output; ddelta is with respect

@@ -480,7 +480,7 @@ ss_status scan_bwd_impl(const void* u, const void* delta, const float* A, const 
     if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
     if (dstate != ssk::kDState) return SS_ERR_UNSUPPORTED;
-    if (options & ~ssk::kOptSoftplus) return SS_ERR_UNSUPPORTED;  // no zero-order hold in the backward
+    if (options & ~ssk::kOptAll) return SS_ERR_UNSUPPORTED;
     if (batch > kMaxGridYZ || batch * dim > INT32_MAX) return SS_ERR_UNSUPPORTED;
     BwdLayout wl;
     if (!bwd_layout(batch, seqlen, dim, dstate, &wl, ckpt == nullptr)) return SS_ERR_INVALID_ARG;

@@ -14,6 +14,10 @@
 //   g *= e_t
 // plus du_t += D dy'_t, dD += dy'_t u_t, dz_t = dy_t ypre_t silu'(z_t), the
 // softplus derivative sigmoid(raw + bias) on ddelta, dbias += ddelta, dh0 = g.
+// Under the zero-order hold (walk-through, section 2.2) the input term is
+// beta B_t u_t with beta = delta_t phi(delta_t A), so delta_t becomes beta in
+// dB and du, B_t u_t in ddelta is weighted by dbeta/ddelta = e_t, and dA gains
+// g B_t u_t dbeta/dA (zoh_dbeta_dA_over_delta).
 //
 // Three launches after the B/C panel:
 //  1. prep_kernel runs the recurrence once and stores the state every kBwdSub
@@ -125,18 +129,22 @@ struct Rows {
 template <int DT, int MODE>
 __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
 {
+    constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using V = Buf<DT>;
     __shared__ float2 s_row[2][kSub][kWave];  // (delta, delta*u), by sub-block parity
+    __shared__ float s_iv[ZOH ? 2 : 1][kSub][kWave];  // 1/delta (zero-order hold)
 
     const Lane<DT> ln(a);
     const int lane = ln.lane, w = ln.w;
     const int64_t D = a.dim, L = a.seqlen, NB = a.batch;
     const auto r_u = ln.rsrc(a.u, a), r_dl = ln.rsrc(a.delta, a);
 
-    float A2[kNS], h[kNS];
+    float A2[kNS], iA[kNS], h[kNS];
 #pragma unroll
     for (int i = 0; i < kNS; ++i) {
-        A2[i] = a.A[ln.d * N + w * kNS + i] * kLog2e;
+        const float av = a.A[ln.d * N + w * kNS + i];
+        A2[i] = av * kLog2e;
+        iA[i] = ZOH ? 1.0f / av : 0.0f;
         h[i] = (a.h0 && ln.active) ? a.h0[(ln.b * D + ln.d) * N + w * kNS + i] : 0.0f;
     }
     const float bias = a.delta_bias ? a.delta_bias[ln.d] : 0.0f;
@@ -165,6 +173,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
             const bool in = ln.active && int64_t(j) * kSub + r < L;
             const float dl = in ? step_size<MODE>(V::widen(rdl[k]), bias) : 0.0f;
             s_row[par][r][lane] = make_float2(dl, dl * V::widen(rx[k]));
+            if constexpr (ZOH) s_iv[par][r][lane] = __builtin_amdgcn_rcpf(dl);
         }
         if (j + 1 < int(a.n_sub)) issue(j + 1);
         // one barrier per sub-block: the next one writes the other parity
@@ -175,8 +184,14 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
 #pragma unroll
             for (int rr = 0; rr < kHalf; ++rr) {
                 const float2 rv = s_row[par][half * kHalf + rr][lane];
+                const float iv = ZOH ? s_iv[ZOH ? par : 0][half * kHalf + rr][lane] : 0.0f;
 #pragma unroll
-                for (int i = 0; i < kNS; ++i) h[i] = fmaf(exp2_hw(rv.x * A2[i]), h[i], rv.y * word(bw, rr, i));
+                for (int i = 0; i < kNS; ++i) {
+                    const float x2 = rv.x * A2[i], e = exp2_hw(x2);
+                    float in_term = rv.y * word(bw, rr, i);
+                    if constexpr (ZOH) in_term *= zoh_phi(x2, e, iA[i] * iv);
+                    h[i] = fmaf(e, h[i], in_term);
+                }
             }
         }
     }
@@ -194,12 +209,16 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
 // dbias terms.
 // ---------------------------------------------------------------------------
 template <int DT, bool HAS_D, bool HAS_Z, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void bwd_kernel(BwdArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE & kOptZoh) ? 2 : 4))) void bwd_kernel(
+    BwdArgs a)
 {
+    constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using V = Buf<DT>;
-    __shared__ float4 s_row[kSub][kWave];        // (delta, delta*u, dy', 0)
-    __shared__ float2 s_par[kGroups][kHalf][kWave];  // per wave (sum g.B, sum g.h.e.A) of one half
+    __shared__ float4 s_row[kSub][kWave];        // (delta, delta*u, dy', 1/delta under the zero-order hold)
+    // per wave (sum g.B, sum g.h.e.A) of one half; under the zero-order hold (sum g.phi.B, ...)
+    __shared__ float2 s_par[kGroups][kHalf][kWave];
     __shared__ float s_yp[HAS_Z ? kGroups : 1][kHalf][kWave];  // per wave C.h_t of one half (for dz)
+    __shared__ float s_ge[ZOH ? kGroups : 1][kHalf][kWave];    // per wave sum g.e.B (zero-order hold)
 
     const Lane<DT> ln(a);
     const int lane = ln.lane, w = ln.w;
@@ -209,11 +228,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const auto r_du = ln.rsrc(a.du, a), r_ddl = ln.rsrc(a.ddelta, a);
     const auto r_dz = ln.rsrc(HAS_Z ? a.dz : a.du, a);
 
-    float A2[kNS], Av[kNS], g[kNS], dA_acc[kNS];
+    float A2[kNS], Av[kNS], iA[kNS], g[kNS], dA_acc[kNS];
 #pragma unroll
     for (int i = 0; i < kNS; ++i) {
         Av[i] = a.A[ln.d * N + w * kNS + i];
         A2[i] = Av[i] * kLog2e;
+        iA[i] = ZOH ? 1.0f / Av[i] : 0.0f;
         g[i] = (a.dh_last && ln.active) ? a.dh_last[(ln.b * D + ln.d) * N + w * kNS + i] : 0.0f;
         dA_acc[i] = 0.0f;
     }
@@ -240,7 +260,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const float dyv = in ? V::widen(rows.dy[k]) : 0.0f;
             const float zv = HAS_Z ? V::widen(rows.z[k]) : 0.0f;
             const float dyp = HAS_Z ? dyv * silu(zv) : dyv;
-            s_row[r][lane] = make_float4(dl, dl * x, dyp, 0.0f);
+            s_row[r][lane] = make_float4(dl, dl * x, dyp, ZOH ? __builtin_amdgcn_rcpf(dl) : 0.0f);
             xf[k] = x;
             dlf[k] = dl;
             sgf[k] = (MODE & kOptSoftplus) ? sigmoid(v) : 1.0f;
@@ -263,8 +283,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const int r = half * kHalf + rr;
                 const float4 rv = s_row[r][lane];
 #pragma unroll
-                for (int i = 0; i < kNS; ++i)
-                    hh[r][i] = fmaf(exp2_hw(rv.x * A2[i]), r ? hh[r - 1][i] : hprev[i], rv.y * word(bw, rr, i));
+                for (int i = 0; i < kNS; ++i) {
+                    const float x2 = rv.x * A2[i], e = exp2_hw(x2);
+                    float in_term = rv.y * word(bw, rr, i);
+                    if constexpr (ZOH) in_term *= zoh_phi(x2, e, iA[i] * rv.w);
+                    hh[r][i] = fmaf(e, r ? hh[r - 1][i] : hprev[i], in_term);
+                }
             }
         }
 
@@ -282,7 +306,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 for (int rq = 3; rq >= 0; --rq) {
                     const int rr = 4 * qt + rq, r = half * kHalf + rr;
                     const float4 rv = s_row[r][lane];
-                    float s1 = 0.0f, s2 = 0.0f, yp = 0.0f;
+                    float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f, yp = 0.0f;
 #pragma unroll
                     for (int i = 0; i < kNS; ++i) {
                         // h_t is last needed here: dC, and C.h_t for dz
@@ -291,16 +315,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                         g[i] = fmaf(rv.z, word(cw, rr, i), g[i]);
                         const float hp = r ? hh[r - 1][i] : hprev[i];
                         // g e is both a factor of g h_{t-1} e and the next row's g
-                        const float ge = g[i] * exp2_hw(rv.x * A2[i]);
+                        const float x2 = rv.x * A2[i], e = exp2_hw(x2);
+                        const float ge = g[i] * e;
                         const float t1 = ge * hp;
                         dA_acc[i] = fmaf(t1, rv.x, dA_acc[i]);
                         s2 = fmaf(t1, Av[i], s2);
-                        s1 = fmaf(g[i], word(bw, rr, i), s1);
-                        db[rq * kNS + i] = g[i] * rv.y;
+                        const float bv = word(bw, rr, i);
+                        if constexpr (ZOH) {
+                            // beta = delta phi: g phi feeds du (times delta) and dB (times delta u)
+                            const float ph = zoh_phi(x2, e, iA[i] * rv.w);
+                            const float gp = g[i] * ph;
+                            s1 = fmaf(gp, bv, s1);
+                            s3 = fmaf(ge, bv, s3);
+                            db[rq * kNS + i] = gp * rv.y;
+                            const float gbx = g[i] * bv * rv.y;  // g B delta u
+                            dA_acc[i] = fmaf(gbx, zoh_dbeta_dA_over_delta(x2, e, ph, iA[i], rv.x), dA_acc[i]);
+                        } else {
+                            s1 = fmaf(g[i], bv, s1);
+                            db[rq * kNS + i] = g[i] * rv.y;
+                        }
                         g[i] = ge;
                     }
                     s_par[w][rr][lane] = make_float2(s1, s2);
                     if (HAS_Z) s_yp[w][rr][lane] = yp;
+                    if (ZOH) s_ge[ZOH ? w : 0][rr][lane] = s3;
                 }
                 // lane l holds the sums of value l/8 = (row, state) of the quarter
                 const float tb = sum8_across_lanes(db), tc = sum8_across_lanes(dc);
@@ -329,7 +367,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                         du = fmaf(dskip, dypf[half], du);
                         dD_acc = fmaf(dypf[half], xf[half], dD_acc);
                     }
-                    const float ddl = fmaf(xf[half], s1, s2) * sgf[half];
+                    // the input path of ddelta: u sum g B (Euler), u sum g e B (zero-order hold)
+                    float s_in = s1;
+                    if constexpr (ZOH) {
+                        s_in = s_ge[0][w][lane];
+#pragma unroll
+                        for (int q = 1; q < kGroups; ++q) s_in += s_ge[ZOH ? q : 0][w][lane];
+                    }
+                    const float ddl = fmaf(xf[half], s_in, s2) * sgf[half];
                     dbias_acc += ddl;
                     V::store(r_du, ln.voff, uint32_t(t) * ln.row_bytes, du);
                     V::store(r_ddl, ln.voff, uint32_t(t) * ln.row_bytes, ddl);
@@ -435,7 +480,12 @@ hipError_t dispatch_bwd_mode(const BwdArgs& a, hipStream_t s)
 template <int DT>
 hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s)
 {
-    return (a.options & kOptSoftplus) ? dispatch_bwd_mode<DT, kOptSoftplus>(a, s) : dispatch_bwd_mode<DT, 0>(a, s);
+    switch (a.options & kOptAll) {
+        case 0: return dispatch_bwd_mode<DT, 0>(a, s);
+        case kOptSoftplus: return dispatch_bwd_mode<DT, kOptSoftplus>(a, s);
+        case kOptZoh: return dispatch_bwd_mode<DT, kOptZoh>(a, s);
+        default: return dispatch_bwd_mode<DT, kOptSoftplus | kOptZoh>(a, s);
+    }
 }
 
 }  // namespace

@@ -90,6 +90,23 @@ __device__ __forceinline__ float zoh_phi(float x2, float e, float inv_x)
     return fabsf(x2) < kZohSeriesBound ? series : direct;
 }
 
+// The backward of the zero-order hold.  Its input coefficient beta = delta *
+// phi(x) = (e^x - 1)/A has dbeta/ddelta = e^x and dbeta/dA = delta^2 psi(x),
+// psi = phi' = (x e^x - e^x + 1)/x^2 = (e^x - phi)/x.  This returns
+// dbeta/dA / delta: (e - phi) * inv_A, or, where e - phi would cancel
+// (|x| < 1/4), delta times the degree-5 series sum_k (k+1) x^k / (k+2)!
+// (truncation 1e-7 relative at the bound; the closed form just above it
+// loses about 3e-6 to the rounding of e and phi).
+constexpr float kZohPsiBound = 0.36067376f;  // |x2| below which psi's series is used (|x| < 1/4)
+__device__ __forceinline__ float zoh_dbeta_dA_over_delta(float x2, float e, float phi, float inv_A, float delta)
+{
+    // (k+1) ln2^k / (k+2)!: the coefficients for x2 = x log2 e
+    constexpr float c1 = 0.23104906f, c2 = 0.060056627f, c3 = 0.011100822f, c4 = 0.0016030215f,
+                    c5 = 0.00019047940f;
+    const float series = fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, c5, c4), c3), c2), c1), 0.5f);
+    return fabsf(x2) < kZohPsiBound ? delta * series : (e - phi) * inv_A;
+}
+
 // Scalar (wave-uniform) reads go through the constant address space so they
 // are issued as scalar loads.
 #define SS_CONST __attribute__((address_space(4)))

@@ -192,11 +192,11 @@ def scan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, wit
 def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
              dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
              h0: Optional[torch.Tensor] = None, *, dh_last: Optional[torch.Tensor] = None,
-             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False,
              want_dh0: bool = True, workspace: Optional[torch.Tensor] = None,
              ckpt: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """Gradients of sum(dy * y) + sum(dh_last * h_last) for ``scan_fwd`` with the same inputs
-    (``ss_scan_bwd``).  dy (B, L, D) in the input dtype; dh_last (B, D, N) float32 or None.
+    and options (``ss_scan_bwd``).  dy (B, L, D) in the input dtype; dh_last (B, D, N) float32 or None.
     With ``ckpt`` (the checkpoints ``scan_fwd(..., ckpt=ckpt)`` wrote) it is ``ss_scan_bwd_ckpt``,
     which reuses them instead of recomputing the states' checkpoints.
 
@@ -242,7 +242,7 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     need = scan_bwd_workspace_bytes(nb, nl, nd, nn, with_ckpt=ckpt is not None)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = ws.numel() * ws.element_size()
-    opts = _options(delta_softplus, False)
+    opts = _options(delta_softplus, zoh)
     grads = (_ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
              _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")))
     lib = _lib.load()

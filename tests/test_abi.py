@@ -280,8 +280,7 @@ def test_bwd_validation(lib):
     assert call_bwd(lib, D=addr(12)) == INVALID
     assert call_bwd(lib, z=addr(12)) == INVALID
     assert call_bwd(lib, bias=addr(12)) == INVALID
-    assert call_bwd(lib, options=2) == UNSUPPORTED            # no zero-order hold in the backward
-    assert call_bwd(lib, options=4) == UNSUPPORTED
+    assert call_bwd(lib, options=4) == UNSUPPORTED            # an unknown option bit
     assert call_bwd(lib, dstate=8) == UNSUPPORTED
     assert call_bwd(lib, batch=70000, seqlen=1, dim=1) == UNSUPPORTED
     assert call_bwd(lib, seqlen=2 ** 20, dim=2 ** 10) == UNSUPPORTED  # a batch row's slab >= 2 GiB
@@ -350,7 +349,7 @@ def test_ckpt_validation(lib):
     assert call_bwd_ckpt(lib, ckpt=near(14, 8)) == INVALID       # not 16-byte aligned
     assert call_bwd_ckpt(lib, du=near(14, 0)) == INVALID         # an output on the checkpoints
     assert call_bwd_ckpt(lib, ws=near(14, 256)) == INVALID       # the workspace on the checkpoints
-    assert call_bwd_ckpt(lib, options=2) == UNSUPPORTED          # no zero-order hold in the backward
+    assert call_bwd_ckpt(lib, options=4) == UNSUPPORTED          # an unknown option bit
     need = lib.ss_scan_bwd_ckpt_workspace_bytes(2, 512, 64, 16)
     assert call_bwd_ckpt(lib, ws_bytes=need - 1) == WORKSPACE
     assert call_bwd_ckpt(lib, dy=None) == INVALID

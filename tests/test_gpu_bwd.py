@@ -39,18 +39,19 @@ def make_case(batch, seqlen, dim, dtype, *, has_D, has_z, has_h0, softplus, seed
     return inp, dy, dhl
 
 
-def gpu_grads(inp, dy, dhl, softplus):
+def gpu_grads(inp, dy, dhl, softplus, zoh=False):
     t = {k: dev(v) for k, v in inp.items()}
     g = ss().scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dev(dy), D=t.get("D"), z=t.get("z"),
-                      h0=t.get("h0"), dh_last=dev(dhl), delta_bias=t.get("delta_bias"), delta_softplus=softplus)
+                      h0=t.get("h0"), dh_last=dev(dhl), delta_bias=t.get("delta_bias"), delta_softplus=softplus,
+                      zoh=zoh)
     torch.cuda.synchronize()
     return g
 
 
-def check(inp, dy, dhl, softplus, what, threads=1):
-    g = gpu_grads(inp, dy, dhl, softplus)
+def check(inp, dy, dhl, softplus, what, threads=1, zoh=False):
+    g = gpu_grads(inp, dy, dhl, softplus, zoh)
     dyw = oracle.widen(dy)
-    ref = oracle.scan_bwd(**inp, dy=dyw, dh_last=dhl, delta_softplus=softplus, threads=threads)
+    ref = oracle.scan_bwd(**inp, dy=dyw, dh_last=dhl, delta_softplus=softplus, zoh=zoh, threads=threads)
     tol = TOL["bf16" if inp["u"].dtype == np.uint16 else "f32"]
     msg = []
     for k in GRADS:
@@ -86,6 +87,43 @@ def test_bwd_small(case):
                              with_dh=with_dh)
     say("backward B%d L%d D%d %s" % (b, l, d, dt))
     check(inp, dy, dhl, sp, "B%d L%d D%d %s" % (b, l, d, dt))
+
+
+ZOH_CASES = [
+    # (batch, seqlen, dim, dtype, has_D, has_z, has_h0, softplus, with_dh): the zero-order-hold input term
+    (2, 100, 100, wl.F32, True, True, True, False, True),
+    (3, 37, 130, wl.F32, True, False, True, True, True),
+    (1, 1, 1, wl.F32, False, False, True, False, True),
+    (2, 33, 70, wl.BF16, True, True, False, True, True),
+]
+
+
+@pytest.mark.parametrize("case", ZOH_CASES, ids=["B%dL%dD%d-%s%s%s%s%s" % (c[0], c[1], c[2], c[3], "-D" * c[4],
+                                                                        "-z" * c[5], "-h0" * c[6], "-sp" * c[7])
+                                                 for c in ZOH_CASES])
+def test_bwd_zoh(case):
+    b, l, d, dt, has_D, has_z, has_h0, sp, with_dh = case
+    inp, dy, dhl = make_case(b, l, d, dt, has_D=has_D, has_z=has_z, has_h0=has_h0, softplus=sp, seed=140 + l,
+                             with_dh=with_dh)
+    say("backward, zero-order hold, B%d L%d D%d %s" % (b, l, d, dt))
+    check(inp, dy, dhl, sp, "ZOH B%d L%d D%d %s" % (b, l, d, dt), zoh=True)
+
+
+def test_bwd_zoh_edge_values():
+    """Zero-order hold where its closed forms break down: A = 0 entries (beta = delta, dbeta/dA =
+    delta^2/2), delta = 0 rows, step sizes of 1e-6 (delta*A deep in the series side) and of 40
+    (exp(delta*A) underflows to 0, beta = -1/A)."""
+    inp, dy, dhl = make_case(2, 48, 70, wl.F32, has_D=True, has_z=True, has_h0=True, softplus=False, seed=150)
+    inp["A"] = inp["A"].copy()
+    inp["A"][3, :] = 0.0
+    inp["A"][:, 5] = 0.0
+    delta = inp["delta"].copy()
+    delta[:, 7, :] = 0.0
+    delta[:, 20, :] = 1e-6
+    delta[:, 31, ::2] = 40.0
+    inp["delta"] = delta
+    say("backward, zero-order hold, edge values")
+    check(inp, dy, dhl, False, "ZOH edge values", zoh=True)
 
 
 def test_bwd_deterministic():
@@ -209,7 +247,7 @@ def test_bwd_from_checkpoints_large_layer():
 
 def test_fwd_ckpt_zoh_states():
     """The checkpointing forward under the zero-order-hold option keeps that recurrence's
-    states (its backward is not built: ss_scan_bwd_ckpt rejects the option)."""
+    states, and the backward from them matches the oracle's and (one chunk) ss_scan_bwd's."""
     inp, _, _ = make_case(2, 90, 80, wl.F32, has_D=True, has_z=True, has_h0=True, softplus=True, seed=77)
     m = ss()
     t = {k: dev(v) for k, v in inp.items()}
@@ -226,3 +264,25 @@ def test_fwd_ckpt_zoh_states():
     got = host64(ck).transpose(1, 3, 0, 2).reshape(b * d, n_sub, 16)
     assert np.array_equal(got[:, 0], inp["h0"].astype(np.float64).reshape(b * d, 16))
     assert rel_err(got[:, 1:], ref["h_rec"]) <= TOL["f32"]
+
+    rng = np.random.default_rng(78)
+    dy = rng.standard_normal((b, l, d)).astype(np.float32)
+    dhl = rng.standard_normal((b, d, 16)).astype(np.float32)
+    kw = dict(D=t["D"], z=t["z"], h0=t["h0"], dh_last=dev(dhl), delta_bias=t["delta_bias"], delta_softplus=True,
+              zoh=True)
+    args = (t["u"], t["delta"], t["A"], t["B"], t["C"], dev(dy))
+    g = m.scan_bwd(*args, ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    g_ref = oracle.scan_bwd(**inp, dy=dy, dh_last=dhl, delta_softplus=True, zoh=True)
+    for k, r in g_ref.items():
+        e = rel_err(host64(g[k]), r)
+        assert e <= TOL["f32"], "%s error %.3e" % (k, e)
+    # after a one-chunk forward the checkpoints, and so the gradients, are ss_scan_bwd's bit for bit
+    assert m.scan_plan(b, l, d, 16, l)[1] == 1
+    m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], h0=t["h0"],
+               delta_bias=t["delta_bias"], delta_softplus=True, zoh=True, chunk_len=l, ckpt=ck)
+    g_ck = m.scan_bwd(*args, ckpt=ck, **kw)
+    g_plain = m.scan_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for k in g_plain:
+        assert torch.equal(g_ck[k], g_plain[k]), "%s differs from ss_scan_bwd" % k
