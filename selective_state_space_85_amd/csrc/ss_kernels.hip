@@ -356,70 +356,81 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Carry kernel.  grid = batch*dim (one wave per channel), block = 64.
-// Lane i of pass p owns chunk c = 64p + i and its affine pair
+// Carry kernel.  Each chunk c < K-1 has its affine pair
 // (P_c, S_c) = (exp(A * sum of delta over chunk c), end state of c from zero).
-// An inclusive Hillis-Steele combine over the lanes, earlier pair first,
+// An inclusive Hillis-Steele combine over lanes, earlier pair first,
 //   (a1, b1) then (a2, b2) -> (a2*a1, a2*b1 + b2),
-// built from DPP row shifts (1, 2, 4, 8 within each row of 16 lanes) and row
-// broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3), gives each
-// lane the composite map of chunks 0..c; applied to the incoming state it
-// yields the carry H_c (state after chunk c), stored in slot c+1.  Slot 0
-// receives the initial state.  Lanes past the last chunk hold the identity
-// pair (1, 0), so lane 63 always ends with the pass's total.
+// gives each lane the composite map of chunks 0..c; applied to the incoming
+// state it yields the carry H_c (state after chunk c), stored in slot c+1.
+// Slot 0 receives the initial state.
+// A wave holds R = 4..64 consecutive chunks (R the power of two covering the
+// K-1 aggregated chunks, 64 and passes of 64 beyond that) for each of 64/R
+// state entries: lane l takes chunk base + l%R of entry n0 + l/R, so that
+// with few chunks the lanes are not left idle.  The combine is a scan within
+// each row of 16 lanes (DPP row shifts 1, 2, 4, 8, masked at the edges of
+// groups narrower than a row), then, for R = 32 and 64, the broadcasts of lane
+// 15 into rows 1 and 3 and of lane 31 into rows 2 and 3.  Lanes past the last
+// chunk hold the identity (1, 0), so a group's last lane ends with the pass's
+// total.  grid = (batch*dim, 16*R/64), block = 64.
 // ---------------------------------------------------------------------------
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void combine_from(float& P, float& S)
+__device__ __forceinline__ void combine_from(float& P, float& S, bool take = true)
 {
     // a source outside the row (or a row left out by ROW_MASK) reads the identity (1, 0)
-    const float Pp = __int_as_float(
+    float Pp = __int_as_float(
         __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(P), CTRL, ROW_MASK, 0xf, false));
-    const float Sp = __int_as_float(
+    float Sp = __int_as_float(
         __builtin_amdgcn_update_dpp(__float_as_int(0.0f), __float_as_int(S), CTRL, ROW_MASK, 0xf, false));
+    if (!take) {  // the source is another group's chunk
+        Pp = 1.0f;
+        Sp = 0.0f;
+    }
     S = fmaf(P, Sp, S);
     P *= Pp;
 }
 
-
+template <int R>
 __global__ __launch_bounds__(kWave) void carry_kernel(ScanArgs a)
 {
+    static_assert(R >= 4 && R <= kWave && (R & (R - 1)) == 0, "R: 4..64, a power of two");
+    constexpr int G = kWave / R;  // state entries per wave
     const int64_t bd = blockIdx.x;
     const int64_t BD = a.batch * a.dim;
     const int64_t d = bd % a.dim;
     const int lane = threadIdx.x;
+    const int i = lane % R;  // chunk within the pass
+    const int n = blockIdx.y * G + lane / R;
     const int64_t n_carry = a.n_chunks - 1;
 
-    float A2[N], hin[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        A2[n] = a.A[d * N + n] * kLog2e;
-        hin[n] = a.h0 ? a.h0[bd * N + n] : 0.0f;
-    }
-    if (lane < N) a.ws_state[bd * N + lane] = a.h0 ? a.h0[bd * N + lane] : 0.0f;
+    const float A2 = a.A[d * N + n] * kLog2e;
+    float hin = a.h0 ? a.h0[bd * N + n] : 0.0f;
+    if (i == 0) a.ws_state[bd * N + n] = hin;
 
-    for (int64_t base = 0; base < n_carry; base += kWave) {
-        const int64_t c = base + lane;
+    for (int64_t base = 0; base < n_carry; base += R) {
+        const int64_t c = base + i;
         const bool valid = c < n_carry;
-        const float dsum = valid ? a.ws_dsum[c * BD + bd] : 0.0f;
-        float* slot = a.ws_state + ((c + 1) * BD + bd) * N;
-        float S[N];
-#pragma unroll
-        for (int n = 0; n < N; ++n) S[n] = valid ? slot[n] : 0.0f;
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            float P = valid ? exp2_hw(A2[n] * dsum) : 1.0f;
-            float Sn = S[n];
-            combine_from<kDppRowShr1, 0xf>(P, Sn);
-            combine_from<kDppRowShr2, 0xf>(P, Sn);
-            combine_from<kDppRowShr4, 0xf>(P, Sn);
-            combine_from<kDppRowShr8, 0xf>(P, Sn);
-            combine_from<kDppRowBcast15, 0xa>(P, Sn);
-            combine_from<kDppRowBcast31, 0xc>(P, Sn);
-            const float H = fmaf(P, hin[n], Sn);
-            if (valid) slot[n] = H;
-            hin[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(H), kWave - 1));
-        }
+        float* slot = a.ws_state + ((c + 1) * BD + bd) * N + n;
+        float P = valid ? exp2_hw(A2 * a.ws_dsum[c * BD + bd]) : 1.0f;
+        float S = valid ? *slot : 0.0f;
+        combine_from<kDppRowShr1, 0xf>(P, S, R >= 16 || i >= 1);
+        combine_from<kDppRowShr2, 0xf>(P, S, R >= 16 || i >= 2);
+        if constexpr (R >= 8) combine_from<kDppRowShr4, 0xf>(P, S, R >= 16 || i >= 4);
+        if constexpr (R >= 16) combine_from<kDppRowShr8, 0xf>(P, S);
+        if constexpr (R >= 32) combine_from<kDppRowBcast15, 0xa>(P, S);
+        if constexpr (R >= 64) combine_from<kDppRowBcast31, 0xc>(P, S);
+        const float H = fmaf(P, hin, S);
+        if (valid) *slot = H;
+        // the next pass (only when R = 64) starts from this pass's total
+        if constexpr (R == kWave) hin = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(H), kWave - 1));
     }
+}
+
+// one wave per (channel, 64/R state entries): N/(64/R) = R/4 waves per channel
+template <int R>
+void launch_carry(const ScanArgs& a, hipStream_t s)
+{
+    static_assert(N * R / kWave == R / 4, "16 state entries");
+    carry_kernel<R><<<dim3(unsigned(a.batch * a.dim), unsigned(N * R / kWave)), dim3(kWave), 0, s>>>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -488,7 +499,18 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
     if (a.n_chunks > 1) {
         scan_kernel<DT, false, false, false, MODE>
             <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), dim3(kThreads), 0, s>>>(a);
-        carry_kernel<<<dim3(unsigned(a.batch * a.dim)), dim3(kWave), 0, s>>>(a);
+        // R lanes per state entry: the power of two covering the K-1 aggregated chunks, 4..64
+        const int64_t n_carry = a.n_chunks - 1;
+        if (n_carry <= 4)
+            launch_carry<4>(a, s);
+        else if (n_carry <= 8)
+            launch_carry<8>(a, s);
+        else if (n_carry <= 16)
+            launch_carry<16>(a, s);
+        else if (n_carry <= 32)
+            launch_carry<32>(a, s);
+        else
+            launch_carry<64>(a, s);
     }
     const dim3 grid(nblk, unsigned(a.batch), unsigned(a.n_chunks));
     if (a.ckpt)

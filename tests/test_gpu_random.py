@@ -75,12 +75,13 @@ def draw_bwd_cases(n, seed):
              bool(rng.random() < 0.5), bool(rng.random() < 0.4)) for i in range(n)]
 
 
-BWD_CASES = draw_bwd_cases(8, 2025)
+BWD_CASES = draw_bwd_cases(10, 2025)
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=["bwd%02d-B%dL%dD%d-%s" % c[:5] for c in BWD_CASES])
 def test_random_bwd(case):
     i, b, l, d, dtype, has_D, has_z, has_h0, sp = case
+    zoh = i % 4 in (1, 2)  # half of the cases under the zero-order-hold input term
     inp = wl.scan_inputs(b, l, d, 16, dtype, has_D=has_D, has_z=has_z, has_h0=has_h0, seed=400 + i)
     if sp:
         inp = wl.with_raw_delta(inp, seed=400 + i)
@@ -90,11 +91,11 @@ def test_random_bwd(case):
         dy = wl.f32_to_bf16_bits(dy)
     dhl = rng.standard_normal((b, d, 16)).astype(np.float32)
     t = {k: dev(v) for k, v in inp.items()}
-    say("random bwd %d: B%d L%d D%d %s D=%s z=%s h0=%s softplus=%s" % case)
+    say("random bwd %d: B%d L%d D%d %s D=%s z=%s h0=%s softplus=%s" % case + " zoh=%s" % zoh)
     g = ss().scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dev(dy), D=t.get("D"), z=t.get("z"),
-                      h0=t.get("h0"), dh_last=dev(dhl), delta_bias=t.get("delta_bias"), delta_softplus=sp)
+                      h0=t.get("h0"), dh_last=dev(dhl), delta_bias=t.get("delta_bias"), delta_softplus=sp, zoh=zoh)
     torch.cuda.synchronize()
-    ref = oracle.scan_bwd(**inp, dy=oracle.widen(dy), dh_last=dhl, delta_softplus=sp, threads=THREADS)
+    ref = oracle.scan_bwd(**inp, dy=oracle.widen(dy), dh_last=dhl, delta_softplus=sp, zoh=zoh, threads=THREADS)
     for k, r in ref.items():
         e = rel_err(host64(g[k]), r)
         assert e <= tol_of(dtype), "%s: %.3e" % (k, e)

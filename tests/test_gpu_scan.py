@@ -169,7 +169,9 @@ def test_large_delta_resets_state():
 # ---------------------------------------------------------------------------
 # chunks and carries
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("T", [16, 64, 100, 256])
+# 1000 rows in chunks of T: 3 .. 124 aggregated chunks, so every lane-group width of
+# the carry pass (4, 8, 16, 32, 64 chunks per state entry) and two passes of 64
+@pytest.mark.parametrize("T", [8, 16, 32, 64, 100, 128, 256])
 def test_carries_match_oracle_states(T):
     nb, nl, nd = 2, 1000, 80
     inp = wl.scan_inputs(nb, nl, nd, 16, wl.F32, delta_mu=-0.5, has_D=True, has_z=True, has_h0=True, seed=8)
