@@ -25,6 +25,15 @@ constexpr int64_t kMinAutoChunk = 64;  // the automatic plan never cuts finer
 // 1.53 ms; the small-model layer (48) at 8 / 16 / 32 chunks 73 / 59 / 69 us.
 constexpr int64_t kSingleChunkBlocks = 208;
 constexpr int64_t kTargetBlocks = 768;
+// Chunks of kLongChunk rows or more still amortise their per-chunk costs after
+// one more halving, so from there the plan goes on up to kTargetBlocksLong
+// workgroups.  Measured, one halving further against the kTargetBlocks plan:
+// long context 1.537 -> 1.493 ms (T 4096 -> 2048), B=2 L=65536 D=2048 1.539 ->
+// 1.471 ms, L=131072 D=1024 0.801 -> 0.779 ms (2048 -> 1024), L=32768 D=4096
+// 0.771 -> 0.743 ms; from shorter chunks it loses: L=16384 D=2048 0.203 ->
+// 0.233 ms (512 -> 256), the small-model layer 54 -> 67 us (128 -> 64).
+constexpr int64_t kLongChunk = 2048;
+constexpr int64_t kTargetBlocksLong = 2048;
 constexpr int64_t kMaxGridYZ = 65535;
 // A chunk's (B, L, D) slab is addressed with 32-bit buffer offsets, and idle
 // lanes use offsets at and above 2^31: one chunk of rows must stay below 2^31
@@ -72,7 +81,8 @@ bool shape_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, Siz
 // Plan: chunk length and count.  Automatic plans start from one chunk; a
 // shape with fewer than kSingleChunkBlocks workgroups then halves the chunk
 // length (staying a power of two, never below kMinAutoChunk) until the emit
-// launch has at least kTargetBlocks workgroups.
+// launch has at least kTargetBlocks workgroups, and while the chunks still
+// have kLongChunk rows or more, until it has kTargetBlocksLong.
 bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* T, int64_t* K)
 {
     if (request < 0) return false;
@@ -85,7 +95,8 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
         if (blocks < kSingleChunkBlocks) {
             while (t > kMinAutoChunk) {
                 int64_t launched;
-                if (!mul(blocks, ceil_div(seqlen, t), &launched) || launched >= kTargetBlocks) break;
+                if (!mul(blocks, ceil_div(seqlen, t), &launched)) break;
+                if (launched >= kTargetBlocks && (t < kLongChunk || launched >= kTargetBlocksLong)) break;
                 t >>= 1;
             }
         }

@@ -363,15 +363,17 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
 // gives each lane the composite map of chunks 0..c; applied to the incoming
 // state it yields the carry H_c (state after chunk c), stored in slot c+1.
 // Slot 0 receives the initial state.
-// A wave holds R = 4..64 consecutive chunks (R the power of two covering the
-// K-1 aggregated chunks, 64 and passes of 64 beyond that) for each of 64/R
-// state entries: lane l takes chunk base + l%R of entry n0 + l/R, so that
-// with few chunks the lanes are not left idle.  The combine is a scan within
+// One wave per channel.  It holds R = 4..64 consecutive chunks (R the power
+// of two covering the K-1 aggregated chunks, 64 and passes of 64 beyond that)
+// for each of 64/R state entries at a time: lane l takes chunk base + l%R of
+// entry n0 + l/R, so that with few chunks the lanes are not left idle, and the
+// wave covers the 16 entries in 64/R groups (the entries of a slot share
+// cache lines, so they stay with one wave).  The combine is a scan within
 // each row of 16 lanes (DPP row shifts 1, 2, 4, 8, masked at the edges of
 // groups narrower than a row), then, for R = 32 and 64, the broadcasts of lane
 // 15 into rows 1 and 3 and of lane 31 into rows 2 and 3.  Lanes past the last
 // chunk hold the identity (1, 0), so a group's last lane ends with the pass's
-// total.  grid = (batch*dim, 16*R/64), block = 64.
+// total.  grid = batch*dim, block = 64.
 // ---------------------------------------------------------------------------
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ void combine_from(float& P, float& S, bool take = true)
@@ -399,38 +401,50 @@ __global__ __launch_bounds__(kWave) void carry_kernel(ScanArgs a)
     const int64_t d = bd % a.dim;
     const int lane = threadIdx.x;
     const int i = lane % R;  // chunk within the pass
-    const int n = blockIdx.y * G + lane / R;
     const int64_t n_carry = a.n_chunks - 1;
 
-    const float A2 = a.A[d * N + n] * kLog2e;
-    float hin = a.h0 ? a.h0[bd * N + n] : 0.0f;
-    if (i == 0) a.ws_state[bd * N + n] = hin;
+    // the wave's entries: n = q*G + lane/R for q < N/G, all advanced together so
+    // that their loads and combines overlap
+    constexpr int NG = N / G;
+    float A2[NG], hin[NG];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        const int n = q * G + lane / R;
+        A2[q] = a.A[d * N + n] * kLog2e;
+        hin[q] = a.h0 ? a.h0[bd * N + n] : 0.0f;
+        if (i == 0) a.ws_state[bd * N + n] = hin[q];
+    }
 
     for (int64_t base = 0; base < n_carry; base += R) {
         const int64_t c = base + i;
         const bool valid = c < n_carry;
-        float* slot = a.ws_state + ((c + 1) * BD + bd) * N + n;
-        float P = valid ? exp2_hw(A2 * a.ws_dsum[c * BD + bd]) : 1.0f;
-        float S = valid ? *slot : 0.0f;
-        combine_from<kDppRowShr1, 0xf>(P, S, R >= 16 || i >= 1);
-        combine_from<kDppRowShr2, 0xf>(P, S, R >= 16 || i >= 2);
-        if constexpr (R >= 8) combine_from<kDppRowShr4, 0xf>(P, S, R >= 16 || i >= 4);
-        if constexpr (R >= 16) combine_from<kDppRowShr8, 0xf>(P, S);
-        if constexpr (R >= 32) combine_from<kDppRowBcast15, 0xa>(P, S);
-        if constexpr (R >= 64) combine_from<kDppRowBcast31, 0xc>(P, S);
-        const float H = fmaf(P, hin, S);
-        if (valid) *slot = H;
-        // the next pass (only when R = 64) starts from this pass's total
-        if constexpr (R == kWave) hin = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(H), kWave - 1));
+        const float dsum = valid ? a.ws_dsum[c * BD + bd] : 0.0f;
+        float* slot = a.ws_state + ((c + 1) * BD + bd) * N + lane / R;
+        float S[NG];
+#pragma unroll
+        for (int q = 0; q < NG; ++q) S[q] = valid ? slot[q * G] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            float P = valid ? exp2_hw(A2[q] * dsum) : 1.0f;
+            float Sq = S[q];
+            combine_from<kDppRowShr1, 0xf>(P, Sq, R >= 16 || i >= 1);
+            combine_from<kDppRowShr2, 0xf>(P, Sq, R >= 16 || i >= 2);
+            if constexpr (R >= 8) combine_from<kDppRowShr4, 0xf>(P, Sq, R >= 16 || i >= 4);
+            if constexpr (R >= 16) combine_from<kDppRowShr8, 0xf>(P, Sq);
+            if constexpr (R >= 32) combine_from<kDppRowBcast15, 0xa>(P, Sq);
+            if constexpr (R >= 64) combine_from<kDppRowBcast31, 0xc>(P, Sq);
+            const float H = fmaf(P, hin[q], Sq);
+            if (valid) slot[q * G] = H;
+            // the next pass (only when R = 64) starts from this pass's total
+            if constexpr (R == kWave) hin[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(H), kWave - 1));
+        }
     }
 }
 
-// one wave per (channel, 64/R state entries): N/(64/R) = R/4 waves per channel
 template <int R>
 void launch_carry(const ScanArgs& a, hipStream_t s)
 {
-    static_assert(N * R / kWave == R / 4, "16 state entries");
-    carry_kernel<R><<<dim3(unsigned(a.batch * a.dim), unsigned(N * R / kWave)), dim3(kWave), 0, s>>>(a);
+    carry_kernel<R><<<dim3(unsigned(a.batch * a.dim)), dim3(kWave), 0, s>>>(a);
 }
 
 // ---------------------------------------------------------------------------

@@ -85,10 +85,13 @@ def check_workspace_size(ws, b, l, d, n, T, K):
 def test_auto_plan_choices(lib):
     """The automatic plan keeps a shape whole when its one-chunk launch has at least 208
     workgroups (64 channels of one batch row each), and otherwise cuts the sequence until
-    the emit launch has 768, in powers of two, never below 64 rows."""
+    the emit launch has 768, in powers of two, never below 64 rows; chunks of 2048 rows or
+    more go on being halved up to 2048 workgroups."""
     assert plan(lib, 8, 2048, 5120, 16) == (OK, 2048, 1)       # large layer: 640 workgroups
     assert plan(lib, 2, 2048, 1536, 16) == (OK, 128, 16)       # small-model layer: 48 -> 768
-    assert plan(lib, 1, 131072, 2048, 16) == (OK, 4096, 32)    # long context: 32 -> 1024
+    assert plan(lib, 1, 131072, 2048, 16) == (OK, 2048, 64)    # long context: 32 -> 1024 -> 2048
+    assert plan(lib, 1, 131072, 1024, 16) == (OK, 1024, 128)   # 16 -> 1024 at T = 2048 -> 2048
+    assert plan(lib, 1, 16384, 2048, 16) == (OK, 512, 32)      # 1024 workgroups at T = 512: stays
     assert plan(lib, 1, 256, 64, 16) == (OK, 64, 4)            # tiny: stops at 64 rows
     assert plan(lib, 1, 2048, 64 * 208, 16) == (OK, 2048, 1)   # 208 workgroups: whole
     assert plan(lib, 1, 2048, 64 * 207, 16) == (OK, 512, 4)    # 207: 4 chunks give 828
