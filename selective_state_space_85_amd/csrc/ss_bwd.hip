@@ -219,6 +219,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
     __shared__ float2 s_par[kGroups][kHalf][kWave];
     __shared__ float s_yp[HAS_Z ? kGroups : 1][kHalf][kWave];  // per wave C.h_t of one half (for dz)
     __shared__ float s_ge[ZOH ? kGroups : 1][kHalf][kWave];    // per wave sum g.e.B (zero-order hold)
+    // the rebuild's phi per row, wave and lane (its two entries), for the adjoint (zero-order
+    // hold: the kernel runs one workgroup per CU, so this 64 KB replaces 8 VALU per element)
+    __shared__ float2 s_phi[ZOH ? kSub : 1][ZOH ? kGroups : 1][kWave];
 
     const Lane<DT> ln(a);
     const int lane = ln.lane, w = ln.w;
@@ -282,13 +285,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
             for (int rr = 0; rr < kHalf; ++rr) {
                 const int r = half * kHalf + rr;
                 const float4 rv = s_row[r][lane];
+                float ph[kNS] = {};
 #pragma unroll
                 for (int i = 0; i < kNS; ++i) {
                     const float x2 = rv.x * A2[i], e = exp2_hw(x2);
                     float in_term = rv.y * word(bw, rr, i);
-                    if constexpr (ZOH) in_term *= zoh_phi(x2, e, iA[i] * rv.w);
+                    if constexpr (ZOH) {
+                        ph[i] = zoh_phi(x2, e, iA[i] * rv.w);
+                        in_term *= ph[i];
+                    }
                     hh[r][i] = fmaf(e, r ? hh[r - 1][i] : hprev[i], in_term);
                 }
+                static_assert(kNS == 2, "two entries per lane");
+                if constexpr (ZOH) s_phi[ZOH ? r : 0][ZOH ? w : 0][lane] = make_float2(ph[0], ph[1]);
             }
         }
 
@@ -306,6 +315,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
                 for (int rq = 3; rq >= 0; --rq) {
                     const int rr = 4 * qt + rq, r = half * kHalf + rr;
                     const float4 rv = s_row[r][lane];
+                    const float2 phr = ZOH ? s_phi[ZOH ? r : 0][ZOH ? w : 0][lane] : make_float2(0.0f, 0.0f);
                     float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f, yp = 0.0f;
 #pragma unroll
                     for (int i = 0; i < kNS; ++i) {
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
                         const float bv = word(bw, rr, i);
                         if constexpr (ZOH) {
                             // beta = delta phi: g phi feeds du (times delta) and dB (times delta u)
-                            const float ph = zoh_phi(x2, e, iA[i] * rv.w);
+                            const float ph = i ? phr.y : phr.x;
                             const float gp = g[i] * ph;
                             s1 = fmaf(gp, bv, s1);
                             s3 = fmaf(ge, bv, s3);
