@@ -84,8 +84,12 @@ __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
 //       slot c+1 and its delta sum.
 // Host guarantees: chunk_len * dim * element size < 2^31.
 // ---------------------------------------------------------------------------
+// The zero-order hold's extra arithmetic would take the kernel just past 80
+// VGPRs, which leaves room for two 8-wave workgroups per CU instead of three;
+// it is held to 80 (six waves per SIMD).
 template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false>
-__global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE & kOptZoh) ? 6 : 2))) void scan_kernel(
+    ScanArgs a)
 {
     constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using T = typename Elem<DT>::T;
