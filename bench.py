@@ -108,7 +108,7 @@ def alu_cobound(w, ms_step):
             "floor_ms": floor_ms, "frac": floor_ms / ms_step}
 
 
-CPU_BASELINE_SECONDS = 10.0  # the oracle repeats the whole workload for at least this long
+CPU_ORACLE_SECONDS = 10.0  # the oracle repeats the whole workload for at least this long
 
 
 def main():
@@ -532,10 +532,10 @@ def main():
         rows = w.batch  # every batch row: the whole workload
         lanes = np.arange(rows * w.dim, dtype=np.int64)
         log("timing the CPU oracle on %d channels x %d steps, %d threads, for at least %.0f s"
-            % (lanes.size, w.seqlen, threads, CPU_BASELINE_SECONDS))
+            % (lanes.size, w.seqlen, threads, CPU_ORACLE_SECONDS))
         reps = 0
         c0 = time.perf_counter()
-        while reps == 0 or time.perf_counter() - c0 < CPU_BASELINE_SECONDS:
+        while reps == 0 or time.perf_counter() - c0 < CPU_ORACLE_SECONDS:
             oracle.scan(**inp, lanes=lanes, threads=threads)
             reps += 1
         cdt = time.perf_counter() - c0
