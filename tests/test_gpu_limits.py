@@ -1,0 +1,110 @@
+"""The scan and its backward at the largest slab the kernels address.
+
+Rows of the (B, L, D) streams are reached through 32-bit buffer offsets, so the
+library rejects a chunk (forward) or a batch row (backward) of 2 GiB or more.
+These tests run fp32 shapes just under that limit: one batch row of L = 65543
+rows of D = 8191 channels is 2 147 450 852 bytes, 32 796 below 2^31, and the
+last 64-channel block has an idle lane whose offsets sit above the range (the
+largest, 2^31 plus the last row's offset, stays below 2^32).  The
+inputs are drawn on the device (torch's seeded generator, the workloads'
+distributions); the oracle checks a sample of channels over the whole sequence,
+which is exact because channels are independent.  For the backward, dy and
+dh_last are zero outside the sampled channels: every other channel then
+contributes exact zeros, so the channel sums dB and dC are the oracle's sums
+over the sampled channels, and the other channels' gradients must be exactly 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import TOL, host64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+NB, NL, ND, NS = 1, 65543, 8191, 16
+SEL = np.array([0, 1, 63, 64, 2047, 4095, 4096, 6000, 8127, 8128, 8189, 8190], dtype=np.int64)
+
+
+def ss():
+    import selective_state_space_85_amd as m
+
+    return m
+
+
+def device_inputs(seed):
+    """fp32 inputs on the device: u, z ~ N(0, 1); delta = softplus(N(-2, 1)); B, C ~ N(0, 1);
+    A = -(n+1) exp(U(-1/2, 1/2)); D ~ N(0, 1); h0 ~ N(0, 1)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    shp = (NB, NL, ND)
+    t = {"u": torch.randn(shp, device="cuda", generator=g),
+         "delta": torch.nn.functional.softplus(torch.randn(shp, device="cuda", generator=g) - 2.0),
+         "z": torch.randn(shp, device="cuda", generator=g),
+         "B": torch.randn(NB, NL, NS, device="cuda", generator=g),
+         "C": torch.randn(NB, NL, NS, device="cuda", generator=g),
+         "A": torch.from_numpy(wl.make_A(ND, NS, True, seed=seed)).cuda(),
+         "D": torch.randn(ND, device="cuda", generator=g),
+         "h0": torch.randn(NB, ND, NS, device="cuda", generator=g)}
+    assert 0 < 2 ** 31 - NL * ND * 4 < 2 ** 16  # within 64 KB of the limit
+    assert 2 ** 31 + (NL - 1) * ND * 4 < 2 ** 32
+    return t
+
+
+def sampled(t):
+    """The oracle's sub-problem: the sampled channels, as float32 host arrays."""
+    sel = torch.from_numpy(SEL).cuda()
+    cols = lambda x: np.ascontiguousarray(x.index_select(2, sel).cpu().numpy())  # noqa: E731
+    return dict(u=cols(t["u"]), delta=cols(t["delta"]), z=cols(t["z"]), B=t["B"].cpu().numpy(),
+                C=t["C"].cpu().numpy(), A=t["A"].cpu().numpy()[SEL], D=t["D"].cpu().numpy()[SEL],
+                h0=np.ascontiguousarray(t["h0"].cpu().numpy()[:, SEL]))
+
+
+def test_forward_at_the_chunk_slab_limit():
+    m = ss()
+    t = device_inputs(1201)
+    say("forward, one chunk of %d x %d fp32 (%d bytes)" % (NL, ND, NL * ND * 4))
+    y, hl = m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], h0=t["h0"], chunk_len=NL,
+                       return_last_state=True)
+    torch.cuda.synchronize()
+    assert m.scan_plan(NB, NL, ND, NS, NL) == (NL, 1)
+    ref = oracle.scan(**sampled(t))
+    ey = rel_err(host64(y[:, :, torch.from_numpy(SEL).cuda()]), ref["y"])
+    eh = rel_err(host64(hl[:, torch.from_numpy(SEL).cuda()]), ref["h_last"])
+    say("  y err %.2e, h_last err %.2e" % (ey, eh))
+    assert ey <= TOL["f32"] and eh <= TOL["f32"]
+    assert torch.isfinite(y).all().item()
+
+
+def test_backward_at_the_row_slab_limit():
+    m = ss()
+    t = device_inputs(1202)
+    sel = torch.from_numpy(SEL).cuda()
+    g = torch.Generator(device="cuda").manual_seed(1203)
+    dy = torch.zeros(NB, NL, ND, device="cuda")
+    dy[:, :, sel] = torch.randn(NB, NL, SEL.size, device="cuda", generator=g)
+    dhl = torch.zeros(NB, ND, NS, device="cuda")
+    dhl[:, sel] = torch.randn(NB, SEL.size, NS, device="cuda", generator=g)
+    say("backward, one batch row of %d x %d fp32 (%d bytes)" % (NL, ND, NL * ND * 4))
+    gr = m.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, D=t["D"], z=t["z"], h0=t["h0"], dh_last=dhl)
+    torch.cuda.synchronize()
+    sub = sampled(t)
+    ref = oracle.scan_bwd(**sub, dy=np.ascontiguousarray(dy.index_select(2, sel).cpu().numpy()),
+                          dh_last=np.ascontiguousarray(dhl[:, sel].cpu().numpy()))
+    errs = {}
+    for k in ("du", "ddelta", "dz"):
+        errs[k] = rel_err(host64(gr[k].index_select(2, sel)), ref[k])
+        rest = gr[k].clone()
+        rest[:, :, sel] = 0
+        assert torch.count_nonzero(rest).item() == 0, "%s of a channel without gradient" % k
+    for k in ("dA", "dD"):
+        errs[k] = rel_err(host64(gr[k][sel]), ref[k])
+        rest = gr[k].clone()
+        rest[sel] = 0
+        assert torch.count_nonzero(rest).item() == 0, "%s of a channel without gradient" % k
+    errs["dh0"] = rel_err(host64(gr["dh0"][:, sel]), ref["dh0"])
+    for k in ("dB", "dC"):
+        errs[k] = rel_err(host64(gr[k]), ref[k])
+    say("  " + ", ".join("%s %.1e" % kv for kv in errs.items()))
+    for k, e in errs.items():
+        assert e <= TOL["f32"], "%s error %.3e" % (k, e)
