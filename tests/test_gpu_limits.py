@@ -1,4 +1,5 @@
-"""The scan and its backward at the largest slab the kernels address.
+"""The scan, its backward and the multi-head recurrence at the largest slab the kernels
+address.
 
 Rows of the (B, L, D) streams are reached through 32-bit buffer offsets, so the
 library rejects a chunk (forward) or a batch row (backward) of 2 GiB or more.
@@ -108,3 +109,34 @@ def test_backward_at_the_row_slab_limit():
     say("  " + ", ".join("%s %.1e" % kv for kv in errs.items()))
     for k, e in errs.items():
         assert e <= TOL["f32"], "%s error %.3e" % (k, e)
+
+
+def bf16_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_ssd_at_the_row_slab_limit():
+    """The multi-head recurrence with one batch row of x just under 2 GiB: 256 heads of 64
+    channels, L = 65535 (the longest the library accepts at this width), bf16, dstate 64;
+    the oracle checks the first and the last head over the whole sequence."""
+    nl, nh, nn = 65535, 256, 64
+    assert 0 < 2 ** 31 - nl * nh * 64 * 2 < 2 ** 16
+    g = torch.Generator(device="cuda").manual_seed(1204)
+    x = torch.randn(1, nl, nh, 64, device="cuda", generator=g).to(torch.bfloat16)
+    dt = torch.nn.functional.softplus(torch.randn(1, nl, nh, device="cuda", generator=g) - 2.0).to(torch.bfloat16)
+    A = -(torch.rand(nh, device="cuda", generator=g) * 15.0 + 1.0)
+    B = torch.randn(1, nl, nn, device="cuda", generator=g).to(torch.bfloat16)
+    C = torch.randn(1, nl, nn, device="cuda", generator=g).to(torch.bfloat16)
+    D = torch.randn(nh, device="cuda", generator=g)
+    h0 = torch.randn(1, nh, nn, 64, device="cuda", generator=g)
+    say("ssd, one batch row of %d x %d heads x 64 bf16 (%d bytes)" % (nl, nh, nl * nh * 128))
+    y, hl = ss().ssd_fwd(x, dt, A, B, C, D=D, h0=h0, return_last_state=True)
+    torch.cuda.synchronize()
+    heads = [0, nh - 1]
+    sel = torch.tensor(heads, device="cuda")
+    ref = oracle.ssd(bf16_bits(x.index_select(2, sel)), bf16_bits(dt.index_select(2, sel)), A[sel].cpu().numpy(),
+                     bf16_bits(B), bf16_bits(C), D=D[sel].cpu().numpy(), h0=h0[:, sel].cpu().numpy())
+    ey = rel_err(host64(y.index_select(2, sel)), ref["y"])
+    eh = rel_err(host64(hl[:, sel]), ref["h_last"])
+    say("  y err %.2e, h_last err %.2e" % (ey, eh))
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
