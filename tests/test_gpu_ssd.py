@@ -51,6 +51,30 @@ def test_ssd_small(case):
     assert np.all(np.isfinite(y)) and ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
+def test_ssd_degenerate_steps():
+    """Step sizes the kernel treats through limits: dt = 0 rows inside chunks (no decay, no
+    input: log2 dt = -inf drops the row from M and from the state update), dt = 40 rows
+    (exp(dt A) underflows: the state restarts from that row), and a head with A = -1e-4
+    that barely decays over the 300 rows."""
+    inp = wl.ssd_inputs(2, 300, 3, 64, 128, has_D=True, has_h0=True, seed=77)
+    dt = inp["dt"].copy()
+    zero, big = wl.f32_to_bf16_bits(np.float32([0.0, 40.0]))
+    dt[:, 5:9, :] = zero        # four rows inside the first chunk
+    dt[:, 64, :] = zero         # the first row of the second chunk
+    dt[:, 150, :] = big         # a reset in the middle of the third chunk
+    dt[1, 255:, 0] = zero       # the tail of one head
+    inp["dt"] = dt
+    inp["A"] = inp["A"].copy()
+    inp["A"][2] = -1e-4
+    say("ssd degenerate steps")
+    y, hl = gpu_ssd(inp)
+    ref = oracle.ssd(**inp)
+    ey, eh = rel_err(y, ref["y"]), rel_err(hl, ref["h_last"])
+    say("  y err %.3e, h_last err %.3e" % (ey, eh))
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hl))
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 def test_ssd_chaining():
     """Two calls chained through h_last -> h0 match one call over the whole sequence."""
     b, l, h, n = 2, 150, 2, 128
