@@ -91,7 +91,7 @@ def read_traffic(src_hash: str):
         return None
 
 
-def alu_cobound(w, ms_step):
+def alu_cobound(w, ms_step, alg_bytes):
     """The vector-ALU ceiling of the same step, from unit counts and clock.
 
     Per scan element the recurrence needs 4 fp32 vector operations (delta*A,
@@ -99,13 +99,26 @@ def alu_cobound(w, ms_step):
     the fma rate on gfx950 (measured: 8.7 vs 4 cycles per wave64 instruction),
     so it costs 2 issue slots.  Per (b, t, d) row: delta*u (1), the D skip (1),
     silu(z) (3 operations + exp2 + reciprocal = 7 slots) and the bf16 rounding
-    (1).  Peak: 256 CUs x 64 fp32 lanes x 2.4 GHz, no packed fp32."""
+    (1).  Peak: 256 CUs x 64 fp32 lanes x 2.4 GHz, no packed fp32.
+
+    ``ceilings_ms`` gives each bound alone: HBM at the 8 TB/s spec, the
+    transcendentals (one exp2 per element, exp2 and reciprocal per gated row) at
+    8.7 cycles per wave64 instruction on each of the 1024 SIMDs, and the other
+    vector operations at 4 cycles.  The last two add up to a little more than
+    ``floor_ms``, which prices each transcendental at two issue slots (8 cycles)."""
+    rows = w.elements // w.dstate
     per_row = 1 + (1 if w.has_D else 0) + (7 if w.has_z else 0) + 1
     slots = 6.0 + per_row / w.dstate
     peak_slots = 256 * 64 * 2.4e9
     floor_ms = w.elements * slots / peak_slots * 1e3
+    simd_cycles_per_s = 1024 * 2.4e9
+    transcendentals = w.elements + (2 * rows if w.has_z else 0)
+    other_ops = 4 * w.elements + rows * (per_row - (4 if w.has_z else 0))
+    ceilings = {"hbm_8TBps": alg_bytes / 8e12 * 1e3,
+                "transcendental": transcendentals / 64 * 8.7 / simd_cycles_per_s * 1e3,
+                "valu_other": other_ops / 64 * 4 / simd_cycles_per_s * 1e3}
     return {"bound": "alu", "slots_per_element": slots, "peak_lane_slots_per_s": peak_slots,
-            "floor_ms": floor_ms, "frac": floor_ms / ms_step}
+            "floor_ms": floor_ms, "frac": floor_ms / ms_step, "ceilings_ms": ceilings}
 
 
 CPU_ORACLE_SECONDS = 10.0  # the oracle repeats the whole workload for at least this long
@@ -201,7 +214,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "kernel": "ss_scan_fwd: scan_kernel (emit)%s" % (" + aggregate + carry" if K > 1 else ""),
                      "kernel_source_hash": src_hash,
-                     "co_bound": alu_cobound(w, ms_step)},
+                     "co_bound": alu_cobound(w, ms_step, alg_bytes)},
     }
 
     if args.copy_reference:
