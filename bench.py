@@ -457,6 +457,28 @@ def main():
                          "mfma_TFLOP/s": sflops / (sms * 1e-3) / 1e12, "frac_of_2.5PF": sflops / (sms * 1e-3) / 2.5e15}
         del stt, sy
 
+        # the same layer at dstate 256: two workgroups per head (one per half of the state
+        # entries) writing fp32 parts of y, then the pass that adds them
+        si = wl.ssd_inputs(sb, sl, sh, 64, 256, seed=0)
+        stt = {k: to_dev(v) for k, v in si.items() if v is not None}
+        sy = torch.empty_like(stt["x"])
+        sws = torch.empty(ss.ssd_workspace_bytes(sb, sl, sh, 64, 256), dtype=torch.uint8, device=device)
+
+        def sstep256():
+            ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy, workspace=sws)
+
+        for _ in range(3):
+            sstep256()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            sstep256()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        result["ssd"]["dstate256"] = {"ms": e0.elapsed_time(e1) / 20,
+                                      "alg_bytes": wl.algorithmic_bytes_ssd(sb, sl, sh, 64, 256)}
+        del stt, sy, sws
+
         # recurrent step workload: one token for B=256, D=5120, state in place
         sw = wl.WORKLOADS["step"]
         sp = wl.step_params(sw)

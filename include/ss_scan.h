@@ -331,15 +331,35 @@ ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weigh
  *   B, C   : (batch, seqlen, dstate)          bf16, 16-byte aligned
  *   h0     : (batch, heads, dstate, headdim)  fp32 or NULL (zero state)
  *   h_last : (batch, heads, dstate, headdim)  fp32 output or NULL
- * Supported: dtype SS_BF16, headdim 64, dstate 64 or 128, and one batch row of
- * x (seqlen*heads*headdim*2 bytes) and of B (seqlen*dstate*2 bytes) below
- * 2 GiB (SS_ERR_UNSUPPORTED otherwise).  y and h_last must not overlap the
- * inputs or each other.
+ * Supported: dtype SS_BF16, headdim 64, dstate 64, 128 or 256, and one batch
+ * row of x (seqlen*heads*headdim*2 bytes) and of B (seqlen*dstate*2 bytes)
+ * below 2 GiB (SS_ERR_UNSUPPORTED otherwise).  y and h_last must not overlap
+ * the inputs or each other.  dstate 256 needs a workspace: ss_ssd_fwd returns
+ * SS_ERR_WORKSPACE for it; call ss_ssd_fwd_ex.
  */
 ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
                      const float* D, const float* h0, void* y, float* h_last,
                      int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
                      ss_dtype dtype, hipStream_t stream);
+
+/*
+ * ss_ssd_workspace_bytes -- device workspace ss_ssd_fwd_ex needs: 0 for dstate
+ * 64 and 128; for dstate 256, 2*batch*seqlen*heads*headdim*4 bytes (two fp32
+ * parts of y, one per half of the state entries, added by a second pass).
+ * (size_t)-1 for sizes <= 0 or overflowing.
+ */
+size_t ss_ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate);
+
+/*
+ * ss_ssd_fwd_ex -- ss_ssd_fwd with a workspace (ss_ssd_workspace_bytes(...)
+ * bytes, 256-byte aligned, overlapping no argument; NULL when that is 0).
+ * dstate 256 also requires (seqlen + 64) * heads * headdim * 2 <= 2^31.
+ */
+ss_status ss_ssd_fwd_ex(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                        const float* D, const float* h0, void* y, float* h_last,
+                        void* workspace, size_t workspace_bytes,
+                        int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                        ss_dtype dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* ss_status_string(ss_status s);

@@ -15,7 +15,8 @@ The library itself is ``libssscan.so`` (``include/ss_scan.h``), built by
 """
 from ._lib import LIB_PATH, SSError, load as load_library  # noqa: F401
 from .ops import (conv1d_silu, scan_bwd, scan_bwd_workspace_bytes, scan_ckpt_shape, scan_fwd,  # noqa: F401
-                  scan_plan, scan_workspace_bytes, ssd_fwd, step)
+                  scan_plan, scan_workspace_bytes, ssd_fwd, ssd_workspace_bytes, step)
 
 __all__ = ["scan_fwd", "scan_bwd", "step", "conv1d_silu", "ssd_fwd", "scan_plan", "scan_workspace_bytes",
-           "scan_bwd_workspace_bytes", "scan_ckpt_shape", "load_library", "LIB_PATH", "SSError"]
+           "scan_bwd_workspace_bytes", "scan_ckpt_shape", "ssd_workspace_bytes", "load_library", "LIB_PATH",
+           "SSError"]

@@ -15,7 +15,7 @@ SS_F32, SS_BF16 = 0, 1
 # Every function the header declares.
 EXPORTS = ("ss_scan_plan", "ss_scan_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_ckpt_bytes",
            "ss_scan_fwd_ckpt", "ss_step", "ss_step_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_bwd",
-           "ss_scan_bwd_ckpt_workspace_bytes", "ss_scan_bwd_ckpt", "ss_conv1d_silu", "ss_ssd_fwd",
+           "ss_scan_bwd_ckpt_workspace_bytes", "ss_scan_bwd_ckpt", "ss_conv1d_silu", "ss_ssd_fwd", "ss_ssd_fwd_ex", "ss_ssd_workspace_bytes",
            "ss_status_string", "ss_last_hip_error")
 SS_DELTA_SOFTPLUS, SS_B_ZOH = 1, 2  # ss_option bits
 
@@ -77,6 +77,10 @@ def load() -> ctypes.CDLL:
     lib.ss_conv1d_silu.restype = ctypes.c_int
     lib.ss_ssd_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_int, vp]
     lib.ss_ssd_fwd.restype = ctypes.c_int
+    lib.ss_ssd_fwd_ex.argtypes = [vp] * 10 + [ctypes.c_size_t] + [i64] * 5 + [ctypes.c_int, vp]
+    lib.ss_ssd_fwd_ex.restype = ctypes.c_int
+    lib.ss_ssd_workspace_bytes.argtypes = [i64] * 5
+    lib.ss_ssd_workspace_bytes.restype = ctypes.c_size_t
     lib.ss_status_string.argtypes = [ctypes.c_int]
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_last_hip_error.argtypes = []

@@ -624,18 +624,40 @@ ss_status ss_conv1d_silu(const void* x, int64_t x_row_stride, const float* weigh
     return SS_OK;
 }
 
+size_t ss_ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate)
+{
+    if (batch <= 0 || seqlen <= 0 || heads <= 0 || headdim <= 0 || dstate <= 0) return static_cast<size_t>(-1);
+    int64_t n;
+    if (!mul(batch, seqlen, &n) || !mul(n, heads, &n) || !mul(n, headdim, &n) || !mul(n, 8, &n))
+        return static_cast<size_t>(-1);
+    return dstate == 256 ? static_cast<size_t>(n) : 0;  // two fp32 parts of y at dstate 256
+}
+
 ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                      const float* h0, void* y, float* h_last, int64_t batch, int64_t seqlen, int64_t heads,
                      int64_t headdim, int64_t dstate, ss_dtype dtype, hipStream_t stream)
 {
+    return ss_ssd_fwd_ex(x, dt, A, B, C, D, h0, y, h_last, nullptr, 0, batch, seqlen, heads, headdim, dstate, dtype,
+                         stream);
+}
+
+ss_status ss_ssd_fwd_ex(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                        const float* h0, void* y, float* h_last, void* workspace, size_t workspace_bytes,
+                        int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, ss_dtype dtype,
+                        hipStream_t stream)
+{
     if (!x || !dt || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
     if (batch <= 0 || seqlen <= 0 || heads <= 0 || headdim <= 0 || dstate <= 0) return SS_ERR_INVALID_ARG;
     if (dtype != SS_BF16 && dtype != SS_F32) return SS_ERR_UNSUPPORTED;
-    if (dtype != SS_BF16 || headdim != 64 || (dstate != 64 && dstate != 128)) return SS_ERR_UNSUPPORTED;
+    if (dtype != SS_BF16 || headdim != 64 || (dstate != 64 && dstate != 128 && dstate != 256))
+        return SS_ERR_UNSUPPORTED;
     if (batch > kMaxGridYZ || heads > INT32_MAX) return SS_ERR_UNSUPPORTED;
     // the kernel addresses one batch row of x, y (and B, C) with 32-bit byte offsets
     const int64_t row_bytes = 2 * (heads * headdim > dstate ? heads * headdim : dstate);
     if (seqlen > (int64_t(1) << 31) / row_bytes - 1) return SS_ERR_UNSUPPORTED;
+    // at dstate 256 also one batch row of the fp32 parts of y, with the rows a ragged
+    // last chunk reaches past the sequence
+    if (dstate == 256 && seqlen + 64 > (int64_t(1) << 31) / (heads * headdim * 2)) return SS_ERR_UNSUPPORTED;
     int64_t bl, xe, se, he, hs;
     if (!mul(batch, seqlen, &bl) || !mul(bl, heads, &he) || !mul(he, headdim, &xe) || !mul(xe, 2, &xe))
         return SS_ERR_INVALID_ARG;
@@ -655,7 +677,19 @@ ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* 
     if (overlap(r_y, r_hl)) return SS_ERR_INVALID_ARG;
     for (const Range& r : inputs)
         if (overlap(r_y, r) || overlap(r_hl, r)) return SS_ERR_INVALID_ARG;
-    ssk::SsdArgs a{x, dt, A, B, C, D, h0, y, h_last, batch, seqlen, heads, dstate};
+    const size_t need = ss_ssd_workspace_bytes(batch, seqlen, heads, headdim, dstate);
+    if (need == static_cast<size_t>(-1)) return SS_ERR_INVALID_ARG;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return SS_ERR_INVALID_ARG;
+        const Range r_ws = span(workspace, static_cast<int64_t>(need));
+        if (overlap(r_ws, r_y) || overlap(r_ws, r_hl)) return SS_ERR_INVALID_ARG;
+        for (const Range& r : inputs)
+            if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
+        if (ceil_div(xe / 2 / 4, 256) > int64_t(UINT32_MAX)) return SS_ERR_UNSUPPORTED;  // the combining pass
+    }
+    ssk::SsdArgs a{x, dt, A, B, C, D, h0, y, h_last, batch, seqlen, heads, dstate,
+                   need > 0 ? static_cast<float*>(workspace) : nullptr};
     const hipError_t err = ssk::launch_ssd(a, stream);
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;

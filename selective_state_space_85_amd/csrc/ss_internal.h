@@ -146,6 +146,10 @@ struct SsdArgs {
     void* y;           // (batch, seqlen, heads, 64)
     float* h_last;     // (batch, heads, dstate, 64), nullable
     int64_t batch, seqlen, heads, dstate;
+    // dstate 256: two workgroups per (b, h), one per half of the state entries,
+    // each writing its fp32 part of y here (2, batch, seqlen, heads, 64); a
+    // second pass adds the parts into y
+    float* y_part;
 };
 
 // Each returns the hipError_t of its launches (hipSuccess when all were enqueued).

@@ -103,7 +103,13 @@ __device__ __forceinline__ void split4(const float (&v)[4], u32x2& hi, u32x2& lo
 // grid = (heads, batch), block = 256.  Host guarantees bf16 operands, headdim
 // 64, dstate NS, 16-byte alignment of x, y, B, C, and byte extents of one
 // batch row of x (seqlen*heads*128) and of B (seqlen*NS*2) below 2^31.
-template <int NS, bool HAS_D>
+// SPLIT (dstate 2*NS): grid = (heads, batch, 2); workgroup z takes state
+// entries z*NS .. z*NS+NS-1.  The entries evolve independently and y sums over
+// them (the intra-chunk G = B C^T too), so each workgroup runs the NS-entry
+// recurrence on its half of B, C, h0 and h_last and writes its fp32 part of y
+// to a.y_part[z] (without the D term in the second half); the host guarantees
+// one batch row of y_part (seqlen*heads*256 bytes) below 2^31 as well.
+template <int NS, bool HAS_D, bool SPLIT = false>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))) void ssd_kernel(SsdArgs a)
 {
     constexpr int kNB = NS / 32;                    // 32-row blocks of the state (index n)
@@ -128,17 +134,25 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int64_t h = blockIdx.x, b = blockIdx.y;
     const int64_t L = a.seqlen, H = a.heads;
     const float A2 = a.A[h] * kLog2e;
-    const float Dh = HAS_D ? a.D[h] : 0.0f;
+    // the state entries of this workgroup: n0 .. n0+NS-1 of NT
+    constexpr int NT = SPLIT ? 2 * NS : NS;
+    const int half = SPLIT ? int(blockIdx.z) : 0;
+    const int n0 = half * NS;
+    const float Dh = (HAS_D && half == 0) ? a.D[h] : 0.0f;
 
     // range-checked views of this (b, h): row t of x and y at t*H*128 bytes, of
-    // dt at t*H*2, of B and C at t*NS*2.  All offsets go in the vector operand.
-    const uint32_t x_row = uint32_t(H) * kP * 2, dt_row = uint32_t(H) * 2, bc_row = NS * 2;
+    // dt at t*H*2, of B and C at t*NT*2 (from entry n0).  All offsets go in the
+    // vector operand.
+    const uint32_t x_row = uint32_t(H) * kP * 2, dt_row = uint32_t(H) * 2, bc_row = NT * 2;
     const uint32_t x_ext = uint32_t(((L - 1) * H + 1) * kP * 2), dt_ext = uint32_t(((L - 1) * H + 1) * 2);
+    const uint32_t bc_ext = uint32_t(L) * bc_row - uint32_t(n0) * 2;
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(static_cast<const uint16_t*>(a.x) + (b * L * H + h) * kP, x_ext);
-    const __amdgpu_buffer_rsrc_t rY = make_rsrc(static_cast<uint16_t*>(a.y) + (b * L * H + h) * kP, x_ext);
+    const __amdgpu_buffer_rsrc_t rY =
+        SPLIT ? make_rsrc(a.y_part + ((half * a.batch + b) * L * H + h) * kP, 2 * x_ext)
+              : make_rsrc(static_cast<uint16_t*>(a.y) + (b * L * H + h) * kP, x_ext);
     const __amdgpu_buffer_rsrc_t rDT = make_rsrc(static_cast<const uint16_t*>(a.dt) + b * L * H + h, dt_ext);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const uint16_t*>(a.B) + b * L * NS, uint32_t(L) * bc_row);
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<const uint16_t*>(a.C) + b * L * NS, uint32_t(L) * bc_row);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const uint16_t*>(a.B) + b * L * NT + n0, bc_ext);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<const uint16_t*>(a.C) + b * L * NT + n0, bc_ext);
 
     // this wave's blocks: G^T block (s block gs, t block tb), Y^T block (p block
     // yp, t block tb), state blocks (n block, p block) number w*kSPW + j
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 32 * nb + 8 * q + 4 * hl + e;
-                v[e] = a.h0 ? a.h0[((b * H + h) * NS + n) * kP + p] : 0.0f;
+                v[e] = a.h0 ? a.h0[((b * H + h) * NT + n0 + n) * kP + p] : 0.0f;
                 acc_s[j][4 * q + e] = v[e];
             }
             u32x2 hi, lo;
@@ -305,8 +319,14 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     v[2] = fmaf(Dh, bf(xr[1]), v[2]);
                     v[3] = fmaf(Dh, bf_hi(xr[1]), v[3]);
                 }
-                const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-                __builtin_amdgcn_raw_buffer_store_b64(o, rY, yrow + p0 * 2, 0, 0);
+                if constexpr (SPLIT) {
+                    const u32x4 o = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                     __float_as_uint(v[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(o, rY, 2 * yrow + p0 * 4, 0, 0);
+                } else {
+                    const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(o, rY, yrow + p0 * 2, 0, 0);
+                }
             }
         }
         // ---- E: S = exp(cs_end) S + B^T (w x); new LDS copy of S^T ----
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int n = 32 * nb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                a.h_last[((b * H + h) * NS + n) * kP + p] = acc_s[j][r];
+                a.h_last[((b * H + h) * NT + n0 + n) * kP + p] = acc_s[j][r];
             }
         }
     }
@@ -401,11 +421,38 @@ hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+// y = bf16(y_part[0] + y_part[1]), four values per thread (16-byte loads,
+// 8-byte store).  grid = ceil(n / 4 / 256), block = 256; n = batch*seqlen*heads*64.
+__global__ __launch_bounds__(256) void ssd_combine_kernel(SsdArgs a)
+{
+    const int64_t n4 = a.batch * a.seqlen * a.heads * kP / 4;
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 p = reinterpret_cast<const float4*>(a.y_part)[i];
+    const float4 q = reinterpret_cast<const float4*>(a.y_part)[n4 + i];
+    const u32x2 o = {pack_bf16(p.x + q.x, p.y + q.y), pack_bf16(p.z + q.z, p.w + q.w)};
+    reinterpret_cast<u32x2*>(a.y)[i] = o;
+}
+
+// dstate 256: the two halves, then their sum
+hipError_t launch_ssd_split(const SsdArgs& a, hipStream_t s)
+{
+    const dim3 grid(unsigned(a.heads), unsigned(a.batch), 2);
+    if (a.D)
+        ssd_kernel<128, true, true><<<grid, dim3(kSsdThreads), 0, s>>>(a);
+    else
+        ssd_kernel<128, false, true><<<grid, dim3(kSsdThreads), 0, s>>>(a);
+    const int64_t n4 = a.batch * a.seqlen * a.heads * kP / 4;
+    ssd_combine_kernel<<<dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_ssd(const SsdArgs& a, hipStream_t stream)
 {
     (void)hipGetLastError();
+    if (a.dstate == 256) return launch_ssd_split(a, stream);
     return a.dstate == 128 ? launch_ssd_n<128>(a, stream) : launch_ssd_n<64>(a, stream);
 }
 

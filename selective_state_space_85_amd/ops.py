@@ -293,13 +293,14 @@ def conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
 
 def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
             D: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None, *,
-            return_last_state: bool = False, out: Optional[torch.Tensor] = None
-            ) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
-    """Multi-head state-space recurrence ``ss_ssd_fwd`` (bf16, 64 channels per head).
+            return_last_state: bool = False, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+    """Multi-head state-space recurrence ``ss_ssd_fwd_ex`` (bf16, 64 channels per head).
 
-    x (B, L, H, 64), dt (B, L, H), B and C (B, L, N) bfloat16 with N 64 or 128; A, D (H,)
+    x (B, L, H, 64), dt (B, L, H), B and C (B, L, N) bfloat16 with N 64, 128 or 256; A, D (H,)
     float32; h0 (B, H, N, 64) float32.  Returns y (B, L, H, 64) bfloat16 and, if asked,
-    h_last (B, H, N, 64) float32."""
+    h_last (B, H, N, 64) float32.  N = 256 needs ``ssd_workspace_bytes`` of workspace,
+    allocated here when not passed."""
     if x.dim() != 4:
         raise ValueError("x must be (batch, seqlen, heads, headdim)")
     dev = x.device
@@ -319,8 +320,21 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
     y = out if out is not None else torch.empty_like(x)
     _need(y, "out", (nb, nl, nh, hp), dt_, dev)
     hl = torch.empty((nb, nh, ns, hp), dtype=torch.float32, device=dev) if return_last_state else None
+    need = ssd_workspace_bytes(nb, nl, nh, hp, ns)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        st = _lib.load().ss_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
-                                    _ptr(hl), nb, nl, nh, hp, ns, _DTYPES.get(dt_, 99), _stream(dev))
-    _lib.check("ss_ssd_fwd", st)
+        st = _lib.load().ss_ssd_fwd_ex(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+                                       _ptr(hl), _ptr(workspace), ws_bytes, nb, nl, nh, hp, ns,
+                                       _DTYPES.get(dt_, 99), _stream(dev))
+    _lib.check("ss_ssd_fwd_ex", st)
     return (y, hl) if return_last_state else y
+
+
+def ssd_workspace_bytes(batch: int, seqlen: int, heads: int, headdim: int, dstate: int) -> int:
+    """Workspace of ``ss_ssd_fwd_ex`` (0 unless dstate is 256)."""
+    n = _lib.load().ss_ssd_workspace_bytes(batch, seqlen, heads, headdim, dstate)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid multi-head recurrence shape")
+    return int(n)

@@ -403,7 +403,8 @@ def test_ssd_validation(lib):
         assert call_ssd(lib, **{name: 0}) == INVALID, name
     assert call_ssd(lib, dtype=F32) == UNSUPPORTED
     assert call_ssd(lib, hdim=32) == UNSUPPORTED
-    assert call_ssd(lib, dstate=256) == UNSUPPORTED
+    assert call_ssd(lib, dstate=256) == WORKSPACE            # dstate 256 needs ss_ssd_fwd_ex's workspace
+    assert call_ssd(lib, dstate=512) == UNSUPPORTED
     assert call_ssd(lib, batch=70000) == UNSUPPORTED
     # one batch row of x must stay below 2 GiB (32-bit offsets): 64 heads of 64
     # channels allow 262143 rows
@@ -416,3 +417,34 @@ def test_ssd_validation(lib):
     assert call_ssd(lib, y=near(0, 4096)) == INVALID            # y inside x
     assert call_ssd(lib, hl=near(3, 64)) == INVALID             # h_last inside B
     assert call_ssd(lib, hl=near(5, 1024)) == INVALID           # h_last inside y
+
+
+def call_ssd_ex(lib, ws=addr(6), ws_bytes=None, **kw):
+    args = dict(x=addr(0), dt=addr(1), A=addr(2), B=addr(3), C=addr(4), D=None, h0=None, y=addr(5), hl=None,
+                batch=2, seqlen=100, heads=4, hdim=64, dstate=256, dtype=BF16)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.ss_ssd_workspace_bytes(args["batch"], args["seqlen"], args["heads"], args["hdim"],
+                                              args["dstate"])
+    return lib.ss_ssd_fwd_ex(args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"], args["h0"],
+                             args["y"], args["hl"], ws, ws_bytes, args["batch"], args["seqlen"], args["heads"],
+                             args["hdim"], args["dstate"], args["dtype"], None)
+
+
+def test_ssd_workspace(lib):
+    """dstate 256 runs as two halves of the state entries, each writing an fp32 part of y."""
+    assert lib.ss_ssd_workspace_bytes(2, 100, 4, 64, 128) == 0
+    assert lib.ss_ssd_workspace_bytes(2, 100, 4, 64, 64) == 0
+    assert lib.ss_ssd_workspace_bytes(2, 100, 4, 64, 256) == 2 * 2 * 100 * 4 * 64 * 4
+    assert lib.ss_ssd_workspace_bytes(0, 100, 4, 64, 256) == ctypes.c_size_t(-1).value
+    assert lib.ss_ssd_workspace_bytes(2 ** 40, 2 ** 40, 4, 64, 256) == ctypes.c_size_t(-1).value
+    assert call_ssd_ex(lib, ws=None) == WORKSPACE
+    assert call_ssd_ex(lib, ws_bytes=1000) == WORKSPACE
+    assert call_ssd_ex(lib, ws=ctypes.c_void_p(BASE + 6 * GAP + 64)) == INVALID  # not 256-byte aligned
+    near = lambda i, off: ctypes.c_void_p(BASE + i * GAP + off)  # noqa: E731
+    assert call_ssd_ex(lib, ws=near(5, 256)) == INVALID         # workspace inside y
+    assert call_ssd_ex(lib, ws=near(0, 0)) == INVALID           # workspace on x
+    assert call_ssd_ex(lib, dstate=512) == UNSUPPORTED
+    # the fp32 parts of one batch row, with the rows past a ragged last chunk, stay below
+    # 2 GiB: at 64 heads, 262080 rows and not 262081 (dstate 128 allows 262143)
+    assert call_ssd_ex(lib, seqlen=262081, heads=64) == UNSUPPORTED

@@ -36,6 +36,10 @@ CASES = [
     (1, 1, 1, 64, False, True),       # one step
     (2, 257, 4, 128, False, False),   # several chunks, 1-row tail
     (3, 130, 2, 64, True, True),
+    # dstate 256: two workgroups per head, one per half of the state entries
+    (2, 100, 3, 256, True, True),     # ragged last chunk
+    (1, 1, 1, 256, False, True),      # one step
+    (2, 257, 2, 256, False, False),   # several chunks, 1-row tail
 ]
 
 
