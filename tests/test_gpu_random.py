@@ -139,9 +139,9 @@ def test_random_conv_and_step():
 def test_random_ssd():
     rng = np.random.default_rng(2027)
     m = ss()
-    for i in range(6):
+    for i in range(8):
         b, l, h, n = int(rng.integers(1, 3)), int(rng.integers(1, 400)), int(rng.integers(1, 5)), \
-            int(rng.choice([64, 128]))
+            int(rng.choice([64, 128, 256]))
         has_D, has_h0 = bool(i % 2), bool(i % 3)
         inp = wl.ssd_inputs(b, l, h, 64, n, has_D=has_D, has_h0=has_h0, seed=700 + i)
         t = {k: dev(v) for k, v in inp.items()}
