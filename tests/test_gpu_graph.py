@@ -145,17 +145,21 @@ def test_graph_backward():
     replay_and_check(graph, outs, eager, between=call)
 
 
-def test_graph_ssd():
-    """The multi-head recurrence in a graph."""
-    b, l, h, n = 1, 200, 2, 64
+@pytest.mark.parametrize("n", [64, 256])
+def test_graph_ssd(n):
+    """The multi-head recurrence in a graph (at dstate 256: the two halves, the combining pass
+    and a caller workspace)."""
+    b, l, h = 1, 200, 2
     inp = wl.ssd_inputs(b, l, h, 64, n, has_D=True, has_h0=True, seed=914)
     m = ss()
     t = {k: dev(v) for k, v in inp.items()}
+    need = m.ssd_workspace_bytes(b, l, h, 64, n)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     say("graph ssd: B%d L%d H%d N%d" % (b, l, h, n))
 
     def call(y):  # h_last comes from the caller's allocator (the graph's pool when captured)
         return m.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], h0=t["h0"], out=y,
-                         return_last_state=True)
+                         return_last_state=True, workspace=ws)
 
     y_e, hl_e = call(torch.empty_like(t["x"]))
     torch.cuda.synchronize()
