@@ -457,8 +457,8 @@ def main():
                          "mfma_TFLOP/s": sflops / (sms * 1e-3) / 1e12, "frac_of_2.5PF": sflops / (sms * 1e-3) / 2.5e15}
         del stt, sy
 
-        # the same layer at dstate 256: two workgroups per head (one per half of the state
-        # entries) writing fp32 parts of y, then the pass that adds them
+        # the same layer at dstate 256: a launch per half of the state entries, the second
+        # adding the first's fp32 part of y to its own
         si = wl.ssd_inputs(sb, sl, sh, 64, 256, seed=0)
         stt = {k: to_dev(v) for k, v in si.items() if v is not None}
         sy = torch.empty_like(stt["x"])

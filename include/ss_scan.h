@@ -344,9 +344,9 @@ ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* 
 
 /*
  * ss_ssd_workspace_bytes -- device workspace ss_ssd_fwd_ex needs: 0 for dstate
- * 64 and 128; for dstate 256, 2*batch*seqlen*heads*headdim*4 bytes (two fp32
- * parts of y, one per half of the state entries, added by a second pass).
- * (size_t)-1 for sizes <= 0 or overflowing.
+ * 64 and 128; for dstate 256, batch*seqlen*heads*headdim*4 bytes (the fp32
+ * part of y from the first half of the state entries, which the pass over the
+ * second half adds to its own).  (size_t)-1 for sizes <= 0 or overflowing.
  */
 size_t ss_ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate);
 

@@ -628,9 +628,9 @@ size_t ss_ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int6
 {
     if (batch <= 0 || seqlen <= 0 || heads <= 0 || headdim <= 0 || dstate <= 0) return static_cast<size_t>(-1);
     int64_t n;
-    if (!mul(batch, seqlen, &n) || !mul(n, heads, &n) || !mul(n, headdim, &n) || !mul(n, 8, &n))
+    if (!mul(batch, seqlen, &n) || !mul(n, heads, &n) || !mul(n, headdim, &n) || !mul(n, 4, &n))
         return static_cast<size_t>(-1);
-    return dstate == 256 ? static_cast<size_t>(n) : 0;  // two fp32 parts of y at dstate 256
+    return dstate == 256 ? static_cast<size_t>(n) : 0;  // the first half's fp32 part of y at dstate 256
 }
 
 ss_status ss_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
@@ -686,7 +686,6 @@ ss_status ss_ssd_fwd_ex(const void* x, const void* dt, const float* A, const voi
         if (overlap(r_ws, r_y) || overlap(r_ws, r_hl)) return SS_ERR_INVALID_ARG;
         for (const Range& r : inputs)
             if (overlap(r_ws, r)) return SS_ERR_INVALID_ARG;
-        if (ceil_div(xe / 2 / 4, 256) > int64_t(UINT32_MAX)) return SS_ERR_UNSUPPORTED;  // the combining pass
     }
     ssk::SsdArgs a{x, dt, A, B, C, D, h0, y, h_last, batch, seqlen, heads, dstate,
                    need > 0 ? static_cast<float*>(workspace) : nullptr};

@@ -146,9 +146,8 @@ struct SsdArgs {
     void* y;           // (batch, seqlen, heads, 64)
     float* h_last;     // (batch, heads, dstate, 64), nullable
     int64_t batch, seqlen, heads, dstate;
-    // dstate 256: two workgroups per (b, h), one per half of the state entries,
-    // each writing its fp32 part of y here (2, batch, seqlen, heads, 64); a
-    // second pass adds the parts into y
+    // dstate 256: the first half of the state entries' fp32 part of y (batch,
+    // seqlen, heads, 64), which the launch for the second half adds to its own
     float* y_part;
 };
 

@@ -103,13 +103,14 @@ __device__ __forceinline__ void split4(const float (&v)[4], u32x2& hi, u32x2& lo
 // grid = (heads, batch), block = 256.  Host guarantees bf16 operands, headdim
 // 64, dstate NS, 16-byte alignment of x, y, B, C, and byte extents of one
 // batch row of x (seqlen*heads*128) and of B (seqlen*NS*2) below 2^31.
-// SPLIT (dstate 2*NS): grid = (heads, batch, 2); workgroup z takes state
-// entries z*NS .. z*NS+NS-1.  The entries evolve independently and y sums over
-// them (the intra-chunk G = B C^T too), so each workgroup runs the NS-entry
-// recurrence on its half of B, C, h0 and h_last and writes its fp32 part of y
-// to a.y_part[z] (without the D term in the second half); the host guarantees
-// one batch row of y_part (seqlen*heads*256 bytes) below 2^31 as well.
-template <int NS, bool HAS_D, bool SPLIT = false>
+// SPLIT (dstate 2*NS) runs the kernel twice.  The state entries evolve
+// independently and y sums over them (the intra-chunk G = B C^T too), so each
+// launch runs the NS-entry recurrence on its half of B, C, h0 and h_last:
+// SPLIT = 1 takes entries 0..NS-1 and writes its fp32 part of y, with the D
+// term, to a.y_part; SPLIT = 2 takes entries NS..2NS-1, adds the first part to
+// its own and writes y.  The host guarantees one batch row of y_part
+// (seqlen*heads*256 bytes, with the rows a ragged last chunk reaches) below 2^31.
+template <int NS, bool HAS_D, int SPLIT = 0>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))) void ssd_kernel(SsdArgs a)
 {
     constexpr int kNB = NS / 32;                    // 32-row blocks of the state (index n)
@@ -136,9 +137,8 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const float A2 = a.A[h] * kLog2e;
     // the state entries of this workgroup: n0 .. n0+NS-1 of NT
     constexpr int NT = SPLIT ? 2 * NS : NS;
-    const int half = SPLIT ? int(blockIdx.z) : 0;
-    const int n0 = half * NS;
-    const float Dh = (HAS_D && half == 0) ? a.D[h] : 0.0f;
+    constexpr int n0 = SPLIT == 2 ? NS : 0;
+    const float Dh = HAS_D ? a.D[h] : 0.0f;
 
     // range-checked views of this (b, h): row t of x and y at t*H*128 bytes, of
     // dt at t*H*2, of B and C at t*NT*2 (from entry n0).  All offsets go in the
@@ -147,9 +147,11 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const uint32_t x_ext = uint32_t(((L - 1) * H + 1) * kP * 2), dt_ext = uint32_t(((L - 1) * H + 1) * 2);
     const uint32_t bc_ext = uint32_t(L) * bc_row - uint32_t(n0) * 2;
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(static_cast<const uint16_t*>(a.x) + (b * L * H + h) * kP, x_ext);
-    const __amdgpu_buffer_rsrc_t rY =
-        SPLIT ? make_rsrc(a.y_part + ((half * a.batch + b) * L * H + h) * kP, 2 * x_ext)
-              : make_rsrc(static_cast<uint16_t*>(a.y) + (b * L * H + h) * kP, x_ext);
+    const __amdgpu_buffer_rsrc_t rY = SPLIT == 1
+                                          ? make_rsrc(a.y_part + (b * L * H + h) * kP, 2 * x_ext)
+                                          : make_rsrc(static_cast<uint16_t*>(a.y) + (b * L * H + h) * kP, x_ext);
+    // the first half's fp32 part of y (read by the second half)
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(SPLIT == 2 ? a.y_part + (b * L * H + h) * kP : nullptr, 2 * x_ext);
     const __amdgpu_buffer_rsrc_t rDT = make_rsrc(static_cast<const uint16_t*>(a.dt) + b * L * H + h, dt_ext);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const uint16_t*>(a.B) + b * L * NT + n0, bc_ext);
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(static_cast<const uint16_t*>(a.C) + b * L * NT + n0, bc_ext);
@@ -294,6 +296,14 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
         // ---- C: Y^T += X^T M^T, + D x; store ----
         {
+            // the second half adds the first half's part: loaded now, used at the store
+            u32x4 part[4];
+            if constexpr (SPLIT == 2) {
+                const uint32_t prow = 2 * (t0 + 32 * tb + l32) * x_row;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    part[q] = __builtin_amdgcn_raw_buffer_load_b128(rP, prow + (32 * yp + 8 * q + 4 * hl) * 4, 0, 0);
+            }
             const int ks_end = tb == 0 ? 2 : 4;  // M[t][s] = 0 for s > t
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_l[r] = 0.0f;
@@ -312,6 +322,10 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc_y[4 * q + e] + acc_l[4 * q + e];
+                if constexpr (SPLIT == 2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(part[q][e]);
+                }
                 if (HAS_D) {
                     const u32x2 xr = *reinterpret_cast<const u32x2*>(&sX[t][p0]);
                     v[0] = fmaf(Dh, bf(xr[0]), v[0]);
@@ -319,7 +333,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     v[2] = fmaf(Dh, bf(xr[1]), v[2]);
                     v[3] = fmaf(Dh, bf_hi(xr[1]), v[3]);
                 }
-                if constexpr (SPLIT) {
+                if constexpr (SPLIT == 1) {
                     const u32x4 o = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                                      __float_as_uint(v[3])};
                     __builtin_amdgcn_raw_buffer_store_b128(o, rY, 2 * yrow + p0 * 4, 0, 0);
@@ -421,29 +435,15 @@ hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-// y = bf16(y_part[0] + y_part[1]), four values per thread (16-byte loads,
-// 8-byte store).  grid = ceil(n / 4 / 256), block = 256; n = batch*seqlen*heads*64.
-__global__ __launch_bounds__(256) void ssd_combine_kernel(SsdArgs a)
-{
-    const int64_t n4 = a.batch * a.seqlen * a.heads * kP / 4;
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= n4) return;
-    const float4 p = reinterpret_cast<const float4*>(a.y_part)[i];
-    const float4 q = reinterpret_cast<const float4*>(a.y_part)[n4 + i];
-    const u32x2 o = {pack_bf16(p.x + q.x, p.y + q.y), pack_bf16(p.z + q.z, p.w + q.w)};
-    reinterpret_cast<u32x2*>(a.y)[i] = o;
-}
-
-// dstate 256: the two halves, then their sum
+// dstate 256: the first half, then the second, which adds the first's part of y
 hipError_t launch_ssd_split(const SsdArgs& a, hipStream_t s)
 {
-    const dim3 grid(unsigned(a.heads), unsigned(a.batch), 2);
+    const dim3 grid(unsigned(a.heads), unsigned(a.batch));
     if (a.D)
-        ssd_kernel<128, true, true><<<grid, dim3(kSsdThreads), 0, s>>>(a);
+        ssd_kernel<128, true, 1><<<grid, dim3(kSsdThreads), 0, s>>>(a);
     else
-        ssd_kernel<128, false, true><<<grid, dim3(kSsdThreads), 0, s>>>(a);
-    const int64_t n4 = a.batch * a.seqlen * a.heads * kP / 4;
-    ssd_combine_kernel<<<dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, s>>>(a);
+        ssd_kernel<128, false, 1><<<grid, dim3(kSsdThreads), 0, s>>>(a);
+    ssd_kernel<128, false, 2><<<grid, dim3(kSsdThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -432,10 +432,10 @@ def call_ssd_ex(lib, ws=addr(6), ws_bytes=None, **kw):
 
 
 def test_ssd_workspace(lib):
-    """dstate 256 runs as two halves of the state entries, each writing an fp32 part of y."""
+    """dstate 256 runs as two halves of the state entries; the first writes an fp32 part of y."""
     assert lib.ss_ssd_workspace_bytes(2, 100, 4, 64, 128) == 0
     assert lib.ss_ssd_workspace_bytes(2, 100, 4, 64, 64) == 0
-    assert lib.ss_ssd_workspace_bytes(2, 100, 4, 64, 256) == 2 * 2 * 100 * 4 * 64 * 4
+    assert lib.ss_ssd_workspace_bytes(2, 100, 4, 64, 256) == 2 * 100 * 4 * 64 * 4
     assert lib.ss_ssd_workspace_bytes(0, 100, 4, 64, 256) == ctypes.c_size_t(-1).value
     assert lib.ss_ssd_workspace_bytes(2 ** 40, 2 ** 40, 4, 64, 256) == ctypes.c_size_t(-1).value
     assert call_ssd_ex(lib, ws=None) == WORKSPACE
