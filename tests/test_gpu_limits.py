@@ -115,12 +115,19 @@ def bf16_bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def test_ssd_at_the_row_slab_limit():
+@pytest.mark.parametrize("nn", [64, 256])
+def test_ssd_at_the_row_slab_limit(nn):
     """The multi-head recurrence with one batch row of x just under 2 GiB: 256 heads of 64
-    channels, L = 65535 (the longest the library accepts at this width), bf16, dstate 64;
-    the oracle checks the first and the last head over the whole sequence."""
-    nl, nh, nn = 65535, 256, 64
-    assert 0 < 2 ** 31 - nl * nh * 64 * 2 < 2 ** 16
+    channels, bf16, L the longest the library accepts at this width: 65535 at dstate 64;
+    65472 at dstate 256, where the fp32 part of y (twice the bytes of y, with the rows a
+    ragged last chunk reaches) must stay below 2^32.  The oracle checks the first and the
+    last head over the whole sequence."""
+    nh = 256
+    nl = 65535 if nn == 64 else 65472
+    if nn == 64:
+        assert 0 < 2 ** 31 - nl * nh * 64 * 2 < 2 ** 16   # x within 64 KB of 2 GiB
+    else:
+        assert 2 * (nl + 63) * nh * 128 < 2 ** 32 <= 2 * (nl + 64 + 63) * nh * 128
     g = torch.Generator(device="cuda").manual_seed(1204)
     x = torch.randn(1, nl, nh, 64, device="cuda", generator=g).to(torch.bfloat16)
     dt = torch.nn.functional.softplus(torch.randn(1, nl, nh, device="cuda", generator=g) - 2.0).to(torch.bfloat16)
