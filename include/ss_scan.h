@@ -73,25 +73,36 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 typedef enum { SS_DELTA_SOFTPLUS = 1, SS_B_ZOH = 2 } ss_option;
 
 /*
- * ss_scan_plan -- how ss_scan_fwd splits the sequence axis.
+ * ss_scan_plan -- how ss_scan_fwd splits the sequence axis for this shape.
  *
- * The scan is cut into n_chunks = ceil(seqlen / chunk_len) chunks; chunk c
- * covers timesteps [c*chunk_len, min((c+1)*chunk_len, seqlen)).  Chunks are
- * joined by an exact associative combine of affine pairs (LTI chapter 3.1,
- * section 3.1.5.2, parallel scan over an associative operator):
+ * The scan is cut into n_chunks_K = ceil(seqlen / chunk_len_T) chunks; chunk c
+ * covers timesteps [c*chunk_len_T, min((c+1)*chunk_len_T, seqlen)).  Chunks
+ * are joined by an exact associative combine of affine pairs (LTI chapter
+ * 3.1, section 3.1.5.2, parallel scan over an associative operator):
  * (a1, b1) then (a2, b2) gives (a2*a1, a2*b1 + b2).
  *
- * chunk_len_request: 0 lets the library choose (a power of two, from the
- * shape only: pure, host-only, deterministic); a positive value forces that
- * chunk length.  Writes *chunk_len and *n_chunks (either may be NULL).
- * Returns SS_ERR_INVALID_ARG for sizes <= 0 or a negative request.
+ * The chunk length is a power of two chosen from the shape only: pure,
+ * host-only, deterministic.  Writes *chunk_len_T and *n_chunks_K (either may
+ * be NULL).  Returns SS_ERR_INVALID_ARG for sizes <= 0 or sizes whose element
+ * counts overflow int64.
  */
 ss_status ss_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                       int64_t chunk_len_request, int64_t* chunk_len, int64_t* n_chunks);
+                       int64_t* chunk_len_T, int64_t* n_chunks_K);
+
+/*
+ * ss_scan_plan_ex -- ss_scan_plan with a chunk length request:
+ * chunk_len_request 0 is ss_scan_plan's choice; a positive value forces that
+ * chunk length (any value >= 1, not only powers of two); a negative one is
+ * SS_ERR_INVALID_ARG.  This is the plan ss_scan_fwd_ex and ss_scan_fwd_ckpt
+ * use for the same request.
+ */
+ss_status ss_scan_plan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                          int64_t chunk_len_request, int64_t* chunk_len_T, int64_t* n_chunks_K);
 
 /*
  * ss_scan_workspace_bytes -- device workspace ss_scan_fwd needs for this
- * shape and chunk request ((size_t)-1 for invalid sizes).  Always > 0.
+ * shape ((size_t)-1 for invalid sizes).  Always > 0: even a one-chunk plan
+ * needs the fp32 copy of B and C described below.
  *
  * Workspace layout (fp32 words, K = n_chunks, BD = batch*dim, N = dstate),
  * valid after the call completes:
@@ -107,8 +118,16 @@ ss_status ss_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
  *                          and zero-padded past each chunk's end; its
  *                          arrangement is internal to the library.
  */
-size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                               int64_t chunk_len_request);
+size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * ss_scan_workspace_bytes_ex -- the workspace of ss_scan_fwd_ex and
+ * ss_scan_fwd_ckpt for a chunk length request (as ss_scan_plan_ex; 0 gives
+ * ss_scan_workspace_bytes).  (size_t)-1 for invalid sizes or a negative
+ * request.  Same layout.
+ */
+size_t ss_scan_workspace_bytes_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                  int64_t chunk_len_request);
 
 /*
  * ss_scan_fwd -- the selective scan over full sequences (Mamba walk-through,
@@ -124,9 +143,10 @@ size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64
  *   y           : (batch, seqlen, dim)   dtype      output
  *   h_last      : (batch, dim, dstate)   fp32       output, state after the
  *                                                   last timestep (NULL: not written)
- *   workspace   : ss_scan_workspace_bytes(...) bytes of device memory
- *   chunk_len_request : as for ss_scan_plan (0 = library's choice)
+ *   workspace   : ss_scan_workspace_bytes(...) bytes of device memory,
+ *                 256-byte aligned, caller-owned (contents on entry unused)
  *
+ * The sequence is split as ss_scan_plan says.
  * y must not overlap any other tensor; h_last must not overlap any input
  * except that it may be exactly h0 (in-place continuation of a state).  The
  * workspace must not overlap any tensor.  dstate must be 16.
@@ -136,15 +156,19 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
                       void* y, float* h_last,
                       void* workspace, size_t workspace_bytes,
                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                      int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
+                      ss_dtype dtype, hipStream_t stream);
 
 /*
- * ss_scan_fwd_ex -- ss_scan_fwd with the step-size and input-term options:
+ * ss_scan_fwd_ex -- ss_scan_fwd with the step-size and input-term options and
+ * a chunk length request:
  *   delta_bias : (dim,) fp32, 4-byte aligned, or NULL (no bias); an input, so
  *                y and h_last must not overlap it
  *   options    : SS_DELTA_SOFTPLUS and/or SS_B_ZOH (see ss_option)
+ *   chunk_len_request : as for ss_scan_plan_ex (0 = ss_scan_plan's choice);
+ *                the workspace is then ss_scan_workspace_bytes_ex(...) bytes
  * Every other argument, the validation and the errors are as for ss_scan_fwd,
- * which is ss_scan_fwd_ex with delta_bias = NULL and options = 0.
+ * which is ss_scan_fwd_ex with delta_bias = NULL, options = 0 and
+ * chunk_len_request = 0.
  */
 ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
                          const float* Dskip, const void* z, const float* h0,

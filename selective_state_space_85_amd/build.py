@@ -5,8 +5,11 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,28 +20,44 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 (v_pk_*_f32) is switched off for all device code.
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source into LIB_PATH (always recompiles)."""
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + list(extra_flags or []) + ["-o", tmp] + SOURCES
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
         raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (res.returncode, res.stdout, res.stderr))
     if verbose and res.stderr.strip():
         print(res.stderr, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+
+
+def build(verbose: bool = False, extra_flags=None, sources=None, out=None) -> str:
+    """Compile every HIP source (one hipcc per source, in parallel) and link them into
+    LIB_PATH (always recompiles)."""
+    sources = list(sources or SOURCES)
+    out = out or LIB_PATH
+    flags = FLAGS + list(extra_flags or [])
+    tmpdir = tempfile.mkdtemp(prefix="ssbuild")
+    tmp = out + ".tmp%d" % os.getpid()
+    try:
+        objs = [os.path.join(tmpdir, "%d_%s.o" % (i, os.path.basename(src))) for i, src in enumerate(sources)]
+        jobs = max(1, min(len(sources), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(jobs) as pool:
+            list(pool.map(lambda so: _run([HIPCC] + flags + ["-c", so[0], "-o", so[1]], verbose),
+                          zip(sources, objs)))
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        os.replace(tmp, out)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
+        if os.path.exists(tmp):
+            os.remove(tmp)
+    return out
 
 
 if __name__ == "__main__":

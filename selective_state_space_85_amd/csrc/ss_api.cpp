@@ -207,20 +207,26 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
 
 extern "C" {
 
-ss_status ss_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t chunk_len_request,
-                       int64_t* chunk_len, int64_t* n_chunks)
+ss_status ss_scan_plan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t chunk_len_request,
+                          int64_t* chunk_len_T, int64_t* n_chunks_K)
 {
     Sizes s;
     if (!shape_sizes(batch, seqlen, dim, dstate, &s)) return SS_ERR_INVALID_ARG;
     int64_t T, K;
     if (!plan(batch, seqlen, dim, chunk_len_request, &T, &K)) return SS_ERR_INVALID_ARG;
-    if (chunk_len) *chunk_len = T;
-    if (n_chunks) *n_chunks = K;
+    if (chunk_len_T) *chunk_len_T = T;
+    if (n_chunks_K) *n_chunks_K = K;
     return SS_OK;
 }
 
-size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                               int64_t chunk_len_request)
+ss_status ss_scan_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t* chunk_len_T,
+                       int64_t* n_chunks_K)
+{
+    return ss_scan_plan_ex(batch, seqlen, dim, dstate, 0, chunk_len_T, n_chunks_K);
+}
+
+size_t ss_scan_workspace_bytes_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                  int64_t chunk_len_request)
 {
     Sizes s;
     int64_t T, K;
@@ -231,13 +237,18 @@ size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64
     return static_cast<size_t>(wl.total);
 }
 
+size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate)
+{
+    return ss_scan_workspace_bytes_ex(batch, seqlen, dim, dstate, 0);
+}
+
 ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                       const float* Dskip, const void* z, const float* h0, void* y, float* h_last,
                       void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
-                      int64_t dstate, int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream)
+                      int64_t dstate, ss_dtype dtype, hipStream_t stream)
 {
     return ss_scan_fwd_ex(u, delta, A, B, C, Dskip, z, h0, nullptr, 0u, y, h_last, workspace, workspace_bytes,
-                          batch, seqlen, dim, dstate, chunk_len_request, dtype, stream);
+                          batch, seqlen, dim, dstate, 0, dtype, stream);
 }
 
 ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,

@@ -36,11 +36,16 @@ def _need(t: torch.Tensor, name: str, shape, dtype, device) -> None:
 
 
 def scan_plan(batch: int, seqlen: int, dim: int, dstate: int, chunk_len: int = 0) -> Tuple[int, int]:
-    """(chunk_len, n_chunks) that ``ss_scan_fwd`` uses for this shape."""
+    """(chunk_len, n_chunks) that ``ss_scan_fwd`` uses for this shape (``ss_scan_plan``), or,
+    with a ``chunk_len`` request, ``ss_scan_fwd_ex`` (``ss_scan_plan_ex``)."""
     T = ctypes.c_int64()
     K = ctypes.c_int64()
-    _lib.check("ss_scan_plan", _lib.load().ss_scan_plan(batch, seqlen, dim, dstate, chunk_len,
-                                                         ctypes.byref(T), ctypes.byref(K)))
+    lib = _lib.load()
+    if chunk_len == 0:
+        _lib.check("ss_scan_plan", lib.ss_scan_plan(batch, seqlen, dim, dstate, ctypes.byref(T), ctypes.byref(K)))
+    else:
+        _lib.check("ss_scan_plan_ex", lib.ss_scan_plan_ex(batch, seqlen, dim, dstate, chunk_len,
+                                                          ctypes.byref(T), ctypes.byref(K)))
     return T.value, K.value
 
 
@@ -49,7 +54,13 @@ def _options(delta_softplus: bool, zoh: bool) -> int:
 
 
 def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, chunk_len: int = 0) -> int:
-    n = _lib.load().ss_scan_workspace_bytes(batch, seqlen, dim, dstate, chunk_len)
+    """Workspace bytes of ``ss_scan_fwd`` (``ss_scan_workspace_bytes``), or for a ``chunk_len``
+    request ``ss_scan_workspace_bytes_ex``."""
+    lib = _lib.load()
+    if chunk_len == 0:
+        n = lib.ss_scan_workspace_bytes(batch, seqlen, dim, dstate)
+    else:
+        n = lib.ss_scan_workspace_bytes_ex(batch, seqlen, dim, dstate, chunk_len)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid scan shape")
     return int(n)
@@ -62,7 +73,8 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              h_last: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
              delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False,
              ckpt: Optional[torch.Tensor] = None) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
-    """Selective scan ``ss_scan_fwd_ex`` on device tensors; with ``ckpt`` (a float32 tensor of
+    """Selective scan on device tensors: ``ss_scan_fwd``, or ``ss_scan_fwd_ex`` when a step-size
+    or input-term option or a ``chunk_len`` request is given; with ``ckpt`` (a float32 tensor of
     ``scan_ckpt_shape(B, L, D, N)``) it is ``ss_scan_fwd_ckpt``, which also writes there the
     state entering every 16th timestep for ``scan_bwd(..., ckpt=ckpt)``.
 
@@ -112,7 +124,11 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     lib = _lib.load()
     with torch.cuda.device(dev):
-        if ckpt is None:
+        if ckpt is None and delta_bias is None and not delta_softplus and not zoh and chunk_len == 0:
+            name = "ss_scan_fwd"
+            st = lib.ss_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                 _ptr(y), _ptr(hl), _ptr(ws), ws_bytes, nb, nl, nd, nn, _DTYPES[dt], _stream(dev))
+        elif ckpt is None:
             name = "ss_scan_fwd_ex"
             st = lib.ss_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                                     _ptr(delta_bias), _options(delta_softplus, zoh), _ptr(y), _ptr(hl),

@@ -40,6 +40,63 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), "libssscan.so does not export %s" % name
 
 
+# The scan and step entry points and their helpers, as types in declaration order.  The scan's
+# operands follow the pages' selective_scan(x, delta, A, B, C) (Mamba walk-through, section 3.3;
+# shapes of the LTI chapter, section 0.4.2), then the D skip and gate of the Mamba block
+# (section 3.4), the initial and last state, the caller's workspace, the sizes, dtype and stream.
+BOUNDARY = {
+    "ss_scan_workspace_bytes": ("size_t", ["int64_t"] * 4),
+    "ss_scan_plan": ("ss_status", ["int64_t"] * 4 + ["int64_t*", "int64_t*"]),
+    "ss_scan_fwd": ("ss_status", ["const void*", "const void*", "const float*", "const void*", "const void*",
+                                  "const float*", "const void*", "const float*", "void*", "float*",
+                                  "void*", "size_t"] + ["int64_t"] * 4 + ["ss_dtype", "hipStream_t"]),
+    "ss_step": ("ss_status", ["float*", "const void*", "const void*", "const float*", "const void*",
+                              "const void*", "const float*", "const void*", "void*"] + ["int64_t"] * 3
+                + ["ss_dtype", "hipStream_t"]),
+    "ss_status_string": ("const char*", ["ss_status"]),
+    "ss_last_hip_error": ("int", []),
+}
+
+
+def header_prototypes():
+    """name -> (return type, [parameter types]) for every ss_* function in the header."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    out = {}
+    for m in re.finditer(r"((?:const\s+)?\w+\s*\**)\s*(ss_\w+)\s*\(([^)]*)\)\s*;", text):
+        ret = re.sub(r"\s+", "", m.group(1)).replace("const", "const ")
+        params = []
+        for p in m.group(3).split(","):
+            p = " ".join(p.split())
+            if p in ("void", ""):
+                continue
+            p = re.sub(r"\s*\*\s*", "* ", p).strip()
+            toks = p.split()
+            if len(toks) > 1 and not toks[-1].endswith("*"):
+                toks = toks[:-1]  # drop the parameter name
+            params.append(" ".join(toks).replace("* ", "*").replace(" *", "*"))
+        out[m.group(2)] = (ret, params)
+    return out
+
+
+def test_boundary_prototypes():
+    """The six calls of the boundary carry exactly these parameter lists; the chunk request and
+    the options live on the _ex forms."""
+    protos = header_prototypes()
+    for name, want in BOUNDARY.items():
+        assert name in protos, name
+        assert protos[name] == want, (name, protos[name], want)
+    assert protos["ss_scan_plan_ex"][1] == ["int64_t"] * 5 + ["int64_t*", "int64_t*"]
+    assert protos["ss_scan_workspace_bytes_ex"][1] == ["int64_t"] * 5
+    ex = protos["ss_scan_fwd_ex"][1]
+    assert ex[:8] == BOUNDARY["ss_scan_fwd"][1][:8] and ex[8:10] == ["const float*", "uint32_t"]
+    text = open(HEADER).read()
+    for enum in ("SS_OK = 0", "SS_ERR_INVALID_ARG = 1", "SS_ERR_UNSUPPORTED = 2", "SS_ERR_WORKSPACE = 3",
+                 "SS_ERR_HIP = 4", "SS_F32 = 0", "SS_BF16 = 1"):
+        assert enum in text, enum
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert lib.ss_status_string(s).decode().startswith("SS_")
@@ -48,10 +105,25 @@ def test_status_strings(lib):
 
 
 def plan(lib, b, l, d, n, req=0):
+    """ss_scan_plan for req == 0, ss_scan_plan_ex otherwise (which must agree at req == 0)."""
     T = ctypes.c_int64()
     K = ctypes.c_int64()
-    st = lib.ss_scan_plan(b, l, d, n, req, ctypes.byref(T), ctypes.byref(K))
+    T2 = ctypes.c_int64()
+    K2 = ctypes.c_int64()
+    st2 = lib.ss_scan_plan_ex(b, l, d, n, req, ctypes.byref(T2), ctypes.byref(K2))
+    if req != 0:
+        return st2, T2.value, K2.value
+    st = lib.ss_scan_plan(b, l, d, n, ctypes.byref(T), ctypes.byref(K))
+    assert (st, T.value, K.value) == (st2, T2.value, K2.value)
     return st, T.value, K.value
+
+
+def ws_bytes(lib, b, l, d, n, req=0):
+    """ss_scan_workspace_bytes for req == 0 (checked against the _ex form), else the _ex form."""
+    ex = lib.ss_scan_workspace_bytes_ex(b, l, d, n, req)
+    if req == 0:
+        assert lib.ss_scan_workspace_bytes(b, l, d, n) == ex
+    return ex
 
 
 @pytest.mark.parametrize("shape", [(1, 256, 64, 16), (2, 2048, 1536, 16), (8, 2048, 5120, 16),
@@ -68,7 +140,7 @@ def test_auto_plan_invariants(lib, shape):
     bounds = [(c * T, min(c * T + T, l)) for c in range(K)]
     assert bounds[0][0] == 0 and bounds[-1][1] == l
     assert all(a1 == b0 for (_, a1), (b0, _) in zip(bounds, bounds[1:]))
-    check_workspace_size(lib.ss_scan_workspace_bytes(b, l, d, n, 0), b, l, d, n, T, K)
+    check_workspace_size(ws_bytes(lib, b, l, d, n), b, l, d, n, T, K)
 
 
 def check_workspace_size(ws, b, l, d, n, T, K):
@@ -106,8 +178,9 @@ def test_forced_plan(lib):
     assert plan(lib, 1, 10, 64, 16, -1)[0] == INVALID
     assert plan(lib, 0, 10, 64, 16)[0] == INVALID
     assert plan(lib, 1, 10, 0, 16)[0] == INVALID
-    assert lib.ss_scan_workspace_bytes(1, 10, 0, 16, 0) == ctypes.c_size_t(-1).value
-    assert lib.ss_scan_workspace_bytes(2 ** 40, 2 ** 40, 16, 16, 0) == ctypes.c_size_t(-1).value
+    assert ws_bytes(lib, 1, 10, 0, 16) == ctypes.c_size_t(-1).value
+    assert ws_bytes(lib, 2 ** 40, 2 ** 40, 16, 16) == ctypes.c_size_t(-1).value
+    assert ws_bytes(lib, 1, 10, 64, 16, -1) == ctypes.c_size_t(-1).value
 
 
 # fake, 256-byte aligned device addresses spaced far apart
@@ -124,10 +197,18 @@ def call_scan(lib, **kw):
                 y=addr(5), h_last=None, ws=addr(6), ws_bytes=1 << 40, batch=2, seqlen=512, dim=64,
                 dstate=16, chunk=0, dtype=BF16)
     args.update(kw)
-    return lib.ss_scan_fwd(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
-                           args["h0"], args["y"], args["h_last"], args["ws"], args["ws_bytes"],
-                           args["batch"], args["seqlen"], args["dim"], args["dstate"], args["chunk"],
-                           args["dtype"], None)
+    ex = lib.ss_scan_fwd_ex(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                            args["h0"], None, 0, args["y"], args["h_last"], args["ws"], args["ws_bytes"],
+                            args["batch"], args["seqlen"], args["dim"], args["dstate"], args["chunk"],
+                            args["dtype"], None)
+    if args["chunk"] != 0:
+        return ex
+    # without a chunk request the plain entry point must decide the same way
+    st = lib.ss_scan_fwd(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                         args["h0"], args["y"], args["h_last"], args["ws"], args["ws_bytes"],
+                         args["batch"], args["seqlen"], args["dim"], args["dstate"], args["dtype"], None)
+    assert st == ex
+    return st
 
 
 def test_scan_rejects_null_and_sizes(lib):
@@ -174,14 +255,14 @@ def test_scan_rejects_overlaps(lib):
 def test_scan_workspace_checks(lib):
     st, T, K = plan(lib, 2, 512, 64, 16, 128)
     assert K == 4
-    need = lib.ss_scan_workspace_bytes(2, 512, 64, 16, 128)
+    need = ws_bytes(lib, 2, 512, 64, 16, 128)
     check_workspace_size(need, 2, 512, 64, 16, T, K)
     assert call_scan(lib, chunk=128, ws=None) == WORKSPACE
     assert call_scan(lib, chunk=128, ws_bytes=need - 1) == WORKSPACE
     # a single-chunk plan needs a workspace too (the B/C copy)
     st, T1, K1 = plan(lib, 2, 50, 64, 16, 0)
     assert K1 == 1
-    need1 = lib.ss_scan_workspace_bytes(2, 50, 64, 16, 0)
+    need1 = ws_bytes(lib, 2, 50, 64, 16)
     check_workspace_size(need1, 2, 50, 64, 16, T1, K1)
     assert call_scan(lib, seqlen=50, ws=None) == WORKSPACE
     assert call_scan(lib, seqlen=50, ws_bytes=need1 - 1) == WORKSPACE
