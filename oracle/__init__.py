@@ -59,14 +59,14 @@ class OracleLib:
         lib.oracle_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, i64,
                                     vp, i64, vp, vp, vp, i64, vp, ip]
         lib.oracle_scan.restype = ctypes.c_int
-        lib.oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, vp, i64, vp]
+        lib.oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, vp, i64, vp, ip]
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, i64, i64, i64, i64,
                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip]
         lib.oracle_scan_bwd.restype = ctypes.c_int
         lib.oracle_conv1d_silu.argtypes = [vp, i64, vp, vp, ip, i64, i64, i64, i64, vp]
         lib.oracle_conv1d_silu.restype = ctypes.c_int
-        lib.oracle_ssd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, i64, i64, vp, i64, vp, vp]
+        lib.oracle_ssd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, i64, i64, vp, i64, vp, vp, ip]
         lib.oracle_ssd.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -172,9 +172,10 @@ def scan(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.n
 def step(h: np.ndarray, u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray,
          C: np.ndarray, D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
          lanes: Optional[Sequence[int]] = None, *, delta_bias: Optional[np.ndarray] = None,
-         delta_softplus: bool = False, zoh: bool = False, _lib=None) -> np.ndarray:
+         delta_softplus: bool = False, zoh: bool = False, threads: int = 1, _lib=None) -> np.ndarray:
     """One recurrent token.  h: float64 (B,D,N), or (n_lanes, N) with ``lanes``; updated
-    in place.  u, delta, z: (B,D); B, C: (B,N).  Returns y float64 (B,D) / (n_lanes,)."""
+    in place.  u, delta, z: (B,D); B, C: (B,N).  Returns y float64 (B,D) / (n_lanes,).
+    ``threads`` > 1 splits the lanes over threads (bit-identical results)."""
     lib = _lib or _load()
     if h.dtype != np.float64 or not h.flags.c_contiguous:
         raise TypeError("h must be a C-contiguous float64 array (updated in place)")
@@ -191,7 +192,8 @@ def step(h: np.ndarray, u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.n
         raise ValueError("h has %d values, expected %d" % (h.size, n_lanes * dstate))
     y = np.empty(n_lanes, dtype=np.float64)
     rc = lib.oracle_step(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                         _ptr(bias), _flags(delta_softplus, zoh), dt, batch, dim, dstate, _ptr(lane_arr), n_lanes, _ptr(y))
+                         _ptr(bias), _flags(delta_softplus, zoh), dt, batch, dim, dstate, _ptr(lane_arr), n_lanes, _ptr(y),
+                         int(threads))
     if rc != 0:
         raise ValueError("oracle_step rejected its arguments")
     return y.reshape(batch, dim) if lane_arr is None else y
@@ -275,10 +277,11 @@ def conv1d_silu(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray] = 
 
 def ssd(x: np.ndarray, dt: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
         D: Optional[np.ndarray] = None, h0: Optional[np.ndarray] = None,
-        heads: Optional[Sequence[int]] = None, _lib=None) -> Dict[str, np.ndarray]:
+        heads: Optional[Sequence[int]] = None, threads: int = 1, _lib=None) -> Dict[str, np.ndarray]:
     """fp64 multi-head recurrence.  x (B, L, H, P), dt (B, L, H), B, C (B, L, N) in float32 or
     bf16 bits; A, D (H,) float32; h0 (B, H, N, P) any float.  Returns ``y`` (B, L, H, P) and
-    ``h_last`` (B, H, N, P) -- or (n, L, P) / (n, N, P) for ``heads`` = flat b*H + h."""
+    ``h_last`` (B, H, N, P) -- or (n, L, P) / (n, N, P) for ``heads`` = flat b*H + h.
+    ``threads`` > 1 splits the (b, h) pairs over threads (bit-identical results)."""
     lib = _lib or _load()
     dtp = _dtype_of(x)
     batch, seqlen, nh, hdim = x.shape
@@ -296,7 +299,7 @@ def ssd(x: np.ndarray, dt: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarr
     y = np.empty((n, seqlen, hdim))
     hl = np.empty((n, dstate, hdim))
     rc = lib.oracle_ssd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), dtp, batch, seqlen, nh,
-                        hdim, dstate, _ptr(sel), n, _ptr(y), _ptr(hl))
+                        hdim, dstate, _ptr(sel), n, _ptr(y), _ptr(hl), int(threads))
     if rc != 0:
         raise ValueError("oracle_ssd rejected its arguments")
     if sel is None:

@@ -219,36 +219,85 @@ int oracle_scan(const void* u, const void* delta, const float* A, const void* B,
  * is carried from one token to the next).  h (n_lanes, N) double is read and
  * overwritten; u, delta, z are
  * (B, D), B and C are (B, N), all in `dtype`; y_out (n_lanes) double.
+ * nthreads > 1 splits the lanes into contiguous blocks, one per thread; lanes
+ * are independent, so the result does not depend on it.
  */
+typedef struct {
+    double* h;
+    const void *u, *delta, *B, *C, *z;
+    const float *A, *Dskip, *delta_bias;
+    int flags, dtype;
+    int64_t batch, dim, dstate;
+    const int64_t* lanes;
+    double* y_out;
+} step_job;
+
+static void step_lane(const step_job* j, int64_t li)
+{
+    const int64_t bd = j->lanes ? j->lanes[li] : li;
+    const int64_t b = bd / j->dim, d = bd % j->dim, N = j->dstate;
+    const double delta_v = step_size(widen(j->delta, bd, j->dtype), j->delta_bias, d, j->flags);
+    const double x = widen(j->u, bd, j->dtype);
+    double* hl = &j->h[li * N];
+    double y = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        const double a = (double)j->A[d * N + n];
+        const double a_bar = exp(delta_v * a);
+        hl[n] = a_bar * hl[n] + input_term(delta_v, a, widen(j->B, b * N + n, j->dtype), x, j->flags);
+    }
+    for (int64_t n = 0; n < N; ++n) y += hl[n] * widen(j->C, b * N + n, j->dtype);
+    if (j->Dskip) y += (double)j->Dskip[d] * x;
+    if (j->z) y *= silu(widen(j->z, bd, j->dtype));
+    if (j->y_out) j->y_out[li] = y;
+}
+
+typedef struct {
+    const step_job* job;
+    int64_t begin, end;
+} step_slice;
+
+static void* step_worker(void* arg)
+{
+    const step_slice* s = (const step_slice*)arg;
+    for (int64_t li = s->begin; li < s->end; ++li) step_lane(s->job, li);
+    return NULL;
+}
+
 int oracle_step(double* h, const void* u, const void* delta, const float* A, const void* B,
                 const void* C, const float* Dskip, const void* z,
                 const float* delta_bias, int flags, int dtype,
                 int64_t batch, int64_t dim, int64_t dstate,
-                const int64_t* lanes, int64_t n_lanes, double* y_out)
+                const int64_t* lanes, int64_t n_lanes, double* y_out, int nthreads)
 {
     if (!h || !u || !delta || !A || !B || !C) return -1;
     if (batch <= 0 || dim <= 0 || dstate <= 0) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
     if (flags & ~(ORACLE_SOFTPLUS | ORACLE_ZOH)) return -1;
     if (!lanes) n_lanes = batch * dim;
-    for (int64_t li = 0; li < n_lanes; ++li) {
-        const int64_t bd = lanes ? lanes[li] : li;
-        if (bd < 0 || bd >= batch * dim) return -1;
-        const int64_t b = bd / dim, d = bd % dim;
-        const double delta_v = step_size(widen(delta, bd, dtype), delta_bias, d, flags);
-        const double x = widen(u, bd, dtype);
-        double* hl = &h[li * dstate];
-        double y = 0.0;
-        for (int64_t n = 0; n < dstate; ++n) {
-            const double a = (double)A[d * dstate + n];
-            const double a_bar = exp(delta_v * a);
-            hl[n] = a_bar * hl[n] + input_term(delta_v, a, widen(B, b * dstate + n, dtype), x, flags);
-        }
-        for (int64_t n = 0; n < dstate; ++n) y += hl[n] * widen(C, b * dstate + n, dtype);
-        if (Dskip) y += (double)Dskip[d] * x;
-        if (z) y *= silu(widen(z, bd, dtype));
-        if (y_out) y_out[li] = y;
+    for (int64_t li = 0; lanes && li < n_lanes; ++li)
+        if (lanes[li] < 0 || lanes[li] >= batch * dim) return -1;
+    step_job job = {h, u, delta, B, C, z, A, Dskip, delta_bias, flags, dtype, batch, dim, dstate, lanes, y_out};
+    if (nthreads <= 1 || n_lanes < 2) {
+        for (int64_t li = 0; li < n_lanes; ++li) step_lane(&job, li);
+        return 0;
     }
+    if (nthreads > n_lanes) nthreads = (int)n_lanes;
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    step_slice* sl = (step_slice*)malloc(sizeof(step_slice) * (size_t)nthreads);
+    if (!th || !sl) {
+        free(th);
+        free(sl);
+        return -1;
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        sl[i].job = &job;
+        sl[i].begin = n_lanes * i / nthreads;
+        sl[i].end = n_lanes * (i + 1) / nthreads;
+        pthread_create(&th[i], NULL, step_worker, &sl[i]);
+    }
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(sl);
     return 0;
 }
 
@@ -550,44 +599,101 @@ int oracle_conv1d_silu(const void* x, int64_t x_row_stride, const float* w, cons
  * P) double or NULL.  Outputs (double): y_out (B, L, H, P), h_last (B, H, N,
  * P), either may be NULL.  heads: NULL for all (b, h) pairs in order, or a
  * list of flat b*H + h (then y_out is (n, L, P) and h_last (n, N, P)).
+ * nthreads > 1 splits the (b, h) pairs into contiguous blocks, one per
+ * thread; pairs are independent, so the result does not depend on it.
  * Returns 0 or -1.
  */
+typedef struct {
+    const void *x, *dt, *B, *C;
+    const float *A, *D;
+    const double* h0;
+    int dtype;
+    int64_t batch, seqlen, heads, hdim, dstate;
+    const int64_t* sel;
+    double *y_out, *h_last;
+} ssd_job;
+
+/* one (b, h) pair, k-th of the selection; S is an (N, P) scratch state */
+static void ssd_pair(const ssd_job* j, int64_t k, double* S)
+{
+    const int64_t L = j->seqlen, H = j->heads, P = j->hdim, N = j->dstate;
+    const int64_t bh = j->sel ? j->sel[k] : k;
+    const int64_t b = bh / H, h = bh % H;
+    for (int64_t i = 0; i < N * P; ++i) S[i] = j->h0 ? j->h0[bh * N * P + i] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double d = widen(j->dt, (b * L + t) * H + h, j->dtype);
+        const double a = exp(d * (double)j->A[h]);
+        const int64_t xrow = ((b * L + t) * H + h) * P, srow = (b * L + t) * N;
+        for (int64_t n = 0; n < N; ++n) {
+            const double bn = widen(j->B, srow + n, j->dtype);
+            for (int64_t p = 0; p < P; ++p) S[n * P + p] = a * S[n * P + p] + d * bn * widen(j->x, xrow + p, j->dtype);
+        }
+        for (int64_t p = 0; p < P; ++p) {
+            double y = 0.0;
+            for (int64_t n = 0; n < N; ++n) y += S[n * P + p] * widen(j->C, srow + n, j->dtype);
+            if (j->D) y += (double)j->D[h] * widen(j->x, xrow + p, j->dtype);
+            if (j->y_out) j->y_out[(k * L + t) * P + p] = y;
+        }
+    }
+    if (j->h_last) memcpy(&j->h_last[k * N * P], S, sizeof(double) * (size_t)(N * P));
+}
+
+typedef struct {
+    const ssd_job* job;
+    int64_t begin, end;
+    int rc;
+} ssd_slice;
+
+static void* ssd_worker(void* arg)
+{
+    ssd_slice* s = (ssd_slice*)arg;
+    double* S = (double*)malloc(sizeof(double) * (size_t)(s->job->dstate * s->job->hdim));
+    if (!S) {
+        s->rc = -1;
+        return NULL;
+    }
+    for (int64_t k = s->begin; k < s->end; ++k) ssd_pair(s->job, k, S);
+    free(S);
+    s->rc = 0;
+    return NULL;
+}
+
 int oracle_ssd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                const double* h0, int dtype, int64_t batch, int64_t seqlen, int64_t heads, int64_t hdim,
-               int64_t dstate, const int64_t* sel, int64_t n_sel, double* y_out, double* h_last)
+               int64_t dstate, const int64_t* sel, int64_t n_sel, double* y_out, double* h_last, int nthreads)
 {
     if (!x || !dt || !A || !B || !C) return -1;
     if (batch <= 0 || seqlen <= 0 || heads <= 0 || hdim <= 0 || dstate <= 0) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
-    const int64_t L = seqlen, H = heads, P = hdim, N = dstate;
-    if (!sel) n_sel = batch * H;
-    double* S = (double*)malloc(sizeof(double) * (size_t)(N * P));
-    if (!S) return -1;
-    for (int64_t k = 0; k < n_sel; ++k) {
-        const int64_t bh = sel ? sel[k] : k;
-        if (bh < 0 || bh >= batch * H) {
-            free(S);
-            return -1;
-        }
-        const int64_t b = bh / H, h = bh % H;
-        for (int64_t i = 0; i < N * P; ++i) S[i] = h0 ? h0[bh * N * P + i] : 0.0;
-        for (int64_t t = 0; t < L; ++t) {
-            const double d = widen(dt, (b * L + t) * H + h, dtype);
-            const double a = exp(d * (double)A[h]);
-            const int64_t xrow = ((b * L + t) * H + h) * P, srow = (b * L + t) * N;
-            for (int64_t n = 0; n < N; ++n) {
-                const double bn = widen(B, srow + n, dtype);
-                for (int64_t p = 0; p < P; ++p) S[n * P + p] = a * S[n * P + p] + d * bn * widen(x, xrow + p, dtype);
-            }
-            for (int64_t p = 0; p < P; ++p) {
-                double y = 0.0;
-                for (int64_t n = 0; n < N; ++n) y += S[n * P + p] * widen(C, srow + n, dtype);
-                if (D) y += (double)D[h] * widen(x, xrow + p, dtype);
-                if (y_out) y_out[(k * L + t) * P + p] = y;
-            }
-        }
-        if (h_last) memcpy(&h_last[k * N * P], S, sizeof(double) * (size_t)(N * P));
+    if (!sel) n_sel = batch * heads;
+    for (int64_t k = 0; sel && k < n_sel; ++k)
+        if (sel[k] < 0 || sel[k] >= batch * heads) return -1;
+    ssd_job job = {x, dt, B, C, A, D, h0, dtype, batch, seqlen, heads, hdim, dstate, sel, y_out, h_last};
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > n_sel) nthreads = (int)(n_sel > 0 ? n_sel : 1);
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    ssd_slice* sl = (ssd_slice*)malloc(sizeof(ssd_slice) * (size_t)nthreads);
+    if (!th || !sl) {
+        free(th);
+        free(sl);
+        return -1;
     }
-    free(S);
-    return 0;
+    for (int i = 0; i < nthreads; ++i) {
+        sl[i].job = &job;
+        sl[i].begin = n_sel * i / nthreads;
+        sl[i].end = n_sel * (i + 1) / nthreads;
+        sl[i].rc = 0;
+    }
+    if (nthreads == 1) {
+        ssd_worker(&sl[0]);
+    } else {
+        for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, ssd_worker, &sl[i]);
+        for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    }
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i)
+        if (sl[i].rc != 0) rc = -1;
+    free(th);
+    free(sl);
+    return rc;
 }

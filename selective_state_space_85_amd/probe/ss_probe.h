@@ -1,0 +1,46 @@
+/*
+ * ss_probe.h -- C ABI of libssprobe.so: two measurement kernels for gfx950 that
+ * give the ceilings the scan is measured against.  Not part of the scan
+ * library; only the bench calls them.
+ *
+ *  ss_probe_stream : a plain stream with n_read input arrays and one output
+ *                    array of `bytes` each (out = in0 ^ in1 ^ ... on 16-byte
+ *                    words), the read:write mix of a memory-bound pass.  With
+ *                    n_read = 3 it is the scan's mix (u, delta, z read, y
+ *                    written); with n_read = 1 a copy.  Pointers are device
+ *                    pointers, 16-byte aligned, bytes a multiple of 16;
+ *                    in1/in2 may be NULL when n_read is 1.
+ *  ss_probe_alu    : a vector-ALU issue probe.  Every lane runs `iters`
+ *                    iterations of a fixed instruction group on 16 independent
+ *                    registers; each wave records the shader-clock cycles it
+ *                    took (s_memtime) in cycles[wave].  kind 0: one fp32 fma
+ *                    per register per iteration; kind 1: one v_exp_f32 per
+ *                    register; kind 2: the scan's per-element group, four fp32
+ *                    multiply/fma plus one v_exp_f32, for 8 rows per iteration
+ *                    (128 groups).  Launch: `blocks`
+ *                    workgroups of 256 lanes (four waves); cycles holds
+ *                    blocks*4 entries (uint64), sink blocks*256 floats.
+ * Both return 0, or the hipError_t of the launch.
+ */
+#ifndef SS_PROBE_H
+#define SS_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int ss_probe_stream(const void* in0, const void* in1, const void* in2, void* out, size_t bytes, int n_read,
+                    int blocks, hipStream_t stream);
+
+int ss_probe_alu(int kind, int iters, int blocks, uint64_t* cycles, float* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_PROBE_H */

@@ -1,0 +1,102 @@
+"""ctypes view of libssprobe.so (probe/ss_probe.h): the HBM stream and vector-ALU issue
+probes that give the ceilings the scan is measured against.  Used by the bench only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict
+
+import torch
+
+PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probe", "libssprobe.so")
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError("libssprobe.so is not built (%s); run "
+                               "`python -m selective_state_space_85_amd.build`" % PROBE_LIB_PATH)
+        lib = ctypes.CDLL(PROBE_LIB_PATH)
+        vp = ctypes.c_void_p
+        lib.ss_probe_stream.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
+        lib.ss_probe_stream.restype = ctypes.c_int
+        lib.ss_probe_alu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        lib.ss_probe_alu.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != 0:
+        raise RuntimeError("%s: hipError_t %d" % (name, rc))
+
+
+def stream_rate(n_read: int, bytes_each: int = 1 << 30, reps: int = 5, device: str = "cuda") -> Dict[str, float]:
+    """GB/s of a plain stream with ``n_read`` input arrays and one output (``bytes_each``
+    bytes each), event-timed over ``reps`` launches after one warm-up launch."""
+    lib = load()
+    words = bytes_each // 4
+    ins = [torch.empty(words, dtype=torch.int32, device=device).fill_(i + 1) for i in range(n_read)]
+    out = torch.empty(words, dtype=torch.int32, device=device)
+    s = torch.cuda.current_stream()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = [ptr(ins[0]), ptr(ins[1]) if n_read > 1 else None, ptr(ins[2]) if n_read > 1 else None, ptr(out)]
+    blocks = 256 * 16
+
+    def launch():
+        _check("ss_probe_stream", lib.ss_probe_stream(*args, bytes_each, n_read, blocks,
+                                                      ctypes.c_void_p(s.cuda_stream)))
+
+    launch()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        launch()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    moved = (n_read + 1) * bytes_each
+    del ins, out
+    return {"read_write": "%d:1" % n_read, "bytes_per_launch": moved, "ms": ms, "GB/s": moved / (ms * 1e-3) / 1e9}
+
+
+def alu_rate(kind: int, iters: int = 0, waves_per_simd: int = 4, device: str = "cuda") -> Dict[str, float]:
+    """The vector-ALU issue probe with ``waves_per_simd`` waves resident on every SIMD:
+    kind 0 one fp32 fma per group, kind 1 one v_exp_f32, kind 2 the scan's element (mul,
+    exp2, mul, fma, fma).  Returns the shader-clock cycles per wave64 group on one SIMD
+    (median over waves of s_memtime cycles / groups, times the waves sharing the SIMD),
+    the chip-wide group rate from event time (lane-groups per second), and the clock
+    those two imply."""
+    lib = load()
+    groups_per_iter = 128 if kind == 2 else 16
+    if iters <= 0:
+        iters = 1024 if kind == 2 else 16384
+    blocks = 256 * waves_per_simd  # four waves per workgroup, one per SIMD
+    cycles = torch.zeros(blocks * 4, dtype=torch.int64, device=device)
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    s = torch.cuda.current_stream()
+
+    def launch():
+        _check("ss_probe_alu", lib.ss_probe_alu(kind, iters, blocks, ctypes.c_void_p(cycles.data_ptr()),
+                                                ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
+
+    launch()  # warms the clocks up
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    launch()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    cyc = float(cycles.cpu().double().median())
+    groups = float(blocks) * 256 * iters * groups_per_iter  # lane-groups over the chip
+    return {"kind": ("fma", "exp2", "scan element: mul, exp2, mul, fma, fma")[kind],
+            "waves_per_simd": waves_per_simd, "iters": iters,
+            "cycles_per_wave_group_per_simd": cyc / (iters * groups_per_iter) / waves_per_simd,
+            "lane_groups_per_s": groups / (ms * 1e-3), "ms": ms,
+            "clock_GHz_implied": cyc / (ms * 1e-3) / 1e9}

@@ -330,6 +330,18 @@ def pin_bookkeeping(orc):
     assert np.array_equal(sub["h_last"], full["h_last"].reshape(10, 16)[lanes]), "lane subset h"
     thr = orc.scan(**c, threads=4)
     assert np.array_equal(thr["y"], full["y"]), "threaded run must be bit-identical"
+    # the step: threads and lane subsets change nothing either
+    sc = {k: (v[:, 5] if k in ("u", "delta", "B", "C", "z") else v) for k, v in c.items()}
+    h1 = c["h0"].astype(np.float64).copy()
+    y1 = orc.step(h1, sc["u"], sc["delta"], c["A"], sc["B"], sc["C"], D=c["D"], z=sc["z"])
+    h4 = c["h0"].astype(np.float64).copy()
+    y4 = orc.step(h4, sc["u"], sc["delta"], c["A"], sc["B"], sc["C"], D=c["D"], z=sc["z"], threads=4)
+    assert np.array_equal(y1, y4) and np.array_equal(h1, h4), "threaded step must be bit-identical"
+    hs = c["h0"].astype(np.float64).reshape(10, 16)[lanes].copy()
+    ys = orc.step(hs, sc["u"], sc["delta"], c["A"], sc["B"], sc["C"], D=c["D"], z=sc["z"], lanes=lanes,
+                  threads=3)
+    assert np.array_equal(ys, y1.reshape(-1)[lanes]) and np.array_equal(hs, h1.reshape(10, 16)[lanes]), \
+        "step lane subset"
     cf = dict(c)
     for k in ("u", "delta", "B", "C", "z"):
         cf[k] = bf16_bits_to_f32(c[k])
@@ -708,6 +720,11 @@ def pin_ssd_reduces_to_scan(orc):
     sel = [1, 4, 5]
     part = orc.ssd(**c, heads=sel)
     assert np.array_equal(part["y"], got["y"].transpose(0, 2, 1, 3).reshape(nb * nh, nl, hp)[sel]), "SSD head subset"
+    thr = orc.ssd(**c, threads=4)
+    assert np.array_equal(thr["y"], got["y"]) and np.array_equal(thr["h_last"], got["h_last"]), \
+        "threaded SSD must be bit-identical"
+    part3 = orc.ssd(**c, heads=sel, threads=2)
+    assert np.array_equal(part3["y"], part["y"]), "threaded SSD head subset"
 
 
 ALL_PINS = [pin_hand_worked, pin_single_step_closed_form, pin_lti_convolution, pin_zero_input,

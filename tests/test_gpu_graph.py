@@ -147,8 +147,8 @@ def test_graph_backward():
 
 @pytest.mark.parametrize("n", [64, 256])
 def test_graph_ssd(n):
-    """The multi-head recurrence in a graph (at dstate 256: the two halves, the combining pass
-    and a caller workspace)."""
+    """The multi-head recurrence in a graph (at dstate 256: one launch per half of the state
+    entries, the second adding the first's fp32 part of y, held in a caller workspace)."""
     b, l, h = 1, 200, 2
     inp = wl.ssd_inputs(b, l, h, 64, n, has_D=True, has_h0=True, seed=914)
     m = ss()

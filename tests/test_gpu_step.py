@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import TOL, dev, host64, rel_err, sample_lanes, say
+from gpu_util import TOL, dev, host64, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -21,38 +21,29 @@ def ss():
 
 
 def test_step_chain_1000():
-    """The recurrent-step workload: B=256, D=5120, N=16, 1000 chained tokens."""
+    """The recurrent-step workload: B=256, D=5120, N=16, 1000 chained tokens; every lane's y at
+    every token, and every lane's state every 250 tokens and at the end."""
     w = wl.WORKLOADS["step"]
     m = ss()
     p = wl.step_params(w)
     A_t, D_t = dev(p["A"]), dev(p["D"])
     h = dev(p["h0"]).clone()
-    lanes = sample_lanes(w.batch, w.dim, 512, seed=5)
-    h_ref = np.ascontiguousarray(p["h0"].reshape(-1, 16)[lanes].astype(np.float64))
-    h_full = p["h0"].astype(np.float64).copy()  # every lane, for the first steps
+    h_ref = p["h0"].astype(np.float64).copy()
     worst = 0.0
-    say("step chain: %d steps, B=%d D=%d" % (w.steps, w.batch, w.dim))
+    say("step chain: %d steps, B=%d D=%d, every lane" % (w.steps, w.batch, w.dim))
     for s, inp in enumerate(wl.iter_step_inputs(w, w.steps, workers=8)):
         t = {k: dev(v) for k, v in inp.items()}
         y = m.step(h, t["u"], t["delta"], A_t, t["B"], t["C"], D=D_t, z=t["z"])
         y_ref = oracle.step(h_ref, inp["u"], inp["delta"], p["A"], inp["B"], inp["C"], D=p["D"],
-                            z=inp["z"], lanes=lanes)
-        yg = host64(y)
-        e = rel_err(yg.reshape(-1)[lanes], y_ref)
+                            z=inp["z"], threads=THREADS)
+        e = rel_err(host64(y), y_ref)
         worst = max(worst, e)
-        if s < 3:  # every lane for the first tokens
-            y_all = oracle.step(h_full, inp["u"], inp["delta"], p["A"], inp["B"], inp["C"], D=p["D"],
-                                z=inp["z"])
-            ef = rel_err(yg, y_all)
-            eh = rel_err(host64(h), h_full)
-            say("  step %d, all lanes: y err %.3e, h err %.3e" % (s, ef, eh))
-            assert ef <= TOL["bf16"] and eh <= TOL["bf16"]
-        if s % 200 == 0 or s == w.steps - 1:
-            say("  step %d: sampled y err %.3e (worst so far %.3e)" % (s, e, worst))
+        if s % 250 == 0 or s == w.steps - 1:
+            eh = rel_err(host64(h), h_ref)
+            say("  step %d: y err %.3e (worst so far %.3e), h err %.3e" % (s, e, worst, eh))
+            assert eh <= TOL["bf16"], "step %d: h error %.3e" % (s, eh)
         assert e <= TOL["bf16"], "step %d: y error %.3e" % (s, e)
-    eh = rel_err(host64(h).reshape(-1, 16)[lanes], h_ref)
-    say("  after %d steps: h err %.3e, worst y err %.3e" % (w.steps, eh, worst))
-    assert eh <= TOL["bf16"]
+    say("  after %d steps: worst y err %.3e" % (w.steps, worst))
 
 
 @pytest.mark.parametrize("shape", [(1, 1), (1, 64), (3, 100), (2, 5), (7, 1000)], ids=str)

@@ -18,12 +18,14 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
 MUTANTS = [
     ("input term drops x", "return b_bar * x;", "return b_bar;"),
     ("sign of the exponent", "const double a_bar = exp(delta * a);", "const double a_bar = exp(-delta * a);"),
-    ("A transposed", "(double)j->A[d * N + n]", "(double)j->A[n * D + d]"),
-    ("C read from B", "widen(j->C, srow + n, j->dtype)", "widen(j->B, srow + n, j->dtype)"),
+    ("A transposed", "            const double a = (double)j->A[d * N + n];",
+     "            const double a = (double)j->A[n * D + d];"),
+    ("C read from B", "y += h[n] * widen(j->C, srow + n, j->dtype)", "y += h[n] * widen(j->B, srow + n, j->dtype)"),
     ("B one step late", "input_term(delta, a, widen(j->B, srow + n, j->dtype), x, j->flags)",
      "input_term(delta, a, widen(j->B, (t > 0 ? srow - N : srow) + n, j->dtype), x, j->flags)"),
     ("Bbar without delta", "double b_bar = delta * bm; /* Euler */", "double b_bar = bm; /* Euler */"),
-    ("D skip without x", "y += (double)j->Dskip[d] * x;", "y += (double)j->Dskip[d];"),
+    ("D skip without x", "y += (double)j->Dskip[d] * x;\n        if (j->z) y *= silu(widen(j->z, row, j->dtype));",
+     "y += (double)j->Dskip[d];\n        if (j->z) y *= silu(widen(j->z, row, j->dtype));"),
     ("sigmoid gate instead of silu", "static double silu(double z) { return z / (1.0 + exp(-z)); }",
      "static double silu(double z) { return 1.0 / (1.0 + exp(-z)); }"),
     ("h0 ignored", "h[n] = j->h0 ? j->h0[bd * N + n] : 0.0;", "h[n] = 0.0;"),
@@ -38,6 +40,11 @@ MUTANTS = [
      "        for (int64_t n = 0; n < N; ++n) h[n] = exp(delta * (double)j->A[d * N + n]) * h[n]"
      " + input_term(delta, (double)j->A[d * N + n], widen(j->B, srow + n, j->dtype), x, j->flags);"),
     ("step forgets the decay", "hl[n] = a_bar * hl[n] + input_term(", "hl[n] = hl[n] + input_term("),
+    ("step without its skip", "if (j->Dskip) y += (double)j->Dskip[d] * x;\n    if (j->z)", "if (j->z)"),
+    ("step threads overlap", "sl[i].begin = n_lanes * i / nthreads;\n        sl[i].end = n_lanes * (i + 1) / nthreads;\n"
+     "        pthread_create(&th[i], NULL, step_worker",
+     "sl[i].begin = n_lanes * i / nthreads;\n        sl[i].end = n_lanes * (i + 1) / nthreads + (i + 1 < nthreads);\n"
+     "        pthread_create(&th[i], NULL, step_worker"),
     ("state recorded one step late", "j->rec_t[next_rec] == t)", "j->rec_t[next_rec] == t - 1)"),
     # the delta / Bbar options
     ("ZOH ignored", "if (flags & ORACLE_ZOH) {", "if (0) {"),
@@ -81,14 +88,14 @@ MUTANTS = [
     ("conv rows read contiguous", "widen(x, (b * seqlen + s) * x_row_stride + d, dtype)",
      "widen(x, (b * seqlen + s) * dim + d, dtype)"),
     # the multi-head recurrence
-    ("SSD decay sign flipped", "const double a = exp(d * (double)A[h]);", "const double a = exp(-d * (double)A[h]);"),
-    ("SSD input without dt", "S[n * P + p] = a * S[n * P + p] + d * bn * widen(x, xrow + p, dtype);",
-     "S[n * P + p] = a * S[n * P + p] + bn * widen(x, xrow + p, dtype);"),
-    ("SSD output reads B", "y += S[n * P + p] * widen(C, srow + n, dtype);", "y += S[n * P + p] * widen(B, srow + n, dtype);"),
-    ("SSD state transposed", "y += S[n * P + p] * widen(C, srow + n, dtype);",
-     "y += S[(p % N) * P + (n % P)] * widen(C, srow + n, dtype);"),
-    ("SSD dt of head 0", "const double d = widen(dt, (b * L + t) * H + h, dtype);",
-     "const double d = widen(dt, (b * L + t) * H, dtype);"),
+    ("SSD decay sign flipped", "const double a = exp(d * (double)j->A[h]);", "const double a = exp(-d * (double)j->A[h]);"),
+    ("SSD input without dt", "S[n * P + p] = a * S[n * P + p] + d * bn * widen(j->x, xrow + p, j->dtype);",
+     "S[n * P + p] = a * S[n * P + p] + bn * widen(j->x, xrow + p, j->dtype);"),
+    ("SSD output reads B", "y += S[n * P + p] * widen(j->C, srow + n, j->dtype);", "y += S[n * P + p] * widen(j->B, srow + n, j->dtype);"),
+    ("SSD state transposed", "y += S[n * P + p] * widen(j->C, srow + n, j->dtype);",
+     "y += S[(p % N) * P + (n % P)] * widen(j->C, srow + n, j->dtype);"),
+    ("SSD dt of head 0", "const double d = widen(j->dt, (b * L + t) * H + h, j->dtype);",
+     "const double d = widen(j->dt, (b * L + t) * H, j->dtype);"),
     ("dh0 before the last decay", "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n];",
      "for (int64_t n = 0; n < N; ++n) j->dh0[bd * N + n] = g[n] / exp(dl[0] * (double)f->A[d * N + n]);"),
 ]
