@@ -178,6 +178,32 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
                          int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                          int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
 
+/* Size in bytes of ss_scan_fwd_noalloc's per-GPU array (the largest workspace it serves). */
+#define SS_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/*
+ * ss_scan_fwd_noalloc -- ss_scan_fwd for callers that cannot allocate device
+ * memory: code under stream (graph) capture, tight serving loops, harnesses
+ * that forbid allocation.  It takes no workspace: the library keeps one static
+ * device array of SS_NOALLOC_MAX_WORKSPACE_BYTES (32 MiB) per GPU,
+ * created with the code object and held until the process ends, and the call
+ * allocates nothing (no hipMalloc, no allocating library routine).  The first
+ * call on a device looks up that device's array address (one HIP symbol query
+ * per device, kept for later calls).
+ *
+ * Arguments, results, validation and errors are as for ss_scan_fwd, plus:
+ * a shape whose ss_scan_workspace_bytes exceeds the array returns
+ * SS_ERR_WORKSPACE (before any HIP call); SS_ERR_HIP if the symbol query
+ * fails.  Every call on one GPU shares that GPU's array and leaves its own
+ * contents there: calls that overlap in time on one GPU (two streams, or two
+ * host threads) race and must be ordered by the caller.  Nothing in the array
+ * needs clearing between calls: each call writes every word it reads.
+ */
+ss_status ss_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                              const float* Dskip, const void* z, const float* h0, void* y, float* h_last,
+                              int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ss_dtype dtype,
+                              hipStream_t stream);
+
 /*
  * ss_scan_ckpt_bytes -- size of the state checkpoints of a (batch, seqlen,
  * dim, dstate) scan: ceil(seqlen/16) * batch * dim * dstate fp32 words, in

@@ -13,11 +13,13 @@ SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE, SS_ERR_HIP = ra
 SS_F32, SS_BF16 = 0, 1
 
 # Every function the header declares.
-EXPORTS = ("ss_scan_plan", "ss_scan_plan_ex", "ss_scan_workspace_bytes", "ss_scan_workspace_bytes_ex", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_ckpt_bytes",
+EXPORTS = ("ss_scan_plan", "ss_scan_plan_ex", "ss_scan_workspace_bytes", "ss_scan_workspace_bytes_ex", "ss_scan_fwd", "ss_scan_fwd_ex",
+           "ss_scan_fwd_noalloc", "ss_scan_ckpt_bytes",
            "ss_scan_fwd_ckpt", "ss_step", "ss_step_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_bwd",
            "ss_scan_bwd_ckpt_workspace_bytes", "ss_scan_bwd_ckpt", "ss_conv1d_silu", "ss_ssd_fwd", "ss_ssd_fwd_ex", "ss_ssd_workspace_bytes",
            "ss_status_string", "ss_last_hip_error")
 SS_DELTA_SOFTPLUS, SS_B_ZOH = 1, 2  # ss_option bits
+SS_NOALLOC_MAX_WORKSPACE_BYTES = 32 << 20  # ss_scan_fwd_noalloc's per-GPU array
 
 _lib = None
 
@@ -55,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.ss_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                 i64, i64, i64, i64, ctypes.c_int, vp]
     lib.ss_scan_fwd.restype = ctypes.c_int
+    lib.ss_scan_fwd_noalloc.argtypes = [vp] * 10 + [i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.ss_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ss_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp, sz,
                                    i64, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.ss_scan_fwd_ex.restype = ctypes.c_int

@@ -7,6 +7,8 @@
 #include "ss_internal.h"
 #include "ss_scan.h"
 
+static_assert(ssk::kScratchBytes == SS_NOALLOC_MAX_WORKSPACE_BYTES, "the header states the scratch size");
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -196,12 +198,14 @@ ss_status scan_bwd_impl(const void* u, const void* delta, const float* A, const 
                         void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
                         int64_t dstate, ss_dtype dtype, hipStream_t stream);
 
-// ss_scan_fwd_ex with an optional checkpoint output (see ss_scan_fwd_ckpt)
+// ss_scan_fwd_ex with an optional checkpoint output (see ss_scan_fwd_ckpt);
+// with use_scratch the workspace arguments are ignored and the library's
+// static per-GPU array is used instead (see ss_scan_fwd_noalloc)
 ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
                         const float* Dskip, const void* z, const float* h0, const float* delta_bias,
                         uint32_t options, void* y, float* h_last, float* ckpt, void* workspace,
                         size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                        int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream);
+                        int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream, bool use_scratch = false);
 
 }  // namespace
 
@@ -261,6 +265,15 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
                          workspace_bytes, batch, seqlen, dim, dstate, chunk_len_request, dtype, stream);
 }
 
+ss_status ss_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                              const float* Dskip, const void* z, const float* h0, void* y, float* h_last,
+                              int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ss_dtype dtype,
+                              hipStream_t stream)
+{
+    return scan_fwd_impl(u, delta, A, B, C, Dskip, z, h0, nullptr, 0u, y, h_last, nullptr, nullptr, 0, batch,
+                         seqlen, dim, dstate, 0, dtype, stream, true);
+}
+
 size_t ss_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate)
 {
     Sizes s;
@@ -290,7 +303,7 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
                         const float* Dskip, const void* z, const float* h0, const float* delta_bias,
                         uint32_t options, void* y, float* h_last, float* ckpt, void* workspace,
                         size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                        int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream)
+                        int64_t chunk_len_request, ss_dtype dtype, hipStream_t stream, bool use_scratch)
 {
     if (!u || !delta || !A || !B || !C || !y) return SS_ERR_INVALID_ARG;
     Sizes s;
@@ -347,6 +360,13 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
         if (overlap(r_hl, r)) return SS_ERR_INVALID_ARG;
     }
 
+    if (use_scratch) {
+        // every argument is checked above, on the host; the first HIP call comes only now
+        if (static_cast<size_t>(need) > ssk::kScratchBytes) return SS_ERR_WORKSPACE;
+        const hipError_t se = ssk::scratch_pointer(&workspace);
+        if (se != hipSuccess) return hip_fail(se);
+        workspace_bytes = ssk::kScratchBytes;
+    }
     if (!workspace || workspace_bytes < static_cast<size_t>(need)) return SS_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SS_ERR_INVALID_ARG;
     const Range r_ws = span(workspace, need);

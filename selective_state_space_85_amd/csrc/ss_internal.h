@@ -151,6 +151,12 @@ struct SsdArgs {
     float* y_part;
 };
 
+// The allocation-free scan entry point's workspace: a static device array of
+// kScratchBytes per GPU.  scratch_pointer looks up its address on the current
+// device (once per device; later calls return the kept address).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_pointer(void** ptr);
+
 // Each returns the hipError_t of its launches (hipSuccess when all were enqueued).
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, int dtype, hipStream_t stream);

@@ -39,9 +39,47 @@
 //    section 3.1.5.3).
 //  * exp(x) is evaluated as exp2(x * log2 e) on the hardware exp2 unit, with
 //    A pre-scaled by log2 e once per lane.
+#include <atomic>
+#include <mutex>
+
 #include "ss_device.h"
 
+// The workspace of ss_scan_fwd_noalloc: one array per GPU (each device holds
+// its own copy of a __device__ variable), alive until the process ends.  Host
+// code never uses the name itself as an address -- on the host it is only a
+// stand-in for the symbol -- but the device address that scratch_pointer looks
+// up for the current device.
+static __device__ __align__(256) unsigned char scratch[ssk::kScratchBytes];
+
 namespace ssk {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+hipError_t scratch_pointer(void** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 namespace {
 
 // ---------------------------------------------------------------------------

@@ -145,6 +145,41 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     return y
 
 
+def scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                     D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                     h0: Optional[torch.Tensor] = None, *, out: torch.Tensor,
+                     h_last: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``ss_scan_fwd_noalloc``: the scan with the library's static per-GPU workspace, for
+    callers that cannot allocate device memory.  ``out`` (and ``h_last`` if wanted) are the
+    caller's; nothing is allocated here or in the library.  Shapes as for ``scan_fwd``; a
+    shape whose workspace exceeds ``_lib.SS_NOALLOC_MAX_WORKSPACE_BYTES`` raises SSError.
+    Calls that overlap in time on one GPU share that workspace and must not overlap."""
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, seqlen, dim)")
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd_noalloc runs on the GPU; u is on %s" % dev)
+    dt = u.dtype
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    nb, nl, nd = u.shape
+    nn = A.shape[-1]
+    for t, name, shp, tdt in ((u, "u", (nb, nl, nd), dt), (delta, "delta", (nb, nl, nd), dt),
+                              (A, "A", (nd, nn), torch.float32), (B, "B", (nb, nl, nn), dt),
+                              (C, "C", (nb, nl, nn), dt), (out, "out", (nb, nl, nd), dt)):
+        _need(t, name, shp, tdt, dev)
+    for t, name, shp, tdt in ((D, "D", (nd,), torch.float32), (z, "z", (nb, nl, nd), dt),
+                              (h0, "h0", (nb, nd, nn), torch.float32), (h_last, "h_last", (nb, nd, nn), torch.float32)):
+        if t is not None:
+            _need(t, name, shp, tdt, dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().ss_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                             _ptr(h0), _ptr(out), _ptr(h_last), nb, nl, nd, nn, _DTYPES[dt],
+                                             _stream(dev))
+    _lib.check("ss_scan_fwd_noalloc", st)
+    return out
+
+
 def step(h: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
          C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
          *, out: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
