@@ -11,15 +11,19 @@
  *                    pointers, 16-byte aligned, bytes a multiple of 16;
  *                    in1/in2 may be NULL when n_read is 1.
  *  ss_probe_alu    : a vector-ALU issue probe.  Every lane runs `iters`
- *                    iterations of a fixed instruction group on 16 independent
- *                    registers; each wave records the shader-clock cycles it
- *                    took (s_memtime) in cycles[wave].  kind 0: one fp32 fma
- *                    per register per iteration; kind 1: one v_exp_f32 per
- *                    register; kind 2: the scan's per-element group, four fp32
- *                    multiply/fma plus one v_exp_f32, for 8 rows per iteration
- *                    (128 groups).  Launch: `blocks`
- *                    workgroups of 256 lanes (four waves); cycles holds
- *                    blocks*4 entries (uint64), sink blocks*256 floats.
+ *                    iterations of a fixed instruction group; each wave
+ *                    records the shader-clock cycles (s_memtime) and the
+ *                    100 MHz reference-clock ticks (s_memrealtime) it took in
+ *                    cycles[2*wave] and cycles[2*wave+1].  kind 0: 16
+ *                    independent fp32 fma chains, one fma each per iteration;
+ *                    kind 1: 16 independent v_exp_f32 chains; kind 2: the
+ *                    scan's per-element group (four fp32 multiply/fma plus one
+ *                    v_exp_f32) for 8 rows x 16 states per iteration (128
+ *                    groups); kind 3: one dependent chain of 16 fma per
+ *                    iteration; kind 4: one dependent chain of 16 v_exp_f32.
+ *                    Launch: `blocks` workgroups of 256 lanes (four waves);
+ *                    cycles holds blocks*8 entries (uint64), sink blocks*256
+ *                    floats.
  * Both return 0, or the hipError_t of the launch.
  */
 #ifndef SS_PROBE_H

@@ -30,14 +30,17 @@ __global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ a
     }
 }
 
-// 16 independent registers per lane.  KIND 0: v = fma(v, s, t); KIND 1:
-// v = exp2(-v) (converges to a fixed point in (0, 1), no overflow).  KIND 2:
-// the scan's element, for 8 rows r per loop trip and 16 state registers i:
-// x = d[r] * a[i] (mul), e = exp2(x), in = xb[r] * b[i] (mul),
-// v[i] = fma(e, v[i], in), acc[r] = fma(c[i], v[i], acc[r]) -- four vector
-// operations and one v_exp_f32 per element, as in the recurrence.  The
-// empty asm statements keep the compiler from hoisting loop-invariant
-// products or merging iterations.
+// KIND 0: 16 independent fma chains per lane, v = fma(v, s, t).  KIND 1: 16
+// independent exp2 chains, v = exp2(-v) (converges to a fixed point in (0, 1),
+// no overflow).  KIND 2: the scan's element, for 8 rows r per loop trip and 16
+// state registers i: x = d[r] * a[i] (mul), e = exp2(x), in = xb[r] * b[i]
+// (mul), v[i] = fma(e, v[i], in), acc[r] = fma(c[i], v[i], acc[r]) -- four
+// vector operations and one v_exp_f32 per element, as in the recurrence.
+// KIND 3: one dependent fma chain of 16 per trip (latency).  KIND 4: one
+// dependent exp2 chain of 16 per trip (latency).  The empty asm statements
+// keep the compiler from hoisting loop-invariant products or merging
+// iterations.  Each wave records its shader-clock (s_memtime) and 100 MHz
+// reference-clock (s_memrealtime) cycles.
 template <int KIND>
 __global__ __launch_bounds__(256) void alu_kernel(int iters, uint64_t* __restrict__ cycles, float* __restrict__ sink)
 {
@@ -54,6 +57,7 @@ __global__ __launch_bounds__(256) void alu_kernel(int iters, uint64_t* __restric
     }
     __syncthreads();
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
     for (int k = 0; k < iters; ++k) {
         if constexpr (KIND == 2) {
 #pragma unroll
@@ -69,6 +73,12 @@ __global__ __launch_bounds__(256) void alu_kernel(int iters, uint64_t* __restric
                     acc[r] = fmaf(0.125f + 0.0078125f * float(i), v[i], acc[r]);
                 }
             }
+        } else if constexpr (KIND == 3) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[0] = fmaf(v[0], s, t);
+        } else if constexpr (KIND == 4) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[0] = __builtin_amdgcn_exp2f(-v[0]);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -84,13 +94,18 @@ __global__ __launch_bounds__(256) void alu_kernel(int iters, uint64_t* __restric
                          "+v"(v[14]), "+v"(v[15]));
     }
     const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
     float r = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) r += v[i];
 #pragma unroll
     for (int j = 0; j < 8; ++j) r += acc[j];
     sink[int64_t(blockIdx.x) * 256 + threadIdx.x] = r;
-    if ((threadIdx.x & 63) == 0) cycles[int64_t(blockIdx.x) * 4 + threadIdx.x / 64] = t1 - t0;
+    if ((threadIdx.x & 63) == 0) {
+        const int64_t wv = int64_t(blockIdx.x) * 4 + threadIdx.x / 64;
+        cycles[2 * wv] = t1 - t0;
+        cycles[2 * wv + 1] = r1 - r0;
+    }
 }
 
 }  // namespace
@@ -115,14 +130,15 @@ extern "C" int ss_probe_stream(const void* in0, const void* in1, const void* in2
 
 extern "C" int ss_probe_alu(int kind, int iters, int blocks, uint64_t* cycles, float* sink, hipStream_t stream)
 {
-    if (!cycles || !sink || iters <= 0 || blocks <= 0 || kind < 0 || kind > 2) return int(hipErrorInvalidValue);
+    if (!cycles || !sink || iters <= 0 || blocks <= 0 || kind < 0 || kind > 4) return int(hipErrorInvalidValue);
     (void)hipGetLastError();
     const dim3 g(blocks), b(256);
-    if (kind == 0)
-        alu_kernel<0><<<g, b, 0, stream>>>(iters, cycles, sink);
-    else if (kind == 1)
-        alu_kernel<1><<<g, b, 0, stream>>>(iters, cycles, sink);
-    else
-        alu_kernel<2><<<g, b, 0, stream>>>(iters, cycles, sink);
+    switch (kind) {
+        case 0: alu_kernel<0><<<g, b, 0, stream>>>(iters, cycles, sink); break;
+        case 1: alu_kernel<1><<<g, b, 0, stream>>>(iters, cycles, sink); break;
+        case 2: alu_kernel<2><<<g, b, 0, stream>>>(iters, cycles, sink); break;
+        case 3: alu_kernel<3><<<g, b, 0, stream>>>(iters, cycles, sink); break;
+        default: alu_kernel<4><<<g, b, 0, stream>>>(iters, cycles, sink); break;
+    }
     return int(hipGetLastError());
 }

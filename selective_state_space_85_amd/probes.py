@@ -64,19 +64,23 @@ def stream_rate(n_read: int, bytes_each: int = 1 << 30, reps: int = 5, device: s
     return {"read_write": "%d:1" % n_read, "bytes_per_launch": moved, "ms": ms, "GB/s": moved / (ms * 1e-3) / 1e9}
 
 
+KINDS = ("fma", "exp2", "scan element: mul, exp2, mul, fma, fma", "dependent fma chain", "dependent exp2 chain")
+
+
 def alu_rate(kind: int, iters: int = 0, waves_per_simd: int = 4, device: str = "cuda") -> Dict[str, float]:
-    """The vector-ALU issue probe with ``waves_per_simd`` waves resident on every SIMD:
-    kind 0 one fp32 fma per group, kind 1 one v_exp_f32, kind 2 the scan's element (mul,
-    exp2, mul, fma, fma).  Returns the shader-clock cycles per wave64 group on one SIMD
-    (median over waves of s_memtime cycles / groups, times the waves sharing the SIMD),
-    the chip-wide group rate from event time (lane-groups per second), and the clock
-    those two imply."""
+    """The vector-ALU issue probe with ``waves_per_simd`` waves resident on every SIMD (see
+    ss_probe.h for the kinds).  Returns per wave64 instruction group: the shader-clock
+    cycles one SIMD spends (median over waves of s_memtime cycles / groups, divided by
+    the waves sharing the SIMD: the issue cost when the SIMD is saturated), the same per
+    wave (the latency when one wave runs alone), the chip-wide rate of lane-groups per
+    second from event time, and the shader clock implied by s_memtime against the
+    100 MHz reference clock."""
     lib = load()
     groups_per_iter = 128 if kind == 2 else 16
     if iters <= 0:
-        iters = 1024 if kind == 2 else 16384
+        iters = {0: 16384, 1: 8192, 2: 1024, 3: 8192, 4: 2048}[kind]
     blocks = 256 * waves_per_simd  # four waves per workgroup, one per SIMD
-    cycles = torch.zeros(blocks * 4, dtype=torch.int64, device=device)
+    cycles = torch.zeros(blocks * 8, dtype=torch.int64, device=device)
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=device)
     s = torch.cuda.current_stream()
 
@@ -93,10 +97,13 @@ def alu_rate(kind: int, iters: int = 0, waves_per_simd: int = 4, device: str = "
     e1.record(s)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    cyc = float(cycles.cpu().double().median())
+    c = cycles.cpu().double().view(-1, 2)
+    cyc = float(c[:, 0].median())
+    ref = float(c[:, 1].median())
     groups = float(blocks) * 256 * iters * groups_per_iter  # lane-groups over the chip
-    return {"kind": ("fma", "exp2", "scan element: mul, exp2, mul, fma, fma")[kind],
-            "waves_per_simd": waves_per_simd, "iters": iters,
-            "cycles_per_wave_group_per_simd": cyc / (iters * groups_per_iter) / waves_per_simd,
+    per_wave = cyc / (iters * groups_per_iter)
+    return {"kind": KINDS[kind], "waves_per_simd": waves_per_simd, "iters": iters,
+            "cycles_per_wave_group_per_simd": per_wave / waves_per_simd,
+            "cycles_per_group_per_wave": per_wave,
             "lane_groups_per_s": groups / (ms * 1e-3), "ms": ms,
-            "clock_GHz_implied": cyc / (ms * 1e-3) / 1e9}
+            "shader_clock_GHz": cyc / ref * 0.1 if ref > 0 else None}
