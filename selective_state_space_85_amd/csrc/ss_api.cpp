@@ -110,6 +110,26 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
     return true;
 }
 
+// Scan layout: whole-wave workgroups (8 waves, 64 channels) or half-wave ones
+// (4 waves, 32 channels), for the same work.  The CUs run their workgroups
+// side by side and the call ends with the most loaded CU, so the layout whose
+// busiest CU holds less work wins: ceil(wg / 256) workgroups of 64 channels
+// against ceil(2 * wg / 256) of 32.  On a tie the whole-wave layout stays (its
+// B and C are scalar operands).  SS_SCAN_LAYOUT forces one at build time
+// (1 whole-wave, 2 half-wave) for measurements.
+#ifndef SS_SCAN_LAYOUT
+#define SS_SCAN_LAYOUT 0
+#endif
+constexpr int64_t kCUs = 256;
+bool half_layout(int64_t batch, int64_t dim, int64_t K)
+{
+    if (SS_SCAN_LAYOUT == 1) return false;
+    if (SS_SCAN_LAYOUT == 2) return true;
+    const int64_t whole = batch * ceil_div(dim, kWave) * K;
+    const int64_t halves = batch * ceil_div(dim, kWave / 2) * K;
+    return ceil_div(halves, kCUs) < 2 * ceil_div(whole, kCUs);
+}
+
 // Workspace layout for K chunks of T rows (fp32 words):
 //   K > 1: K state slots of batch*dim*dstate, then (K-1)*batch*dim delta sums;
 //   then, at the next multiple of 256 bytes, the B/C panel of
@@ -397,6 +417,7 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
     a.dim = dim;
     a.chunk_len = T;
     a.n_chunks = K;
+    a.half = half_layout(batch, dim, K);
     const hipError_t err = ssk::launch_scan(a, dtype == SS_F32 ? 0 : 1, stream);
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;

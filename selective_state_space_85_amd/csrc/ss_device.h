@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "ss_internal.h"
 
@@ -178,6 +179,63 @@ __device__ __forceinline__ void pin_rows(float (&v)[R][C])
             __asm__ volatile("" : "+v"(v[r][0]), "+v"(v[r][1]), "+v"(v[r][2]), "+v"(v[r][3]), "+v"(v[r][4]),
                              "+v"(v[r][5]), "+v"(v[r][6]), "+v"(v[r][7]));
     }
+}
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}), unrolled
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Value K of the lane's row of 16 lanes, broadcast across that row (DPP
+// row_newbcast:K).  Used as the first operand of a multiply, the compiler folds
+// it into the multiply itself (v_mul_f32_dpp).
+constexpr int kDppRowNewBcast = 0x150;
+template <int K>
+__device__ __forceinline__ float row_bcast(float v)
+{
+    static_assert(K >= 0 && K < 16, "a row has 16 lanes");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowNewBcast + K, 0xf, 0xf, false));
+}
+
+// acc[r] = C[r][0] * hh[r][0] + C[r][1] * hh[r][1] for the 8 rows of a tile,
+// with C[r][i] value 2r + i of the lane's row of 16 lanes in cv (as row_bcast).
+// The compiler does not fold a row broadcast into an fma, so the 16 products
+// are written out: a multiply and an fma per row, each reading cv through
+// DPP.  The leading s_nop gives the two wait states a DPP read needs after a
+// vector write of its source register (cv comes from a load, but the
+// compiler could have copied it).
+__device__ __forceinline__ void contract_rows_bcast(float (&acc)[8], float cv, const float (&hh)[8][2])
+{
+    __asm__("s_nop 1\n\t"
+                     "v_mul_f32_dpp %0, %8, %9 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %0, %8, %10 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_mul_f32_dpp %1, %8, %11 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %1, %8, %12 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_mul_f32_dpp %2, %8, %13 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %2, %8, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_mul_f32_dpp %3, %8, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %3, %8, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_mul_f32_dpp %4, %8, %17 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %4, %8, %18 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_mul_f32_dpp %5, %8, %19 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %5, %8, %20 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_mul_f32_dpp %6, %8, %21 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %6, %8, %22 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_mul_f32_dpp %7, %8, %23 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+                     "v_fmac_f32_dpp %7, %8, %24 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5]),
+              "=&v"(acc[6]), "=&v"(acc[7])
+            : "v"(cv), "v"(hh[0][0]), "v"(hh[0][1]), "v"(hh[1][0]), "v"(hh[1][1]), "v"(hh[2][0]), "v"(hh[2][1]),
+              "v"(hh[3][0]), "v"(hh[3][1]), "v"(hh[4][0]), "v"(hh[4][1]), "v"(hh[5][0]), "v"(hh[5][1]),
+              "v"(hh[6][0]), "v"(hh[6][1]), "v"(hh[7][0]), "v"(hh[7][1]));
 }
 
 // DPP controls: row shifts by 1/2/4/8 lanes within rows of 16, and the

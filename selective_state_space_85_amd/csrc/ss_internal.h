@@ -65,6 +65,9 @@ struct ScanArgs {
     float* ckpt;
     int64_t batch, seqlen, dim;
     int64_t chunk_len, n_chunks;
+    // the half-wave layout (32 channels per 4-wave workgroup) instead of the
+    // whole-wave one (64 channels per 8-wave workgroup)
+    bool half;
 };
 
 struct StepArgs {

@@ -115,36 +115,79 @@ __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Scan kernel.  grid = (ceil(dim/64), batch, chunks), block = 64 * kGroups.
+// Scan kernel.  Two layouts of the same work, both with the 16 state entries
+// of a channel split into 8 groups of 2 (one group per 64 lanes of state):
+//  * whole-wave (HALF = false): a workgroup of 8 waves owns 64 channels of one
+//    batch row and chunk; wave w holds group w of every channel (lane =
+//    channel), so B and C are wave-uniform scalar operands.
+//    grid = (ceil(dim/64), batch, chunks), block = 512.
+//  * half-wave (HALF = true): a workgroup of 4 waves owns 32 channels; the two
+//    32-lane halves of wave w hold groups 2w and 2w+1 (lane = channel within
+//    a half).  B and C then differ between the halves: each wave loads a
+//    tile's 16 values of its two groups into one register (lane 16q + k holds
+//    value k of the group of its half: row k/2, entry k%2) and every use takes
+//    value k by a broadcast within the lane's row of 16 lanes (DPP
+//    row_newbcast, folded into the multiply or the fma).  Twice as many
+//    workgroups of half the size: the large layer's 640 whole-wave blocks on
+//    256 CUs leave half of the CUs with three and half with two, its 1280
+//    half-wave blocks give every CU five.
+//    grid = (ceil(dim/32), batch, chunks), block = 256.
+// In both, each (row, channel) of a tile is widened and published by one lane
+// and finished by the same lane.
 // EMIT: start from the chunk's carry (or h0), write y and, for the last chunk,
 //       h_last.
 // !EMIT (aggregate): start from zero, write the chunk's end state into state
 //       slot c+1 and its delta sum.
 // Host guarantees: chunk_len * dim * element size < 2^31.
 // ---------------------------------------------------------------------------
-// The zero-order hold's extra arithmetic would take the kernel just past 80
-// VGPRs, which leaves room for two 8-wave workgroups per CU instead of three;
-// it is held to 80 (six waves per SIMD).
-template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE & kOptZoh) ? 6 : 2))) void scan_kernel(
-    ScanArgs a)
+// The zero-order hold's extra arithmetic would take the whole-wave kernel just
+// past 80 VGPRs, which leaves room for two 8-wave workgroups per CU instead of
+// three; it is held to 80 (six waves per SIMD).
+template <bool HALF>
+struct ScanShape {
+    static constexpr int kWaves = HALF ? 4 : kGroups;  // waves per workgroup
+    static constexpr int kCh = HALF ? 32 : kWave;      // channels per workgroup
+};
+
+template <bool HALF>
+constexpr int scan_threads()
+{
+    return HALF ? 4 * kWave : kGroups * kWave;
+}
+template <int MODE>
+constexpr int scan_waves_per_eu()
+{
+    return (MODE & kOptZoh) ? 6 : 2;
+}
+
+template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false, bool HALF = false>
+__global__ __launch_bounds__(scan_threads<HALF>())
+    __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<MODE>()))) void scan_kernel(ScanArgs a)
 {
     constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using T = typename Elem<DT>::T;
     using V = Buf<DT>;
     using Raw = typename V::Raw;
     constexpr int TT = kTileRows;
-    constexpr int RPW = TT / kGroups;     // rows each wave widens and finishes per tile
-    constexpr int PW = TT * kNS / 16;     // 16-word panel loads per tile and plane
+    constexpr int CH = ScanShape<HALF>::kCh;
+    // rows each lane widens and finishes per tile: one in the half-wave layout
+    // (wave w, half h: row 2w + h); TT / kGroups in the whole-wave one
+    constexpr int RPW = HALF ? 1 : TT / kGroups;
+    constexpr int PW = TT * kNS / 16;  // 16-word panel loads per tile and plane (whole-wave)
+    static_assert(!HALF || (TT == 8 && kNS == 2 && kGroups == 8),
+                  "half-wave layout: 8-row tiles, a tile's 16 values of a group in one register");
 
-    __shared__ float2 s_xd[2][TT][kWave];                       // (delta, delta*u) per row and channel
-    __shared__ float s_iv[ZOH ? 2 : 1][TT][kWave];              // 1/delta per row and channel (ZOH)
-    __shared__ float s_part[EMIT ? 2 : 1][kGroups][TT][kWave];  // partial C.h per wave
+    __shared__ float2 s_xd[2][TT][CH];                       // (delta, delta*u) per row and channel
+    __shared__ float s_iv[ZOH ? 2 : 1][TT][CH];              // 1/delta per row and channel (ZOH)
+    __shared__ float s_part[EMIT ? 2 : 1][kGroups][TT][CH];  // partial C.h per state group
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int half = HALF ? (lane >> 5) : 0;
+    const int ch = HALF ? (lane & 31) : lane;  // channel within the workgroup's block
+    const int g = HALF ? 2 * w + half : w;     // state group: entries kNS*g .. kNS*g+kNS-1
     const int64_t D = a.dim, L = a.seqlen, BD = a.batch * a.dim;
-    const int64_t d_raw = int64_t(blockIdx.x) * kWave + lane;
+    const int64_t d_raw = int64_t(blockIdx.x) * CH + ch;
     const bool active = d_raw < D;
     const int64_t d = active ? d_raw : D - 1;  // idle lanes shadow the last channel
     const int64_t b = blockIdx.y;
@@ -158,22 +201,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
 
     const uint32_t row_bytes = uint32_t(D) * V::kBytes;
     const uint32_t span = uint32_t(len) * row_bytes;
-    const uint32_t voff = active ? uint32_t(d_raw) * V::kBytes : kIdleOffset;
+    // vector offsets: the lane's channel, plus (half-wave) one row for the odd half.  The
+    // range check covers the vector offset only, so a half's row that is past the chunk
+    // end is never addressed: voff_lo (both halves on the even row) stands in for it.
+    const uint32_t voff_lo = active ? uint32_t(d_raw) * V::kBytes : kIdleOffset;
+    const uint32_t voff_hi = voff_lo + (active && half ? row_bytes : 0u);
     const __amdgpu_buffer_rsrc_t r_u = make_rsrc(static_cast<const T*>(a.u) + row0, span);
     const __amdgpu_buffer_rsrc_t r_dl = make_rsrc(static_cast<const T*>(a.delta) + row0, span);
     const __amdgpu_buffer_rsrc_t r_z = make_rsrc(HAS_Z ? static_cast<const T*>(a.z) + row0 : nullptr, span);
     const __amdgpu_buffer_rsrc_t r_y = make_rsrc(EMIT ? static_cast<T*>(a.y) + row0 : nullptr, span);
-    // the wave's B and C planes of the chunk's panel (address-space casts need the C cast form)
+    // the B and C planes of the chunk's panel
     const int64_t plane = a.panel_rows * kNS;
     const SS_CONST char* pB =
-        (const SS_CONST char*)(a.ws_panel + ((b * a.n_chunks + c) * kGroups + w) * 2 * plane);
+        (const SS_CONST char*)(a.ws_panel + ((b * a.n_chunks + c) * kGroups + g) * 2 * plane);
     const SS_CONST char* pC = pB + plane * 4;
+    // half-wave: the chunk's panel block as a buffer; lane 16q + k reads word k of a
+    // tile of its group's planes
+    const __amdgpu_buffer_rsrc_t r_pan =
+        make_rsrc(a.ws_panel + (b * a.n_chunks + c) * kGroups * 2 * plane, uint32_t(kGroups * 2 * plane * 4));
+    const uint32_t voff_pan = uint32_t((g * 2 * plane + (lane & 15)) * 4);
 
-    const int64_t sbase = bd * N + w * kNS;  // this lane's entries in a (B, D, N) state array
+    const int64_t sbase = bd * N + g * kNS;  // this lane's entries in a (B, D, N) state array
     float A2[kNS], iA[kNS];  // A * log2 e, and 1/A for the zero-order hold
 #pragma unroll
     for (int i = 0; i < kNS; ++i) {
-        const float av = a.A[d * N + w * kNS + i];
+        const float av = a.A[d * N + g * kNS + i];
         A2[i] = av * kLog2e;
         iA[i] = ZOH ? 1.0f / av : 0.0f;
     }
@@ -195,33 +247,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
 
     Raw rdl[2][RPW], ru[2][RPW], rz[2][RPW];  // raw rows in flight, by tile parity
     float xf[2][RPW], zf[2][RPW];             // widened u, z kept for the epilogue
-    Words16 bw[2][PW], cw[2][PW];             // the tile's panel words, by tile parity
+    Words16 bw[2][HALF ? 1 : PW], cw[2][HALF ? 1 : PW];  // whole-wave: the tile's panel words
+    float bv[2], cv[2];                                  // half-wave: the tile's B, C values
 
-    // row r of the chunk, clamped to the last one
-    auto clamp_row = [&](int r) { return r < len ? r : len - 1; };
+    // first row (within the chunk) a lane's wave widens in a tile: its rows are that
+    // row + j (whole-wave) or that row + its half (half-wave)
+    auto wave_row = [&](int tile) { return tile * TT + (HALF ? 2 * w : w * RPW); };
+    // the row a lane widens and finishes
+    auto lane_row = [&](int tile, int j) { return wave_row(tile) + (HALF ? half : j); };
 
     auto issue_rows = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
+        if constexpr (HALF) {
+            // the odd half reads the next row only when it is inside the chunk
+            const int r0 = wave_row(tile);
+            const int rs = r0 < len ? r0 : len - 1;
+            const uint32_t vo = r0 + 1 < len ? voff_hi : voff_lo;
+            const uint32_t so = uint32_t(rs) * row_bytes;
+            rdl[S][0] = V::load(r_dl, vo, so);
+            ru[S][0] = V::load(r_u, vo, so);
+            if (EMIT && HAS_Z) rz[S][0] = V::load(r_z, vo, so);
+        } else {
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            const uint32_t so = uint32_t(clamp_row(tile * TT + w * RPW + j)) * row_bytes;
-            rdl[S][j] = V::load(r_dl, voff, so);
-            ru[S][j] = V::load(r_u, voff, so);
-            if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, voff, so);
+            for (int j = 0; j < RPW; ++j) {
+                const int r = lane_row(tile, j);
+                const uint32_t so = uint32_t(r < len ? r : len - 1) * row_bytes;
+                rdl[S][j] = V::load(r_dl, voff_lo, so);
+                ru[S][j] = V::load(r_u, voff_lo, so);
+                if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, voff_lo, so);
+            }
         }
     };
-    // widen this wave's rows of a tile and publish (delta, delta*u).  Rows past
+    // widen this lane's rows of a tile and publish (delta, delta*u).  Rows past
     // the chunk end are published as (0, 0): exp2(0) = 1 and 0*B = 0 leave the
     // state bit-unchanged, so the last tiles need no row-count branches.
     auto publish_rows = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-            const bool in = tile * TT + w * RPW + j < len;
+            const int r = lane_row(tile, j) - tile * TT;
+            const bool in = lane_row(tile, j) < len;
             const float dl = in ? step_size<MODE>(V::widen(rdl[S][j]), bias) : 0.0f;
             const float x = V::widen(ru[S][j]);
-            s_xd[S][w * RPW + j][lane] = make_float2(dl, dl * x);
-            if constexpr (ZOH) s_iv[S][w * RPW + j][lane] = __builtin_amdgcn_rcpf(dl);
+            s_xd[S][r][ch] = make_float2(dl, dl * x);
+            if constexpr (ZOH) s_iv[S][r][ch] = __builtin_amdgcn_rcpf(dl);
             if (EMIT) {
                 xf[S][j] = x;
                 if (HAS_Z) {
@@ -233,55 +302,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
             }
         }
     };
-    // a tile's panel rows are contiguous: 16-word scalar loads at a 32-bit
-    // byte offset from the plane's 64-bit base, no clamping (the panel holds
-    // zero rows past the chunk end and one spare tile)
+    // a tile's panel rows are contiguous: whole-wave, 16-word scalar loads at a
+    // 32-bit byte offset from the plane's 64-bit base; half-wave, one word per
+    // lane.  No clamping: the panel holds zero rows past the chunk end and one
+    // spare tile.
     auto issue_words = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
         const uint32_t off = uint32_t(tile) * uint32_t(TT * kNS * 4);
-        const SS_CONST Words16* qb = (const SS_CONST Words16*)(pB + off);
-        const SS_CONST Words16* qc = (const SS_CONST Words16*)(pC + off);
+        if constexpr (HALF) {
+            bv[S] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_pan, voff_pan, off, 0));
+            if (EMIT)
+                cv[S] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_pan, voff_pan + uint32_t(plane * 4),
+                                                                             off, 0));
+        } else {
+            const SS_CONST Words16* qb = (const SS_CONST Words16*)(pB + off);
+            const SS_CONST Words16* qc = (const SS_CONST Words16*)(pC + off);
 #pragma unroll
-        for (int q = 0; q < PW; ++q) {
-            bw[S][q] = qb[q];
-            if (EMIT) cw[S][q] = qc[q];
+            for (int q = 0; q < PW; ++q) {
+                bw[S][q] = qb[q];
+                if (EMIT) cw[S][q] = qc[q];
+            }
         }
     };
-    // entry i of row r of a tile, from its panel words
-    auto word = [&](const Words16 (&wv)[PW], int r, int i) {
+    // entry i of row r of a tile, from its panel words (whole-wave)
+    auto word = [&](const Words16 (&wv)[HALF ? 1 : PW], int r, int i) {
         const int k = r * kNS + i;
         return __uint_as_float(wv[k / 16][k % 16]);
     };
-    // finish this wave's rows of a tile: sum the partials, skip, gate, store
+    // finish this lane's rows of a tile: sum the partials, skip, gate, store
     auto finish_rows = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-            const int r = w * RPW + j;
-            const int t = tile * TT + r;
+            const int t = lane_row(tile, j);
+            const int r = t - tile * TT;
             if (t < len) {
-                float acc = s_part[S][0][r][lane];
+                float acc = s_part[S][0][r][ch];
 #pragma unroll
-                for (int g = 1; g < kGroups; ++g) acc += s_part[S][g][r][lane];
+                for (int q = 1; q < kGroups; ++q) acc += s_part[S][q][r][ch];
                 if (HAS_D) acc = fmaf(dskip, xf[S][j], acc);
                 if (HAS_Z) acc *= silu(zf[S][j]);
-                V::store(r_y, voff, uint32_t(t) * row_bytes, acc);
+                if constexpr (HALF)
+                    V::store(r_y, voff_hi, uint32_t(wave_row(tile)) * row_bytes, acc);
+                else
+                    V::store(r_y, voff_lo, uint32_t(t) * row_bytes, acc);
             }
         }
     };
-    // the recurrence over one tile for this wave's state entries
+    // the recurrence over one tile for this lane's state entries
     auto scan_rows = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
         float2 xd[TT];
 #pragma unroll
-        for (int r = 0; r < TT; ++r) xd[r] = s_xd[S][r][lane];
-        // the next tile's scalar loads go out only after all of this tile's LDS
-        // reads have landed (LDS and scalar loads share one counter, and scalar
-        // loads return out of order: a later LDS wait would drain them too)
+        for (int r = 0; r < TT; ++r) xd[r] = s_xd[S][r][ch];
+        // whole-wave: the next tile's scalar loads go out only after all of this
+        // tile's LDS reads have landed (LDS and scalar loads share one counter, and
+        // scalar loads return out of order: a later LDS wait would drain them too)
         static_assert(TT == 8, "the wait below names eight rows");
         float iv[TT];  // 1/delta per row (zero-order hold only)
 #pragma unroll
-        for (int r = 0; r < TT; ++r) iv[r] = ZOH ? s_iv[ZOH ? S : 0][r][lane] : 0.0f;
+        for (int r = 0; r < TT; ++r) iv[r] = ZOH ? s_iv[ZOH ? S : 0][r][ch] : 0.0f;
         __asm__ volatile("" ::"v"(xd[0].x), "v"(xd[0].y), "v"(xd[1].x), "v"(xd[1].y), "v"(xd[2].x), "v"(xd[2].y),
                          "v"(xd[3].x), "v"(xd[3].y), "v"(xd[4].x), "v"(xd[4].y), "v"(xd[5].x), "v"(xd[5].y),
                          "v"(xd[6].x), "v"(xd[6].y), "v"(xd[7].x), "v"(xd[7].y)
@@ -307,22 +387,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
 #pragma unroll
             for (int i = 0; i < kNS; ++i) e[r][i] = exp2_hw(x2[r][i]);
         }
-#pragma unroll
-        for (int r = 0; r < TT; ++r) {
-            const float xb = xd[r].y;
-#pragma unroll
-            for (int i = 0; i < kNS; ++i) {
-                float in_term = xb * word(bw[S], r, i);  // delta*B*u (Euler)
-                if constexpr (ZOH) in_term *= zoh_phi(x2[r][i], e[r][i], iA[i] * iv[r]);
-                h[i] = fmaf(e[r][i], h[i], in_term);
-            }
+        if constexpr (HALF) {
+            float hh[TT][kNS];  // the state after each row, for the C contraction
+            static_for<TT>([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                const float xb = xd[r].y;
+                static_for<kNS>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    float in_term = xb * row_bcast<r * kNS + i>(bv[S]);  // delta*B*u (Euler)
+                    if constexpr (ZOH) in_term *= zoh_phi(x2[r][i], e[r][i], iA[i] * iv[r]);
+                    h[i] = fmaf(e[r][i], h[i], in_term);
+                    hh[r][i] = h[i];
+                });
+                if constexpr (!EMIT) dsum += xd[r].x;
+            });
             if constexpr (EMIT) {
-                float acc = 0.0f;
+                float acc[TT];
+                contract_rows_bcast(acc, cv[S], hh);
 #pragma unroll
-                for (int i = 0; i < kNS; ++i) acc = fmaf(word(cw[S], r, i), h[i], acc);
-                s_part[S][w][r][lane] = acc;
-            } else {
-                dsum += xd[r].x;
+                for (int r = 0; r < TT; ++r) s_part[S][g][r][ch] = acc[r];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < TT; ++r) {
+                const float xb = xd[r].y;
+#pragma unroll
+                for (int i = 0; i < kNS; ++i) {
+                    float in_term = xb * word(bw[S], r, i);  // delta*B*u (Euler)
+                    if constexpr (ZOH) in_term *= zoh_phi(x2[r][i], e[r][i], iA[i] * iv[r]);
+                    h[i] = fmaf(e[r][i], h[i], in_term);
+                }
+                if constexpr (EMIT) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < kNS; ++i) acc = fmaf(word(cw[S], r, i), h[i], acc);
+                    s_part[S][g][r][ch] = acc;
+                } else {
+                    dsum += xd[r].x;
+                }
             }
         }
     };
@@ -359,7 +461,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
     float* ck_row = nullptr;
     int64_t ck_step = 0;
     if constexpr (CKPT) {
-        ck_row = a.ckpt + ((t0 / kBwdSub * a.batch + b) * N + w * kNS) * D + d;
+        ck_row = a.ckpt + ((t0 / kBwdSub * a.batch + b) * N + g * kNS) * D + d;
         ck_step = a.batch * N * D;
     }
     const int quarter = (ntiles / 4) & ~1;
@@ -393,7 +495,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
         float* dst = a.ws_state + (c + 1) * BD * N + sbase;
 #pragma unroll
         for (int i = 0; i < kNS; ++i) dst[i] = h[i];
-        if (w == 0) a.ws_dsum[c * BD + bd] = dsum;
+        if (g == 0) a.ws_dsum[c * BD + bd] = dsum;
     }
 }
 
@@ -546,15 +648,17 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     }
 }
 
-template <int DT, bool HAS_D, bool HAS_Z, int MODE>
-hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
+template <int DT, bool HAS_D, bool HAS_Z, int MODE, bool HALF>
+hipError_t launch_scan_layout(const ScanArgs& a, hipStream_t s)
 {
-    const unsigned nblk = unsigned((a.dim + kWave - 1) / kWave);
+    constexpr int CH = ScanShape<HALF>::kCh;
+    const dim3 block(ScanShape<HALF>::kWaves * kWave);
+    const unsigned nblk = unsigned((a.dim + CH - 1) / CH);
     const int64_t words = a.batch * a.n_chunks * 2 * a.panel_rows * N;
     panel_kernel<DT><<<dim3(unsigned((words + 255) / 256)), dim3(256), 0, s>>>(a);
     if (a.n_chunks > 1) {
-        scan_kernel<DT, false, false, false, MODE>
-            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), dim3(kThreads), 0, s>>>(a);
+        scan_kernel<DT, false, false, false, MODE, false, HALF>
+            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), block, 0, s>>>(a);
         // R lanes per state entry: the power of two covering the K-1 aggregated chunks, 4..64
         const int64_t n_carry = a.n_chunks - 1;
         if (n_carry <= 4)
@@ -570,10 +674,17 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
     }
     const dim3 grid(nblk, unsigned(a.batch), unsigned(a.n_chunks));
     if (a.ckpt)
-        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, true><<<grid, dim3(kThreads), 0, s>>>(a);
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, true, HALF><<<grid, block, 0, s>>>(a);
     else
-        scan_kernel<DT, true, HAS_D, HAS_Z, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, HALF><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
+}
+
+template <int DT, bool HAS_D, bool HAS_Z, int MODE>
+hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
+{
+    return a.half ? launch_scan_layout<DT, HAS_D, HAS_Z, MODE, true>(a, s)
+                  : launch_scan_layout<DT, HAS_D, HAS_Z, MODE, false>(a, s);
 }
 
 template <int DT, bool HAS_D, bool HAS_Z, int MODE>

@@ -20,7 +20,14 @@
  *                    scan's per-element group (four fp32 multiply/fma plus one
  *                    v_exp_f32) for 8 rows x 16 states per iteration (128
  *                    groups); kind 3: one dependent chain of 16 fma per
- *                    iteration; kind 4: one dependent chain of 16 v_exp_f32.
+ *                    iteration; kind 4: one dependent chain of 16 v_exp_f32;
+ *                    kind 5: kind 2 without its v_exp_f32; kind 6: kind 2
+ *                    with each pair of rows' 32 exp2 issued as one batch;
+ *                    kind 7: waves of even workgroups kind 0, of odd ones kind 1;
+ *                    kind 8: kind 6 with a workgroup barrier before and after
+ *                    each batch of exp2 (the waves of a workgroup change phase
+ *                    together); kinds 9, 10, 11: one v_exp_f32 beside 2, 4
+ *                    or 8 independent fp32 fma, 8 groups per iteration.
  *                    Launch: `blocks` workgroups of 256 lanes (four waves);
  *                    cycles holds blocks*8 entries (uint64), sink blocks*256
  *                    floats.
@@ -42,6 +49,10 @@ int ss_probe_stream(const void* in0, const void* in1, const void* in2, void* out
                     int blocks, hipStream_t stream);
 
 int ss_probe_alu(int kind, int iters, int blocks, uint64_t* cycles, float* sink, hipStream_t stream);
+
+/* ss_probe_alu with workgroups of `threads` lanes (256, 512 or 1024: 1, 2 or 4 waves per
+ * SIMD from one workgroup); cycles holds blocks*threads/64*2 entries, sink blocks*threads. */
+int ss_probe_alu_wg(int kind, int iters, int blocks, int threads, uint64_t* cycles, float* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

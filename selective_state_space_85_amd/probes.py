@@ -24,6 +24,8 @@ def load() -> ctypes.CDLL:
         lib.ss_probe_stream.restype = ctypes.c_int
         lib.ss_probe_alu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         lib.ss_probe_alu.restype = ctypes.c_int
+        lib.ss_probe_alu_wg.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        lib.ss_probe_alu_wg.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -64,10 +66,14 @@ def stream_rate(n_read: int, bytes_each: int = 1 << 30, reps: int = 5, device: s
     return {"read_write": "%d:1" % n_read, "bytes_per_launch": moved, "ms": ms, "GB/s": moved / (ms * 1e-3) / 1e9}
 
 
-KINDS = ("fma", "exp2", "scan element: mul, exp2, mul, fma, fma", "dependent fma chain", "dependent exp2 chain")
+KINDS = ("fma", "exp2", "scan element: mul, exp2, mul, fma, fma", "dependent fma chain", "dependent exp2 chain",
+         "scan element without exp2", "scan element, exp2 batched per two rows", "fma waves beside exp2 waves",
+         "scan element, exp2 batched, workgroup in phase", "exp2 + 2 independent fma", "exp2 + 4 independent fma",
+         "exp2 + 8 independent fma")
 
 
-def alu_rate(kind: int, iters: int = 0, waves_per_simd: int = 4, device: str = "cuda") -> Dict[str, float]:
+def alu_rate(kind: int, iters: int = 0, waves_per_simd: int = 4, device: str = "cuda",
+             wg_waves_per_simd: int = 1) -> Dict[str, float]:
     """The vector-ALU issue probe with ``waves_per_simd`` waves resident on every SIMD (see
     ss_probe.h for the kinds).  Returns per wave64 instruction group: the shader-clock
     cycles one SIMD spends (median over waves of s_memtime cycles / groups, divided by
@@ -76,17 +82,19 @@ def alu_rate(kind: int, iters: int = 0, waves_per_simd: int = 4, device: str = "
     second from event time, and the shader clock implied by s_memtime against the
     100 MHz reference clock."""
     lib = load()
-    groups_per_iter = 128 if kind == 2 else 16
+    groups_per_iter = 128 if kind in (2, 5, 6, 8) else (8 if kind >= 9 else 16)
     if iters <= 0:
-        iters = {0: 16384, 1: 8192, 2: 1024, 3: 8192, 4: 2048}[kind]
-    blocks = 256 * waves_per_simd  # four waves per workgroup, one per SIMD
-    cycles = torch.zeros(blocks * 8, dtype=torch.int64, device=device)
-    sink = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+        iters = {0: 16384, 1: 8192, 2: 1024, 3: 8192, 4: 2048, 5: 1024, 6: 1024, 7: 8192, 8: 1024, 9: 8192,
+                 10: 8192, 11: 4096}[kind]
+    threads = 256 * wg_waves_per_simd  # a workgroup holds wg_waves_per_simd waves on each SIMD
+    blocks = 256 * waves_per_simd // wg_waves_per_simd
+    cycles = torch.zeros(blocks * threads // 64 * 2, dtype=torch.int64, device=device)
+    sink = torch.empty(blocks * threads, dtype=torch.float32, device=device)
     s = torch.cuda.current_stream()
 
     def launch():
-        _check("ss_probe_alu", lib.ss_probe_alu(kind, iters, blocks, ctypes.c_void_p(cycles.data_ptr()),
-                                                ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
+        _check("ss_probe_alu", lib.ss_probe_alu_wg(kind, iters, blocks, threads, ctypes.c_void_p(cycles.data_ptr()),
+                                                   ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
 
     launch()  # warms the clocks up
     torch.cuda.synchronize()
@@ -100,9 +108,10 @@ def alu_rate(kind: int, iters: int = 0, waves_per_simd: int = 4, device: str = "
     c = cycles.cpu().double().view(-1, 2)
     cyc = float(c[:, 0].median())
     ref = float(c[:, 1].median())
-    groups = float(blocks) * 256 * iters * groups_per_iter  # lane-groups over the chip
+    groups = float(blocks) * threads * iters * groups_per_iter  # lane-groups over the chip
     per_wave = cyc / (iters * groups_per_iter)
-    return {"kind": KINDS[kind], "waves_per_simd": waves_per_simd, "iters": iters,
+    return {"kind": KINDS[kind], "waves_per_simd": waves_per_simd, "wg_waves_per_simd": wg_waves_per_simd,
+            "iters": iters,
             "cycles_per_wave_group_per_simd": per_wave / waves_per_simd,
             "cycles_per_group_per_wave": per_wave,
             "lane_groups_per_s": groups / (ms * 1e-3), "ms": ms,
