@@ -79,7 +79,18 @@ typedef enum { SS_DELTA_SOFTPLUS = 1, SS_B_ZOH = 2 } ss_option;
  * covers timesteps [c*chunk_len_T, min((c+1)*chunk_len_T, seqlen)).  Chunks
  * are joined by an exact associative combine of affine pairs (LTI chapter
  * 3.1, section 3.1.5.2, parallel scan over an associative operator):
- * (a1, b1) then (a2, b2) gives (a2*a1, a2*b1 + b2).
+ * (a1, b1) then (a2, b2) gives (a2*a1, a2*b1 + b2).  Chunks shorter than
+ * 1024 rows: every chunk but the last first has its end state from a zero
+ * start found (its affine pair), the pairs are combined into each chunk's
+ * carry, and every chunk is run from its carry to produce y.  Chunks of 1024
+ * rows or more (a multiple of 16), without checkpoints: every chunk is first
+ * run from its own start (h0 for the first, zero for the others), writing y
+ * and its end state; the carries follow; then each later chunk is rerun from
+ * its carry over its first 384 rows, and over the rest only where the
+ * carry's effect has not decayed below fp32 resolution by then (all step
+ * sizes of the chunk >= 0, A <= 0, and exp(A * sum of delta) * |carry| <=
+ * 2^-24 of the lane's largest state entry).  Either way the result is the
+ * one-pass recurrence up to fp32 rounding.
  *
  * The chunk length is a power of two chosen from the shape only: pure,
  * host-only, deterministic.  Writes *chunk_len_T and *n_chunks_K (either may
@@ -110,8 +121,15 @@ ss_status ss_scan_plan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
  *   [0, K*BD*N)            state slots (K, batch, dim, N): slot 0 holds the
  *                          initial state (h0, or zeros); slot c, 1 <= c < K,
  *                          holds the state right after timestep c*chunk_len-1,
- *                          i.e. the carry into chunk c.
- *   [K*BD*N, +(K-1)*BD)    sum of delta over chunk c, (K-1, batch, dim).
+ *                          i.e. the carry into chunk c.  (With a checkpoint
+ *                          output the chunked plans always take the
+ *                          aggregate pass.)
+ *   [K*BD*N, +K*BD)        sum of delta over chunk c, (K, batch, dim).
+ *   then, when chunk_len >= 1024 and a multiple of 16 (emit first, see
+ *   ss_scan_plan): (K-1, batch, ceil(dim/32)) uint32 words, 1 where chunk c+1
+ *   was rerun over its whole length, 0 where over its first 384 rows only;
+ *   then (K, batch, ceil(dim/32)) uint32 words, 1 where chunk c has a
+ *   negative step size.
  *   always, from the next multiple of 256 bytes to the end:
  *                          an fp32 copy of B and C, per (batch row, chunk),
  *                          regrouped in the order the scan kernels read it

@@ -130,11 +130,26 @@ bool half_layout(int64_t batch, int64_t dim, int64_t K)
     return ceil_div(halves, kCUs) < 2 * ceil_div(whole, kCUs);
 }
 
+// Emit first, then correct: for chunks of kCorrMinChunk rows or more (a
+// multiple of two 8-row tiles) every chunk is first run from its own start,
+// and chunks 1..K-1 are then rerun from their carries over their first
+// kCorrHead rows (and further only where the carry's effect has not decayed
+// below fp32 resolution by then).  Shorter chunks take the aggregate pass
+// instead.  Not with checkpoints.  Returns the rerun head in tiles, or 0.
+constexpr int64_t kCorrMinChunk = 1024, kCorrHead = 384;
+int corr_head_tiles(int64_t T, int64_t K)
+{
+    if (K < 2 || T < kCorrMinChunk || T % (2 * ssk::kTileRows) != 0) return 0;
+    return int(kCorrHead / ssk::kTileRows);
+}
+
 // Workspace layout for K chunks of T rows (fp32 words):
 //   K > 1: K state slots of batch*dim*dstate, then (K-1)*batch*dim delta sums;
 //   then, at the next multiple of 256 bytes, the B/C panel of
 //   batch*K*2*panel_rows(min(T, seqlen))*dstate words.
 struct WsLayout {
+    int64_t flags_offset = 0;  // bytes (K > 1, emit first): "whole chunk rerun" flags
+    int64_t neg_offset = 0;    // bytes: "negative step size" flags
     int64_t panel_offset;  // bytes
     int64_t panel_words;
     int64_t panel_rows;
@@ -145,11 +160,17 @@ bool ws_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64
 {
     int64_t front = 0;
     if (K > 1) {
-        int64_t bd, slots, dsums;
+        int64_t bd, slots, dsums, flags = 0;
         if (!mul(batch, dim, &bd)) return false;
         if (!mul(bd, dstate, &slots) || !mul(slots, K, &slots)) return false;
-        if (!mul(bd, K - 1, &dsums)) return false;
-        if (__builtin_add_overflow(slots, dsums, &front) || !mul(front, 4, &front)) return false;
+        if (!mul(bd, K, &dsums)) return false;
+        // emit first: (K-1) "whole chunk rerun" and K "negative step" flags per block
+        if (corr_head_tiles(T, K) > 0 && !mul(batch * ceil_div(dim, 32), 2 * K - 1, &flags)) return false;
+        w->flags_offset = (slots + dsums) * 4;
+        w->neg_offset = w->flags_offset + batch * ceil_div(dim, 32) * (K - 1) * 4;
+        if (__builtin_add_overflow(slots, dsums, &front) || __builtin_add_overflow(front, flags, &front) ||
+            !mul(front, 4, &front))
+            return false;
     }
     if (__builtin_add_overflow(front, int64_t(255), &front)) return false;
     w->panel_offset = front & ~int64_t(255);
@@ -409,6 +430,8 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
     a.h_last = h_last;
     a.ws_state = K > 1 ? static_cast<float*>(workspace) : nullptr;
     a.ws_dsum = K > 1 ? static_cast<float*>(workspace) + K * batch * dim * dstate : nullptr;
+    a.ws_whole = K > 1 ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + wl.flags_offset) : nullptr;
+    a.ws_neg = K > 1 ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + wl.neg_offset) : nullptr;
     a.ws_panel = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.panel_offset);
     a.panel_rows = wl.panel_rows;
     a.ckpt = ckpt;
@@ -418,6 +441,8 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
     a.chunk_len = T;
     a.n_chunks = K;
     a.half = half_layout(batch, dim, K);
+    a.corr_head_tiles = ckpt ? 0 : corr_head_tiles(T, K);
+    a.pass = 0;
     const hipError_t err = ssk::launch_scan(a, dtype == SS_F32 ? 0 : 1, stream);
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;
@@ -478,6 +503,7 @@ ss_status ss_step_ex(float* h, const void* u, const void* delta, const float* A,
     a.y = y;
     a.batch = batch;
     a.dim = dim;
+    a.vec_bc = aligned(B, 16) && aligned(C, 16);
     const hipError_t err = ssk::launch_step(a, dtype == SS_F32 ? 0 : 1, stream);
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;

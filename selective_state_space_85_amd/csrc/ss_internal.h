@@ -54,7 +54,10 @@ struct ScanArgs {
     void* y;
     float* h_last;       // nullable
     float* ws_state;     // (K, batch, dim, N) state slots, nullable when K == 1
-    float* ws_dsum;      // (K-1, batch, dim) per-chunk delta sums
+    float* ws_dsum;      // (K, batch, dim) per-chunk delta sums
+    // (K-1, batch, ceil(dim/32)), emit first: 1 where the correction pass reran
+    // the whole chunk c+1, 0 where only its head
+    uint32_t* ws_whole;
     // (batch, K, waves, {B, C}, panel_rows, kGroupStates) fp32 copy of B and C,
     // regrouped so that a wave's entries of consecutive rows are contiguous
     float* ws_panel;
@@ -68,6 +71,14 @@ struct ScanArgs {
     // the half-wave layout (32 channels per 4-wave workgroup) instead of the
     // whole-wave one (64 channels per 8-wave workgroup)
     bool half;
+    // > 0 (with K > 1 and no checkpoints): emit first, then correct.  Pass 1
+    // runs every chunk from its own start and writes y; the carry pass follows;
+    // pass 2 reruns chunks 1..K-1 from their carries over their first
+    // corr_head_tiles tiles (even), and over the rest only where the carry's
+    // effect has not decayed below fp32 resolution by then
+    int corr_head_tiles;
+    int pass;  // 0: a plain emit pass; 1, 2: the emit-first passes
+    uint32_t* ws_neg;  // (K, batch, ceil(dim/32)): pass 1 met a negative step size
 };
 
 struct StepArgs {
@@ -83,6 +94,7 @@ struct StepArgs {
     uint32_t options;         // kOpt* bits
     void* y;
     int64_t batch, dim;
+    bool vec_bc;  // B and C are 16-byte aligned: their rows are read 16 bytes at a time
 };
 
 // Backward: rows per sub-block, which is also the spacing of the state

@@ -160,10 +160,12 @@ constexpr int scan_waves_per_eu()
     return (MODE & kOptZoh) ? 6 : 2;
 }
 
-template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false, bool HALF = false>
+template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false, bool HALF = false,
+          bool CORR = false>
 __global__ __launch_bounds__(scan_threads<HALF>())
     __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<MODE>()))) void scan_kernel(ScanArgs a)
 {
+    static_assert(!CORR || (EMIT && !CKPT), "the emit-first passes are emit passes without checkpoints");
     constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using T = typename Elem<DT>::T;
     using V = Buf<DT>;
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const bool active = d_raw < D;
     const int64_t d = active ? d_raw : D - 1;  // idle lanes shadow the last channel
     const int64_t b = blockIdx.y;
-    const int64_t c = blockIdx.z;
+    const int64_t c = blockIdx.z + ((CORR && a.pass == 2) ? 1 : 0);  // the correction pass skips chunk 0
     const int64_t t0 = c * a.chunk_len;
     const int len = int(((t0 + a.chunk_len < L) ? t0 + a.chunk_len : L) - t0);
     // an even number of tiles; rows past the chunk end are neutral (see publish_rows)
@@ -232,8 +234,12 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const float bias = a.delta_bias ? a.delta_bias[d] : 0.0f;
 
     float h[kNS];
-    const bool from_ws = EMIT && a.n_chunks > 1;
-    const bool from_h0 = EMIT && a.n_chunks == 1 && a.h0 != nullptr;
+    // whole sequence, or the emit after an aggregate pass: from h0 or the carry;
+    // emit first (pass 1): chunk 0 from h0, the others from zero; correction
+    // (pass 2): from the carry
+    const bool first = CORR && a.pass == 1;
+    const bool from_ws = EMIT && a.n_chunks > 1 && !first;
+    const bool from_h0 = EMIT && a.h0 != nullptr && (a.n_chunks == 1 || (first && c == 0));
     if (from_ws || from_h0) {
         const float* init = from_ws ? a.ws_state + c * BD * N + sbase : a.h0 + sbase;
 #pragma unroll
@@ -244,6 +250,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     }
     const float dskip = (EMIT && HAS_D) ? a.Dskip[d] : 0.0f;
     float dsum = 0.0f;
+    float dmin = __builtin_inff();  // emit first: the smallest step size of the chunk
 
     Raw rdl[2][RPW], ru[2][RPW], rz[2][RPW];  // raw rows in flight, by tile parity
     float xf[2][RPW], zf[2][RPW];             // widened u, z kept for the epilogue
@@ -371,6 +378,14 @@ __global__ __launch_bounds__(scan_threads<HALF>())
                              "v"(iv[7])
                              : "memory");
         issue_words(tile + 1, Slot<1 - S>{});
+        if constexpr (CORR) {
+            // rows past the chunk end are published with delta = 0: no effect on either
+#pragma unroll
+            for (int r = 0; r < TT; ++r) {
+                dsum += xd[r].x;
+                dmin = fminf(dmin, xd[r].x);
+            }
+        }
         // All delta*A products of the tile are formed before the first exp2 is
         // issued (the empty asm statements pin them in registers), so every
         // exp2 reads an operand produced many instructions earlier instead of
@@ -431,10 +446,11 @@ __global__ __launch_bounds__(scan_threads<HALF>())
 
     // one tile step: finish tile k-1, publish tile k+1, scan tile k
     // every load below is clamped to a valid row, so all of it runs unconditionally
-    auto step = [&](int k, auto slot) {
+    // k0: the first tile of the current run (the tile before it is finished already)
+    auto step = [&](int k, int k0, auto slot) {
         constexpr int S = decltype(slot)::value;
         if constexpr (EMIT) {
-            if (k >= 1) finish_rows(k - 1, Slot<1 - S>{});
+            if (k > k0) finish_rows(k - 1, Slot<1 - S>{});
         }
         publish_rows(k + 1, Slot<1 - S>{});
         issue_rows(k + 3, Slot<1 - S>{});
@@ -442,19 +458,13 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         __syncthreads();
     };
 
-    issue_rows(0, Slot<0>{});
-    issue_rows(1, Slot<1>{});
-    publish_rows(0, Slot<0>{});
-    issue_rows(2, Slot<0>{});
-    issue_words(0, Slot<0>{});
-    __syncthreads();
-
     // Two or three workgroups share a CU, and the wave arbiter favours older
     // waves: left alone, the first workgroup finishes far ahead of the last and
     // the CU ends its run with a single latency-bound workgroup.  Lowering a
     // wave's priority at each quarter of the chunk lets the laggards catch up,
     // so the workgroups of a CU stay within a quarter of each other.
     static_assert(2 * kTileRows == kBwdSub, "checkpoints fall at the start of every tile pair");
+    constexpr float kCorrTol = 5.9604645e-8f;  // 2^-24
     // checkpoints (a separate instantiation: the plain kernel has no scalar
     // registers to spare): this lane's entries of the one at row t0 + k*TT,
     // advanced by one checkpoint per tile pair
@@ -464,32 +474,111 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         ck_row = a.ckpt + ((t0 / kBwdSub * a.batch + b) * N + g * kNS) * D + d;
         ck_step = a.batch * N * D;
     }
-    const int quarter = (ntiles / 4) & ~1;
-    __builtin_amdgcn_s_setprio(3);
-    for (int k = 0; k < ntiles; k += 2) {
-        if (quarter > 0) {
-            if (k == quarter) __builtin_amdgcn_s_setprio(2);
-            else if (k == 2 * quarter) __builtin_amdgcn_s_setprio(1);
-            else if (k == 3 * quarter) __builtin_amdgcn_s_setprio(0);
-        }
-        if constexpr (CKPT) {
-            // the state entering row t0 + k*TT, a multiple of kBwdSub (k is even)
-            if (active && k * TT < len) {
-#pragma unroll
-                for (int i = 0; i < kNS; ++i) ck_row[int64_t(i) * D] = h[i];
+    // tiles [k0, k1) (both even) of the chunk, with the prefetch pipeline primed at k0
+    auto run = [&](int k0, int k1) {
+        issue_rows(k0, Slot<0>{});
+        issue_rows(k0 + 1, Slot<1>{});
+        publish_rows(k0, Slot<0>{});
+        issue_rows(k0 + 2, Slot<0>{});
+        issue_words(k0, Slot<0>{});
+        __syncthreads();
+        const int quarter = ((k1 - k0) / 4) & ~1;
+        __builtin_amdgcn_s_setprio(3);
+        for (int k = k0; k < k1; k += 2) {
+            if (quarter > 0) {
+                if (k - k0 == quarter) __builtin_amdgcn_s_setprio(2);
+                else if (k - k0 == 2 * quarter) __builtin_amdgcn_s_setprio(1);
+                else if (k - k0 == 3 * quarter) __builtin_amdgcn_s_setprio(0);
             }
-            ck_row += ck_step;
+            if constexpr (CKPT) {
+                // the state entering row t0 + k*TT, a multiple of kBwdSub (k is even)
+                if (active && k * TT < len) {
+#pragma unroll
+                    for (int i = 0; i < kNS; ++i) ck_row[int64_t(i) * D] = h[i];
+                }
+                ck_row += ck_step;
+            }
+            step(k, k0, Slot<0>{});
+            step(k + 1, k0, Slot<1>{});
         }
-        step(k, Slot<0>{});
-        step(k + 1, Slot<1>{});
+        if constexpr (EMIT) finish_rows(k1 - 1, Slot<1>{});
+    };
+
+    if constexpr (CORR) {
+        if (a.pass == 2) {
+            // Correction of chunk c >= 1 after the emit-first pass, which ran it from
+            // a zero state.  From the carry H, rows [0, head) are rerun exactly.  The
+            // state then differs from the zero-start one by P * H, P = exp(A * sum of
+            // delta so far); where the chunk's step sizes are all >= 0 and A <= 0
+            // that difference only decays, so the first pass's later rows are right
+            // to fp32 resolution once P*|H| <= 2^-24 of the lane's largest |state|.
+            // Otherwise the workgroup reruns the rest of the chunk too.
+            float H[kNS];
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) H[i] = h[i];
+            const int head = a.corr_head_tiles < ntiles ? a.corr_head_tiles : ntiles;
+            run(0, head);
+            const int64_t n32 = (D + 31) / 32;
+            const int64_t fl = (c * a.batch + b) * n32 + int64_t(blockIdx.x) * (CH / 32);
+            float smax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) smax = fmaxf(smax, fabsf(h[i]));
+            // no negative step size in the chunk (first pass); idle lanes have no say
+            bool ok = a.ws_neg[fl] == 0u;
+#pragma unroll
+            for (int i = 0; i < kNS; ++i)
+                ok = ok && A2[i] <= 0.0f && exp2_hw(A2[i] * dsum) * fabsf(H[i]) <= kCorrTol * smax;
+            ok = ok || !active;
+            const bool whole = __syncthreads_or(!ok) != 0;
+            if (threadIdx.x == 0) {
+                // one flag per 32-channel block (a whole-wave workgroup holds two)
+                uint32_t* f = a.ws_whole + ((c - 1) * a.batch + b) * n32 + int64_t(blockIdx.x) * (CH / 32);
+                f[0] = whole ? 1u : 0u;
+                if (CH == 64 && int64_t(blockIdx.x) * 2 + 1 < n32) f[1] = whole ? 1u : 0u;
+            }
+            if (whole) run(head, ntiles);
+            if (!active || c != a.n_chunks - 1 || !a.h_last) return;
+            if (whole) {
+#pragma unroll
+                for (int i = 0; i < kNS; ++i) a.h_last[sbase + i] = h[i];
+            } else {
+                // the first pass's end state from zero, plus the carry decayed over
+                // the whole chunk
+                const float dtot = a.ws_dsum[c * BD + bd];
+#pragma unroll
+                for (int i = 0; i < kNS; ++i)
+                    a.h_last[sbase + i] = fmaf(exp2_hw(A2[i] * dtot), H[i], a.h_last[sbase + i]);
+            }
+            return;
+        }
     }
-    if constexpr (EMIT) finish_rows(ntiles - 1, Slot<1>{});
+    run(0, ntiles);
+    if constexpr (CORR) {
+        // emit first: whether any step size of the chunk is negative, per workgroup
+        const bool neg = __syncthreads_or(dmin < 0.0f) != 0;
+        if (threadIdx.x == 0) {
+            const int64_t n32 = (D + 31) / 32;
+            uint32_t* f = a.ws_neg + (c * a.batch + b) * n32 + int64_t(blockIdx.x) * (CH / 32);
+            f[0] = neg ? 1u : 0u;
+            if (CH == 64 && int64_t(blockIdx.x) * 2 + 1 < n32) f[1] = neg ? 1u : 0u;
+        }
+    }
 
     if (!active) return;
     if (EMIT) {
         if (c == a.n_chunks - 1 && a.h_last) {
 #pragma unroll
             for (int i = 0; i < kNS; ++i) a.h_last[sbase + i] = h[i];
+        }
+        if (CORR) {
+            // emit first: the end state from the chunk's own start (h0 for chunk 0,
+            // zero for the others) and the chunk's delta sum, for the carry pass
+            if (c < a.n_chunks - 1) {
+                float* dst = a.ws_state + (c + 1) * BD * N + sbase;
+#pragma unroll
+                for (int i = 0; i < kNS; ++i) dst[i] = h[i];
+            }
+            if (g == 0) a.ws_dsum[c * BD + bd] = dsum;
         }
     } else {
         float* dst = a.ws_state + (c + 1) * BD * N + sbase;
@@ -591,14 +680,71 @@ void launch_carry(const ScanArgs& a, hipStream_t s)
     carry_kernel<R><<<dim3(unsigned(a.batch * a.dim)), dim3(kWave), 0, s>>>(a);
 }
 
+// R lanes per state entry: the power of two covering the K-1 aggregated chunks, 4..64
+void launch_carry_for(const ScanArgs& a, hipStream_t s)
+{
+    const int64_t n_carry = a.n_chunks - 1;
+    if (n_carry <= 4)
+        launch_carry<4>(a, s);
+    else if (n_carry <= 8)
+        launch_carry<8>(a, s);
+    else if (n_carry <= 16)
+        launch_carry<16>(a, s);
+    else if (n_carry <= 32)
+        launch_carry<32>(a, s);
+    else
+        launch_carry<64>(a, s);
+}
+
 // ---------------------------------------------------------------------------
-// Recurrent step.  Four lanes per channel (b, d), each with 4 of the 16 state
-// entries (16-byte loads/stores of h), the quad's partial C.h summed with two
-// butterfly exchanges.  grid = ceil(batch*dim*4 / 256), block = 256.
+// Recurrent step.  Q lanes per channel (b, d), each with S = 16/Q of the 16
+// state entries: S/4 16-byte loads and stores of h and of A, and (VEC, when
+// the host has checked B and C for 16-byte alignment) B and C as 16-byte
+// loads too; the partial C.h of the Q lanes summed with log2(Q) butterfly
+// exchanges.  grid = ceil(batch*dim*Q / 256), block = 256.
 // ---------------------------------------------------------------------------
-template <int DT, bool HAS_D, bool HAS_Z, int MODE>
+template <int DT, int S, bool VEC>
+__device__ __forceinline__ void load_row(const typename Elem<DT>::T* p, float (&out)[S])
+{
+    if constexpr (VEC && DT == 1 && S == 4) {
+        // bf16: 4 values per 8 bytes
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        out[0] = __uint_as_float(v.x << 16);
+        out[1] = __uint_as_float(v.x & 0xffff0000u);
+        out[2] = __uint_as_float(v.y << 16);
+        out[3] = __uint_as_float(v.y & 0xffff0000u);
+    } else if constexpr (VEC && DT == 1 && S >= 8) {
+        // bf16: 8 values per 16 bytes
+#pragma unroll
+        for (int k = 0; k < S / 8; ++k) {
+            const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                out[8 * k + 2 * j] = __uint_as_float(wv[j] << 16);
+                out[8 * k + 2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+            }
+        }
+    } else if constexpr (VEC && DT == 0) {
+#pragma unroll
+        for (int k = 0; k < S / 4; ++k) {
+            const float4 v = reinterpret_cast<const float4*>(p)[k];
+            out[4 * k] = v.x;
+            out[4 * k + 1] = v.y;
+            out[4 * k + 2] = v.z;
+            out[4 * k + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < S; ++i) out[i] = Elem<DT>::load(p, i);
+    }
+}
+
+template <int DT, bool HAS_D, bool HAS_Z, int MODE, int Q, bool VEC, int CPL>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
 {
+    constexpr int S = N / Q;  // state entries per lane
+    static_assert(Q == 1 || Q == 2 || Q == 4, "1, 2 or 4 lanes per channel");
     using E = Elem<DT>;
     using T = typename E::T;
     const T* __restrict__ u = static_cast<const T*>(a.u);
@@ -608,43 +754,73 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     const T* __restrict__ z = static_cast<const T*>(a.z);
     T* __restrict__ y = static_cast<T*>(a.y);
 
-    const int64_t total = a.batch * a.dim * 4;
-    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const bool active = gid < total;
-    const int64_t g = active ? gid : total - 1;  // whole quads are idle together
-    const int64_t bd = g >> 2;
-    const int q = int(g & 3);
-    const int64_t b = bd / a.dim, d = bd - b * a.dim;
-
-    float4 hv = *reinterpret_cast<const float4*>(a.h + bd * N + q * 4);
-    const float4 av = *reinterpret_cast<const float4*>(a.A + d * N + q * 4);
-    const float dl = step_size<MODE>(E::load(delta, bd), a.delta_bias ? a.delta_bias[d] : 0.0f);
-    const float x = E::load(u, bd);
-    const float xb = dl * x;
-    const float inv_dl = (MODE & kOptZoh) ? __builtin_amdgcn_rcpf(dl) : 0.0f;
-    const int64_t s0 = b * N + q * 4;
-
-    float hs[4] = {hv.x, hv.y, hv.z, hv.w};
-    const float as[4] = {av.x, av.y, av.z, av.w};
-    float part = 0.0f;
+    // CPL channels per lane, a grid's width apart: every load of all of them is
+    // issued before the first is used, so more of the state is in flight
+    const int64_t total = a.batch * a.dim * Q;
+    const int64_t width = (a.batch * a.dim + CPL - 1) / CPL * Q;  // a multiple of Q
+    const int64_t gid0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    bool active[CPL];
+    int64_t bd[CPL], b[CPL], d[CPL];
+    // the lane's state entries: the same for every j, as width is a multiple of Q
+    const int q = int(gid0 % Q);
+    float hs[CPL][S], as[CPL][S], bs[CPL][S], cs[CPL][S], dl[CPL], x[CPL], zv[CPL], dsk[CPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x2 = dl * (as[i] * kLog2e);
-        const float abar = exp2_hw(x2);
-        float in_term = xb * E::load(Bm, s0 + i);
-        if constexpr ((MODE & kOptZoh) != 0) in_term *= zoh_phi(x2, abar, (1.0f / as[i]) * inv_dl);
-        hs[i] = fmaf(abar, hs[i], in_term);
-        part = fmaf(E::load(Cm, s0 + i), hs[i], part);
+    for (int j = 0; j < CPL; ++j) {
+        const int64_t gid = gid0 + j * width;
+        active[j] = gid0 < width && gid < total;
+        // a channel's lanes are idle together; idle lanes read the last channel's entries q
+        const int64_t g = active[j] ? gid : total - Q + q;
+        bd[j] = g / Q;
+        b[j] = bd[j] / a.dim;
+        d[j] = bd[j] - b[j] * a.dim;
+#pragma unroll
+        for (int k = 0; k < S / 4; ++k) {
+            const float4 hv = reinterpret_cast<const float4*>(a.h + bd[j] * N + q * S)[k];
+            const float4 av = reinterpret_cast<const float4*>(a.A + d[j] * N + q * S)[k];
+            hs[j][4 * k] = hv.x;
+            hs[j][4 * k + 1] = hv.y;
+            hs[j][4 * k + 2] = hv.z;
+            hs[j][4 * k + 3] = hv.w;
+            as[j][4 * k] = av.x;
+            as[j][4 * k + 1] = av.y;
+            as[j][4 * k + 2] = av.z;
+            as[j][4 * k + 3] = av.w;
+        }
+        load_row<DT, S, VEC>(Bm + b[j] * N + q * S, bs[j]);
+        load_row<DT, S, VEC>(Cm + b[j] * N + q * S, cs[j]);
+        dl[j] = step_size<MODE>(E::load(delta, bd[j]), a.delta_bias ? a.delta_bias[d[j]] : 0.0f);
+        x[j] = E::load(u, bd[j]);
+        zv[j] = HAS_Z ? E::load(z, bd[j]) : 0.0f;
+        dsk[j] = HAS_D ? a.Dskip[d[j]] : 0.0f;
     }
-    float acc = part + __shfl_xor(part, 1, 4);
-    acc += __shfl_xor(acc, 2, 4);
-
-    if (!active) return;
-    *reinterpret_cast<float4*>(a.h + bd * N + q * 4) = make_float4(hs[0], hs[1], hs[2], hs[3]);
-    if (q == 0) {
-        if (HAS_D) acc = fmaf(a.Dskip[d], x, acc);
-        if (HAS_Z) acc *= silu(E::load(z, bd));
-        E::store(y, bd, acc);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const float xb = dl[j] * x[j];
+        const float inv_dl = (MODE & kOptZoh) ? __builtin_amdgcn_rcpf(dl[j]) : 0.0f;
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const float x2 = dl[j] * (as[j][i] * kLog2e);
+            const float abar = exp2_hw(x2);
+            float in_term = xb * bs[j][i];
+            if constexpr ((MODE & kOptZoh) != 0) in_term *= zoh_phi(x2, abar, (1.0f / as[j][i]) * inv_dl);
+            hs[j][i] = fmaf(abar, hs[j][i], in_term);
+            part = fmaf(cs[j][i], hs[j][i], part);
+        }
+        float acc = part;
+        if constexpr (Q >= 2) acc += __shfl_xor(acc, 1, Q);
+        if constexpr (Q >= 4) acc += __shfl_xor(acc, 2, Q);
+        if (active[j]) {
+#pragma unroll
+            for (int k = 0; k < S / 4; ++k)
+                reinterpret_cast<float4*>(a.h + bd[j] * N + q * S)[k] =
+                    make_float4(hs[j][4 * k], hs[j][4 * k + 1], hs[j][4 * k + 2], hs[j][4 * k + 3]);
+            if (q == 0) {
+                if (HAS_D) acc = fmaf(dsk[j], x[j], acc);
+                if (HAS_Z) acc *= silu(zv[j]);
+                E::store(y, bd[j], acc);
+            }
+        }
     }
 }
 
@@ -656,21 +832,26 @@ hipError_t launch_scan_layout(const ScanArgs& a, hipStream_t s)
     const unsigned nblk = unsigned((a.dim + CH - 1) / CH);
     const int64_t words = a.batch * a.n_chunks * 2 * a.panel_rows * N;
     panel_kernel<DT><<<dim3(unsigned((words + 255) / 256)), dim3(256), 0, s>>>(a);
+    if (a.n_chunks > 1 && a.corr_head_tiles > 0 && !a.ckpt) {
+        // emit first: every chunk from its own start (h0 or zero), writing y and its
+        // end state; the carries; then chunks 1..K-1 corrected from their carries
+        ScanArgs p1 = a;
+        p1.pass = 1;
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, HALF, true>
+            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), block, 0, s>>>(p1);
+        ScanArgs cc = a;
+        cc.h0 = nullptr;  // chunk 0's end state already starts from h0
+        launch_carry_for(cc, s);
+        ScanArgs p2 = a;
+        p2.pass = 2;
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, HALF, true>
+            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), block, 0, s>>>(p2);
+        return hipGetLastError();
+    }
     if (a.n_chunks > 1) {
         scan_kernel<DT, false, false, false, MODE, false, HALF>
             <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), block, 0, s>>>(a);
-        // R lanes per state entry: the power of two covering the K-1 aggregated chunks, 4..64
-        const int64_t n_carry = a.n_chunks - 1;
-        if (n_carry <= 4)
-            launch_carry<4>(a, s);
-        else if (n_carry <= 8)
-            launch_carry<8>(a, s);
-        else if (n_carry <= 16)
-            launch_carry<16>(a, s);
-        else if (n_carry <= 32)
-            launch_carry<32>(a, s);
-        else
-            launch_carry<64>(a, s);
+        launch_carry_for(a, s);
     }
     const dim3 grid(nblk, unsigned(a.batch), unsigned(a.n_chunks));
     if (a.ckpt)
@@ -687,12 +868,22 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s)
                   : launch_scan_layout<DT, HAS_D, HAS_Z, MODE, false>(a, s);
 }
 
+#ifndef SS_STEP_LANES
+#define SS_STEP_LANES 4
+#endif
+#ifndef SS_STEP_CPL
+#define SS_STEP_CPL 2
+#endif
 template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 hipError_t launch_step_t(const StepArgs& a, hipStream_t s)
 {
-    const int64_t threads = a.batch * a.dim * 4;
-    const unsigned blocks = unsigned((threads + 255) / 256);
-    step_kernel<DT, HAS_D, HAS_Z, MODE><<<dim3(blocks), dim3(256), 0, s>>>(a);
+    constexpr int Q = SS_STEP_LANES, CPL = SS_STEP_CPL;
+    const int64_t width = (a.batch * a.dim + CPL - 1) / CPL * Q;
+    const unsigned blocks = unsigned((width + 255) / 256);
+    if (a.vec_bc)
+        step_kernel<DT, HAS_D, HAS_Z, MODE, Q, true, CPL><<<dim3(blocks), dim3(256), 0, s>>>(a);
+    else
+        step_kernel<DT, HAS_D, HAS_Z, MODE, Q, false, CPL><<<dim3(blocks), dim3(256), 0, s>>>(a);
     return hipGetLastError();
 }
 

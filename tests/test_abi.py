@@ -144,10 +144,11 @@ def test_auto_plan_invariants(lib, shape):
 
 
 def check_workspace_size(ws, b, l, d, n, T, K):
-    """The documented layout: carries and delta sums (K > 1), then from the next
-    256-byte boundary an fp32 B/C copy of every chunk, padded by at most a few
-    tiles of rows per chunk."""
-    front = 0 if K == 1 else 4 * (K * b * d * n + (K - 1) * b * d)
+    """The documented layout: carries and delta sums (K > 1), the emit-first scheme's
+    flags (chunks of 1024 rows or more), then from the next 256-byte boundary an fp32
+    B/C copy of every chunk, padded by at most a few tiles of rows per chunk."""
+    corr = K > 1 and T >= 1024 and T % 16 == 0  # emit first: per-block flags
+    front = 0 if K == 1 else 4 * (K * b * d * n + K * b * d + (2 * K - 1) * b * (-(-d // 32)) * corr)
     panel_min = 4 * b * K * 2 * n * min(T, l)
     assert ws > 0
     assert ws >= -(-front // 256) * 256 + panel_min

@@ -197,6 +197,82 @@ def test_carries_match_oracle_states(T):
                 assert off > 100 * TOL["f32"], "carry %d is indistinguishable from t=%d" % (c, t)
 
 
+# ---------------------------------------------------------------------------
+# emit first, then correct: with chunks of 1024 rows or more every chunk is run
+# from its own start, then chunks 1..K-1 are rerun from their carries over 384
+# rows, and over their whole length where the carry's effect has not decayed
+# below fp32 resolution by then.  Both branches against the oracle, with every
+# carry checked.
+# ---------------------------------------------------------------------------
+def _carries_vs_oracle(inp, T, what):
+    """Scan with chunks of T rows; check y, h_last and every carry against the oracle.
+    Returns y and the emit-first flags (K-1, batch, ceil(D/32)): 1 where chunk c+1 was
+    rerun over its whole length."""
+    nb, nl, nd = inp["u"].shape
+    m = ss()
+    Tp, K = m.scan_plan(nb, nl, nd, 16, T)
+    assert (Tp, K) == (T, -(-nl // T)) and K >= 3
+    y, hl, ws = gpu_scan(inp, chunk_len=T, return_ws=True)
+    slots = host64(ws[: K * nb * nd * 16 * 4].view(torch.float32)).reshape(K, nb * nd, 16)
+    off = (K * nb * nd * 16 + K * nb * nd) * 4
+    n32 = -(-nd // 32)
+    flags = ws[off: off + (K - 1) * nb * n32 * 4].view(torch.int32).cpu().numpy().reshape(K - 1, nb, n32)
+    rec = [c * T - 1 for c in range(1, K)]
+    ref = oracle.scan(**inp, record_t=rec, threads=THREADS)
+    check_full(inp, y, hl, what, ref)
+    tol = TOL[dtype_of(inp)]
+    ec = rel_err(slots[1:].transpose(1, 0, 2), ref["h_rec"])
+    say("  %s: carries err %.3e; chunks rerun whole %d of %d" % (what, ec, int(flags.sum()), flags.size))
+    assert ec <= tol
+    assert set(np.unique(flags)) <= {0, 1}
+    return y, flags
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_emit_first_decayed_carry(dtype):
+    """Step sizes of the long-context workload (a carry's effect decays below fp32
+    resolution within 384 rows): only the heads are rerun; the result matches the oracle
+    and, within tolerance, the aggregate plan (chunks of 512 rows)."""
+    inp = wl.scan_inputs(2, 3000, 100, 16, dtype, delta_mu=-3.0, a_perturbed=False, has_D=True, has_z=True,
+                         has_h0=True, seed=41)
+    say("emit first, decayed carry (%s)" % dtype)
+    y1, flags = _carries_vs_oracle(inp, 1024, "T=1024 (emit first)")
+    assert flags.sum() == 0, "every correction stops after the head"
+    y2, _ = gpu_scan(inp, chunk_len=512)
+    assert rel_err(y1, y2) <= TOL["f32" if dtype == wl.F32 else "bf16"]
+
+
+@pytest.mark.parametrize("case", ["slow decay", "some positive A", "mixed channels", "negative delta"])
+def test_emit_first_whole_rerun(case):
+    """Inputs for which a carry's effect does not decay (tiny step sizes), or is not bounded
+    (A > 0 entries, a negative step size): the chunks are rerun over their whole length,
+    and the results and carries still match the oracle at the fp32 tolerance."""
+    inp = wl.scan_inputs(1, 2600, 130, 16, wl.F32, delta_mu=-1.0, delta_sigma=0.5, has_h0=True, seed=42)
+    dl = inp["delta"].copy()
+    if case == "slow decay":
+        dl *= np.float32(1e-3)
+    elif case == "some positive A":
+        inp["A"] = inp["A"].copy()
+        inp["A"][::7, 3] = np.float32(0.01)
+        dl *= np.float32(0.05)
+    elif case == "mixed channels":
+        dl[:, :, ::3] *= np.float32(1e-3)   # every third channel barely decays
+    else:
+        dl[:, 1500:1510, 5] = np.float32(-0.01)  # negative steps for one channel in chunk 1
+    inp["delta"] = dl
+    say("emit first, whole reruns: %s" % case)
+    _, flags = _carries_vs_oracle(inp, 1024, case)
+    if case == "negative delta":
+        # only chunk 1 of the workgroup holding channel 5: its 32-channel block (and, in
+        # the whole-wave layout, the other half of its 64 channels)
+        assert flags[0, 0, 0] == 1, flags
+        rest = flags.copy()
+        rest[0, 0, :2] = 0
+        assert not rest.any(), flags
+    else:
+        assert flags.all(), "every chunk is rerun whole"
+
+
 def test_chunk_invariance():
     inp = wl.scan_inputs(2, 777, 130, 16, wl.BF16, seed=9)
     ys = []
