@@ -189,7 +189,17 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const int ch = HALF ? (lane & 31) : lane;  // channel within the workgroup's block
     const int g = HALF ? 2 * w + half : w;     // state group: entries kNS*g .. kNS*g+kNS-1
     const int64_t D = a.dim, L = a.seqlen, BD = a.batch * a.dim;
-    const int64_t d_raw = int64_t(blockIdx.x) * CH + ch;
+    // The workgroup's channel block.  Workgroups are dealt to the 8 XCDs in turn
+    // (linear id mod 8), each with its own L2.  Half-wave blocks 2p and 2p+1 share
+    // the 128-byte lines of every bf16 row, so they are given ids 8 apart (the same
+    // XCD): otherwise both XCDs fetch each line.  Needs the grid's x extent to be a
+    // multiple of 16 (then linear id mod 8 = x mod 8); otherwise blocks stay in order.
+    const int blk = [&] {
+        const int x = int(blockIdx.x);
+        if (!HALF || (gridDim.x & 15) != 0) return x;
+        return (x & ~15) + 2 * (x & 7) + ((x >> 3) & 1);
+    }();
+    const int64_t d_raw = int64_t(blk) * CH + ch;
     const bool active = d_raw < D;
     const int64_t d = active ? d_raw : D - 1;  // idle lanes shadow the last channel
     const int64_t b = blockIdx.y;
@@ -519,7 +529,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
             const int head = a.corr_head_tiles < ntiles ? a.corr_head_tiles : ntiles;
             run(0, head);
             const int64_t n32 = (D + 31) / 32;
-            const int64_t fl = (c * a.batch + b) * n32 + int64_t(blockIdx.x) * (CH / 32);
+            const int64_t fl = (c * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
             float smax = 0.0f;
 #pragma unroll
             for (int i = 0; i < kNS; ++i) smax = fmaxf(smax, fabsf(h[i]));
@@ -532,9 +542,9 @@ __global__ __launch_bounds__(scan_threads<HALF>())
             const bool whole = __syncthreads_or(!ok) != 0;
             if (threadIdx.x == 0) {
                 // one flag per 32-channel block (a whole-wave workgroup holds two)
-                uint32_t* f = a.ws_whole + ((c - 1) * a.batch + b) * n32 + int64_t(blockIdx.x) * (CH / 32);
+                uint32_t* f = a.ws_whole + ((c - 1) * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
                 f[0] = whole ? 1u : 0u;
-                if (CH == 64 && int64_t(blockIdx.x) * 2 + 1 < n32) f[1] = whole ? 1u : 0u;
+                if (CH == 64 && int64_t(blk) * 2 + 1 < n32) f[1] = whole ? 1u : 0u;
             }
             if (whole) run(head, ntiles);
             if (!active || c != a.n_chunks - 1 || !a.h_last) return;
@@ -558,9 +568,9 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         const bool neg = __syncthreads_or(dmin < 0.0f) != 0;
         if (threadIdx.x == 0) {
             const int64_t n32 = (D + 31) / 32;
-            uint32_t* f = a.ws_neg + (c * a.batch + b) * n32 + int64_t(blockIdx.x) * (CH / 32);
+            uint32_t* f = a.ws_neg + (c * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
             f[0] = neg ? 1u : 0u;
-            if (CH == 64 && int64_t(blockIdx.x) * 2 + 1 < n32) f[1] = neg ? 1u : 0u;
+            if (CH == 64 && int64_t(blk) * 2 + 1 < n32) f[1] = neg ? 1u : 0u;
         }
     }
 
