@@ -1,14 +1,18 @@
 """NumPy statement of the selective scan, used only to cross-check the C oracle.
 
-TEST INFRASTRUCTURE ONLY.  Tiny shapes only: it materialises the discretised
-(B, L, D, N) operands the way the Mamba walk-through's section 3.3 explains the
-method (every Abar_t = exp(delta_t A) and every Bbar_t u_t formed up front, then
-the state is advanced one timestep at a time), which is exactly what a fused
-kernel must avoid at real sizes.
+TEST INFRASTRUCTURE ONLY.  Tiny shapes only: it forms the discretised operands
+Abar_t = exp(delta_t A) and Bbar_t u_t for every (b, t, d, n), then solves the
+recurrence h_t = Abar_t h_{t-1} + Bbar_t u_t not step by step but as an inclusive
+scan of the affine maps h -> a h + c by recursive doubling (the parallel scan over
+an associative operator of the LTI chapter, section 3.1.5.2): after the round with
+offset k, entry t holds the composition of the maps of steps max(0, t-2k+1) .. t,
+combined earlier map first, (a1, c1) then (a2, c2) -> (a2 a1, a2 c1 + c2).  After
+ceil(log2 L) rounds entry t maps h0 to h_t.  The C oracle's sequential loop shares
+neither the order of operations nor any code with this.
 """
 from __future__ import annotations
 
-from typing import Optional, Tuple
+from typing import Tuple
 
 import numpy as np
 import scipy.special
@@ -25,8 +29,8 @@ def twin_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None, de
     """Return (y (B,L,D), h_last (B,D,N)) in float64.
 
     delta_bias / delta_softplus: step size softplus(delta + bias[d]) (LTI chapter,
-    section 3.1.4.2).  zoh: Bbar = (delta A)^-1 (exp(delta A) - 1) delta B
-    (walk-through, section 2.2), here through scipy's exprel, (e^x - 1)/x."""
+    section 3.1.4.2), here numpy's logaddexp(0, v).  zoh: Bbar = (delta A)^-1 (exp(delta
+    A) - 1) delta B (walk-through, section 2.2), here through scipy's exprel, (e^x - 1)/x."""
     x = _f64(u)
     dl = _f64(delta)
     if delta_bias is not None:
@@ -40,19 +44,28 @@ def twin_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None, de
     nn = a.shape[1]
     # discretised operands for all (b, t, d, n)
     da = dl[:, :, :, None] * a[None, None, :, :]
-    a_bar = np.exp(da)
-    b_bar = dl[:, :, :, None] * bm[:, :, None, :]
+    abar = np.exp(da)
+    bbar = dl[:, :, :, None] * bm[:, :, None, :]
     if zoh:
-        b_bar = scipy.special.exprel(da) * b_bar
-    bu = b_bar * x[:, :, :, None]
-    state = np.zeros((nb, nd, nn)) if h0 is None else np.array(h0, dtype=np.float64).reshape(nb, nd, nn)
-    y = np.empty((nb, nl, nd))
-    for t in range(nl):
-        state = a_bar[:, t] * state + bu[:, t]
-        y[:, t] = np.einsum("bdn,bn->bd", state, cm[:, t])
+        bbar = scipy.special.exprel(da) * bbar
+    # the map of step t: h -> abar_t h + c_t
+    P = abar
+    S = bbar * x[:, :, :, None]
+    k = 1
+    while k < nl:
+        # compose every entry t >= k with entry t - k (the earlier map first)
+        P_new = P.copy()
+        S_new = S.copy()
+        P_new[:, k:] = P[:, k:] * P[:, :-k]
+        S_new[:, k:] = P[:, k:] * S[:, :-k] + S[:, k:]
+        P, S = P_new, S_new
+        k *= 2
+    start = np.zeros((nb, nd, nn)) if h0 is None else np.array(h0, dtype=np.float64).reshape(nb, nd, nn)
+    h = P * start[:, None, :, :] + S  # (B, L, D, N): the state after every step
+    y = np.sum(h * cm[:, :, None, :], axis=3)
     if D is not None:
         y = y + np.asarray(D, dtype=np.float64)[None, None, :] * x
     if z is not None:
         zz = _f64(z)
         y = y * (zz / (1.0 + np.exp(-zz)))
-    return y, state
+    return y, h[:, -1]

@@ -349,7 +349,7 @@ def pin_bookkeeping(orc):
 
 
 # ---------------------------------------------------------------------------
-# 11. NumPy twin (materialised operands, vectorised over lanes)
+# 11. NumPy twin (materialised operands, recursive-doubling scan over time)
 # ---------------------------------------------------------------------------
 def pin_twin(orc):
     from oracle.twin import twin_scan
