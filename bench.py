@@ -22,8 +22,11 @@ and the issue cost of fp32 fma, v_exp_f32 and the scan's per-element group),
 counters), ``flushed`` (the same scan timed with the 256 MB last-level cache flushed
 before every step), ``options`` (the same layer with the softplus(delta +
 bias) step size and/or the zero-order-hold input term), ``configs``
-(the small-model layer and the long context at their own shapes; the long
-context runs the chunked plan: aggregate, carry and emit passes), ``backward``
+(the small-model layer and the long context at their own shapes, both
+chunked: the small layer's 128-row chunks take an aggregate pass, the carries
+and an emit pass; the long context's 4096-row chunks run first from their own
+starts, then the carries, then each later chunk's head is rerun from its carry
+until the carry has decayed below fp32 resolution), ``backward``
 (ss_scan_bwd on the same layer: all input gradients from dy; and the training
 path, ss_scan_fwd_ckpt keeping every 16th state and ss_scan_bwd_ckpt reusing
 them), ``conv1d``
@@ -403,9 +406,8 @@ def main():
         del ck, cws, yk
 
         # the other scan configurations at their own shapes: the small-model layer and the
-        # long context, whose automatic plan cuts the sequence into chunks (aggregate pass,
-        # carry pass, emit pass).  Inputs drawn on the device with the configurations'
-        # distributions.
+        # long context, whose automatic plans cut the sequence into chunks.  Inputs drawn on
+        # the device with the configurations' distributions.
         cfgs = {}
         for name in ("small", "long"):
             cw_ = wl.WORKLOADS[name]

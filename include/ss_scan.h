@@ -86,10 +86,10 @@ typedef enum { SS_DELTA_SOFTPLUS = 1, SS_B_ZOH = 2 } ss_option;
  * rows or more (a multiple of 16), without checkpoints: every chunk is first
  * run from its own start (h0 for the first, zero for the others), writing y
  * and its end state; the carries follow; then each later chunk is rerun from
- * its carry over its first 384 rows, and over the rest only where the
- * carry's effect has not decayed below fp32 resolution by then (all step
- * sizes of the chunk >= 0, A <= 0, and exp(A * sum of delta) * |carry| <=
- * 2^-24 of the lane's largest state entry).  Either way the result is the
+ * its carry until the carry's effect has decayed below fp32 resolution
+ * (all step sizes of the chunk >= 0, A <= 0, and exp(A * sum of delta) *
+ * |carry| <= 2^-24 of the lane's largest state entry, checked after 128 rows
+ * and then every 64 rows for each 32 or 64 channels), else to its end.  Either way the result is the
  * one-pass recurrence up to fp32 rounding.
  *
  * The chunk length is a power of two chosen from the shape only: pure,
@@ -127,7 +127,7 @@ ss_status ss_scan_plan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
  *   [K*BD*N, +K*BD)        sum of delta over chunk c, (K, batch, dim).
  *   then, when chunk_len >= 1024 and a multiple of 16 (emit first, see
  *   ss_scan_plan): (K-1, batch, ceil(dim/32)) uint32 words, 1 where chunk c+1
- *   was rerun over its whole length, 0 where over its first 384 rows only;
+ *   was rerun over its whole length, 0 where the rerun stopped early;
  *   then (K, batch, ceil(dim/32)) uint32 words, 1 where chunk c has a
  *   negative step size.
  *   always, from the next multiple of 256 bytes to the end:

@@ -22,20 +22,15 @@ constexpr int64_t kMinAutoChunk = 64;  // the automatic plan never cuts finer
 // whole; below that the chunk length halves until the emit launch has
 // kTargetBlocks (three per CU).  Measured at L = 2048 (one chunk against the
 // best cut): 128 workgroups 180 against 125 us, 160: 196 / 157, 192: 185 / 171,
-// 240: 201 / 226, 480: 256 / 376, 640 (the large layer): 380 / 475.  The long
-// context (32 per chunk) at 8 / 16 / 32 / 64 chunks takes 2.75 / 1.89 / 1.60 /
-// 1.53 ms; the small-model layer (48) at 8 / 16 / 32 chunks 73 / 59 / 69 us.
+// 240: 201 / 226, 480: 256 / 376, 640 (the large layer): 380 / 475; the
+// small-model layer (48) at 8 / 16 / 32 chunks 73 / 59 / 69 us.
 constexpr int64_t kSingleChunkBlocks = 208;
 constexpr int64_t kTargetBlocks = 768;
-// Chunks of kLongChunk rows or more still amortise their per-chunk costs after
-// one more halving, so from there the plan goes on up to kTargetBlocksLong
-// workgroups.  Measured, one halving further against the kTargetBlocks plan:
-// long context 1.537 -> 1.493 ms (T 4096 -> 2048), B=2 L=65536 D=2048 1.539 ->
-// 1.471 ms, L=131072 D=1024 0.801 -> 0.779 ms (2048 -> 1024), L=32768 D=4096
-// 0.771 -> 0.743 ms; from shorter chunks it loses: L=16384 D=2048 0.203 ->
-// 0.233 ms (512 -> 256), the small-model layer 54 -> 67 us (128 -> 64).
-constexpr int64_t kLongChunk = 2048;
-constexpr int64_t kTargetBlocksLong = 2048;
+// (Chunks of 1024 rows or more take the emit-first scheme, whose extra cost is
+// a correction per chunk, not an aggregate pass: there more chunks only add
+// work.  An earlier rule halved such chunks on up to 2048 workgroups; dropping
+// it, B=4 L=16384 D=2048 went from 0.59 to 0.54 ms (T 1024 -> 2048) and the
+// long context from 1.03 to 1.01 ms (T 2048 -> 4096), half-wave layout.)
 constexpr int64_t kMaxGridYZ = 65535;
 // A chunk's (B, L, D) slab is addressed with 32-bit buffer offsets, and idle
 // lanes use offsets at and above 2^31: one chunk of rows must stay below 2^31
@@ -83,8 +78,7 @@ bool shape_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, Siz
 // Plan: chunk length and count.  Automatic plans start from one chunk; a
 // shape with fewer than kSingleChunkBlocks workgroups then halves the chunk
 // length (staying a power of two, never below kMinAutoChunk) until the emit
-// launch has at least kTargetBlocks workgroups, and while the chunks still
-// have kLongChunk rows or more, until it has kTargetBlocksLong.
+// launch has at least kTargetBlocks workgroups.
 bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* T, int64_t* K)
 {
     if (request < 0) return false;
@@ -98,7 +92,7 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
             while (t > kMinAutoChunk) {
                 int64_t launched;
                 if (!mul(blocks, ceil_div(seqlen, t), &launched)) break;
-                if (launched >= kTargetBlocks && (t < kLongChunk || launched >= kTargetBlocksLong)) break;
+                if (launched >= kTargetBlocks) break;
                 t >>= 1;
             }
         }
@@ -115,16 +109,20 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
 // side by side and the call ends with the most loaded CU, so the layout whose
 // busiest CU holds less work wins: ceil(wg / 256) workgroups of 64 channels
 // against ceil(2 * wg / 256) of 32.  On a tie the whole-wave layout stays (its
-// B and C are scalar operands).  SS_SCAN_LAYOUT forces one at build time
-// (1 whole-wave, 2 half-wave) for measurements.
+// B and C are scalar operands), except for the emit-first scheme (emit_first):
+// there the half-wave one was faster on every shape measured, 1.5-6% (the long
+// context 1.013 against 1.044 ms at T = 4096; B=4 L=16384 D=2048 0.540 against
+// 0.572 ms at T = 2048).  SS_SCAN_LAYOUT forces one at build time (1
+// whole-wave, 2 half-wave) for measurements.
 #ifndef SS_SCAN_LAYOUT
 #define SS_SCAN_LAYOUT 0
 #endif
 constexpr int64_t kCUs = 256;
-bool half_layout(int64_t batch, int64_t dim, int64_t K)
+bool half_layout(int64_t batch, int64_t dim, int64_t K, bool emit_first)
 {
     if (SS_SCAN_LAYOUT == 1) return false;
     if (SS_SCAN_LAYOUT == 2) return true;
+    if (emit_first) return true;
     const int64_t whole = batch * ceil_div(dim, kWave) * K;
     const int64_t halves = batch * ceil_div(dim, kWave / 2) * K;
     return ceil_div(halves, kCUs) < 2 * ceil_div(whole, kCUs);
@@ -132,11 +130,14 @@ bool half_layout(int64_t batch, int64_t dim, int64_t K)
 
 // Emit first, then correct: for chunks of kCorrMinChunk rows or more (a
 // multiple of two 8-row tiles) every chunk is first run from its own start,
-// and chunks 1..K-1 are then rerun from their carries over their first
-// kCorrHead rows (and further only where the carry's effect has not decayed
-// below fp32 resolution by then).  Shorter chunks take the aggregate pass
-// instead.  Not with checkpoints.  Returns the rerun head in tiles, or 0.
-constexpr int64_t kCorrMinChunk = 1024, kCorrHead = 384;
+// and chunks 1..K-1 are then rerun from their carries until the carry's effect
+// has decayed below fp32 resolution: checked first after kCorrHead rows, then
+// every kCorrEveryTiles tiles.  Shorter chunks take the aggregate pass instead.
+// Not with checkpoints.  Returns the first check in tiles, or 0.
+#ifndef SS_CORR_MIN_CHUNK
+#define SS_CORR_MIN_CHUNK 1024
+#endif
+constexpr int64_t kCorrMinChunk = SS_CORR_MIN_CHUNK, kCorrHead = 128;
 int corr_head_tiles(int64_t T, int64_t K)
 {
     if (K < 2 || T < kCorrMinChunk || T % (2 * ssk::kTileRows) != 0) return 0;
@@ -440,9 +441,8 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
     a.dim = dim;
     a.chunk_len = T;
     a.n_chunks = K;
-    a.half = half_layout(batch, dim, K);
     a.corr_head_tiles = ckpt ? 0 : corr_head_tiles(T, K);
-    a.pass = 0;
+    a.half = half_layout(batch, dim, K, a.corr_head_tiles > 0);
     const hipError_t err = ssk::launch_scan(a, dtype == SS_F32 ? 0 : 1, stream);
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;

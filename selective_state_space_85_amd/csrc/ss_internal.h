@@ -73,11 +73,10 @@ struct ScanArgs {
     bool half;
     // > 0 (with K > 1 and no checkpoints): emit first, then correct.  Pass 1
     // runs every chunk from its own start and writes y; the carry pass follows;
-    // pass 2 reruns chunks 1..K-1 from their carries over their first
-    // corr_head_tiles tiles (even), and over the rest only where the carry's
-    // effect has not decayed below fp32 resolution by then
+    // pass 2 reruns chunks 1..K-1 from their carries until the carry's effect
+    // has decayed below fp32 resolution, checked after corr_head_tiles tiles
+    // (even) and then every kCorrEveryTiles, or to the chunk's end
     int corr_head_tiles;
-    int pass;  // 0: a plain emit pass; 1, 2: the emit-first passes
     uint32_t* ws_neg;  // (K, batch, ceil(dim/32)): pass 1 met a negative step size
 };
 
@@ -100,6 +99,9 @@ struct StepArgs {
 // Backward: rows per sub-block, which is also the spacing of the state
 // checkpoints the backward recomputes from.
 constexpr int kBwdSub = 16;
+// emit first, then correct: the correction pass checks whether the carry has
+// decayed every kCorrEveryTiles tiles after its first check
+constexpr int kCorrEveryTiles = 8;
 
 struct BwdArgs {
     // forward inputs

@@ -26,13 +26,24 @@
 //    vector instruction); the wave's B/C words one tile ahead, issued right
 //    after the tile's LDS reads have landed so that no LDS wait drains them.
 //  * The sequence can be cut into chunks (LTI chapter 3.1, section 3.1.5.2:
-//    the recurrence is a scan over an associative operator).  For K > 1:
+//    the recurrence is a scan over an associative operator).  For K > 1 and
+//    chunks shorter than 1024 rows:
 //      1. scan_kernel<aggregate> runs chunks 0..K-2 from a zero state and
 //         keeps only each chunk's end state S_c and its delta sum;
 //      2. carry_kernel combines the affine pairs (P_c, S_c),
 //         P_c = exp(A * sum_t delta_t), with a wave-level inclusive prefix over
 //         chunks (64 chunks per pass) into the carry of every chunk;
 //      3. scan_kernel<emit> reruns every chunk from its carry and writes y.
+//    For chunks of 1024 rows or more (emit first, CORR):
+//      1. scan_kernel<emit, CORR> pass 1 runs every chunk from its own start
+//         (h0 for chunk 0, zero for the others), writes y and keeps S_c and the
+//         delta sum, as the aggregate pass would;
+//      2. carry_kernel as above;
+//      3. pass 2 reruns each chunk c >= 1 from its carry over its first rows
+//         only, rewriting y there.  The carry's share of the state decays as
+//         exp(A * sum of delta); once it is below fp32 resolution of the state
+//         the first pass's y is already right.  A workgroup where that does not
+//         hold (or with A > 0 or a negative step size) reruns the whole chunk.
 //    Only y, the chunk carries and h_last reach memory: the per-timestep
 //    states and the discretised operands exp(delta*A), delta*B*u never do (the
 //    fused, state-in-fast-memory point of section 3.3 and of LTI chapter
@@ -142,7 +153,9 @@ __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
 // ---------------------------------------------------------------------------
 // The zero-order hold's extra arithmetic would take the whole-wave kernel just
 // past 80 VGPRs, which leaves room for two 8-wave workgroups per CU instead of
-// three; it is held to 80 (six waves per SIMD).
+// three; it is held to 80 (six waves per SIMD).  (Holding the whole-wave
+// emit-first passes to 64 VGPRs, four workgroups per CU instead of three, made
+// the long context 23% slower.)
 template <bool HALF>
 struct ScanShape {
     static constexpr int kWaves = HALF ? 4 : kGroups;  // waves per workgroup
@@ -161,11 +174,11 @@ constexpr int scan_waves_per_eu()
 }
 
 template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false, bool HALF = false,
-          bool CORR = false>
+          int CORR = 0>
 __global__ __launch_bounds__(scan_threads<HALF>())
     __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<MODE>()))) void scan_kernel(ScanArgs a)
 {
-    static_assert(!CORR || (EMIT && !CKPT), "the emit-first passes are emit passes without checkpoints");
+    static_assert(CORR == 0 || (EMIT && !CKPT), "the emit-first passes are emit passes without checkpoints");
     constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using T = typename Elem<DT>::T;
     using V = Buf<DT>;
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const bool active = d_raw < D;
     const int64_t d = active ? d_raw : D - 1;  // idle lanes shadow the last channel
     const int64_t b = blockIdx.y;
-    const int64_t c = blockIdx.z + ((CORR && a.pass == 2) ? 1 : 0);  // the correction pass skips chunk 0
+    const int64_t c = blockIdx.z + (CORR == 2 ? 1 : 0);  // the correction pass skips chunk 0
     const int64_t t0 = c * a.chunk_len;
     const int len = int(((t0 + a.chunk_len < L) ? t0 + a.chunk_len : L) - t0);
     // an even number of tiles; rows past the chunk end are neutral (see publish_rows)
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     // whole sequence, or the emit after an aggregate pass: from h0 or the carry;
     // emit first (pass 1): chunk 0 from h0, the others from zero; correction
     // (pass 2): from the carry
-    const bool first = CORR && a.pass == 1;
+    const bool first = CORR == 1;
     const bool from_ws = EMIT && a.n_chunks > 1 && !first;
     const bool from_h0 = EMIT && a.h0 != nullptr && (a.n_chunks == 1 || (first && c == 0));
     if (from_ws || from_h0) {
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
                              "v"(iv[7])
                              : "memory");
         issue_words(tile + 1, Slot<1 - S>{});
-        if constexpr (CORR) {
+        if constexpr (CORR != 0) {
             // rows past the chunk end are published with delta = 0: no effect on either
 #pragma unroll
             for (int r = 0; r < TT; ++r) {
@@ -484,8 +497,11 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         ck_row = a.ckpt + ((t0 / kBwdSub * a.batch + b) * N + g * kNS) * D + d;
         ck_step = a.batch * N * D;
     }
-    // tiles [k0, k1) (both even) of the chunk, with the prefetch pipeline primed at k0
-    auto run = [&](int k0, int k1) {
+    // tiles [k0, k1) (both even) of the chunk, with the prefetch pipeline primed at
+    // k0.  stop(n) is asked after every tile pair (n tiles run so far) and ends the
+    // run early when it returns true; it must return the same for every wave.
+    // Returns the tile the run ended before.
+    auto run = [&](int k0, int k1, auto stop) {
         issue_rows(k0, Slot<0>{});
         issue_rows(k0 + 1, Slot<1>{});
         publish_rows(k0, Slot<0>{});
@@ -494,7 +510,8 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         __syncthreads();
         const int quarter = ((k1 - k0) / 4) & ~1;
         __builtin_amdgcn_s_setprio(3);
-        for (int k = k0; k < k1; k += 2) {
+        int k = k0;
+        while (k < k1) {
             if (quarter > 0) {
                 if (k - k0 == quarter) __builtin_amdgcn_s_setprio(2);
                 else if (k - k0 == 2 * quarter) __builtin_amdgcn_s_setprio(1);
@@ -510,91 +527,116 @@ __global__ __launch_bounds__(scan_threads<HALF>())
             }
             step(k, k0, Slot<0>{});
             step(k + 1, k0, Slot<1>{});
+            k += 2;
+            if (stop(k - k0)) break;
         }
-        if constexpr (EMIT) finish_rows(k1 - 1, Slot<1>{});
+        // the rows, loads and publication of tiles past k are left unused
+        if constexpr (EMIT) finish_rows(k - 1, Slot<1>{});
+        return k;
+    };
+    const auto never = [](int) { return false; };
+    // emit first: whether p holds for any lane of the workgroup.  Every wave calls
+    // it at the same point, right after a tile pair, where the even tiles' partial
+    // sums are finished and not yet rewritten: each wave leaves its ballot in a
+    // word of that buffer, a barrier, every wave reads them all, and a second
+    // barrier before the buffer is written again.  (__syncthreads_or would add
+    // LDS of its own: a quarter of the CU's LDS is exactly what the whole-wave
+    // kernel uses, so four workgroups per CU would no longer fit.)
+    auto wg_any = [&](bool p) {
+        const bool any = __builtin_amdgcn_ballot_w64(p) != 0;
+        if (lane == 0) s_part[0][0][0][w] = any ? 1.0f : 0.0f;
+        __syncthreads();
+        bool r = false;
+#pragma unroll
+        for (int q = 0; q < ScanShape<HALF>::kWaves; ++q) r = r || s_part[0][0][0][q] != 0.0f;
+        __syncthreads();
+        return r;
     };
 
-    if constexpr (CORR) {
-        if (a.pass == 2) {
-            // Correction of chunk c >= 1 after the emit-first pass, which ran it from
-            // a zero state.  From the carry H, rows [0, head) are rerun exactly.  The
-            // state then differs from the zero-start one by P * H, P = exp(A * sum of
-            // delta so far); where the chunk's step sizes are all >= 0 and A <= 0
-            // that difference only decays, so the first pass's later rows are right
-            // to fp32 resolution once P*|H| <= 2^-24 of the lane's largest |state|.
-            // Otherwise the workgroup reruns the rest of the chunk too.
-            float H[kNS];
+    if constexpr (CORR == 2) {
+        // Correction of chunk c >= 1 after the emit-first pass, which ran it from
+        // a zero state: rerun from the carry H.  After rows [0, r) the state
+        // differs from the zero-start one by P * H, P = exp(A * sum of delta over
+        // those rows); where the chunk's step sizes are all >= 0 and A <= 0 that
+        // difference only decays, so the first pass's later rows are right to
+        // fp32 resolution once P*|H| <= 2^-24 of the lane's largest |state|.
+        // That is checked after corr_head_tiles tiles and then every
+        // kCorrEveryTiles; the rerun stops at the first check every lane of the
+        // workgroup passes, else runs to the chunk's end.
+        float H[kNS];
 #pragma unroll
-            for (int i = 0; i < kNS; ++i) H[i] = h[i];
-            const int head = a.corr_head_tiles < ntiles ? a.corr_head_tiles : ntiles;
-            run(0, head);
-            const int64_t n32 = (D + 31) / 32;
-            const int64_t fl = (c * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
+        for (int i = 0; i < kNS; ++i) H[i] = h[i];
+        const int64_t n32 = (D + 31) / 32;
+        const int64_t fl = (c * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
+        // a negative step size anywhere in the chunk (first pass): no early stop
+        const bool can_stop = a.ws_neg[fl] == 0u;
+        const int first = a.corr_head_tiles;
+        auto decayed = [&](int n) {
+            if (!can_stop || n < first || (n - first) % kCorrEveryTiles != 0) return false;
             float smax = 0.0f;
 #pragma unroll
             for (int i = 0; i < kNS; ++i) smax = fmaxf(smax, fabsf(h[i]));
-            // no negative step size in the chunk (first pass); idle lanes have no say
-            bool ok = a.ws_neg[fl] == 0u;
+            bool ok = true;
 #pragma unroll
             for (int i = 0; i < kNS; ++i)
                 ok = ok && A2[i] <= 0.0f && exp2_hw(A2[i] * dsum) * fabsf(H[i]) <= kCorrTol * smax;
-            ok = ok || !active;
-            const bool whole = __syncthreads_or(!ok) != 0;
-            if (threadIdx.x == 0) {
-                // one flag per 32-channel block (a whole-wave workgroup holds two)
-                uint32_t* f = a.ws_whole + ((c - 1) * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
-                f[0] = whole ? 1u : 0u;
-                if (CH == 64 && int64_t(blk) * 2 + 1 < n32) f[1] = whole ? 1u : 0u;
-            }
-            if (whole) run(head, ntiles);
-            if (!active || c != a.n_chunks - 1 || !a.h_last) return;
-            if (whole) {
-#pragma unroll
-                for (int i = 0; i < kNS; ++i) a.h_last[sbase + i] = h[i];
-            } else {
-                // the first pass's end state from zero, plus the carry decayed over
-                // the whole chunk
-                const float dtot = a.ws_dsum[c * BD + bd];
-#pragma unroll
-                for (int i = 0; i < kNS; ++i)
-                    a.h_last[sbase + i] = fmaf(exp2_hw(A2[i] * dtot), H[i], a.h_last[sbase + i]);
-            }
-            return;
-        }
-    }
-    run(0, ntiles);
-    if constexpr (CORR) {
-        // emit first: whether any step size of the chunk is negative, per workgroup
-        const bool neg = __syncthreads_or(dmin < 0.0f) != 0;
+            ok = ok || !active;  // idle lanes have no say
+            return !wg_any(!ok);
+        };
+        const bool whole = run(0, ntiles, decayed) >= ntiles;
         if (threadIdx.x == 0) {
-            const int64_t n32 = (D + 31) / 32;
-            uint32_t* f = a.ws_neg + (c * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
-            f[0] = neg ? 1u : 0u;
-            if (CH == 64 && int64_t(blk) * 2 + 1 < n32) f[1] = neg ? 1u : 0u;
+            // one flag per 32-channel block (a whole-wave workgroup holds two)
+            uint32_t* f = a.ws_whole + ((c - 1) * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
+            f[0] = whole ? 1u : 0u;
+            if (CH == 64 && int64_t(blk) * 2 + 1 < n32) f[1] = whole ? 1u : 0u;
         }
-    }
-
-    if (!active) return;
-    if (EMIT) {
-        if (c == a.n_chunks - 1 && a.h_last) {
+        if (!active || c != a.n_chunks - 1 || !a.h_last) return;
+        if (whole) {
 #pragma unroll
             for (int i = 0; i < kNS; ++i) a.h_last[sbase + i] = h[i];
-        }
-        if (CORR) {
-            // emit first: the end state from the chunk's own start (h0 for chunk 0,
-            // zero for the others) and the chunk's delta sum, for the carry pass
-            if (c < a.n_chunks - 1) {
-                float* dst = a.ws_state + (c + 1) * BD * N + sbase;
+        } else {
+            // the first pass's end state from zero, plus the carry decayed over
+            // the whole chunk
+            const float dtot = a.ws_dsum[c * BD + bd];
 #pragma unroll
-                for (int i = 0; i < kNS; ++i) dst[i] = h[i];
-            }
-            if (g == 0) a.ws_dsum[c * BD + bd] = dsum;
+            for (int i = 0; i < kNS; ++i)
+                a.h_last[sbase + i] = fmaf(exp2_hw(A2[i] * dtot), H[i], a.h_last[sbase + i]);
         }
     } else {
-        float* dst = a.ws_state + (c + 1) * BD * N + sbase;
+        run(0, ntiles, never);
+        if constexpr (CORR == 1) {
+            // emit first: whether any step size of the chunk is negative, per workgroup
+            const bool neg = wg_any(dmin < 0.0f);
+            if (threadIdx.x == 0) {
+                const int64_t n32 = (D + 31) / 32;
+                uint32_t* f = a.ws_neg + (c * a.batch + b) * n32 + int64_t(blk) * (CH / 32);
+                f[0] = neg ? 1u : 0u;
+                if (CH == 64 && int64_t(blk) * 2 + 1 < n32) f[1] = neg ? 1u : 0u;
+            }
+        }
+
+        if (!active) return;
+        if constexpr (EMIT) {
+            if (c == a.n_chunks - 1 && a.h_last) {
 #pragma unroll
-        for (int i = 0; i < kNS; ++i) dst[i] = h[i];
-        if (g == 0) a.ws_dsum[c * BD + bd] = dsum;
+                for (int i = 0; i < kNS; ++i) a.h_last[sbase + i] = h[i];
+            }
+            if constexpr (CORR == 1) {
+                // emit first: the end state from the chunk's own start (h0 for chunk 0,
+                // zero for the others) and the chunk's delta sum, for the carry pass
+                if (c < a.n_chunks - 1) {
+                    float* dst = a.ws_state + (c + 1) * BD * N + sbase;
+#pragma unroll
+                    for (int i = 0; i < kNS; ++i) dst[i] = h[i];
+                }
+                if (g == 0) a.ws_dsum[c * BD + bd] = dsum;
+            }
+        } else {
+            float* dst = a.ws_state + (c + 1) * BD * N + sbase;
+#pragma unroll
+            for (int i = 0; i < kNS; ++i) dst[i] = h[i];
+            if (g == 0) a.ws_dsum[c * BD + bd] = dsum;
+        }
     }
 }
 
@@ -845,17 +887,13 @@ hipError_t launch_scan_layout(const ScanArgs& a, hipStream_t s)
     if (a.n_chunks > 1 && a.corr_head_tiles > 0 && !a.ckpt) {
         // emit first: every chunk from its own start (h0 or zero), writing y and its
         // end state; the carries; then chunks 1..K-1 corrected from their carries
-        ScanArgs p1 = a;
-        p1.pass = 1;
-        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, HALF, true>
-            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), block, 0, s>>>(p1);
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, HALF, 1>
+            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), block, 0, s>>>(a);
         ScanArgs cc = a;
         cc.h0 = nullptr;  // chunk 0's end state already starts from h0
         launch_carry_for(cc, s);
-        ScanArgs p2 = a;
-        p2.pass = 2;
-        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, HALF, true>
-            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), block, 0, s>>>(p2);
+        scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, HALF, 2>
+            <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), block, 0, s>>>(a);
         return hipGetLastError();
     }
     if (a.n_chunks > 1) {

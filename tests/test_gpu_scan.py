@@ -199,10 +199,10 @@ def test_carries_match_oracle_states(T):
 
 # ---------------------------------------------------------------------------
 # emit first, then correct: with chunks of 1024 rows or more every chunk is run
-# from its own start, then chunks 1..K-1 are rerun from their carries over 384
-# rows, and over their whole length where the carry's effect has not decayed
-# below fp32 resolution by then.  Both branches against the oracle, with every
-# carry checked.
+# from its own start, then chunks 1..K-1 are rerun from their carries until the
+# carry's effect has decayed below fp32 resolution (checked after 128 rows, then
+# every 64), and over their whole length where it never does.  Both branches
+# against the oracle, with every carry checked.
 # ---------------------------------------------------------------------------
 def _carries_vs_oracle(inp, T, what):
     """Scan with chunks of T rows; check y, h_last and every carry against the oracle.
@@ -231,8 +231,8 @@ def _carries_vs_oracle(inp, T, what):
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 def test_emit_first_decayed_carry(dtype):
     """Step sizes of the long-context workload (a carry's effect decays below fp32
-    resolution within 384 rows): only the heads are rerun; the result matches the oracle
-    and, within tolerance, the aggregate plan (chunks of 512 rows)."""
+    resolution within a few hundred rows): only the heads are rerun; the result matches
+    the oracle and, within tolerance, the aggregate plan (chunks of 512 rows)."""
     inp = wl.scan_inputs(2, 3000, 100, 16, dtype, delta_mu=-3.0, a_perturbed=False, has_D=True, has_z=True,
                          has_h0=True, seed=41)
     say("emit first, decayed carry (%s)" % dtype)
@@ -240,6 +240,19 @@ def test_emit_first_decayed_carry(dtype):
     assert flags.sum() == 0, "every correction stops after the head"
     y2, _ = gpu_scan(inp, chunk_len=512)
     assert rel_err(y1, y2) <= TOL["f32" if dtype == wl.F32 else "bf16"]
+
+
+def test_emit_first_late_decay():
+    """Step sizes about five times smaller than the large layer's: the carry's effect takes
+    about 576 rows to fall below fp32 resolution (a float64 run of the recurrence puts every
+    32-channel block there), so the rerun passes several checks before it stops, short of
+    the chunk's end.  Stopping at the first check (128 rows) would leave errors near 1e-2
+    in y, far above the fp32 bar."""
+    inp = wl.scan_inputs(1, 3000, 96, 16, wl.F32, delta_mu=-3.4, delta_sigma=0.3, a_perturbed=False,
+                         has_h0=True, seed=43)
+    say("emit first, late decay")
+    _, flags = _carries_vs_oracle(inp, 1024, "late decay")
+    assert flags.sum() == 0, "every correction stops inside the chunk"
 
 
 @pytest.mark.parametrize("case", ["slow decay", "some positive A", "mixed channels", "negative delta"])
@@ -269,6 +282,10 @@ def test_emit_first_whole_rerun(case):
         rest = flags.copy()
         rest[0, 0, :2] = 0
         assert not rest.any(), flags
+    elif case == "some positive A":
+        # every 32-channel block but the last (channels 128, 129) holds a channel 7k; the
+        # last block may stop early wherever its carry has decayed
+        assert flags[:, :, :4].all(), flags
     else:
         assert flags.all(), "every chunk is rerun whole"
 
