@@ -130,6 +130,9 @@ ss_status ss_scan_plan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
  *   was rerun over its whole length, 0 where the rerun stopped early;
  *   then (K, batch, ceil(dim/32)) uint32 words, 1 where chunk c has a
  *   negative step size.
+ *   instead, when chunk_len is shorter than that and K <= 16: (K-1, batch,
+ *   dim, N), the end state of chunk c from a zero start (the emit pass forms
+ *   the carries from these itself).
  *   always, from the next multiple of 256 bytes to the end:
  *                          an fp32 copy of B and C, per (batch row, chunk),
  *                          regrouped in the order the scan kernels read it

@@ -144,6 +144,16 @@ int corr_head_tiles(int64_t T, int64_t K)
     return int(kCorrHead / ssk::kTileRows);
 }
 
+// Short-chunk plans with at most kFuseMaxChunks chunks: the emit pass forms each
+// chunk's carry itself from the aggregate pass's end states and delta sums (a
+// sequential combine of at most 15 affine maps per lane), so there is no carry
+// launch.  The small-model layer (16 chunks of 128 rows) had its carry pass at
+// 7 us of 57.
+bool fuse_carry(int64_t T, int64_t K)
+{
+    return K > 1 && K <= ssk::kFuseMaxChunks && corr_head_tiles(T, K) == 0;
+}
+
 // Workspace layout for K chunks of T rows (fp32 words):
 //   K > 1: K state slots of batch*dim*dstate, then (K-1)*batch*dim delta sums;
 //   then, at the next multiple of 256 bytes, the B/C panel of
@@ -151,6 +161,7 @@ int corr_head_tiles(int64_t T, int64_t K)
 struct WsLayout {
     int64_t flags_offset = 0;  // bytes (K > 1, emit first): "whole chunk rerun" flags
     int64_t neg_offset = 0;    // bytes: "negative step size" flags
+    int64_t agg_offset = 0;    // bytes (fused carry): chunk end states from zero
     int64_t panel_offset;  // bytes
     int64_t panel_words;
     int64_t panel_rows;
@@ -161,16 +172,19 @@ bool ws_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64
 {
     int64_t front = 0;
     if (K > 1) {
-        int64_t bd, slots, dsums, flags = 0;
+        int64_t bd, slots, dsums, flags = 0, agg = 0;
         if (!mul(batch, dim, &bd)) return false;
         if (!mul(bd, dstate, &slots) || !mul(slots, K, &slots)) return false;
         if (!mul(bd, K, &dsums)) return false;
         // emit first: (K-1) "whole chunk rerun" and K "negative step" flags per block
         if (corr_head_tiles(T, K) > 0 && !mul(batch * ceil_div(dim, 32), 2 * K - 1, &flags)) return false;
+        // fused carry: the K-1 end states from zero, apart from the slots
+        if (fuse_carry(T, K) && !mul(slots / K, K - 1, &agg)) return false;
         w->flags_offset = (slots + dsums) * 4;
         w->neg_offset = w->flags_offset + batch * ceil_div(dim, 32) * (K - 1) * 4;
+        w->agg_offset = (slots + dsums) * 4;
         if (__builtin_add_overflow(slots, dsums, &front) || __builtin_add_overflow(front, flags, &front) ||
-            !mul(front, 4, &front))
+            __builtin_add_overflow(front, agg, &front) || !mul(front, 4, &front))
             return false;
     }
     if (__builtin_add_overflow(front, int64_t(255), &front)) return false;
@@ -433,6 +447,10 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
     a.ws_dsum = K > 1 ? static_cast<float*>(workspace) + K * batch * dim * dstate : nullptr;
     a.ws_whole = K > 1 ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + wl.flags_offset) : nullptr;
     a.ws_neg = K > 1 ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + wl.neg_offset) : nullptr;
+    a.fuse_carry = fuse_carry(T, K) ? 1 : 0;
+    a.ws_agg = K <= 1 ? nullptr
+               : a.fuse_carry ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.agg_offset)
+                              : a.ws_state + batch * dim * dstate;
     a.ws_panel = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.panel_offset);
     a.panel_rows = wl.panel_rows;
     a.ckpt = ckpt;

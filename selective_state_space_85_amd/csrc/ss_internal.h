@@ -55,6 +55,14 @@ struct ScanArgs {
     float* h_last;       // nullable
     float* ws_state;     // (K, batch, dim, N) state slots, nullable when K == 1
     float* ws_dsum;      // (K, batch, dim) per-chunk delta sums
+    // end states of chunks 0..K-2 from a zero start, (K-1, batch, dim, N):
+    // the aggregate pass and the emit-first pass write them here; when the
+    // carry is fused (fuse_carry) a region of its own, else slots 1..K-1
+    float* ws_agg;
+    // short-chunk plans with few chunks: the emit pass forms each chunk's carry
+    // from the initial state and the end states and delta sums of the chunks
+    // before it, and writes it to the chunk's slot; no carry pass
+    int fuse_carry;
     // (K-1, batch, ceil(dim/32)), emit first: 1 where the correction pass reran
     // the whole chunk c+1, 0 where only its head
     uint32_t* ws_whole;
@@ -102,6 +110,8 @@ constexpr int kBwdSub = 16;
 // emit first, then correct: the correction pass checks whether the carry has
 // decayed every kCorrEveryTiles tiles after its first check
 constexpr int kCorrEveryTiles = 8;
+// the most chunks for which the emit pass forms the carries itself
+constexpr int kFuseMaxChunks = 16;
 
 struct BwdArgs {
     // forward inputs

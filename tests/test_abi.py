@@ -145,10 +145,13 @@ def test_auto_plan_invariants(lib, shape):
 
 def check_workspace_size(ws, b, l, d, n, T, K):
     """The documented layout: carries and delta sums (K > 1), the emit-first scheme's
-    flags (chunks of 1024 rows or more), then from the next 256-byte boundary an fp32
+    flags (chunks of 1024 rows or more) or the chunk end states (shorter chunks, at most
+    16 of them), then from the next 256-byte boundary an fp32
     B/C copy of every chunk, padded by at most a few tiles of rows per chunk."""
     corr = K > 1 and T >= 1024 and T % 16 == 0  # emit first: per-block flags
-    front = 0 if K == 1 else 4 * (K * b * d * n + K * b * d + (2 * K - 1) * b * (-(-d // 32)) * corr)
+    fused = 1 < K <= 16 and not corr  # the emit pass forms the carries: chunk end states
+    front = 0 if K == 1 else 4 * (K * b * d * n + K * b * d + (2 * K - 1) * b * (-(-d // 32)) * corr
+                                  + (K - 1) * b * d * n * fused)
     panel_min = 4 * b * K * 2 * n * min(T, l)
     assert ws > 0
     assert ws >= -(-front // 256) * 256 + panel_min

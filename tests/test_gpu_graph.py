@@ -89,9 +89,11 @@ def test_graph_decode_loop():
                      between=lambda: (h_x.copy_(h0), loop(h_x, y_x)))
 
 
-def test_graph_chunked_scan():
-    """The chunked forward (panel, aggregate, carry and emit launches) in one graph."""
-    b, l, d, chunk = 2, 700, 130, 64
+@pytest.mark.parametrize("l,chunk", [(700, 64), (3000, 1024)], ids=["aggregate", "emit_first"])
+def test_graph_chunked_scan(l, chunk):
+    """The chunked forward in one graph: 64-row chunks (panel, aggregate, carry and emit
+    launches) and 1024-row chunks (panel, the emit-first pass, carry, correction)."""
+    b, d = 2, 130
     inp = wl.scan_inputs(b, l, d, 16, wl.F32, has_D=True, has_z=True, has_h0=True, seed=911)
     m = ss()
     t = {k: dev(v) for k, v in inp.items()}
