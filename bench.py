@@ -11,7 +11,8 @@ HBM bytes per launch over its event-timed duration, against 8 TB/s), and the
 fp64 CPU oracle timed on a bounded sample of the same workload.
 
 Extra objects: ``decode_step`` (ss_step on the B=256, D=5120 recurrent-step
-workload), ``decode_graph`` (single-sequence decode, B=1: 64 chained ss_step
+workload: chained on the same operands, with the last-level cache flushed
+before each token, and 1000 chained tokens with fresh operands), ``decode_graph`` (single-sequence decode, B=1: 64 chained ss_step
 calls launched one by one against the same loop captured once in a hipGraph
 and replayed), ``parity`` (the timed output against the oracle on every
 channel, taken in the CPU-baseline leg, the one place the oracle runs; it runs
@@ -555,11 +556,35 @@ def main():
             cold.append(e0.elapsed_time(e1) * 1e3)
         del scratch
         us_cold = float(np.median(cold))
+        # 1000 chained tokens, each with fresh operands (drawn on the device beforehand,
+        # with the step workload's distributions), timed as one run
+        n_chain = 1000
+        cg = torch.Generator(device).manual_seed(500)
+        shp_c = (n_chain, sw.batch, sw.dim)
+        cu = torch.randn(shp_c, device=device, generator=cg).to(torch.bfloat16)
+        cd = torch.nn.functional.softplus(torch.randn(shp_c, device=device, generator=cg) - 2.0).to(torch.bfloat16)
+        cz = torch.randn(shp_c, device=device, generator=cg).to(torch.bfloat16)
+        cB = torch.randn(n_chain, sw.batch, sw.dstate, device=device, generator=cg).to(torch.bfloat16)
+        cC = torch.randn(n_chain, sw.batch, sw.dstate, device=device, generator=cg).to(torch.bfloat16)
+        cy = torch.empty_like(cu)
+        ch = h5.clone()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(n_chain):
+            ss.step(ch, cu[k], cd[k], A5, cB[k], cC[k], D=D5, z=cz[k], out=cy[k])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_chain = e0.elapsed_time(e1) * 1e3 / n_chain
+        del cu, cd, cz, cB, cC, cy, ch
         result["decode_step"] = {"workload": "recurrent step B=256 D=5120 N=16, bf16, state (84 MB) in place",
                                  "us_per_token": us, "elements/s": sw.elements / (us * 1e-6),
-                                 "alg_GB/s": sb / (us * 1e-6) / 1e9, "note": "chained, state warm in cache",
+                                 "alg_GB/s": sb / (us * 1e-6) / 1e9,
+                                 "note": "chained on the same operands, state warm in cache",
                                  "cold_us_per_token": us_cold, "cold_alg_GB/s": sb / (us_cold * 1e-6) / 1e9,
-                                 "cold_frac_of_8TB/s": sb / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                                 "cold_frac_of_8TB/s": sb / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                 "chained_1000_us_per_token": us_chain,
+                                 "chained_1000_alg_GB/s": sb / (us_chain * 1e-6) / 1e9,
+                                 "chained_1000_note": "1000 tokens in one run, fresh operands per token"}
         del st, y5, h5
 
         # single-sequence decode (B=1): launch-bound, so the token loop is captured

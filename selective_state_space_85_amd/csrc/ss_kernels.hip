@@ -227,10 +227,18 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const uint32_t row_bytes = uint32_t(D) * V::kBytes;
     const uint32_t span = uint32_t(len) * row_bytes;
     // vector offsets: the lane's channel, plus (half-wave) one row for the odd half.  The
-    // range check covers the vector offset only, so a half's row that is past the chunk
-    // end is never addressed: voff_lo (both halves on the even row) stands in for it.
-    const uint32_t voff_lo = active ? uint32_t(d_raw) * V::kBytes : kIdleOffset;
-    const uint32_t voff_hi = voff_lo + (active && half ? row_bytes : 0u);
+    // row goes into the vector offset too, because the range check covers the vector
+    // offset only: loads of rows past the chunk end then read 0 and stores to them are
+    // dropped, with no clamping or branch per row (offsets stay below 2^32: the chunk
+    // span is below 2^31 and the prefetch runs at most 4 tiles past it).  Idle lanes
+    // shadow the last channel throughout: they load its rows, compute its values bit
+    // for bit and store the same y the lane that owns it stores; their state stores
+    // are skipped.
+    const uint32_t voff_lo = uint32_t(d) * V::kBytes;
+    const uint32_t voff_hi = voff_lo + (half ? row_bytes : 0u);
+    // rows past the chunk end read a zero step size; only a bias or the softplus can
+    // turn that into a non-zero one, so only then are they masked
+    const bool mask_rows = (MODE & kOptSoftplus) != 0 || a.delta_bias != nullptr;
     const __amdgpu_buffer_rsrc_t r_u = make_rsrc(static_cast<const T*>(a.u) + row0, span);
     const __amdgpu_buffer_rsrc_t r_dl = make_rsrc(static_cast<const T*>(a.delta) + row0, span);
     const __amdgpu_buffer_rsrc_t r_z = make_rsrc(HAS_Z ? static_cast<const T*>(a.z) + row0 : nullptr, span);
@@ -315,27 +323,21 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     auto wave_row = [&](int tile) { return tile * TT + (HALF ? 2 * w : w * RPW); };
     // the row a lane widens and finishes
     auto lane_row = [&](int tile, int j) { return wave_row(tile) + (HALF ? half : j); };
+    // a lane's vector offset of row r of the chunk (see voff_lo)
+    // (the row is wave-uniform: readfirstlane keeps its offset in a scalar register)
+    auto row_voff = [&](uint32_t base, int r) {
+        return base + __builtin_amdgcn_readfirstlane(uint32_t(r) * row_bytes);
+    };
 
     auto issue_rows = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
-        if constexpr (HALF) {
-            // the odd half reads the next row only when it is inside the chunk
-            const int r0 = wave_row(tile);
-            const int rs = r0 < len ? r0 : len - 1;
-            const uint32_t vo = r0 + 1 < len ? voff_hi : voff_lo;
-            const uint32_t so = uint32_t(rs) * row_bytes;
-            rdl[S][0] = V::load(r_dl, vo, so);
-            ru[S][0] = V::load(r_u, vo, so);
-            if (EMIT && HAS_Z) rz[S][0] = V::load(r_z, vo, so);
-        } else {
 #pragma unroll
-            for (int j = 0; j < RPW; ++j) {
-                const int r = lane_row(tile, j);
-                const uint32_t so = uint32_t(r < len ? r : len - 1) * row_bytes;
-                rdl[S][j] = V::load(r_dl, voff_lo, so);
-                ru[S][j] = V::load(r_u, voff_lo, so);
-                if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, voff_lo, so);
-            }
+        for (int j = 0; j < RPW; ++j) {
+            // half-wave: voff_hi carries the odd half's row
+            const uint32_t vo = row_voff(HALF ? voff_hi : voff_lo, wave_row(tile) + (HALF ? 0 : j));
+            rdl[S][j] = V::load(r_dl, vo, 0);
+            ru[S][j] = V::load(r_u, vo, 0);
+            if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, vo, 0);
         }
     };
     // widen this lane's rows of a tile and publish (delta, delta*u).  Rows past
@@ -346,8 +348,13 @@ __global__ __launch_bounds__(scan_threads<HALF>())
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
             const int r = lane_row(tile, j) - tile * TT;
-            const bool in = lane_row(tile, j) < len;
-            const float dl = in ? step_size<MODE>(V::widen(rdl[S][j]), bias) : 0.0f;
+            float dl = V::widen(rdl[S][j]);
+            if (mask_rows) {
+                // a uniform branch: the empty asm keeps the compiler from computing this
+                // path everywhere and selecting
+                __asm__ volatile("" ::: "memory");
+                dl = lane_row(tile, j) < len ? step_size<MODE>(dl, bias) : 0.0f;
+            }
             const float x = V::widen(ru[S][j]);
             s_xd[S][r][ch] = make_float2(dl, dl * x);
             if constexpr (ZOH) s_iv[S][r][ch] = __builtin_amdgcn_rcpf(dl);
@@ -394,19 +401,15 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-            const int t = lane_row(tile, j);
-            const int r = t - tile * TT;
-            if (t < len) {
-                float acc = s_part[S][0][r][ch];
+            // rows past the chunk end: the range check drops the store
+            const int r = lane_row(tile, j) - tile * TT;
+            float acc = s_part[S][0][r][ch];
 #pragma unroll
-                for (int q = 1; q < kGroups; ++q) acc += s_part[S][q][r][ch];
-                if (HAS_D) acc = fmaf(dskip, xf[S][j], acc);
-                if (HAS_Z) acc *= silu(zf[S][j]);
-                if constexpr (HALF)
-                    V::store(r_y, voff_hi, uint32_t(wave_row(tile)) * row_bytes, acc);
-                else
-                    V::store(r_y, voff_lo, uint32_t(t) * row_bytes, acc);
-            }
+            for (int q = 1; q < kGroups; ++q) acc += s_part[S][q][r][ch];
+            if (HAS_D) acc = fmaf(dskip, xf[S][j], acc);
+            if (HAS_Z) acc *= silu(zf[S][j]);
+            const uint32_t vo = row_voff(HALF ? voff_hi : voff_lo, wave_row(tile) + (HALF ? 0 : j));
+            V::store(r_y, vo, 0, acc);
         }
     };
     // the recurrence over one tile for this lane's state entries
