@@ -227,17 +227,19 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const uint32_t row_bytes = uint32_t(D) * V::kBytes;
     const uint32_t span = uint32_t(len) * row_bytes;
     // vector offsets: the lane's channel, plus (half-wave) one row for the odd half.  The
-    // row goes into the vector offset too, because the range check covers the vector
-    // offset only: loads of rows past the chunk end then read 0 and stores to them are
-    // dropped, with no clamping or branch per row (offsets stay below 2^32: the chunk
-    // span is below 2^31 and the prefetch runs at most 4 tiles past it).  Idle lanes
+    // row goes into the vector offset too in the half-wave layout, because the range
+    // check covers the vector offset only: loads of rows past the chunk end then read 0
+    // and stores to them are dropped, with no clamping or branch per row (offsets stay
+    // below 2^32: the chunk span is below 2^31 and the prefetch runs at most 4 tiles
+    // past it).  The whole-wave layout's rows are wave-uniform: a clamped scalar
+    // offset, a mask and a scalar branch cost it no vector instruction.  Idle lanes
     // shadow the last channel throughout: they load its rows, compute its values bit
     // for bit and store the same y the lane that owns it stores; their state stores
     // are skipped.
     const uint32_t voff_lo = uint32_t(d) * V::kBytes;
     const uint32_t voff_hi = voff_lo + (half ? row_bytes : 0u);
-    // rows past the chunk end read a zero step size; only a bias or the softplus can
-    // turn that into a non-zero one, so only then are they masked
+    // half-wave: rows past the chunk end read a zero step size; only a bias or the
+    // softplus can turn that into a non-zero one, so only then are they masked
     const bool mask_rows = (MODE & kOptSoftplus) != 0 || a.delta_bias != nullptr;
     const __amdgpu_buffer_rsrc_t r_u = make_rsrc(static_cast<const T*>(a.u) + row0, span);
     const __amdgpu_buffer_rsrc_t r_dl = make_rsrc(static_cast<const T*>(a.delta) + row0, span);
@@ -333,11 +335,21 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-            // half-wave: voff_hi carries the odd half's row
-            const uint32_t vo = row_voff(HALF ? voff_hi : voff_lo, wave_row(tile) + (HALF ? 0 : j));
-            rdl[S][j] = V::load(r_dl, vo, 0);
-            ru[S][j] = V::load(r_u, vo, 0);
-            if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, vo, 0);
+            if constexpr (HALF) {
+                // voff_hi carries the odd half's row; past the chunk end the loads read 0
+                const uint32_t vo = row_voff(voff_hi, wave_row(tile));
+                rdl[S][j] = V::load(r_dl, vo, 0);
+                ru[S][j] = V::load(r_u, vo, 0);
+                if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, vo, 0);
+            } else {
+                // whole-wave: the row is uniform, so it stays a clamped scalar offset
+                // (no vector instruction) and publish_rows masks rows past the end
+                const int r = lane_row(tile, j);
+                const uint32_t so = uint32_t(r < len ? r : len - 1) * row_bytes;
+                rdl[S][j] = V::load(r_dl, voff_lo, so);
+                ru[S][j] = V::load(r_u, voff_lo, so);
+                if (EMIT && HAS_Z) rz[S][j] = V::load(r_z, voff_lo, so);
+            }
         }
     };
     // widen this lane's rows of a tile and publish (delta, delta*u).  Rows past
@@ -349,7 +361,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         for (int j = 0; j < RPW; ++j) {
             const int r = lane_row(tile, j) - tile * TT;
             float dl = V::widen(rdl[S][j]);
-            if (mask_rows) {
+            if (!HALF || mask_rows) {
                 // a uniform branch: the empty asm keeps the compiler from computing this
                 // path everywhere and selecting
                 __asm__ volatile("" ::: "memory");
@@ -401,15 +413,21 @@ __global__ __launch_bounds__(scan_threads<HALF>())
         constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
-            // rows past the chunk end: the range check drops the store
-            const int r = lane_row(tile, j) - tile * TT;
-            float acc = s_part[S][0][r][ch];
+            const int t = lane_row(tile, j);
+            const int r = t - tile * TT;
+            // half-wave: the range check drops stores past the chunk end; whole-wave:
+            // the row is uniform, a scalar branch
+            if (HALF || t < len) {
+                float acc = s_part[S][0][r][ch];
 #pragma unroll
-            for (int q = 1; q < kGroups; ++q) acc += s_part[S][q][r][ch];
-            if (HAS_D) acc = fmaf(dskip, xf[S][j], acc);
-            if (HAS_Z) acc *= silu(zf[S][j]);
-            const uint32_t vo = row_voff(HALF ? voff_hi : voff_lo, wave_row(tile) + (HALF ? 0 : j));
-            V::store(r_y, vo, 0, acc);
+                for (int q = 1; q < kGroups; ++q) acc += s_part[S][q][r][ch];
+                if (HAS_D) acc = fmaf(dskip, xf[S][j], acc);
+                if (HAS_Z) acc *= silu(zf[S][j]);
+                if constexpr (HALF)
+                    V::store(r_y, row_voff(voff_hi, wave_row(tile)), 0, acc);
+                else
+                    V::store(r_y, voff_lo, uint32_t(t) * row_bytes, acc);
+            }
         }
     };
     // the recurrence over one tile for this lane's state entries

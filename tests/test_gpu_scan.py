@@ -108,6 +108,25 @@ def test_long_context_full():
     assert ec <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_ragged_channels_many_blocks(dtype):
+    """D = 6437: the last 64-channel block has 37 channels and 27 idle lanes that shadow
+    channel 6436.  With 202 one-chunk workgroups the plan cuts the sequence into 5 chunks
+    of 128 (1010 whole-wave workgroups, where the layout rule keeps the whole-wave
+    layout), so idle lanes run in the aggregate pass, the fused carry and the emit pass;
+    every output element against the oracle, the last channel and its neighbours
+    included."""
+    inp = wl.scan_inputs(2, 600, 6437, 16, dtype, has_h0=True, seed=47)
+    T, K = ss().scan_plan(2, 600, 6437, 16)
+    say("ragged channels B2 L600 D6437 (%s), plan T=%d K=%d" % (dtype, T, K))
+    assert (T, K) == (128, 5)
+    y, hl = gpu_scan(inp)
+    ref = check_full(inp, y, hl, "D6437")
+    tol = TOL[dtype_of(inp)]
+    # the last block on its own, so a wrong idle-lane store there cannot hide in the rest
+    assert rel_err(y[:, :, 6400:], ref["y"][:, :, 6400:]) <= tol
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
