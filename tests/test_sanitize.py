@@ -67,15 +67,49 @@ def test_oracle_pins_under_sanitizers(tmp_path):
     assert r.returncode == 0 and "pins:" in r.stdout, (r.stdout[-1000:], r.stderr[-3000:])
 
 
-def test_abi_validation_under_sanitizers(tmp_path):
+def _host_lib(tmp_path):
     lib = tmp_path / "libssscan_host_san.so"
     subprocess.run(["g++", "-std=c++17", "-fPIC", "-shared"] + SAN +
                    ["-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
                     "-I", os.path.join(ROOT, "selective_state_space_85_amd", "csrc"),
                     os.path.join(ROOT, "selective_state_space_85_amd", "csrc", "ss_api.cpp"),
                     os.path.join(TESTS, "sanitize", "launch_stubs.cpp"), "-o", str(lib)], check=True)
+    return lib
+
+
+def test_abi_validation_under_sanitizers(tmp_path):
+    lib = _host_lib(tmp_path)
     r = _run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "sanitize.abi_plugin", "-p", "no:cacheprovider",
               os.path.join(TESTS, "test_abi.py"), os.path.join(TESTS, "test_zz_no_alloc.py"), "-m", "not gpu"],
              {"SS_SANITIZED_LIB": str(lib), "PYTHONPATH": TESTS + os.pathsep + ROOT})
     assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
     assert " passed" in r.stdout
+
+
+def test_hip_failure_path(tmp_path):
+    """Valid calls whose launches fail (the stub launchers return the code in
+    SS_STUB_LAUNCH_ERROR) return SS_ERR_HIP and leave the HIP code in ss_last_hip_error:
+    the scan with and without chunks, the allocation-free scan, the step, the backward,
+    the conv1d and the multi-head recurrence."""
+    lib = _host_lib(tmp_path)
+    code = ("import ctypes, sys; sys.path[:0] = [%r, %r]\n"
+            "import sanitize.abi_plugin\n"
+            "from selective_state_space_85_amd import _lib\n"
+            "import test_abi as t\n"
+            "lib = _lib.load()\n"
+            "assert lib.ss_last_hip_error() == 0\n"
+            "assert t.call_scan(lib) == 4, 'one chunk'\n"
+            "assert lib.ss_last_hip_error() == 17\n"
+            "assert t.call_scan(lib, chunk=64) == 4, 'chunked'\n"
+            "assert t.call_scan(lib, chunk=1024, seqlen=4096) == 4, 'emit first'\n"
+            "a = t.addr\n"
+            "assert lib.ss_scan_fwd_noalloc(a(0), a(1), a(2), a(3), a(4), None, None, None, a(5), None,"
+            " 2, 512, 64, 16, t.BF16, None) == 4, 'allocation-free'\n"
+            "assert t.call_step(lib) == 4, 'step'\n"
+            "assert t.call_bwd(lib) == 4, 'backward'\n"
+            "assert t.call_conv(lib) == 4, 'conv1d'\n"
+            "assert t.call_ssd(lib) == 4, 'ssd'\n"
+            "assert lib.ss_status_string(4).startswith(b'SS_ERR_HIP')\n"
+            "print('hip failure path ok')\n") % (TESTS, ROOT)
+    r = _run([sys.executable, "-c", code], {"SS_SANITIZED_LIB": str(lib), "SS_STUB_LAUNCH_ERROR": "17"})
+    assert r.returncode == 0 and "hip failure path ok" in r.stdout, (r.stdout[-2000:], r.stderr[-3000:])
