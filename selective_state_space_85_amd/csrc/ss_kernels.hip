@@ -519,7 +519,8 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     };
 
     // one tile step: finish tile k-1, publish tile k+1, scan tile k
-    // every load below is clamped to a valid row, so all of it runs unconditionally
+    // every load below is of a valid row (whole-wave: clamped) or range-checked (half-wave:
+    // rows past the chunk end read 0), so all of it runs unconditionally
     // k0: the first tile of the current run (the tile before it is finished already)
     auto step = [&](int k, int k0, auto slot) {
         constexpr int S = decltype(slot)::value;
