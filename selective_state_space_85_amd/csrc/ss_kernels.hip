@@ -153,9 +153,12 @@ __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
 // ---------------------------------------------------------------------------
 // The zero-order hold's extra arithmetic would take the whole-wave kernel just
 // past 80 VGPRs, which leaves room for two 8-wave workgroups per CU instead of
-// three; it is held to 80 (six waves per SIMD).  (Holding the whole-wave
-// emit-first passes to 64 VGPRs, four workgroups per CU instead of three, made
-// the long context 23% slower.)
+// three; it is held to 80 (six waves per SIMD).  The half-wave emit-first pass
+// 1 (every chunk of a long sequence) is held to 64 (eight workgroups per CU, as
+// its LDS allows, instead of seven): a handful of values spill, outside the tile
+// loop, and the long context took 0.94 against 0.955 ms, B=4 L=16384 D=2048 0.499
+// against 0.511 ms.  (Holding the whole-wave emit-first passes to 64, four
+// workgroups per CU instead of three, made the long context 23% slower.)
 template <bool HALF>
 struct ScanShape {
     static constexpr int kWaves = HALF ? 4 : kGroups;  // waves per workgroup
@@ -167,16 +170,16 @@ constexpr int scan_threads()
 {
     return HALF ? 4 * kWave : kGroups * kWave;
 }
-template <int MODE>
+template <int MODE, int CORR, bool HALF>
 constexpr int scan_waves_per_eu()
 {
-    return (MODE & kOptZoh) ? 6 : 2;
+    return (MODE & kOptZoh) ? 6 : (CORR == 1 && HALF ? 8 : 2);
 }
 
 template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false, bool HALF = false,
           int CORR = 0>
 __global__ __launch_bounds__(scan_threads<HALF>())
-    __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<MODE>()))) void scan_kernel(ScanArgs a)
+    __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<MODE, CORR, HALF>()))) void scan_kernel(ScanArgs a)
 {
     static_assert(CORR == 0 || (EMIT && !CKPT), "the emit-first passes are emit passes without checkpoints");
     constexpr bool ZOH = (MODE & kOptZoh) != 0;
@@ -273,7 +276,9 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const bool first = CORR == 1;
     const bool from_ws = EMIT && a.n_chunks > 1 && !first;
     const bool from_h0 = EMIT && a.h0 != nullptr && (a.n_chunks == 1 || (first && c == 0));
-    if (CORR == 0 && from_ws && a.fuse_carry) {
+    const bool fused = CORR == 0 && from_ws && a.fuse_carry != 0;
+    // fused carry: run() forms h with this once the first tiles' loads are in flight
+    auto fuse_carry_init = [&]() {
         // the carry into chunk c: the initial state through the affine maps of chunks
         // 0..c-1, (P_j, S_j) with P_j = exp(A * sum of delta over chunk j) and S_j the
         // chunk's end state from zero, applied earlier chunk first.  The loads are
@@ -303,6 +308,10 @@ __global__ __launch_bounds__(scan_threads<HALF>())
 #pragma unroll
             for (int i = 0; i < kNS; ++i) dst[i] = h[i];
         }
+    };
+    if (fused) {
+#pragma unroll
+        for (int i = 0; i < kNS; ++i) h[i] = 0.0f;  // set by fuse_carry_init before the first tile
     } else if (from_ws || from_h0) {
         const float* init = from_ws ? a.ws_state + c * BD * N + sbase : a.h0 + sbase;
 #pragma unroll
@@ -556,6 +565,8 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     auto run = [&](int k0, int k1, auto stop) {
         issue_rows(k0, Slot<0>{});
         issue_rows(k0 + 1, Slot<1>{});
+        // its loads go out after the first two tiles', so their latencies overlap
+        if (fused && k0 == 0) fuse_carry_init();
         publish_rows(k0, Slot<0>{});
         issue_rows(k0 + 2, Slot<0>{});
         issue_words(k0, Slot<0>{});
