@@ -80,17 +80,19 @@ typedef enum { SS_DELTA_SOFTPLUS = 1, SS_B_ZOH = 2 } ss_option;
  * are joined by an exact associative combine of affine pairs (LTI chapter
  * 3.1, section 3.1.5.2, parallel scan over an associative operator):
  * (a1, b1) then (a2, b2) gives (a2*a1, a2*b1 + b2).  Chunks shorter than
- * 1024 rows: every chunk but the last first has its end state from a zero
- * start found (its affine pair), the pairs are combined into each chunk's
- * carry, and every chunk is run from its carry to produce y.  Chunks of 1024
- * rows or more (a multiple of 16), without checkpoints: every chunk is first
- * run from its own start (h0 for the first, zero for the others), writing y
- * and its end state; the carries follow; then each later chunk is rerun from
- * its carry until the carry's effect has decayed below fp32 resolution
- * (all step sizes of the chunk >= 0, A <= 0, and exp(A * sum of delta) *
- * |carry| <= 2^-24 of the lane's largest state entry, checked after 128 rows
- * and then every 64 rows for each 32 or 64 channels), else to its end.  Either way the result is the
- * one-pass recurrence up to fp32 rounding.
+ * 1024 rows (or with checkpoints): every chunk but the last first has its end
+ * state from a zero start found (its affine pair), the pairs are combined
+ * into each chunk's carry (with at most 16 chunks by the pass that produces
+ * y, at the start of each chunk), and every chunk is run from its carry to
+ * produce y.  Chunks of 1024 rows or more (a multiple of 16), without
+ * checkpoints: every chunk is first run from its own start (h0 for the
+ * first, zero for the others), writing y and its end state; the carries
+ * follow; then each later chunk is rerun from its carry until the carry's
+ * effect has decayed below fp32 resolution (all step sizes of the chunk >= 0,
+ * A <= 0, and exp(A * sum of delta) * |carry| <= 2^-24 of the lane's largest
+ * state entry, checked after 128 rows and then every 64 rows for each 32 or
+ * 64 channels), else to its end.  Either way the result is the one-pass
+ * recurrence up to fp32 rounding.
  *
  * The chunk length is a power of two chosen from the shape only: pure,
  * host-only, deterministic.  Writes *chunk_len_T and *n_chunks_K (either may
@@ -130,8 +132,8 @@ ss_status ss_scan_plan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
  *   was rerun over its whole length, 0 where the rerun stopped early;
  *   then (K, batch, ceil(dim/32)) uint32 words, 1 where chunk c has a
  *   negative step size.
- *   instead, when chunk_len is shorter than that and K <= 16: (K-1, batch,
- *   dim, N), the end state of chunk c from a zero start (the emit pass forms
+ *   otherwise (the aggregate pass), when K <= 16: (K-1, batch, dim, N), the
+ *   end state of chunk c from a zero start (the pass that produces y forms
  *   the carries from these itself).
  *   always, from the next multiple of 256 bytes to the end:
  *                          an fp32 copy of B and C, per (batch row, chunk),
