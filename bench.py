@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the selective scan on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras a,b,... | --no-extras]
 
 One step = one ss_scan_fwd call over the large-layer workload (B=8, L=2048,
 D=5120, N=16; bf16 u/delta/B/C/z and y, fp32 A/D and state, D skip and silu(z)
@@ -12,9 +12,10 @@ fp64 CPU oracle timed on a bounded sample of the same workload.
 
 Extra objects: ``decode_step`` (ss_step on the B=256, D=5120 recurrent-step
 workload: chained on the same operands, with the last-level cache flushed
-before each token, and 1000 chained tokens with fresh operands), ``decode_graph`` (single-sequence decode, B=1: 64 chained ss_step
-calls launched one by one against the same loop captured once in a hipGraph
-and replayed), ``parity`` (the timed output against the oracle on every
+before each token, and 1000 chained tokens with fresh operands),
+``decode_graph`` (single-sequence decode, B=1: 64 chained ss_step calls
+launched one by one against the same loop captured once in a hipGraph and
+replayed), ``parity`` (the timed output against the oracle on every
 channel, taken in the CPU-baseline leg, the one place the oracle runs; it runs
 even when the oracle's timed repetitions are skipped), ``probes`` (the
 measured ceilings: a 3:1 read:write HBM stream like the scan's, a plain copy,
@@ -34,7 +35,9 @@ them), ``conv1d``
 (ss_conv1d_silu producing the layer's u from the x half of a (B, L, 2D)
 in-projection output, with its HBM roofline) and ``ssd`` (ss_ssd_fwd, the
 multi-head recurrence on the matrix cores, B=8 L=2048, 64 heads of 64
-channels, dstate 128).
+channels, dstate 128).  ``--extras`` picks which of the sections after the
+timed region run (flushed, options, backward, configs, conv1d, ssd, decode;
+decode covers decode_step and decode_graph); all by default.
 """
 from __future__ import annotations
 
@@ -54,6 +57,10 @@ METRIC = "selective-scan elements/s (B·L·D·N) + achieved HBM GB/s vs peak, 1 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_large_layer.txt")
 
 
+# the sections run after the timed region, each timing one more workload or option
+EXTRA_SECTIONS = ("flushed", "options", "backward", "configs", "conv1d", "ssd", "decode")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,9 +69,17 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle's timed repetitions (the parity check of the timed output still runs)")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads and flushed timing")
+    ap.add_argument("--extras", default="all",
+                    help="comma-separated extra sections to run (default all): " + ",".join(EXTRA_SECTIONS))
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the ceiling probes and the plain device copy of known size (counter scaling)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.extra_set = set() if args.no_extras else (
+        set(EXTRA_SECTIONS) if args.extras == "all" else set(x for x in args.extras.split(",") if x))
+    unknown = args.extra_set - set(EXTRA_SECTIONS)
+    if unknown:
+        ap.error("unknown --extras section(s): %s" % ",".join(sorted(unknown)))
+    return args
 
 
 def kernel_source_hash() -> str:
@@ -291,86 +306,10 @@ def main():
                                     "GB/s": 2 * n * 4 / (ms * 1e-3) / 1e9}
         del a, b
 
-    if not args.no_extras:
-        # the same scan with the last-level cache flushed before each step
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)  # 1 GiB
-        times = []
-        for _ in range(10):
-            scratch.fill_(1.0)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        del scratch
-        fl = float(np.median(times))
-        result["flushed"] = {"ms_per_step_median": fl, "elements/s": elements / (fl * 1e-3),
-                             "alg_GB/s": alg_bytes / (fl * 1e-3) / 1e9}
-
-
-        # the same layer with the step-size / input-term options
-        raw = wl.with_raw_delta(inp, seed=0, cfg_id=w.cfg_id)
-        dl_raw, bias = to_dev(raw["delta"]), to_dev(raw["delta_bias"])
-        opt_res = {}
-        for name, kw in (("softplus+bias", dict(delta_softplus=True)), ("zoh", dict(zoh=True)),
-                         ("softplus+bias+zoh", dict(delta_softplus=True, zoh=True))):
-            sp = kw.get("delta_softplus", False)
-
-            def ostep():
-                ss.scan_fwd(t["u"], dl_raw if sp else t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                            out=y, workspace=ws, delta_bias=bias if sp else None, **kw)
-
-            for _ in range(3):
-                ostep()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                ostep()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            oms = e0.elapsed_time(e1) / 20
-            opt_res[name] = {"ms_per_step": oms, "elements/s": elements / (oms * 1e-3),
-                             "alg_GB/s": (alg_bytes + 4 * w.dim * sp) / (oms * 1e-3) / 1e9}
-        result["options"] = opt_res
-
-        # the backward on the same layer
-        dy_t = torch.randn(w.batch, w.seqlen, w.dim, device=device, generator=torch.Generator(device).manual_seed(5)
-                           ).to(torch.bfloat16)
-        bws = torch.empty(ss.scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate), dtype=torch.uint8,
-                          device=device)
-
-        def bstep():
-            ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=bws)
-
-        for _ in range(2):
-            bstep()
-        torch.cuda.synchronize()
+    extras = args.extra_set
+    if extras:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            bstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / 10
-        del bws
-
-        # training path: the forward keeps every 16th state, the backward reuses them
-        ck = torch.empty(ss.scan_ckpt_shape(w.batch, w.seqlen, w.dim, w.dstate), device=device)
-        cws = torch.empty(ss.scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate, with_ckpt=True),
-                          dtype=torch.uint8, device=device)
-        yk = torch.empty_like(t["u"])
-
-        def fkstep():
-            ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=yk, workspace=ws,
-                        ckpt=ck)
-
-        def bkstep():
-            ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=cws, ckpt=ck)
 
         def timed(fn, reps=10):
             fn()
@@ -382,250 +321,339 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
-        fk_ms, bk_ms = timed(fkstep), timed(bkstep)
+        if "flushed" in extras:
+            # the same scan with the last-level cache flushed before each step
+            scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)  # 1 GiB
+            times = []
+            for _ in range(10):
+                scratch.fill_(1.0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            del scratch
+            fl = float(np.median(times))
+            result["flushed"] = {"ms_per_step_median": fl, "elements/s": elements / (fl * 1e-3),
+                                 "alg_GB/s": alg_bytes / (fl * 1e-3) / 1e9}
 
-        # the same training pair under the zero-order-hold input term
-        def fzstep():
-            ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=yk, workspace=ws,
-                        ckpt=ck, zoh=True)
+        if "options" in extras:
+            # the same layer with the step-size / input-term options
+            raw = wl.with_raw_delta(inp, seed=0, cfg_id=w.cfg_id)
+            dl_raw, bias = to_dev(raw["delta"]), to_dev(raw["delta_bias"])
+            opt_res = {}
+            for name, kw in (("softplus+bias", dict(delta_softplus=True)), ("zoh", dict(zoh=True)),
+                             ("softplus+bias+zoh", dict(delta_softplus=True, zoh=True))):
+                sp = kw.get("delta_softplus", False)
 
-        def bzstep():
-            ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=cws, ckpt=ck,
-                        zoh=True)
+                def ostep():
+                    ss.scan_fwd(t["u"], dl_raw if sp else t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                out=y, workspace=ws, delta_bias=bias if sp else None, **kw)
 
-        fz_ms, bz_ms = timed(fzstep), timed(bzstep)
-        result["backward"] = {"ms_per_step": bms, "elements/s": elements / (bms * 1e-3),
-                              "vs_forward": bms / ms_step, "note": "panel + checkpoint pass + adjoint + reduce",
-                              "training": {"fwd_ckpt_ms": fk_ms, "bwd_from_ckpt_ms": bk_ms,
-                                           "fwd_plus_bwd_ms": fk_ms + bk_ms,
-                                           "fwd_plus_standalone_bwd_ms": ms_step + bms,
-                                           "ckpt_bytes": ck.numel() * 4,
-                                           "note": "ss_scan_fwd_ckpt keeps the state every 16 rows; "
-                                                   "ss_scan_bwd_ckpt skips the checkpoint pass"},
-                              "training_zoh": {"fwd_ckpt_ms": fz_ms, "bwd_from_ckpt_ms": bz_ms,
-                                               "fwd_plus_bwd_ms": fz_ms + bz_ms}}
-        del ck, cws, yk
+                for _ in range(3):
+                    ostep()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(20):
+                    ostep()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                oms = e0.elapsed_time(e1) / 20
+                opt_res[name] = {"ms_per_step": oms, "elements/s": elements / (oms * 1e-3),
+                                 "alg_GB/s": (alg_bytes + 4 * w.dim * sp) / (oms * 1e-3) / 1e9}
+            result["options"] = opt_res
 
-        # the other scan configurations at their own shapes: the small-model layer and the
-        # long context, whose automatic plans cut the sequence into chunks.  Inputs drawn on
-        # the device with the configurations' distributions.
-        cfgs = {}
-        for name in ("small", "long"):
-            cw_ = wl.WORKLOADS[name]
-            gen = torch.Generator(device).manual_seed(100 + cw_.cfg_id)
-            shp = (cw_.batch, cw_.seqlen, cw_.dim)
-            tdt = torch.bfloat16 if cw_.dtype == wl.BF16 else torch.float32
-            cu_ = torch.randn(shp, device=device, generator=gen).to(tdt)
-            cd_ = torch.nn.functional.softplus(torch.randn(shp, device=device, generator=gen) * cw_.delta_sigma
-                                               + cw_.delta_mu).to(tdt)
-            cB_ = torch.randn(cw_.batch, cw_.seqlen, cw_.dstate, device=device, generator=gen).to(tdt)
-            cC_ = torch.randn(cw_.batch, cw_.seqlen, cw_.dstate, device=device, generator=gen).to(tdt)
-            cA_ = to_dev(wl.make_A(cw_.dim, cw_.dstate, cw_.a_perturbed, cfg_id=cw_.cfg_id))
-            cD_ = torch.randn(cw_.dim, device=device, generator=gen) if cw_.has_D else None
-            cz_ = torch.randn(shp, device=device, generator=gen).to(tdt) if cw_.has_z else None
-            cy_ = torch.empty_like(cu_)
-            cT, cK = ss.scan_plan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate)
-            cws = torch.empty(max(ss.scan_workspace_bytes(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate), 1),
-                              dtype=torch.uint8, device=device)
+        if "backward" in extras:
+            # the backward on the same layer
+            dy_t = torch.randn(w.batch, w.seqlen, w.dim, device=device, generator=torch.Generator(device).manual_seed(5)
+                               ).to(torch.bfloat16)
+            bws = torch.empty(ss.scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate), dtype=torch.uint8,
+                              device=device)
 
-            def cstep_():
-                ss.scan_fwd(cu_, cd_, cA_, cB_, cC_, D=cD_, z=cz_, out=cy_, workspace=cws)
+            def bstep():
+                ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=bws)
 
-            cms = timed(cstep_)
-            cel = cw_.batch * cw_.seqlen * cw_.dim * cw_.dstate
-            cby = wl.algorithmic_bytes_scan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate, cw_.dtype, cw_.has_D,
-                                            cw_.has_z)
-            cfgs[name] = {"workload": "%s: B=%d L=%d D=%d N=%d, %s" % (cw_.note, cw_.batch, cw_.seqlen, cw_.dim,
-                                                                      cw_.dstate, cw_.dtype),
-                          "chunk_len": cT, "n_chunks": cK, "ms_per_call": cms, "elements/s": cel / (cms * 1e-3),
-                          "alg_GB/s": cby / (cms * 1e-3) / 1e9, "frac_of_8TB/s": cby / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-            del cu_, cd_, cB_, cC_, cz_, cy_, cws
-        result["configs"] = cfgs
-
-        # the block's causal depthwise convolution + SiLU producing u (x read in place from xz)
-        xz = torch.randn(w.batch, w.seqlen, 2 * w.dim, device=device,
-                         generator=torch.Generator(device).manual_seed(6)).to(torch.bfloat16)
-        cw = torch.randn(w.dim, 4, device=device, generator=torch.Generator(device).manual_seed(7)) * 0.5
-        cb = torch.randn(w.dim, device=device, generator=torch.Generator(device).manual_seed(8))
-        cu = torch.empty(w.batch, w.seqlen, w.dim, dtype=torch.bfloat16, device=device)
-
-        def cstep():
-            ss.conv1d_silu(xz[..., :w.dim], cw, cb, out=cu)
-
-        for _ in range(3):
-            cstep()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(20):
-            cstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cms = e0.elapsed_time(e1) / 20
-        cbytes = 2 * 2 * w.batch * w.seqlen * w.dim + 4 * w.dim * 5  # x read + u written (bf16), weights, bias
-        cgbs = cbytes / (cms * 1e-3) / 1e9
-        result["conv1d"] = {"workload": "B=8 L=2048 D=5120 bf16, width 4, x = first half of xz (B, L, 2D)",
-                            "ms": cms, "alg_bytes": cbytes, "alg_GB/s": cgbs, "frac_of_8TB/s": cgbs / HBM_PEAK_GBS}
-        del xz, cu
-
-        # the multi-head (Mamba-2) recurrence on the matrix cores
-        sb, sl, sh, sn = 8, 2048, 64, 128
-        si = wl.ssd_inputs(sb, sl, sh, 64, sn, seed=0)
-        stt = {k: to_dev(v) for k, v in si.items() if v is not None}
-        sy = torch.empty_like(stt["x"])
-
-        def sstep():
-            ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy)
-
-        for _ in range(3):
-            sstep()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(20):
-            sstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        sms = e0.elapsed_time(e1) / 20
-        sbytes = wl.algorithmic_bytes_ssd(sb, sl, sh, 64, sn)
-        # executed bf16 MFMA 32x32x16 per 64-row chunk and head: 24 (C B^T, upper block skipped)
-        # + 64 (C S_in, hi + lo) + 24 (M X, hi + lo, upper half skipped) + 64 (state, hi + lo)
-        sflops = 176 * 32 * 32 * 16 * 2 * (sl // 64) * sb * sh
-        result["ssd"] = {"workload": "B=8 L=2048 H=64 headdim=64 dstate=128 bf16, D skip",
-                         "ms": sms, "alg_bytes": sbytes, "alg_GB/s": sbytes / (sms * 1e-3) / 1e9,
-                         "frac_of_8TB/s": sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "mfma_TFLOP/s": sflops / (sms * 1e-3) / 1e12, "frac_of_2.5PF": sflops / (sms * 1e-3) / 2.5e15}
-        del stt, sy
-
-        # the same layer at dstate 256: a launch per half of the state entries, the second
-        # adding the first's fp32 part of y to its own
-        si = wl.ssd_inputs(sb, sl, sh, 64, 256, seed=0)
-        stt = {k: to_dev(v) for k, v in si.items() if v is not None}
-        sy = torch.empty_like(stt["x"])
-        sws = torch.empty(ss.ssd_workspace_bytes(sb, sl, sh, 64, 256), dtype=torch.uint8, device=device)
-
-        def sstep256():
-            ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy, workspace=sws)
-
-        for _ in range(3):
-            sstep256()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(20):
-            sstep256()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        result["ssd"]["dstate256"] = {"ms": e0.elapsed_time(e1) / 20,
-                                      "alg_bytes": wl.algorithmic_bytes_ssd(sb, sl, sh, 64, 256)}
-        del stt, sy, sws
-
-        # recurrent step workload: one token for B=256, D=5120, state in place
-        sw = wl.WORKLOADS["step"]
-        sp = wl.step_params(sw)
-        si = wl.step_inputs(sw, 0)
-        st = {k: to_dev(v) for k, v in si.items()}
-        A5, D5, h5 = to_dev(sp["A"]), to_dev(sp["D"]), to_dev(sp["h0"])
-        y5 = torch.empty_like(st["u"])
-
-        def dstep():
-            ss.step(h5, st["u"], st["delta"], A5, st["B"], st["C"], D=D5, z=st["z"], out=y5)
-
-        for _ in range(5):
-            dstep()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(100):
-            dstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / 100
-        sb = wl.algorithmic_bytes_step(sw.batch, sw.dim, sw.dstate, sw.dtype, sw.has_D, sw.has_z)
-        # cold: the 256 MB last-level cache flushed before each token (median of 20)
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)
-        cold = []
-        for _ in range(20):
-            scratch.fill_(1.0)
+            for _ in range(2):
+                bstep()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            dstep()
+            for _ in range(10):
+                bstep()
             e1.record(stream)
             torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1) * 1e3)
-        del scratch
-        us_cold = float(np.median(cold))
-        # 1000 chained tokens, each with fresh operands (drawn on the device beforehand,
-        # with the step workload's distributions), timed as one run
-        n_chain = 1000
-        cg = torch.Generator(device).manual_seed(500)
-        shp_c = (n_chain, sw.batch, sw.dim)
-        cu = torch.randn(shp_c, device=device, generator=cg).to(torch.bfloat16)
-        cd = torch.nn.functional.softplus(torch.randn(shp_c, device=device, generator=cg) - 2.0).to(torch.bfloat16)
-        cz = torch.randn(shp_c, device=device, generator=cg).to(torch.bfloat16)
-        cB = torch.randn(n_chain, sw.batch, sw.dstate, device=device, generator=cg).to(torch.bfloat16)
-        cC = torch.randn(n_chain, sw.batch, sw.dstate, device=device, generator=cg).to(torch.bfloat16)
-        cy = torch.empty_like(cu)
-        ch = h5.clone()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for k in range(n_chain):
-            ss.step(ch, cu[k], cd[k], A5, cB[k], cC[k], D=D5, z=cz[k], out=cy[k])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us_chain = e0.elapsed_time(e1) * 1e3 / n_chain
-        del cu, cd, cz, cB, cC, cy, ch
-        result["decode_step"] = {"workload": "recurrent step B=256 D=5120 N=16, bf16, state (84 MB) in place",
-                                 "us_per_token": us, "elements/s": sw.elements / (us * 1e-6),
-                                 "alg_GB/s": sb / (us * 1e-6) / 1e9,
-                                 "note": "chained on the same operands, state warm in cache",
-                                 "cold_us_per_token": us_cold, "cold_alg_GB/s": sb / (us_cold * 1e-6) / 1e9,
-                                 "cold_frac_of_8TB/s": sb / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                 "chained_1000_us_per_token": us_chain,
-                                 "chained_1000_alg_GB/s": sb / (us_chain * 1e-6) / 1e9,
-                                 "chained_1000_note": "1000 tokens in one run, fresh operands per token"}
-        del st, y5, h5
+            bms = e0.elapsed_time(e1) / 10
+            del bws
 
-        # single-sequence decode (B=1): launch-bound, so the token loop is captured
-        # once in a hipGraph and replayed, against the same loop launched eagerly
-        n_tok, gd = 64, 5120
-        gi = wl.scan_inputs(1, n_tok, gd, 16, wl.BF16, has_D=True, has_z=True, has_h0=True, seed=77)
-        gt = {k: to_dev(v) for k, v in gi.items()}
-        gcol = {k: [gt[k][:, s].contiguous() for s in range(n_tok)] for k in ("u", "delta", "B", "C", "z")}
-        gh = gt["h0"].clone()
-        gy = torch.empty(n_tok, 1, gd, dtype=torch.bfloat16, device=device)
+            # training path: the forward keeps every 16th state, the backward reuses them
+            ck = torch.empty(ss.scan_ckpt_shape(w.batch, w.seqlen, w.dim, w.dstate), device=device)
+            cws = torch.empty(ss.scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate, with_ckpt=True),
+                              dtype=torch.uint8, device=device)
+            yk = torch.empty_like(t["u"])
 
-        def gloop():
-            for s_ in range(n_tok):
-                ss.step(gh, gcol["u"][s_], gcol["delta"][s_], gt["A"], gcol["B"][s_], gcol["C"][s_], D=gt["D"],
-                        z=gcol["z"][s_], out=gy[s_])
+            def fkstep():
+                ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=yk, workspace=ws,
+                            ckpt=ck)
 
-        def per_token(fn, reps=10):
-            fn()
+            def bkstep():
+                ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=cws,
+                            ckpt=ck)
+
+            fk_ms, bk_ms = timed(fkstep), timed(bkstep)
+
+            # the same training pair under the zero-order-hold input term
+            def fzstep():
+                ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=yk, workspace=ws,
+                            ckpt=ck, zoh=True)
+
+            def bzstep():
+                ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=cws,
+                            ckpt=ck, zoh=True)
+
+            fz_ms, bz_ms = timed(fzstep), timed(bzstep)
+            result["backward"] = {"ms_per_step": bms, "elements/s": elements / (bms * 1e-3),
+                                  "vs_forward": bms / ms_step, "note": "panel + checkpoint pass + adjoint + reduce",
+                                  "training": {"fwd_ckpt_ms": fk_ms, "bwd_from_ckpt_ms": bk_ms,
+                                               "fwd_plus_bwd_ms": fk_ms + bk_ms,
+                                               "fwd_plus_standalone_bwd_ms": ms_step + bms,
+                                               "ckpt_bytes": ck.numel() * 4,
+                                               "note": "ss_scan_fwd_ckpt keeps the state every 16 rows; "
+                                                       "ss_scan_bwd_ckpt skips the checkpoint pass"},
+                                  "training_zoh": {"fwd_ckpt_ms": fz_ms, "bwd_from_ckpt_ms": bz_ms,
+                                                   "fwd_plus_bwd_ms": fz_ms + bz_ms}}
+            del ck, cws, yk
+
+        if "configs" in extras:
+            # the other scan configurations at their own shapes: the small-model layer and the
+            # long context, whose automatic plans cut the sequence into chunks.  Inputs drawn on
+            # the device with the configurations' distributions.
+            cfgs = {}
+            for name in ("small", "long"):
+                cw_ = wl.WORKLOADS[name]
+                gen = torch.Generator(device).manual_seed(100 + cw_.cfg_id)
+                shp = (cw_.batch, cw_.seqlen, cw_.dim)
+                tdt = torch.bfloat16 if cw_.dtype == wl.BF16 else torch.float32
+                cu_ = torch.randn(shp, device=device, generator=gen).to(tdt)
+                cd_ = torch.nn.functional.softplus(torch.randn(shp, device=device, generator=gen) * cw_.delta_sigma
+                                                   + cw_.delta_mu).to(tdt)
+                cB_ = torch.randn(cw_.batch, cw_.seqlen, cw_.dstate, device=device, generator=gen).to(tdt)
+                cC_ = torch.randn(cw_.batch, cw_.seqlen, cw_.dstate, device=device, generator=gen).to(tdt)
+                cA_ = to_dev(wl.make_A(cw_.dim, cw_.dstate, cw_.a_perturbed, cfg_id=cw_.cfg_id))
+                cD_ = torch.randn(cw_.dim, device=device, generator=gen) if cw_.has_D else None
+                cz_ = torch.randn(shp, device=device, generator=gen).to(tdt) if cw_.has_z else None
+                cy_ = torch.empty_like(cu_)
+                cT, cK = ss.scan_plan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate)
+                cws = torch.empty(max(ss.scan_workspace_bytes(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate), 1),
+                                  dtype=torch.uint8, device=device)
+
+                def cstep_():
+                    ss.scan_fwd(cu_, cd_, cA_, cB_, cC_, D=cD_, z=cz_, out=cy_, workspace=cws)
+
+                cms = timed(cstep_)
+                cel = cw_.batch * cw_.seqlen * cw_.dim * cw_.dstate
+                cby = wl.algorithmic_bytes_scan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate, cw_.dtype, cw_.has_D,
+                                                cw_.has_z)
+                cfgs[name] = {"workload": "%s: B=%d L=%d D=%d N=%d, %s" % (cw_.note, cw_.batch, cw_.seqlen, cw_.dim,
+                                                                          cw_.dstate, cw_.dtype),
+                              "chunk_len": cT, "n_chunks": cK, "ms_per_call": cms, "elements/s": cel / (cms * 1e-3),
+                              "alg_GB/s": cby / (cms * 1e-3) / 1e9,
+                              "frac_of_8TB/s": cby / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                del cu_, cd_, cB_, cC_, cz_, cy_, cws
+            result["configs"] = cfgs
+
+        if "conv1d" in extras:
+            # the block's causal depthwise convolution + SiLU producing u (x read in place from xz)
+            xz = torch.randn(w.batch, w.seqlen, 2 * w.dim, device=device,
+                             generator=torch.Generator(device).manual_seed(6)).to(torch.bfloat16)
+            cw = torch.randn(w.dim, 4, device=device, generator=torch.Generator(device).manual_seed(7)) * 0.5
+            cb = torch.randn(w.dim, device=device, generator=torch.Generator(device).manual_seed(8))
+            cu = torch.empty(w.batch, w.seqlen, w.dim, dtype=torch.bfloat16, device=device)
+
+            def cstep():
+                ss.conv1d_silu(xz[..., :w.dim], cw, cb, out=cu)
+
+            for _ in range(3):
+                cstep()
             torch.cuda.synchronize()
-            e0.record(torch.cuda.current_stream())
-            for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                cstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cms = e0.elapsed_time(e1) / 20
+            cbytes = 2 * 2 * w.batch * w.seqlen * w.dim + 4 * w.dim * 5  # x read + u written (bf16), weights, bias
+            cgbs = cbytes / (cms * 1e-3) / 1e9
+            result["conv1d"] = {"workload": "B=8 L=2048 D=5120 bf16, width 4, x = first half of xz (B, L, 2D)",
+                                "ms": cms, "alg_bytes": cbytes, "alg_GB/s": cgbs, "frac_of_8TB/s": cgbs / HBM_PEAK_GBS}
+            del xz, cu
+
+        if "ssd" in extras:
+            # the multi-head (Mamba-2) recurrence on the matrix cores
+            sb, sl, sh, sn = 8, 2048, 64, 128
+            si = wl.ssd_inputs(sb, sl, sh, 64, sn, seed=0)
+            stt = {k: to_dev(v) for k, v in si.items() if v is not None}
+            sy = torch.empty_like(stt["x"])
+
+            def sstep():
+                ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy)
+
+            for _ in range(3):
+                sstep()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                sstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sms = e0.elapsed_time(e1) / 20
+            sbytes = wl.algorithmic_bytes_ssd(sb, sl, sh, 64, sn)
+            # executed bf16 MFMA 32x32x16 per 64-row chunk and head: 24 (C B^T, upper block skipped)
+            # + 64 (C S_in, hi + lo) + 24 (M X, hi + lo, upper half skipped) + 64 (state, hi + lo)
+            sflops = 176 * 32 * 32 * 16 * 2 * (sl // 64) * sb * sh
+            result["ssd"] = {"workload": "B=8 L=2048 H=64 headdim=64 dstate=128 bf16, D skip",
+                             "ms": sms, "alg_bytes": sbytes, "alg_GB/s": sbytes / (sms * 1e-3) / 1e9,
+                             "frac_of_8TB/s": sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "mfma_TFLOP/s": sflops / (sms * 1e-3) / 1e12,
+                             "frac_of_2.5PF": sflops / (sms * 1e-3) / 2.5e15}
+            del stt, sy
+
+            # the same layer at dstate 256: a launch per half of the state entries, the second
+            # adding the first's fp32 part of y to its own
+            si = wl.ssd_inputs(sb, sl, sh, 64, 256, seed=0)
+            stt = {k: to_dev(v) for k, v in si.items() if v is not None}
+            sy = torch.empty_like(stt["x"])
+            sws = torch.empty(ss.ssd_workspace_bytes(sb, sl, sh, 64, 256), dtype=torch.uint8, device=device)
+
+            def sstep256():
+                ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy, workspace=sws)
+
+            for _ in range(3):
+                sstep256()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(20):
+                sstep256()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            result["ssd"]["dstate256"] = {"ms": e0.elapsed_time(e1) / 20,
+                                          "alg_bytes": wl.algorithmic_bytes_ssd(sb, sl, sh, 64, 256)}
+            del stt, sy, sws
+
+        if "decode" in extras:
+            # recurrent step workload: one token for B=256, D=5120, state in place
+            sw = wl.WORKLOADS["step"]
+            sp = wl.step_params(sw)
+            si = wl.step_inputs(sw, 0)
+            st = {k: to_dev(v) for k, v in si.items()}
+            A5, D5, h5 = to_dev(sp["A"]), to_dev(sp["D"]), to_dev(sp["h0"])
+            y5 = torch.empty_like(st["u"])
+
+            def dstep():
+                ss.step(h5, st["u"], st["delta"], A5, st["B"], st["C"], D=D5, z=st["z"], out=y5)
+
+            for _ in range(5):
+                dstep()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(100):
+                dstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 100
+            sb = wl.algorithmic_bytes_step(sw.batch, sw.dim, sw.dstate, sw.dtype, sw.has_D, sw.has_z)
+            # cold: the 256 MB last-level cache flushed before each token (median of 20)
+            scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)
+            cold = []
+            for _ in range(20):
+                scratch.fill_(1.0)
+                e0.record(stream)
+                dstep()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1) * 1e3)
+            del scratch
+            us_cold = float(np.median(cold))
+            # 1000 chained tokens, each with fresh operands (drawn on the device beforehand,
+            # with the step workload's distributions), timed as one run
+            n_chain = 1000
+            cg = torch.Generator(device).manual_seed(500)
+            shp_c = (n_chain, sw.batch, sw.dim)
+            cu = torch.randn(shp_c, device=device, generator=cg).to(torch.bfloat16)
+            cd = torch.nn.functional.softplus(torch.randn(shp_c, device=device, generator=cg) - 2.0).to(torch.bfloat16)
+            cz = torch.randn(shp_c, device=device, generator=cg).to(torch.bfloat16)
+            cB = torch.randn(n_chain, sw.batch, sw.dstate, device=device, generator=cg).to(torch.bfloat16)
+            cC = torch.randn(n_chain, sw.batch, sw.dstate, device=device, generator=cg).to(torch.bfloat16)
+            cy = torch.empty_like(cu)
+            ch = h5.clone()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for k in range(n_chain):
+                ss.step(ch, cu[k], cd[k], A5, cB[k], cC[k], D=D5, z=cz[k], out=cy[k])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us_chain = e0.elapsed_time(e1) * 1e3 / n_chain
+            del cu, cd, cz, cB, cC, cy, ch
+            result["decode_step"] = {"workload": "recurrent step B=256 D=5120 N=16, bf16, state (84 MB) in place",
+                                     "us_per_token": us, "elements/s": sw.elements / (us * 1e-6),
+                                     "alg_GB/s": sb / (us * 1e-6) / 1e9,
+                                     "note": "chained on the same operands, state warm in cache",
+                                     "cold_us_per_token": us_cold, "cold_alg_GB/s": sb / (us_cold * 1e-6) / 1e9,
+                                     "cold_frac_of_8TB/s": sb / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                     "chained_1000_us_per_token": us_chain,
+                                     "chained_1000_alg_GB/s": sb / (us_chain * 1e-6) / 1e9,
+                                     "chained_1000_note": "1000 tokens in one run, fresh operands per token"}
+            del st, y5, h5
+
+            # single-sequence decode (B=1): launch-bound, so the token loop is captured
+            # once in a hipGraph and replayed, against the same loop launched eagerly
+            n_tok, gd = 64, 5120
+            gi = wl.scan_inputs(1, n_tok, gd, 16, wl.BF16, has_D=True, has_z=True, has_h0=True, seed=77)
+            gt = {k: to_dev(v) for k, v in gi.items()}
+            gcol = {k: [gt[k][:, s].contiguous() for s in range(n_tok)] for k in ("u", "delta", "B", "C", "z")}
+            gh = gt["h0"].clone()
+            gy = torch.empty(n_tok, 1, gd, dtype=torch.bfloat16, device=device)
+
+            def gloop():
+                for s_ in range(n_tok):
+                    ss.step(gh, gcol["u"][s_], gcol["delta"][s_], gt["A"], gcol["B"][s_], gcol["C"][s_], D=gt["D"],
+                            z=gcol["z"][s_], out=gy[s_])
+
+            def per_token(fn, reps=10):
                 fn()
-            e1.record(torch.cuda.current_stream())
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / (reps * n_tok)
+                torch.cuda.synchronize()
+                e0.record(torch.cuda.current_stream())
+                for _ in range(reps):
+                    fn()
+                e1.record(torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / (reps * n_tok)
 
-        us_eager = per_token(gloop)
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            gloop()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            gloop()
-        torch.cuda.synchronize()
-        us_graph = per_token(graph.replay)
-        result["decode_graph"] = {"workload": "recurrent step B=1 D=5120 N=16, bf16, D skip + gate, %d tokens "
-                                              "per hipGraph" % n_tok,
-                                  "eager_us_per_token": us_eager, "graph_us_per_token": us_graph}
-        del graph, gt, gcol, gy, gh
+            us_eager = per_token(gloop)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                gloop()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                gloop()
+            torch.cuda.synchronize()
+            us_graph = per_token(graph.replay)
+            result["decode_graph"] = {"workload": "recurrent step B=1 D=5120 N=16, bf16, D skip + gate, %d tokens "
+                                                  "per hipGraph" % n_tok,
+                                      "eager_us_per_token": us_eager, "graph_us_per_token": us_graph}
+            del graph, gt, gcol, gy, gh
 
     # the CPU-baseline leg: the oracle checks the timed output on every channel, and (unless
     # skipped) is timed on this host's cores, all threads and one thread
