@@ -82,13 +82,19 @@ def parse():
     return args
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code: comments and whitespace are left out,
-    so that only a change of the code marks stored counter figures as stale."""
+# the sources that define the scan kernel and how it is launched (the backward, conv1d and
+# SSD kernels live in files of their own)
+SCAN_SOURCES = ("ss_api.cpp", "ss_device.h", "ss_internal.h", "ss_kernels.hip")
+
+
+def kernel_source_hash(names=SCAN_SOURCES) -> str:
+    """Hash of the code of the given kernel sources (default: the scan kernel's; None:
+    every file): comments and whitespace are left out, so that only a change of the
+    code marks counter figures stored for those kernels as stale."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_85_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(os.listdir(csrc) if names is None else names):
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)

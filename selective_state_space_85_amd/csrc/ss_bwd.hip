@@ -278,6 +278,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
 
         // the sub-block's states, rebuilt from its checkpoint
         float hh[kSub][kNS];
+        // Euler: the second half's decays e_t, kept for its adjoint, which runs right after
+        // the rebuild (the first half's would not fit beside the states: 29 values spill)
+        float ee[kHalf][kNS];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const Words16 bw = ln.words_B(j, half);
@@ -289,6 +292,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
 #pragma unroll
                 for (int i = 0; i < kNS; ++i) {
                     const float x2 = rv.x * A2[i], e = exp2_hw(x2);
+                    if (!ZOH && half == 1) ee[rr][i] = e;
                     float in_term = rv.y * word(bw, rr, i);
                     if constexpr (ZOH) {
                         ph[i] = zoh_phi(x2, e, iA[i] * rv.w);
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((MODE 
                         g[i] = fmaf(rv.z, word(cw, rr, i), g[i]);
                         const float hp = r ? hh[r - 1][i] : hprev[i];
                         // g e is both a factor of g h_{t-1} e and the next row's g
-                        const float x2 = rv.x * A2[i], e = exp2_hw(x2);
+                        const float x2 = rv.x * A2[i], e = (!ZOH && half == 1) ? ee[rr][i] : exp2_hw(x2);
                         const float ge = g[i] * e;
                         const float t1 = ge * hp;
                         dA_acc[i] = fmaf(t1, rv.x, dA_acc[i]);
@@ -440,8 +444,24 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a)
     const int64_t BLN = a.batch * a.seqlen * N;
     if (blockIdx.y == 0) {
         if (k >= BLN) return;
+        // in block order; eight blocks' loads in flight at a time
+        constexpr int U = 8;
         float sb = 0.0f, sc = 0.0f;
-        for (int64_t q = 0; q < a.nblk; ++q) {
+        int64_t q = 0;
+        for (; q + U <= a.nblk; q += U) {
+            float vb[U], vc[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                vb[j] = a.part_dB[(q + j) * BLN + k];
+                vc[j] = a.part_dC[(q + j) * BLN + k];
+            }
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                sb += vb[j];
+                sc += vc[j];
+            }
+        }
+        for (; q < a.nblk; ++q) {
             sb += a.part_dB[q * BLN + k];
             sc += a.part_dC[q * BLN + k];
         }
