@@ -139,7 +139,11 @@ ss_status ss_scan_plan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
  *                          an fp32 copy of B and C, per (batch row, chunk),
  *                          regrouped in the order the scan kernels read it
  *                          and zero-padded past each chunk's end; its
- *                          arrangement is internal to the library.
+ *                          arrangement is internal to the library.  (The
+ *                          aggregate-pass plans without checkpoints read B
+ *                          and C directly and leave this region untouched;
+ *                          it stays in the size so that the size depends on
+ *                          the shape alone.)
  */
 size_t ss_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 

@@ -112,17 +112,25 @@ bool plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t request, int64_t* 
 // B and C are scalar operands), except for the emit-first scheme (emit_first):
 // there the half-wave one was faster on every shape measured, 1.5-6% (the long
 // context 1.013 against 1.044 ms at T = 4096; B=4 L=16384 D=2048 0.540 against
-// 0.572 ms at T = 2048).  SS_SCAN_LAYOUT forces one at build time (1
-// whole-wave, 2 half-wave) for measurements.
+// 0.572 ms at T = 2048), and for the short-chunk scheme without checkpoints
+// (raw_ok), where the half-wave passes read B and C from their arrays and the
+// panel pass goes: B=2 L=2048 D=1536 47.6 -> 45.8 us, B=1 L=2048 D=1024 28.7 ->
+// 25.8 us, B=4 L=1024 D=2048 59.9 -> 57.5 us, B=3 L=2048 D=4096 145 -> 144 us
+// (B=2 L=4096 D=1536 without skip or gate 78.0 against 79.2 us).
+// SS_SCAN_LAYOUT forces a layout at build time (1 whole-wave, 2 half-wave) and
+// SS_RAW_BC=0 keeps the panel pass, for measurements.
 #ifndef SS_SCAN_LAYOUT
 #define SS_SCAN_LAYOUT 0
 #endif
+#ifndef SS_RAW_BC
+#define SS_RAW_BC 1
+#endif
 constexpr int64_t kCUs = 256;
-bool half_layout(int64_t batch, int64_t dim, int64_t K, bool emit_first)
+bool half_layout(int64_t batch, int64_t dim, int64_t K, bool emit_first, bool raw_ok)
 {
     if (SS_SCAN_LAYOUT == 1) return false;
     if (SS_SCAN_LAYOUT == 2) return true;
-    if (emit_first) return true;
+    if (emit_first || (raw_ok && SS_RAW_BC)) return true;
     const int64_t whole = batch * ceil_div(dim, kWave) * K;
     const int64_t halves = batch * ceil_div(dim, kWave / 2) * K;
     return ceil_div(halves, kCUs) < 2 * ceil_div(whole, kCUs);
@@ -460,7 +468,10 @@ ss_status scan_fwd_impl(const void* u, const void* delta, const float* A, const 
     a.chunk_len = T;
     a.n_chunks = K;
     a.corr_head_tiles = ckpt ? 0 : corr_head_tiles(T, K);
-    a.half = half_layout(batch, dim, K, a.corr_head_tiles > 0);
+    // the short-chunk scheme without checkpoints reads B and C unpanelled
+    const bool raw_ok = K > 1 && a.corr_head_tiles == 0 && !ckpt;
+    a.half = half_layout(batch, dim, K, a.corr_head_tiles > 0, raw_ok);
+    a.raw_bc = (SS_RAW_BC && a.half && raw_ok) ? 1 : 0;
     const hipError_t err = ssk::launch_scan(a, dtype == SS_F32 ? 0 : 1, stream);
     if (err != hipSuccess) return hip_fail(err);
     return SS_OK;

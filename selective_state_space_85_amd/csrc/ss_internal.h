@@ -79,6 +79,9 @@ struct ScanArgs {
     // the half-wave layout (32 channels per 4-wave workgroup) instead of the
     // whole-wave one (64 channels per 8-wave workgroup)
     bool half;
+    // half-wave layout, chunks shorter than the emit-first threshold, no checkpoints:
+    // the aggregate and emit passes read B and C from their arrays (no panel pass)
+    int raw_bc;
     // > 0 (with K > 1 and no checkpoints): emit first, then correct.  Pass 1
     // runs every chunk from its own start and writes y; the carry pass follows;
     // pass 2 reruns chunks 1..K-1 from their carries until the carry's effect

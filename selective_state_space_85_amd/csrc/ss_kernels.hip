@@ -141,7 +141,11 @@ __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
 //    row_newbcast, folded into the multiply or the fma).  Twice as many
 //    workgroups of half the size: the large layer's 640 whole-wave blocks on
 //    256 CUs leave half of the CUs with three and half with two, its 1280
-//    half-wave blocks give every CU five.
+//    half-wave blocks give every CU five.  RAW (the aggregate and emit passes
+//    of the short-chunk scheme, without checkpoints) loads that register from
+//    the (B, L, N) arrays themselves, widening bf16 with a shift, so the call
+//    needs no panel pass: one launch fewer, where the launches are a large
+//    part of a short call, for one or two more vector instructions per tile.
 //    grid = (ceil(dim/32), batch, chunks), block = 256.
 // In both, each (row, channel) of a tile is widened and published by one lane
 // and finished by the same lane.
@@ -177,11 +181,12 @@ constexpr int scan_waves_per_eu()
 }
 
 template <int DT, bool EMIT, bool HAS_D, bool HAS_Z, int MODE, bool CKPT = false, bool HALF = false,
-          int CORR = 0>
+          int CORR = 0, bool RAW = false>
 __global__ __launch_bounds__(scan_threads<HALF>())
     __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<MODE, CORR, HALF>()))) void scan_kernel(ScanArgs a)
 {
     static_assert(CORR == 0 || (EMIT && !CKPT), "the emit-first passes are emit passes without checkpoints");
+    static_assert(!RAW || (HALF && CORR == 0 && !CKPT), "B and C unpanelled: the half-wave aggregate scheme only");
     constexpr bool ZOH = (MODE & kOptZoh) != 0;
     using T = typename Elem<DT>::T;
     using V = Buf<DT>;
@@ -258,6 +263,15 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     const __amdgpu_buffer_rsrc_t r_pan =
         make_rsrc(a.ws_panel + (b * a.n_chunks + c) * kGroups * 2 * plane, uint32_t(kGroups * 2 * plane * 4));
     const uint32_t voff_pan = uint32_t((g * 2 * plane + (lane & 15)) * 4);
+    // RAW: no panel; the same values read from the (B, L, N) arrays themselves.  Lane
+    // 16q + k reads row k/2, entry k%2 of its group; the tile goes into the vector
+    // offset too, so rows past the chunk end read 0 (the range covers the chunk's rows)
+    const uint32_t raw_span = RAW ? uint32_t(len * N) * V::kBytes : 0u;
+    const __amdgpu_buffer_rsrc_t r_Braw =
+        make_rsrc(RAW ? static_cast<const T*>(a.B) + (b * L + t0) * N : nullptr, raw_span);
+    const __amdgpu_buffer_rsrc_t r_Craw =
+        make_rsrc((RAW && EMIT) ? static_cast<const T*>(a.C) + (b * L + t0) * N : nullptr, raw_span);
+    const uint32_t voff_raw = uint32_t((((lane & 15) >> 1) * N + g * kNS + (lane & 1)) * V::kBytes);
 
     const int64_t sbase = bd * N + g * kNS;  // this lane's entries in a (B, D, N) state array
     float A2[kNS], iA[kNS];  // A * log2 e, and 1/A for the zero-order hold
@@ -397,7 +411,11 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     auto issue_words = [&](int tile, auto slot) {
         constexpr int S = decltype(slot)::value;
         const uint32_t off = uint32_t(tile) * uint32_t(TT * kNS * 4);
-        if constexpr (HALF) {
+        if constexpr (RAW) {
+            const uint32_t vo = voff_raw + __builtin_amdgcn_readfirstlane(uint32_t(tile) * uint32_t(TT * N * V::kBytes));
+            bv[S] = V::widen(V::load(r_Braw, vo, 0));
+            if (EMIT) cv[S] = V::widen(V::load(r_Craw, vo, 0));
+        } else if constexpr (HALF) {
             bv[S] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_pan, voff_pan, off, 0));
             if (EMIT)
                 cv[S] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_pan, voff_pan + uint32_t(plane * 4),
@@ -953,6 +971,17 @@ hipError_t launch_scan_layout(const ScanArgs& a, hipStream_t s)
     const dim3 block(ScanShape<HALF>::kWaves * kWave);
     const unsigned nblk = unsigned((a.dim + CH - 1) / CH);
     const int64_t words = a.batch * a.n_chunks * 2 * a.panel_rows * N;
+    if constexpr (HALF) {
+        if (a.raw_bc) {
+            // the short-chunk scheme's passes read B and C as they are: no panel pass
+            scan_kernel<DT, false, false, false, MODE, false, true, 0, true>
+                <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks - 1)), block, 0, s>>>(a);
+            if (!a.fuse_carry) launch_carry_for(a, s);
+            scan_kernel<DT, true, HAS_D, HAS_Z, MODE, false, true, 0, true>
+                <<<dim3(nblk, unsigned(a.batch), unsigned(a.n_chunks)), block, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
     panel_kernel<DT><<<dim3(unsigned((words + 255) / 256)), dim3(256), 0, s>>>(a);
     if (a.n_chunks > 1 && a.corr_head_tiles > 0 && !a.ckpt) {
         // emit first: every chunk from its own start (h0 or zero), writing y and its
