@@ -331,8 +331,9 @@ def main():
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
 
-        def timed(fn, reps=10):
-            fn()
+        def timed(fn, reps=10, warm=1):
+            for _ in range(warm):
+                fn()
             torch.cuda.synchronize()
             e0.record(stream)
             for _ in range(reps):
@@ -474,7 +475,8 @@ def main():
                 def cstep_():
                     ss.scan_fwd(cu_, cd_, cA_, cB_, cC_, D=cD_, z=cz_, out=cy_, workspace=cws)
 
-                cms = timed(cstep_)
+                # calls of tens of microseconds: enough of them to average over the clock's moves
+                cms = timed(cstep_, reps=200 if name == "small" else 20, warm=20 if name == "small" else 2)
                 cel = cw_.batch * cw_.seqlen * cw_.dim * cw_.dstate
                 cby = wl.algorithmic_bytes_scan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate, cw_.dtype, cw_.has_D,
                                                 cw_.has_z)
