@@ -835,7 +835,9 @@ typedef float F32x4 __attribute__((ext_vector_type(4)));
 // state entries: S/4 16-byte loads and stores of h and of A, and (VEC, when
 // the host has checked B and C for 16-byte alignment) B and C as 16-byte
 // loads too; the partial C.h of the Q lanes summed with log2(Q) butterfly
-// exchanges.  grid = ceil(batch*dim*Q / 256), block = 256.
+// exchanges.  grid = (ceil(ceil(dim/CPL)*Q / 256), batch rows of the launch),
+// block = 256: a lane's channels are found with shifts, never a 64-bit
+// division.
 // The state is loaded and stored nontemporally.  In a model a layer's state
 // comes back after every other layer has run, out of every cache; timed that
 // way (the 256 MB last-level cache flushed before each token) at B=256 D=5120
@@ -893,25 +895,25 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     const T* __restrict__ z = static_cast<const T*>(a.z);
     T* __restrict__ y = static_cast<T*>(a.y);
 
-    // CPL channels per lane, a grid's width apart: every load of all of them is
-    // issued before the first is used, so more of the state is in flight
-    const int64_t total = a.batch * a.dim * Q;
-    const int64_t width = (a.batch * a.dim + CPL - 1) / CPL * Q;  // a multiple of Q
-    const int64_t gid0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    // one batch row per grid row (b0 + blockIdx.y); CPL channels per lane, ceil(dim/CPL)
+    // apart, so every load of all of them is issued before the first is used and more
+    // of the state is in flight.  No 64-bit division: the channel comes from a shift.
+    const int64_t b = a.b0 + blockIdx.y;
+    const int64_t span = (a.dim + CPL - 1) / CPL;  // channels between a lane's channels
+    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    // the lane's state entries (q) and first channel
+    const int q = int(gid & (Q - 1));
+    const int64_t d0 = gid / Q;
     bool active[CPL];
-    int64_t bd[CPL], b[CPL], d[CPL];
-    // the lane's state entries: the same for every j, as width is a multiple of Q
-    const int q = int(gid0 % Q);
+    int64_t bd[CPL], d[CPL];
     float hs[CPL][S], as[CPL][S], bs[CPL][S], cs[CPL][S], dl[CPL], x[CPL], zv[CPL], dsk[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int64_t gid = gid0 + j * width;
-        active[j] = gid0 < width && gid < total;
+        const int64_t dj = d0 + j * span;
+        active[j] = d0 < span && dj < a.dim;
         // a channel's lanes are idle together; idle lanes read the last channel's entries q
-        const int64_t g = active[j] ? gid : total - Q + q;
-        bd[j] = g / Q;
-        b[j] = bd[j] / a.dim;
-        d[j] = bd[j] - b[j] * a.dim;
+        d[j] = active[j] ? dj : a.dim - 1;
+        bd[j] = b * a.dim + d[j];
 #pragma unroll
         for (int k = 0; k < S / 4; ++k) {
             const F32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const F32x4*>(a.h + bd[j] * N + q * S) + k);
@@ -925,8 +927,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
             as[j][4 * k + 2] = av.z;
             as[j][4 * k + 3] = av.w;
         }
-        load_row<DT, S, VEC>(Bm + b[j] * N + q * S, bs[j]);
-        load_row<DT, S, VEC>(Cm + b[j] * N + q * S, cs[j]);
+        load_row<DT, S, VEC>(Bm + b * N + q * S, bs[j]);
+        load_row<DT, S, VEC>(Cm + b * N + q * S, cs[j]);
         dl[j] = step_size<MODE>(E::load(delta, bd[j]), a.delta_bias ? a.delta_bias[d[j]] : 0.0f);
         x[j] = E::load(u, bd[j]);
         zv[j] = HAS_Z ? E::load(z, bd[j]) : 0.0f;
@@ -1025,12 +1027,18 @@ template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 hipError_t launch_step_t(const StepArgs& a, hipStream_t s)
 {
     constexpr int Q = SS_STEP_LANES, CPL = SS_STEP_CPL;
-    const int64_t width = (a.batch * a.dim + CPL - 1) / CPL * Q;
+    const int64_t width = (a.dim + CPL - 1) / CPL * Q;  // lanes per batch row
     const unsigned blocks = unsigned((width + 255) / 256);
-    if (a.vec_bc)
-        step_kernel<DT, HAS_D, HAS_Z, MODE, Q, true, CPL><<<dim3(blocks), dim3(256), 0, s>>>(a);
-    else
-        step_kernel<DT, HAS_D, HAS_Z, MODE, Q, false, CPL><<<dim3(blocks), dim3(256), 0, s>>>(a);
+    constexpr int64_t kMaxRows = 65535;  // grid rows per launch
+    for (int64_t b0 = 0; b0 < a.batch; b0 += kMaxRows) {
+        StepArgs p = a;
+        p.b0 = b0;
+        const dim3 grid(blocks, unsigned(a.batch - b0 < kMaxRows ? a.batch - b0 : kMaxRows));
+        if (a.vec_bc)
+            step_kernel<DT, HAS_D, HAS_Z, MODE, Q, true, CPL><<<grid, dim3(256), 0, s>>>(p);
+        else
+            step_kernel<DT, HAS_D, HAS_Z, MODE, Q, false, CPL><<<grid, dim3(256), 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 
