@@ -104,7 +104,7 @@ struct StepArgs {
     uint32_t options;         // kOpt* bits
     void* y;
     int64_t batch, dim;
-    int64_t b0;   // the first batch row of this launch (grid row r is batch row b0 + r)
+    int64_t b0, rows;  // the batch rows [b0, b0 + rows) this launch covers
     bool vec_bc;  // B and C are 16-byte aligned: their rows are read 16 bytes at a time
 };
 

@@ -835,8 +835,9 @@ typedef float F32x4 __attribute__((ext_vector_type(4)));
 // state entries: S/4 16-byte loads and stores of h and of A, and (VEC, when
 // the host has checked B and C for 16-byte alignment) B and C as 16-byte
 // loads too; the partial C.h of the Q lanes summed with log2(Q) butterfly
-// exchanges.  grid = (ceil(ceil(dim/CPL)*Q / 256), batch rows of the launch),
-// block = 256: a lane's channels are found with shifts, never a 64-bit
+// exchanges.  grid = (ceil(dim*Q / 256), ceil(batch rows of the launch / CPL)),
+// block = 256: each lane steps CPL batch rows of one channel, so A is read
+// once for them, and its channel is found with a shift, never a 64-bit
 // division.
 // The state is loaded and stored nontemporally.  In a model a layer's state
 // comes back after every other layer has run, out of every cache; timed that
@@ -895,44 +896,49 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     const T* __restrict__ z = static_cast<const T*>(a.z);
     T* __restrict__ y = static_cast<T*>(a.y);
 
-    // one batch row per grid row (b0 + blockIdx.y); CPL channels per lane, ceil(dim/CPL)
-    // apart, so every load of all of them is issued before the first is used and more
-    // of the state is in flight.  No 64-bit division: the channel comes from a shift.
-    const int64_t b = a.b0 + blockIdx.y;
-    const int64_t span = (a.dim + CPL - 1) / CPL;  // channels between a lane's channels
+    // One channel per lane (Q lanes per channel), CPL batch rows ceil(rows/CPL) apart
+    // (grid row r: rows b0 + r + j * ceil(rows/CPL)): A is read once for all of them,
+    // every load is issued before the first is used, and the channel comes from a
+    // shift, never a 64-bit division.
+    const int64_t rows = (a.rows + CPL - 1) / CPL;  // grid rows between a lane's rows
     const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    // the lane's state entries (q) and first channel
+    // the lane's state entries (q) and channel; a channel's lanes are idle together, and
+    // idle lanes read the last channel's entries q
     const int q = int(gid & (Q - 1));
-    const int64_t d0 = gid / Q;
+    const bool in_dim = gid / Q < a.dim;
+    const int64_t d = in_dim ? gid / Q : a.dim - 1;
     bool active[CPL];
-    int64_t bd[CPL], d[CPL];
-    float hs[CPL][S], as[CPL][S], bs[CPL][S], cs[CPL][S], dl[CPL], x[CPL], zv[CPL], dsk[CPL];
+    int64_t bd[CPL], b[CPL];
+    float hs[CPL][S], as[S], bs[CPL][S], cs[CPL][S], dl[CPL], x[CPL], zv[CPL];
+#pragma unroll
+    for (int k = 0; k < S / 4; ++k) {
+        const float4 av = reinterpret_cast<const float4*>(a.A + d * N + q * S)[k];
+        as[4 * k] = av.x;
+        as[4 * k + 1] = av.y;
+        as[4 * k + 2] = av.z;
+        as[4 * k + 3] = av.w;
+    }
+    const float bias = a.delta_bias ? a.delta_bias[d] : 0.0f;
+    const float dsk = HAS_D ? a.Dskip[d] : 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int64_t dj = d0 + j * span;
-        active[j] = d0 < span && dj < a.dim;
-        // a channel's lanes are idle together; idle lanes read the last channel's entries q
-        d[j] = active[j] ? dj : a.dim - 1;
-        bd[j] = b * a.dim + d[j];
+        const int64_t rj = int64_t(blockIdx.y) + j * rows;
+        active[j] = in_dim && rj < a.rows;
+        b[j] = a.b0 + (rj < a.rows ? rj : a.rows - 1);
+        bd[j] = b[j] * a.dim + d;
 #pragma unroll
         for (int k = 0; k < S / 4; ++k) {
             const F32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const F32x4*>(a.h + bd[j] * N + q * S) + k);
-            const float4 av = reinterpret_cast<const float4*>(a.A + d[j] * N + q * S)[k];
             hs[j][4 * k] = hv.x;
             hs[j][4 * k + 1] = hv.y;
             hs[j][4 * k + 2] = hv.z;
             hs[j][4 * k + 3] = hv.w;
-            as[j][4 * k] = av.x;
-            as[j][4 * k + 1] = av.y;
-            as[j][4 * k + 2] = av.z;
-            as[j][4 * k + 3] = av.w;
         }
-        load_row<DT, S, VEC>(Bm + b * N + q * S, bs[j]);
-        load_row<DT, S, VEC>(Cm + b * N + q * S, cs[j]);
-        dl[j] = step_size<MODE>(E::load(delta, bd[j]), a.delta_bias ? a.delta_bias[d[j]] : 0.0f);
+        load_row<DT, S, VEC>(Bm + b[j] * N + q * S, bs[j]);
+        load_row<DT, S, VEC>(Cm + b[j] * N + q * S, cs[j]);
+        dl[j] = step_size<MODE>(E::load(delta, bd[j]), bias);
         x[j] = E::load(u, bd[j]);
         zv[j] = HAS_Z ? E::load(z, bd[j]) : 0.0f;
-        dsk[j] = HAS_D ? a.Dskip[d[j]] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -941,10 +947,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const float x2 = dl[j] * (as[j][i] * kLog2e);
+            const float x2 = dl[j] * (as[i] * kLog2e);
             const float abar = exp2_hw(x2);
             float in_term = xb * bs[j][i];
-            if constexpr ((MODE & kOptZoh) != 0) in_term *= zoh_phi(x2, abar, (1.0f / as[j][i]) * inv_dl);
+            if constexpr ((MODE & kOptZoh) != 0) in_term *= zoh_phi(x2, abar, (1.0f / as[i]) * inv_dl);
             hs[j][i] = fmaf(abar, hs[j][i], in_term);
             part = fmaf(cs[j][i], hs[j][i], part);
         }
@@ -958,7 +964,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
                 __builtin_nontemporal_store(hv, reinterpret_cast<F32x4*>(a.h + bd[j] * N + q * S) + k);
             }
             if (q == 0) {
-                if (HAS_D) acc = fmaf(dsk[j], x[j], acc);
+                if (HAS_D) acc = fmaf(dsk, x[j], acc);
                 if (HAS_Z) acc *= silu(zv[j]);
                 E::store(y, bd[j], acc);
             }
@@ -1027,13 +1033,14 @@ template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 hipError_t launch_step_t(const StepArgs& a, hipStream_t s)
 {
     constexpr int Q = SS_STEP_LANES, CPL = SS_STEP_CPL;
-    const int64_t width = (a.dim + CPL - 1) / CPL * Q;  // lanes per batch row
-    const unsigned blocks = unsigned((width + 255) / 256);
-    constexpr int64_t kMaxRows = 65535;  // grid rows per launch
+    const unsigned blocks = unsigned((a.dim * Q + 255) / 256);
+    // batch rows per launch: a grid row covers CPL of them
+    constexpr int64_t kMaxRows = 65535 * int64_t(CPL);
     for (int64_t b0 = 0; b0 < a.batch; b0 += kMaxRows) {
         StepArgs p = a;
         p.b0 = b0;
-        const dim3 grid(blocks, unsigned(a.batch - b0 < kMaxRows ? a.batch - b0 : kMaxRows));
+        p.rows = a.batch - b0 < kMaxRows ? a.batch - b0 : kMaxRows;
+        const dim3 grid(blocks, unsigned((p.rows + CPL - 1) / CPL));
         if (a.vec_bc)
             step_kernel<DT, HAS_D, HAS_Z, MODE, Q, true, CPL><<<grid, dim3(256), 0, s>>>(p);
         else
