@@ -97,32 +97,41 @@ namespace {
 // Panel kernel: the fp32 B/C panel of every (batch row, chunk),
 //   panel[b][c][w][part][p][i] = (part ? C : B)[b, c*chunk_len + p, w*kNS + i]
 // for rows p inside the chunk and 0 for the rest of the chunk's panel_rows.
-// One thread per panel word; grid = ceil(words / 256), block = 256.
-// ---------------------------------------------------------------------------
+// One thread per panel word; grid = (ceil(panel_rows * kNS / 256), kGroups * 2,
+// the launch's (batch row, chunk) pairs from bc0 on), block = 256.  The word's
+// place comes from the grid and a shift: the first version split one flat
+// index with 64-bit divisions, which took most of its time.
 template <int DT>
-__global__ __launch_bounds__(256) void panel_kernel(ScanArgs a)
+__global__ __launch_bounds__(256) void panel_kernel(ScanArgs a, int64_t bc0)
 {
     using E = Elem<DT>;
     using T = typename E::T;
     const int64_t P = a.panel_rows;
-    const int64_t total = a.batch * a.n_chunks * kGroups * 2 * P * kNS;
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= total) return;
-    const int i = int(idx % kNS);
-    int64_t rest = idx / kNS;
-    const int64_t p = rest % P;
-    rest /= P;
-    const int part = int(rest % 2);
-    rest /= 2;
-    const int g = int(rest % kGroups);
-    rest /= kGroups;
-    const int64_t c = rest % a.n_chunks;
-    const int64_t b = rest / a.n_chunks;
+    const int64_t k = int64_t(blockIdx.x) * 256 + threadIdx.x;  // word within the plane: row k/kNS
+    if (k >= P * kNS) return;
+    const int64_t bc = bc0 + blockIdx.z;  // b * n_chunks + c
+    const int64_t b = bc / a.n_chunks;     // uniform: a scalar division per wave
+    const int64_t c = bc - b * a.n_chunks;
+    const int g = int(blockIdx.y >> 1), part = int(blockIdx.y & 1);
+    const int64_t p = k / kNS;
+    const int i = int(k % kNS);
     const int64_t t0 = c * a.chunk_len;
     const int64_t len = (a.seqlen - t0 < a.chunk_len) ? a.seqlen - t0 : a.chunk_len;
     float v = 0.0f;
     if (p < len) v = E::load(static_cast<const T*>(part ? a.C : a.B), (b * a.seqlen + t0 + p) * N + g * kNS + i);
-    a.ws_panel[idx] = v;
+    a.ws_panel[((bc * kGroups + g) * 2 + part) * P * kNS + k] = v;
+}
+
+template <int DT>
+void launch_panel_t(const ScanArgs& a, hipStream_t s)
+{
+    const int64_t bcs = a.batch * a.n_chunks;
+    const unsigned gx = unsigned((a.panel_rows * kNS + 255) / 256);
+    constexpr int64_t kMaxZ = 65535;
+    for (int64_t bc0 = 0; bc0 < bcs; bc0 += kMaxZ) {
+        const dim3 grid(gx, unsigned(kGroups * 2), unsigned(bcs - bc0 < kMaxZ ? bcs - bc0 : kMaxZ));
+        panel_kernel<DT><<<grid, dim3(256), 0, s>>>(a, bc0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -978,7 +987,6 @@ hipError_t launch_scan_layout(const ScanArgs& a, hipStream_t s)
     constexpr int CH = ScanShape<HALF>::kCh;
     const dim3 block(ScanShape<HALF>::kWaves * kWave);
     const unsigned nblk = unsigned((a.dim + CH - 1) / CH);
-    const int64_t words = a.batch * a.n_chunks * 2 * a.panel_rows * N;
     if constexpr (HALF) {
         if (a.raw_bc) {
             // the short-chunk scheme's passes read B and C as they are: no panel pass
@@ -990,7 +998,7 @@ hipError_t launch_scan_layout(const ScanArgs& a, hipStream_t s)
             return hipGetLastError();
         }
     }
-    panel_kernel<DT><<<dim3(unsigned((words + 255) / 256)), dim3(256), 0, s>>>(a);
+    launch_panel_t<DT>(a, s);
     if (a.n_chunks > 1 && a.corr_head_tiles > 0 && !a.ckpt) {
         // emit first: every chunk from its own start (h0 or zero), writing y and its
         // end state; the carries; then chunks 1..K-1 corrected from their carries
@@ -1102,12 +1110,10 @@ hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t stream)
 hipError_t launch_panel(const ScanArgs& a, int dtype, hipStream_t stream)
 {
     (void)hipGetLastError();
-    const int64_t words = a.batch * a.n_chunks * 2 * a.panel_rows * N;
-    const dim3 grid(unsigned((words + 255) / 256));
     if (dtype == 0)
-        panel_kernel<0><<<grid, dim3(256), 0, stream>>>(a);
+        launch_panel_t<0>(a, stream);
     else
-        panel_kernel<1><<<grid, dim3(256), 0, stream>>>(a);
+        launch_panel_t<1>(a, stream);
     return hipGetLastError();
 }
 
