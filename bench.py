@@ -10,7 +10,8 @@ steps, 500 timed) measure the part at its settled clock: over the first ~60
 back-to-back steps the clock dips (per-step time ~0.31 -> 0.40 ms) and climbs
 back (~0.28-0.30 ms from about step 70 on), so a short region right after a
 short warmup mostly times the dip.  The warmup's own average is reported as
-``warmup_ms_per_step``.  Prints ONE JSON line:
+``warmup_ms_per_step``; every later section also runs its workload back to back
+for 60 ms before timing it.  Prints ONE JSON line:
 elements/s (B*L*D*N per second), the roofline of the scan kernel (algorithmic
 HBM bytes per launch over its event-timed duration, against 8 TB/s), and the
 fp64 CPU oracle timed on a bounded sample of the same workload.
@@ -62,7 +63,10 @@ METRIC = "selective-scan elements/s (B·L·D·N) + achieved HBM GB/s vs peak, 1 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_large_layer.txt")
 
 
-# the sections run after the timed region, each timing one more workload or option
+# the sections run after the timed region, each timing one more workload or option, each
+# after running it back to back for SETTLE_MS (the clock moves for some tens of ms after
+# the load changes: a ~50 us call takes ~48 us for its first 200 calls, 45.5 after ~600)
+SETTLE_MS = 60.0
 EXTRA_SECTIONS = ("flushed", "options", "backward", "configs", "conv1d", "ssd", "decode")
 
 
@@ -331,10 +335,19 @@ def main():
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
 
-        def timed(fn, reps=10, warm=1):
-            for _ in range(warm):
-                fn()
+        def settle(fn, ms=SETTLE_MS):
+            # run the workload back to back for a while first: like the timed region's
+            # warmup, this times it at the settled clock, not during the ramp after a change
+            fn()
             torch.cuda.synchronize()
+            c0 = time.perf_counter()
+            while (time.perf_counter() - c0) * 1e3 < ms:
+                for _ in range(4):
+                    fn()
+                torch.cuda.synchronize()
+
+        def timed(fn, reps=10):
+            settle(fn)
             e0.record(stream)
             for _ in range(reps):
                 fn()
@@ -373,9 +386,7 @@ def main():
                     ss.scan_fwd(t["u"], dl_raw if sp else t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                                 out=y, workspace=ws, delta_bias=bias if sp else None, **kw)
 
-                for _ in range(3):
-                    ostep()
-                torch.cuda.synchronize()
+                settle(ostep)
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -398,9 +409,7 @@ def main():
             def bstep():
                 ss.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy_t, D=t["D"], z=t["z"], workspace=bws)
 
-            for _ in range(2):
-                bstep()
-            torch.cuda.synchronize()
+            settle(bstep)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -476,7 +485,7 @@ def main():
                     ss.scan_fwd(cu_, cd_, cA_, cB_, cC_, D=cD_, z=cz_, out=cy_, workspace=cws)
 
                 # calls of tens of microseconds: enough of them to average over the clock's moves
-                cms = timed(cstep_, reps=200 if name == "small" else 20, warm=20 if name == "small" else 2)
+                cms = timed(cstep_, reps=400 if name == "small" else 20)
                 cel = cw_.batch * cw_.seqlen * cw_.dim * cw_.dstate
                 cby = wl.algorithmic_bytes_scan(cw_.batch, cw_.seqlen, cw_.dim, cw_.dstate, cw_.dtype, cw_.has_D,
                                                 cw_.has_z)
@@ -499,9 +508,7 @@ def main():
             def cstep():
                 ss.conv1d_silu(xz[..., :w.dim], cw, cb, out=cu)
 
-            for _ in range(3):
-                cstep()
-            torch.cuda.synchronize()
+            settle(cstep)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -526,9 +533,7 @@ def main():
             def sstep():
                 ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy)
 
-            for _ in range(3):
-                sstep()
-            torch.cuda.synchronize()
+            settle(sstep)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -558,9 +563,7 @@ def main():
             def sstep256():
                 ss.ssd_fwd(stt["x"], stt["dt"], stt["A"], stt["B"], stt["C"], D=stt["D"], out=sy, workspace=sws)
 
-            for _ in range(3):
-                sstep256()
-            torch.cuda.synchronize()
+            settle(sstep256)
             e0.record(stream)
             for _ in range(20):
                 sstep256()
@@ -582,9 +585,7 @@ def main():
             def dstep():
                 ss.step(h5, st["u"], st["delta"], A5, st["B"], st["C"], D=D5, z=st["z"], out=y5)
 
-            for _ in range(5):
-                dstep()
-            torch.cuda.synchronize()
+            settle(dstep)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
