@@ -99,8 +99,8 @@ namespace {
 // for rows p inside the chunk and 0 for the rest of the chunk's panel_rows.
 // One thread per panel word; grid = (ceil(panel_rows * kNS / 256), kGroups * 2,
 // the launch's (batch row, chunk) pairs from bc0 on), block = 256.  The word's
-// place comes from the grid and a shift: the first version split one flat
-// index with 64-bit divisions, which took most of its time.
+// place comes from the grid and a shift (one flat index split by 64-bit
+// divisions took the long context's panel 14.9 -> 18.2 us).
 template <int DT>
 __global__ __launch_bounds__(256) void panel_kernel(ScanArgs a, int64_t bc0)
 {
