@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import TOL, host64, rel_err, say
+from gpu_util import TOL, dev, host64, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -146,4 +146,46 @@ def test_ssd_at_the_row_slab_limit(nn):
     ey = rel_err(host64(y.index_select(2, sel)), ref["y"])
     eh = rel_err(host64(hl[:, sel]), ref["h_last"])
     say("  y err %.2e, h_last err %.2e" % (ey, eh))
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_step_rows_over_one_launch():
+    """ss_step over more batch rows than one launch's grid covers (65535 grid rows of two
+    batch rows each): 131075 rows of 24 channels, bf16, skip, gate and h0, in two launches.
+    Every output and state against the oracle."""
+    nb, nd = 2 * 65535 + 5, 24
+    m = ss()
+    inp = wl.scan_inputs(nb, 1, nd, NS, wl.BF16, has_D=True, has_z=True, has_h0=True, seed=31)
+    t = {k: dev(v) for k, v in inp.items()}
+    h = t["h0"].clone()
+    say("step over two launches: B=%d D=%d" % (nb, nd))
+    y = m.step(h, t["u"][:, 0].contiguous(), t["delta"][:, 0].contiguous(), t["A"], t["B"][:, 0].contiguous(),
+               t["C"][:, 0].contiguous(), D=t["D"], z=t["z"][:, 0].contiguous())
+    href = inp["h0"].astype(np.float64).copy()
+    yref = oracle.step(href, np.ascontiguousarray(inp["u"][:, 0]), np.ascontiguousarray(inp["delta"][:, 0]),
+                       inp["A"], np.ascontiguousarray(inp["B"][:, 0]), np.ascontiguousarray(inp["C"][:, 0]),
+                       D=inp["D"], z=np.ascontiguousarray(inp["z"][:, 0]), threads=16)
+    ey, eh = rel_err(host64(y), yref), rel_err(host64(h), href)
+    say("  y err %.3e, h err %.3e" % (ey, eh))
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_panel_over_one_launch():
+    """The B/C panel pass over more (batch row, chunk) pairs than one launch's grid covers:
+    33000 batch rows of 40 rows in chunks of 16 (3 chunks, the last ragged), with the
+    checkpointing forward, whose chunked plans keep the panel.  Every output against the
+    oracle."""
+    nb, nl, nd = 33000, 40, 8
+    m = ss()
+    inp = wl.scan_inputs(nb, nl, nd, NS, wl.BF16, has_D=True, has_z=True, has_h0=True, seed=32)
+    t = {k: dev(v) for k, v in inp.items()}
+    T, K = m.scan_plan(nb, nl, nd, NS, chunk_len=16)
+    assert (T, K) == (16, 3) and nb * K > 65535
+    ck = torch.empty(m.scan_ckpt_shape(nb, nl, nd, NS), device="cuda")
+    say("panel over two launches: B=%d L=%d D=%d, %d chunks" % (nb, nl, nd, K))
+    y, hl = m.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], h0=t["h0"],
+                       return_last_state=True, chunk_len=16, ckpt=ck)
+    ref = oracle.scan(**inp, threads=16)
+    ey, eh = rel_err(host64(y), ref["y"]), rel_err(host64(hl), ref["h_last"])
+    say("  y err %.3e, h_last err %.3e" % (ey, eh))
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
