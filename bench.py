@@ -5,11 +5,13 @@
 
 One step = one ss_scan_fwd call over the large-layer workload (B=8, L=2048,
 D=5120, N=16; bf16 u/delta/B/C/z and y, fp32 A/D and state, D skip and silu(z)
-gate), inputs already resident in device memory.  The defaults (200 warmup
-steps, 500 timed) measure the part at its settled clock: over the first ~60
-back-to-back steps the clock dips (per-step time ~0.31 -> 0.40 ms) and climbs
-back (~0.28-0.30 ms from about step 70 on), so a short region right after a
-short warmup mostly times the dip.  The warmup's own average is reported as
+gate), inputs already resident in device memory.  Over the first ~60
+back-to-back steps the part's clock dips (per-step time ~0.31 -> 0.40 ms) and
+climbs back (~0.28-0.30 ms from about step 70 on), so a short region right
+after a short warmup mostly times the dip.  Before the W warmup steps the bench
+therefore runs the same step back to back for ``--settle-ms`` (100 ms, about
+300 steps; 0 turns it off) and reports that phase as ``settle``; the timed
+region is then the sustained rate.  The warmup's own average is reported as
 ``warmup_ms_per_step``; every later section also runs its workload back to back
 for 60 ms before timing it.  Prints ONE JSON line:
 elements/s (B*L*D*N per second), the roofline of the scan kernel (algorithmic
@@ -77,6 +79,9 @@ def parse():
     # ~0.40 ms per step, then a climb back to ~0.29 ms), so the default warmup runs past it
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="run the step back to back for this long before the warmup steps "
+                         "(untimed; 0 = off), so that short runs time the settled clock")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle's timed repetitions (the parity check of the timed output still runs)")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads and flushed timing")
@@ -243,6 +248,19 @@ def main():
         ss.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], out=y, workspace=ws)
 
     log("plan: chunk_len=%d n_chunks=%d, workspace %d bytes; warmup %d" % (T, K, ws_bytes, args.warmup))
+    # settle phase: the step back to back, in groups of 32 between synchronisations, until
+    # --settle-ms have passed (untimed; the clock's dip and recovery happen here)
+    settle_steps = 0
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    while (time.perf_counter() - c0) * 1e3 < args.settle_ms:
+        for _ in range(32):
+            step()
+        settle_steps += 32
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - c0
+    if settle_steps:
+        log("settle: %d steps in %.1f ms" % (settle_steps, settle_s * 1e3))
     # the warmup is timed too (reported beside the timed region, not used for the metric)
     ew0 = torch.cuda.Event(enable_timing=True)
     ew1 = torch.cuda.Event(enable_timing=True)
@@ -285,6 +303,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_ms_per_step": ms_warm,
+        "settle": {"ms": settle_s * 1e3, "steps": settle_steps,
+                   "note": "untimed back-to-back steps before the warmup, past the clock's dip"},
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
