@@ -655,6 +655,22 @@ ss_status scan_bwd_impl(const void* u, const void* delta, const float* A, const 
     pa.n_chunks = 1;
     hipError_t err = ssk::launch_panel(pa, dtype == SS_F32 ? 0 : 1, stream);
     if (err != hipSuccess) return hip_fail(err);
+    if (!ckpt) {
+        // the checkpoints: the half-wave scan kernel's checkpoint-only pass (1280
+        // workgroups for the large layer, five per CU; a pass of its own in the
+        // adjoint's whole-wave shape ran 640 as 2.5 per CU: 329 against ~250 us)
+        ssk::ScanArgs ca = pa;
+        ca.u = u;
+        ca.delta = delta;
+        ca.A = A;
+        ca.h0 = h0;
+        ca.delta_bias = delta_bias;
+        ca.options = options;
+        ca.ckpt = reinterpret_cast<float*>(ws + wl.off_ckpt);
+        ca.half = 1;
+        err = ssk::launch_ckpt_pass(ca, dtype == SS_F32 ? 0 : 1, stream);
+        if (err != hipSuccess) return hip_fail(err);
+    }
 
     ssk::BwdArgs a{};
     a.u = u;
@@ -678,9 +694,8 @@ ss_status scan_bwd_impl(const void* u, const void* delta, const float* A, const 
     a.ddelta_bias = ddelta_bias;
     a.panel = pa.ws_panel;
     a.panel_rows = wl.panel_rows;
-    // the kernels only read caller checkpoints (prep_kernel, the writer, is not launched)
+    // the adjoint only reads the checkpoints (the caller's, or the pass above wrote them)
     a.ckpt = ckpt ? const_cast<float*>(ckpt) : reinterpret_cast<float*>(ws + wl.off_ckpt);
-    a.ckpt_given = ckpt != nullptr;
     a.part_dB = reinterpret_cast<float*>(ws + wl.off_pdB);
     a.part_dC = reinterpret_cast<float*>(ws + wl.off_pdC);
     a.part_dA = reinterpret_cast<float*>(ws + wl.off_pdA);

@@ -20,11 +20,13 @@
 // g B_t u_t dbeta/dA (zoh_dbeta_dA_over_delta).
 //
 // Three launches after the B/C panel:
-//  1. prep_kernel runs the recurrence once and stores the state every kBwdSub
-//     rows (the checkpoints).  It is skipped when the caller passes the
-//     checkpoints of its forward pass (ss_scan_fwd_ckpt writes them), which
-//     reuses the forward's states the way the chunked forward reuses its
-//     chunk carries;
+//  1. the checkpoint pass runs the recurrence once and stores the state every
+//     kBwdSub rows (the checkpoints): the forward scan kernel's checkpoint-only
+//     instantiation (ss_kernels.hip, launch_ckpt_pass), so the checkpoints are
+//     bit for bit those a one-chunk ss_scan_fwd_ckpt writes.  It is skipped
+//     when the caller passes the checkpoints of its forward pass, which reuses
+//     the forward's states the way the chunked forward reuses its chunk
+//     carries;
 //  2. bwd_kernel walks the sub-blocks from the last to the first: it rebuilds
 //     the sub-block's states in registers from its checkpoint, then runs the
 //     adjoint down the sub-block, writing du, ddelta and dz and the
@@ -33,8 +35,9 @@
 //  3. bwd_reduce_kernel adds the per-workgroup and per-batch-row partial sums
 //     in a fixed order (the result does not depend on scheduling) and rounds
 //     dB, dC to the operand type.
-// The workgroup shape is the forward's: 64 channels of one batch row, the 16
-// state entries split over 8 waves (2 per wave), B and C as scalar operands.
+// The adjoint's workgroup shape is the forward's whole-wave one: 64 channels of
+// one batch row, the 16 state entries split over 8 waves (2 per wave), B and C
+// as scalar operands.
 #include "ss_device.h"
 
 namespace ssk {
@@ -119,83 +122,6 @@ struct Rows {
         }
     }
 };
-
-// ---------------------------------------------------------------------------
-// prep_kernel: the recurrence once, from h0, storing the state entering every
-// sub-block (the checkpoints).  grid = (ceil(dim/64), batch), block = 64 *
-// kGroups.  Per sub-block: store the state, publish (delta, delta*u) per row in
-// LDS, advance the state over the sub-block's 16 rows.
-// ---------------------------------------------------------------------------
-template <int DT, int MODE>
-__global__ __launch_bounds__(kThreads) void prep_kernel(BwdArgs a)
-{
-    constexpr bool ZOH = (MODE & kOptZoh) != 0;
-    using V = Buf<DT>;
-    __shared__ float2 s_row[2][kSub][kWave];  // (delta, delta*u), by sub-block parity
-    __shared__ float s_iv[ZOH ? 2 : 1][kSub][kWave];  // 1/delta (zero-order hold)
-
-    const Lane<DT> ln(a);
-    const int lane = ln.lane, w = ln.w;
-    const int64_t D = a.dim, L = a.seqlen, NB = a.batch;
-    const auto r_u = ln.rsrc(a.u, a), r_dl = ln.rsrc(a.delta, a);
-
-    float A2[kNS], iA[kNS], h[kNS];
-#pragma unroll
-    for (int i = 0; i < kNS; ++i) {
-        const float av = a.A[ln.d * N + w * kNS + i];
-        A2[i] = av * kLog2e;
-        iA[i] = ZOH ? 1.0f / av : 0.0f;
-        h[i] = (a.h0 && ln.active) ? a.h0[(ln.b * D + ln.d) * N + w * kNS + i] : 0.0f;
-    }
-    const float bias = a.delta_bias ? a.delta_bias[ln.d] : 0.0f;
-
-    // this wave's two rows of sub-block j (row w of each half), raw
-    typename V::Raw rdl[2], rx[2];
-    auto issue = [&](int j) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int64_t t = int64_t(j) * kSub + row_of(w, k);
-            const uint32_t so = uint32_t(t < L ? t : L - 1) * ln.row_bytes;
-            rdl[k] = V::load(r_dl, ln.voff, so);
-            rx[k] = V::load(r_u, ln.voff, so);
-        }
-    };
-    issue(0);
-    for (int j = 0; j < int(a.n_sub); ++j) {
-        const int par = j & 1;
-        if (ln.active) {
-#pragma unroll
-            for (int i = 0; i < kNS; ++i) a.ckpt[((int64_t(j) * NB + ln.b) * N + w * kNS + i) * D + ln.d] = h[i];
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int r = row_of(w, k);
-            const bool in = ln.active && int64_t(j) * kSub + r < L;
-            const float dl = in ? step_size<MODE>(V::widen(rdl[k]), bias) : 0.0f;
-            s_row[par][r][lane] = make_float2(dl, dl * V::widen(rx[k]));
-            if constexpr (ZOH) s_iv[par][r][lane] = __builtin_amdgcn_rcpf(dl);
-        }
-        if (j + 1 < int(a.n_sub)) issue(j + 1);
-        // one barrier per sub-block: the next one writes the other parity
-        __syncthreads();
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const Words16 bw = ln.words_B(j, half);
-#pragma unroll
-            for (int rr = 0; rr < kHalf; ++rr) {
-                const float2 rv = s_row[par][half * kHalf + rr][lane];
-                const float iv = ZOH ? s_iv[ZOH ? par : 0][half * kHalf + rr][lane] : 0.0f;
-#pragma unroll
-                for (int i = 0; i < kNS; ++i) {
-                    const float x2 = rv.x * A2[i], e = exp2_hw(x2);
-                    float in_term = rv.y * word(bw, rr, i);
-                    if constexpr (ZOH) in_term *= zoh_phi(x2, e, iA[i] * iv);
-                    h[i] = fmaf(e, h[i], in_term);
-                }
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // bwd_kernel: the adjoint, sub-block by sub-block from the last.  grid =
@@ -489,7 +415,6 @@ template <int DT, bool HAS_D, bool HAS_Z, int MODE>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s)
 {
     const dim3 grid(unsigned(a.nblk), unsigned(a.batch));
-    if (!a.ckpt_given) prep_kernel<DT, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
     bwd_kernel<DT, HAS_D, HAS_Z, MODE><<<grid, dim3(kThreads), 0, s>>>(a);
     int64_t most = a.batch * a.seqlen * N;
     if (a.dim * N > most) most = a.dim * N;

@@ -71,8 +71,9 @@ struct ScanArgs {
     float* ws_panel;
     int64_t panel_rows;
     // (ceil(seqlen / kBwdSub), batch, N, dim) fp32: the state entering every
-    // kBwdSub-th row, written by the emit pass when not null (chunk_len is then
-    // a multiple of kBwdSub or n_chunks is 1)
+    // kBwdSub-th row, written when not null by the emit pass (chunk_len is then
+    // a multiple of kBwdSub or n_chunks is 1) or by the backward's
+    // checkpoint-only pass (launch_ckpt_pass)
     float* ckpt;
     int64_t batch, seqlen, dim;
     int64_t chunk_len, n_chunks;
@@ -144,7 +145,6 @@ struct BwdArgs {
     const float* panel;       // the fp32 B/C panel, one chunk per batch row
     int64_t panel_rows;
     float* ckpt;              // (n_sub, batch, N, dim): state entering row kBwdSub*j
-    bool ckpt_given;          // ckpt holds the forward's checkpoints: no recompute pass
     float* part_dB;           // (nblk, batch, seqlen, N): per-workgroup sums over its channels
     float* part_dC;
     float* part_dA;           // (batch, dim, N): per-batch-row sums over time
@@ -194,6 +194,10 @@ hipError_t launch_step(const StepArgs& a, int dtype, hipStream_t stream);
 // the B/C panel alone (a.B, a.C, a.ws_panel, a.panel_rows, a.batch, a.seqlen,
 // a.chunk_len, a.n_chunks)
 hipError_t launch_panel(const ScanArgs& a, int dtype, hipStream_t stream);
+// the backward's checkpoint pass over one chunk of the whole sequence (a.u, a.delta,
+// a.A, a.h0, a.delta_bias, a.options, a.ws_panel (filled), a.panel_rows, a.ckpt,
+// a.batch, a.seqlen, a.dim, a.chunk_len = seqlen, a.n_chunks = 1)
+hipError_t launch_ckpt_pass(const ScanArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
 // vec: channels per thread, 1, or 4 (bf16) / 2 (fp32) when the host has checked alignment
 hipError_t launch_conv(const ConvArgs& a, int dtype, int vec, hipStream_t stream);

@@ -162,6 +162,10 @@ void launch_panel_t(const ScanArgs& a, hipStream_t s)
 //       h_last.
 // !EMIT (aggregate): start from zero, write the chunk's end state into state
 //       slot c+1 and its delta sum.
+// CKPT: also store the state entering every second tile (every kBwdSub rows)
+//       in a.ckpt.  With !EMIT (the backward's checkpoint pass, one chunk,
+//       half-wave) that is all it writes: it starts from h0 and keeps no end
+//       state or delta sum.
 // Host guarantees: chunk_len * dim * element size < 2^31.
 // ---------------------------------------------------------------------------
 // The zero-order hold's extra arithmetic would take the whole-wave kernel just
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     // (pass 2): from the carry
     const bool first = CORR == 1;
     const bool from_ws = EMIT && a.n_chunks > 1 && !first;
-    const bool from_h0 = EMIT && a.h0 != nullptr && (a.n_chunks == 1 || (first && c == 0));
+    const bool from_h0 = (EMIT || CKPT) && a.h0 != nullptr && (a.n_chunks == 1 || (first && c == 0));
     const bool fused = CORR == 0 && from_ws && a.fuse_carry != 0;
     // fused carry: run() forms h with this once the first tiles' loads are in flight
     auto fuse_carry_init = [&]() {
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
                     h[i] = fmaf(e[r][i], h[i], in_term);
                     hh[r][i] = h[i];
                 });
-                if constexpr (!EMIT) dsum += xd[r].x;
+                if constexpr (!EMIT && !CKPT) dsum += xd[r].x;
             });
             if constexpr (EMIT) {
                 float acc[TT];
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
 #pragma unroll
                     for (int i = 0; i < kNS; ++i) acc = fmaf(word(cw[S], r, i), h[i], acc);
                     s_part[S][g][r][ch] = acc;
-                } else {
+                } else if constexpr (!CKPT) {
                     dsum += xd[r].x;
                 }
             }
@@ -578,7 +582,10 @@ __global__ __launch_bounds__(scan_threads<HALF>())
     constexpr float kCorrTol = 5.9604645e-8f;  // 2^-24
     // checkpoints (a separate instantiation: the plain kernel has no scalar
     // registers to spare): this lane's entries of the one at row t0 + k*TT,
-    // advanced by one checkpoint per tile pair
+    // advanced by one checkpoint per tile pair.  Stored nontemporal: nothing
+    // reads them before the backward, and the large layer's 335 MB would only
+    // push the rows in flight out of the caches (checkpointing forward 0.347 ->
+    // 0.334 ms)
     float* ck_row = nullptr;
     int64_t ck_step = 0;
     if constexpr (CKPT) {
@@ -611,7 +618,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
                 // the state entering row t0 + k*TT, a multiple of kBwdSub (k is even)
                 if (active && k * TT < len) {
 #pragma unroll
-                    for (int i = 0; i < kNS; ++i) ck_row[int64_t(i) * D] = h[i];
+                    for (int i = 0; i < kNS; ++i) __builtin_nontemporal_store(h[i], &ck_row[int64_t(i) * D]);
                 }
                 ck_row += ck_step;
             }
@@ -721,7 +728,7 @@ __global__ __launch_bounds__(scan_threads<HALF>())
                 }
                 if (g == 0) a.ws_dsum[c * BD + bd] = dsum;
             }
-        } else {
+        } else if constexpr (!CKPT) {
             float* dst = a.ws_agg + c * BD * N + sbase;
 #pragma unroll
             for (int i = 0; i < kNS; ++i) dst[i] = h[i];
@@ -1078,6 +1085,30 @@ hipError_t dispatch_scan(const ScanArgs& a, hipStream_t s)
     }
 }
 
+// The backward's checkpoint pass: the recurrence once over the whole sequence (one
+// chunk), from h0, keeping only the state entering every kBwdSub-th row in a.ckpt.
+// The half-wave scan kernel without its contraction and epilogue: the same states,
+// bit for bit, as the checkpoints a one-chunk ss_scan_fwd_ckpt writes.
+template <int DT, int MODE>
+hipError_t launch_ckpt_pass_t(const ScanArgs& a, hipStream_t s)
+{
+    constexpr int CH = ScanShape<true>::kCh;
+    const dim3 grid(unsigned((a.dim + CH - 1) / CH), unsigned(a.batch), 1u);
+    scan_kernel<DT, false, false, false, MODE, true, true><<<grid, dim3(scan_threads<true>()), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dispatch_ckpt_pass(const ScanArgs& a, hipStream_t s)
+{
+    switch (a.options & kOptAll) {
+        case 0: return launch_ckpt_pass_t<DT, 0>(a, s);
+        case kOptSoftplus: return launch_ckpt_pass_t<DT, kOptSoftplus>(a, s);
+        case kOptZoh: return launch_ckpt_pass_t<DT, kOptZoh>(a, s);
+        default: return launch_ckpt_pass_t<DT, kOptSoftplus | kOptZoh>(a, s);
+    }
+}
+
 template <int DT, int MODE>
 hipError_t dispatch_step_mode(const StepArgs& a, hipStream_t s)
 {
@@ -1115,6 +1146,12 @@ hipError_t launch_panel(const ScanArgs& a, int dtype, hipStream_t stream)
     else
         launch_panel_t<1>(a, stream);
     return hipGetLastError();
+}
+
+hipError_t launch_ckpt_pass(const ScanArgs& a, int dtype, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    return dtype == 0 ? dispatch_ckpt_pass<0>(a, stream) : dispatch_ckpt_pass<1>(a, stream);
 }
 
 hipError_t launch_step(const StepArgs& a, int dtype, hipStream_t stream)

@@ -20,6 +20,7 @@ namespace ssk {
 hipError_t launch_scan(const ScanArgs&, int, hipStream_t) { return stub_status(); }
 hipError_t launch_step(const StepArgs&, int, hipStream_t) { return stub_status(); }
 hipError_t launch_panel(const ScanArgs&, int, hipStream_t) { return stub_status(); }
+hipError_t launch_ckpt_pass(const ScanArgs&, int, hipStream_t) { return stub_status(); }
 hipError_t launch_bwd(const BwdArgs&, int, hipStream_t) { return stub_status(); }
 hipError_t launch_conv(const ConvArgs&, int, int, hipStream_t) { return stub_status(); }
 hipError_t launch_ssd(const SsdArgs&, hipStream_t) { return stub_status(); }
