@@ -524,6 +524,11 @@ __global__ __launch_bounds__(scan_threads<HALF>())
                 static_for<kNS>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
                     float in_term = xb * row_bcast<r * kNS + i>(bv[S]);  // delta*B*u (Euler)
+                    // Without the emit path the compiler would otherwise form half of the
+                    // broadcasts above the barrier, apart from their multiplies, as moves
+                    // of their own (32 more vector instructions per tile pair); held
+                    // here, each folds into its multiply
+                    if constexpr (!EMIT) __asm__ volatile("" : "+v"(in_term));
                     if constexpr (ZOH) in_term *= zoh_phi(x2[r][i], e[r][i], iA[i] * iv[r]);
                     h[i] = fmaf(e[r][i], h[i], in_term);
                     hh[r][i] = h[i];
