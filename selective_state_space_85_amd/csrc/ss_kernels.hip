@@ -492,12 +492,26 @@ __global__ __launch_bounds__(scan_threads<HALF>())
                              "v"(iv[7])
                              : "memory");
         issue_words(tile + 1, Slot<1 - S>{});
-        if constexpr (CORR != 0) {
-            // rows past the chunk end are published with delta = 0: no effect on either
+        // rows past the chunk end are published with delta = 0: no effect on the sum or
+        // the minimum
+        if constexpr (CORR == 2) {
+            // the correction: every lane checks the decay with the sum over its rows
 #pragma unroll
-            for (int r = 0; r < TT; ++r) {
-                dsum += xd[r].x;
-                dmin = fminf(dmin, xd[r].x);
+            for (int r = 0; r < TT; ++r) dsum += xd[r].x;
+        } else if constexpr (CORR == 1) {
+            // pass 1: only wave 0's sum and minimum are used (it stores the delta sums of
+            // the workgroup's channels, and its vote on a negative step size covers all of
+            // them), so the other waves skip them (long context 958 -> 920 us; the same in
+            // the aggregate pass of the short chunks made it slower, 43.7 -> 45.9 us: wave
+            // 0 then lags at every barrier).  A uniform branch: the empty asm keeps the
+            // compiler from computing this everywhere and selecting
+            if (w == 0) {
+                __asm__ volatile("" ::: "memory");
+#pragma unroll
+                for (int r = 0; r < TT; ++r) {
+                    dsum += xd[r].x;
+                    dmin = fminf(dmin, xd[r].x);
+                }
             }
         }
         // All delta*A products of the tile are formed before the first exp2 is
